@@ -1,0 +1,413 @@
+/*
+ * oracle.c -- plain, slow, scalar CPU oracle of the W8A8 INT8 fused-MoE layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no code with
+ * the HIP path: no kernels, headers, helpers or tables.
+ *
+ * Sources (the pages):
+ *  - SGLang PR #3888 "[Feature] DeepSeek V3/R1 INT8 Quantization
+ *    (channel-wise)", Modifications and Performance sections: the fused MoE
+ *    kernel with channel-wise int8 weights and an int32 accumulator.
+ *  - jiqizhixin, Meituan INT8 DeepSeek R1 article, section "Quantization
+ *    exploration": block-wise quantization in [128,128] weight tiles with
+ *    activations quantized online per token-group; channel-wise quantization
+ *    with one weight group per output channel, activations quantized online
+ *    per token, and a single dequantization after the INT8 matmul.
+ *  - SGLang PR #8273 "support cutlass_moe_fp8 for deepepmoe", review on
+ *    m_indices: expert offsets are the zero-padded cumulative sum of the
+ *    per-expert token counts; the scatter emits the expert id of every row.
+ *    Its highlights: MoE = scatter inputs, GEMM (w13), activation, GEMM (w2),
+ *    gather outputs.
+ * Where the pages are silent, the plainest reading is taken:
+ *  - symmetric int8 in [-127, 127]; scale = max(max|x| / 127, 1e-8);
+ *    q = round-half-even(x / scale) with an IEEE division;
+ *  - w13 rows [0, I) are the gate, rows [I, 2I) the up projection;
+ *    activation SiLU(gate) * up with silu(g) = g / (1 + exp(-g));
+ *  - dequantization order ((float)acc * a_scale) * w_scale;
+ *  - the intermediate is requantized per (token, expert) row (channel-wise) or
+ *    per (row, 128-group) (block-wise), by the same rule as the activations;
+ *  - combine: out = 0, then out = out + w_j * y_j for slots j = 0..k-1, fp32;
+ *  - routing (the pages only name topk_idx): softmax top-k renormalised, or
+ *    sigmoid scores with node-limited grouped selection (group score = sum of
+ *    the group's two best scores), as in the DeepSeek-V3 technical report the
+ *    article cites; ties go to the lower index everywhere.
+ * Build: -O2 -fno-fast-math -ffp-contract=off, so every fp32 operation below
+ * is one IEEE operation in the written order.  Outer loops run under OpenMP.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_EXPORT __attribute__((visibility("default")))
+
+/* ------------------------------------------------------------------ quantization */
+
+/* Symmetric INT8 quantization with one scale per br x bc block of a row-major
+ * [rows, cols] fp32 matrix.  br=1, bc=cols: one scale per row (per-token
+ * activations; per-output-channel weights, whose rows are output channels).
+ * br=1, bc=128: per-token-group activations.  br=bc=128: block-wise weights.
+ * Scale grid is [ceil(rows/br), ceil(cols/bc)], row-major. */
+ORACLE_EXPORT void oracle_quant_blocks(const float* x, int64_t rows, int64_t cols, int64_t br,
+                                       int64_t bc, int8_t* q, float* s) {
+  const int64_t nbr = (rows + br - 1) / br, nbc = (cols + bc - 1) / bc;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t b = 0; b < nbr * nbc; ++b) {
+    const int64_t bi = b / nbc, bj = b % nbc;
+    const int64_t r0 = bi * br, r1 = (r0 + br < rows) ? r0 + br : rows;
+    const int64_t c0 = bj * bc, c1 = (c0 + bc < cols) ? c0 + bc : cols;
+    float amax = 0.0f;
+    for (int64_t r = r0; r < r1; ++r)
+      for (int64_t c = c0; c < c1; ++c) {
+        float a = fabsf(x[r * cols + c]);
+        if (a > amax) amax = a;
+      }
+    float sc = amax / 127.0f;
+    if (sc < 1e-8f) sc = 1e-8f;
+    s[b] = sc;
+    for (int64_t r = r0; r < r1; ++r)
+      for (int64_t c = c0; c < c1; ++c) {
+        float v = nearbyintf(x[r * cols + c] / sc);
+        if (v > 127.0f) v = 127.0f;
+        if (v < -127.0f) v = -127.0f;
+        q[r * cols + c] = (int8_t)v;
+      }
+  }
+}
+
+/* ------------------------------------------------------------------ routing */
+
+/* a beats b: larger value first, equal values to the lower index. */
+static int beats(float va, int64_t a, float vb, int64_t b) { return va > vb || (va == vb && a < b); }
+
+/* Index of the best candidate (cand[i] != 0) of v[0..n), -1 if none. */
+static int64_t best_of(const float* v, const unsigned char* cand, int64_t n) {
+  int64_t best = -1;
+  for (int64_t i = 0; i < n; ++i)
+    if (cand[i] && (best < 0 || beats(v[i], i, v[best], best))) best = i;
+  return best;
+}
+
+/* score_fn 0 = softmax, 1 = sigmoid.  n_group = 1 means ungrouped.
+ * softmax: select the k largest logits.  renormalize: w_j = exp(l_j - m) / sum
+ *   over the selected (m = largest selected), i.e. softmax over the selection;
+ *   otherwise w_j = exp(l_j - m) / (sum over all E in index order).
+ * sigmoid: s = 1/(1+exp(-l)), c = s + bias; group score = best + second best c
+ *   of the group; keep the topk_group best groups; select the k best c among
+ *   the kept groups' experts; w_j = s_j (/ sum of selected s if renormalize).
+ * Finally w_j = w_j * routed_scaling.  Slots are in selection order. */
+ORACLE_EXPORT void oracle_route(const float* logits, int64_t T, int64_t E, int64_t k, int32_t score_fn,
+                                int64_t n_group, int64_t topk_group, int32_t renormalize,
+                                float routed_scaling, const float* bias, int32_t* ids, float* w) {
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int64_t t = 0; t < T; ++t) {
+    const float* l = logits + t * E;
+    float* s = (float*)malloc(sizeof(float) * E);
+    float* c = (float*)malloc(sizeof(float) * E);
+    unsigned char* cand = (unsigned char*)malloc(E);
+    int32_t* sel = ids + t * k;
+    float* wt = w + t * k;
+    if (score_fn == 0) {
+      for (int64_t e = 0; e < E; ++e) cand[e] = 1;
+      for (int64_t j = 0; j < k; ++j) {
+        int64_t b = best_of(l, cand, E);
+        sel[j] = (int32_t)b;
+        cand[b] = 0;
+      }
+      const float m = l[sel[0]];
+      float sum = 0.0f;
+      if (renormalize) {
+        for (int64_t j = 0; j < k; ++j) sum = sum + expf(l[sel[j]] - m);
+      } else {
+        for (int64_t e = 0; e < E; ++e) sum = sum + expf(l[e] - m);
+      }
+      for (int64_t j = 0; j < k; ++j) wt[j] = (expf(l[sel[j]] - m) / sum) * routed_scaling;
+    } else {
+      for (int64_t e = 0; e < E; ++e) {
+        s[e] = 1.0f / (1.0f + expf(-l[e]));
+        c[e] = bias ? s[e] + bias[e] : s[e];
+      }
+      if (n_group > 1) {
+        const int64_t gs = E / n_group;
+        float* gscore = (float*)malloc(sizeof(float) * n_group);
+        unsigned char* gcand = (unsigned char*)malloc(n_group);
+        for (int64_t g = 0; g < n_group; ++g) {
+          /* the group's best and second-best c */
+          for (int64_t e = 0; e < gs; ++e) cand[e] = 1;
+          int64_t b1 = best_of(c + g * gs, cand, gs);
+          if (gs >= 2) {
+            cand[b1] = 0;
+            int64_t b2 = best_of(c + g * gs, cand, gs);
+            gscore[g] = c[g * gs + b1] + c[g * gs + b2];
+          } else {
+            gscore[g] = c[g * gs + b1];
+          }
+          gcand[g] = 1;
+        }
+        for (int64_t e = 0; e < E; ++e) cand[e] = 0;
+        for (int64_t j = 0; j < topk_group; ++j) {
+          int64_t g = best_of(gscore, gcand, n_group);
+          gcand[g] = 0;
+          for (int64_t e = g * gs; e < (g + 1) * gs; ++e) cand[e] = 1;
+        }
+        free(gscore);
+        free(gcand);
+      } else {
+        for (int64_t e = 0; e < E; ++e) cand[e] = 1;
+      }
+      for (int64_t j = 0; j < k; ++j) {
+        int64_t b = best_of(c, cand, E);
+        sel[j] = (int32_t)b;
+        cand[b] = 0;
+      }
+      float sum = 0.0f;
+      for (int64_t j = 0; j < k; ++j) sum = sum + s[sel[j]];
+      for (int64_t j = 0; j < k; ++j) {
+        float v = renormalize ? s[sel[j]] / sum : s[sel[j]];
+        wt[j] = v * routed_scaling;
+      }
+    }
+    free(s);
+    free(c);
+    free(cand);
+  }
+}
+
+/* ------------------------------------------------------------------ align */
+
+/* Stable grouping of the P = T*k (token, slot) pairs by expert (pair id
+ * p = t*k + j).  counts[e]; offsets = [0, cumsum(counts)] (E+1 entries);
+ * each expert's segment is padded to a multiple of block_m with the sentinel
+ * P; padded_offsets = [0, cumsum(padded counts)]; tile_expert[i] = expert of
+ * tile i; num_tiles = padded_offsets[E] / block_m.  Pair ids ascend within an
+ * expert. */
+ORACLE_EXPORT void oracle_align(const int32_t* ids, int64_t T, int64_t k, int64_t E, int64_t block_m,
+                                int32_t* counts, int32_t* offsets, int32_t* padded_offsets,
+                                int32_t* sorted_pair_ids, int32_t* tile_expert, int32_t* num_tiles) {
+  const int64_t P = T * k;
+  for (int64_t e = 0; e < E; ++e) counts[e] = 0;
+  for (int64_t p = 0; p < P; ++p) counts[ids[p]] += 1;
+  offsets[0] = 0;
+  padded_offsets[0] = 0;
+  for (int64_t e = 0; e < E; ++e) {
+    offsets[e + 1] = offsets[e] + counts[e];
+    int64_t pc = (counts[e] + block_m - 1) / block_m * block_m;
+    padded_offsets[e + 1] = padded_offsets[e] + (int32_t)pc;
+  }
+  int64_t* fill = (int64_t*)malloc(sizeof(int64_t) * (E > 0 ? E : 1));
+  for (int64_t e = 0; e < E; ++e) fill[e] = padded_offsets[e];
+  for (int64_t p = 0; p < P; ++p) sorted_pair_ids[fill[ids[p]]++] = (int32_t)p;
+  for (int64_t e = 0; e < E; ++e)
+    for (int64_t r = fill[e]; r < padded_offsets[e + 1]; ++r) sorted_pair_ids[r] = (int32_t)P;
+  free(fill);
+  for (int64_t e = 0; e < E; ++e)
+    for (int64_t i = padded_offsets[e] / block_m; i < padded_offsets[e + 1] / block_m; ++i)
+      tile_expert[i] = (int32_t)e;
+  *num_tiles = (int32_t)(padded_offsets[E] / block_m);
+}
+
+/* ------------------------------------------------------------------ GEMM pieces */
+
+/* Exact int8 x int8 dot product with int32 accumulation (|sum| <= K*127*127 < 2^31). */
+static int32_t dot_i8(const int8_t* a, const int8_t* b, int64_t K) {
+  int32_t acc = 0;
+  for (int64_t i = 0; i < K; ++i) acc += (int32_t)a[i] * (int32_t)b[i];
+  return acc;
+}
+
+static float silu_mul(float g, float u) { return (g / (1.0f + expf(-g))) * u; }
+
+/* Requantize one row of fp32 values by the activation rule, per group of `group`
+ * columns (group = n for a single scale). */
+static void requant_row(const float* hf, int64_t n, int64_t group, int8_t* q, float* s) {
+  for (int64_t g0 = 0, gi = 0; g0 < n; g0 += group, ++gi) {
+    float amax = 0.0f;
+    for (int64_t i = g0; i < g0 + group; ++i) {
+      float a = fabsf(hf[i]);
+      if (a > amax) amax = a;
+    }
+    float sc = amax / 127.0f;
+    if (sc < 1e-8f) sc = 1e-8f;
+    s[gi] = sc;
+    for (int64_t i = g0; i < g0 + group; ++i) {
+      float v = nearbyintf(hf[i] / sc);
+      if (v > 127.0f) v = 127.0f;
+      if (v < -127.0f) v = -127.0f;
+      q[i] = (int8_t)v;
+    }
+  }
+}
+
+/* One expert row of the first GEMM + activation + requantization.
+ * a: the token's int8 activations [H]; channel mode: a_s points at the token's
+ * scale, w_s at the expert's [2I] channel scales; block mode: a_s -> [H/128],
+ * w_s -> [2I/128, H/128].  Writes h_q [I] and h_s ([1] or [I/128]). */
+static void w13_row(const int8_t* a, const float* a_s, const int8_t* w13, const float* w_s, int64_t H,
+                    int64_t I, int32_t block, float* hf, int8_t* h_q, float* h_s) {
+  for (int64_t n = 0; n < I; ++n) {
+    float g, u;
+    if (!block) {
+      int32_t ag = dot_i8(a, w13 + n * H, H);
+      int32_t au = dot_i8(a, w13 + (n + I) * H, H);
+      g = ((float)ag * a_s[0]) * w_s[n];
+      u = ((float)au * a_s[0]) * w_s[n + I];
+    } else {
+      const int64_t nkb = H / 128;
+      g = 0.0f;
+      u = 0.0f;
+      for (int64_t kb = 0; kb < nkb; ++kb) {
+        int32_t pg = dot_i8(a + kb * 128, w13 + n * H + kb * 128, 128);
+        int32_t pu = dot_i8(a + kb * 128, w13 + (n + I) * H + kb * 128, 128);
+        g = g + (((float)pg * a_s[kb]) * w_s[(n / 128) * nkb + kb]);
+        u = u + (((float)pu * a_s[kb]) * w_s[((n + I) / 128) * nkb + kb]);
+      }
+    }
+    hf[n] = silu_mul(g, u);
+  }
+  requant_row(hf, I, block ? 128 : I, h_q, h_s);
+}
+
+/* One expert row of the second GEMM, dequantized: y [H]. */
+static void w2_row(const int8_t* hq, const float* h_s, const int8_t* w2, const float* w_s, int64_t H,
+                   int64_t I, int32_t block, float* y) {
+  for (int64_t n = 0; n < H; ++n) {
+    if (!block) {
+      int32_t acc = dot_i8(hq, w2 + n * I, I);
+      y[n] = ((float)acc * h_s[0]) * w_s[n];
+    } else {
+      const int64_t nkb = I / 128;
+      float acc_f = 0.0f;
+      for (int64_t kb = 0; kb < nkb; ++kb) {
+        int32_t part = dot_i8(hq + kb * 128, w2 + n * I + kb * 128, 128);
+        acc_f = acc_f + (((float)part * h_s[kb]) * w_s[(n / 128) * nkb + kb]);
+      }
+      y[n] = acc_f;
+    }
+  }
+}
+
+/* ------------------------------------------------------------------ grouped (sorted-row) stages
+ *
+ * Experts' weights are passed as arrays of per-expert pointers (NULL for
+ * experts that are not needed), so full-size checks can materialise only the
+ * experts they touch.  Rows are the padded expert-sorted rows of the align
+ * step; `rows` / `nrows` select which rows to compute (NULL = all rows below
+ * num_tiles * block_m).  Pad rows (sentinel P) are skipped. */
+
+static int64_t row_at(const int64_t* rows, int64_t i) { return rows ? rows[i] : i; }
+
+/* Raw int32 accumulators.  gather = 1: A row of sorted row r is a[sorted[r] / k]
+ * (first GEMM on the token activations); gather = 0: A row is a[r] (second GEMM
+ * on the sorted intermediate).  out [*, N] int32 indexed by sorted row. */
+ORACLE_EXPORT void oracle_grouped_gemm_i32(const int8_t* a, int64_t K, int32_t gather,
+                                           const int8_t* const* w, int64_t N,
+                                           const int32_t* sorted_pair_ids, const int32_t* tile_expert,
+                                           int64_t block_m, int64_t P, int64_t k, const int64_t* rows,
+                                           int64_t nrows, int32_t* out) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t i = 0; i < nrows; ++i) {
+    const int64_t r = row_at(rows, i);
+    const int64_t p = sorted_pair_ids[r];
+    if (p >= P) continue;
+    const int8_t* arow = gather ? a + (p / k) * K : a + r * K;
+    const int8_t* we = w[tile_expert[r / block_m]];
+    for (int64_t n = 0; n < N; ++n) out[r * N + n] = dot_i8(arow, we + n * K, K);
+  }
+}
+
+/* First GEMM + SiLU(gate)*up + requantization over sorted rows.
+ * channel: a_s [T], w13_s[e] -> [2I], h_s [rows]; block: a_s [T, H/128],
+ * w13_s[e] -> [2I/128, H/128], h_s [rows, I/128]. */
+ORACLE_EXPORT void oracle_w13_silu(const int8_t* a_q, const float* a_s, const int8_t* const* w13,
+                                   const float* const* w13_s, const int32_t* sorted_pair_ids,
+                                   const int32_t* tile_expert, int64_t block_m, int64_t T, int64_t k,
+                                   int64_t H, int64_t I, int32_t block, const int64_t* rows, int64_t nrows,
+                                   int8_t* h_q, float* h_s) {
+  const int64_t P = T * k;
+  const int64_t nsa = block ? H / 128 : 1, nsh = block ? I / 128 : 1;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t i = 0; i < nrows; ++i) {
+    const int64_t r = row_at(rows, i);
+    const int64_t p = sorted_pair_ids[r];
+    if (p >= P) continue;
+    const int64_t t = p / k, e = tile_expert[r / block_m];
+    float* hf = (float*)malloc(sizeof(float) * I);
+    w13_row(a_q + t * H, a_s + t * nsa, w13[e], w13_s[e], H, I, block, hf, h_q + r * I, h_s + r * nsh);
+    free(hf);
+  }
+}
+
+/* Second GEMM + top-k weighted combine: out [T, H] fp32, fully overwritten.
+ * pair_row is built here from sorted_pair_ids (the inverse map). */
+ORACLE_EXPORT void oracle_w2_combine(const int8_t* h_q, const float* h_s, const int8_t* const* w2,
+                                     const float* const* w2_s, const int32_t* sorted_pair_ids,
+                                     const int32_t* tile_expert, int32_t num_tiles, int64_t block_m,
+                                     const float* topk_weights, int64_t T, int64_t k, int64_t H, int64_t I,
+                                     int32_t block, float* out) {
+  const int64_t P = T * k, R = (int64_t)num_tiles * block_m;
+  const int64_t nsh = block ? I / 128 : 1;
+  int64_t* pair_row = (int64_t*)malloc(sizeof(int64_t) * (P > 0 ? P : 1));
+  for (int64_t p = 0; p < P; ++p) pair_row[p] = -1;
+  for (int64_t r = 0; r < R; ++r)
+    if (sorted_pair_ids[r] < P) pair_row[sorted_pair_ids[r]] = r;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t t = 0; t < T; ++t) {
+    float* y = (float*)malloc(sizeof(float) * H);
+    float* o = out + t * H;
+    for (int64_t n = 0; n < H; ++n) o[n] = 0.0f;
+    for (int64_t j = 0; j < k; ++j) {
+      const int64_t r = pair_row[t * k + j];
+      if (r < 0) continue;
+      const int64_t e = tile_expert[r / block_m];
+      w2_row(h_q + r * I, h_s + r * nsh, w2[e], w2_s[e], H, I, block, y);
+      const float wj = topk_weights[t * k + j];
+      for (int64_t n = 0; n < H; ++n) o[n] = o[n] + (wj * y[n]);
+    }
+    free(y);
+  }
+  free(pair_row);
+}
+
+/* ------------------------------------------------------------------ dense per-token reference
+ *
+ * The whole layer for a list of tokens, computed straight from the routing
+ * with no sorting: for token t, quantize its activations, then for each slot
+ * j run the expert MLP on the int8 row and accumulate out = out + w_j * y_j.
+ * x: fp32 activations of the listed tokens [ntok, H] (bf16 inputs widened
+ * exactly by the caller); ids/weights [ntok, k]; out [ntok, H].  The
+ * operations and their order are those of the sorted pipeline, so the two
+ * results must agree bit for bit. */
+ORACLE_EXPORT void oracle_moe_tokens(const float* x, int64_t ntok, int64_t H, int64_t I, int64_t k,
+                                     const int32_t* ids, const float* topk_weights,
+                                     const int8_t* const* w13, const float* const* w13_s,
+                                     const int8_t* const* w2, const float* const* w2_s, int32_t block,
+                                     float* out) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t t = 0; t < ntok; ++t) {
+    const int64_t nsa = block ? H / 128 : 1, nsh = block ? I / 128 : 1;
+    int8_t* aq = (int8_t*)malloc(H);
+    float* as = (float*)malloc(sizeof(float) * nsa);
+    float* hf = (float*)malloc(sizeof(float) * I);
+    int8_t* hq = (int8_t*)malloc(I);
+    float* hs = (float*)malloc(sizeof(float) * nsh);
+    float* y = (float*)malloc(sizeof(float) * H);
+    /* online activation quantization: one scale per token or per 128-group */
+    requant_row(x + t * H, H, block ? 128 : H, aq, as);
+    float* o = out + t * H;
+    for (int64_t n = 0; n < H; ++n) o[n] = 0.0f;
+    for (int64_t j = 0; j < k; ++j) {
+      const int64_t e = ids[t * k + j];
+      w13_row(aq, as, w13[e], w13_s[e], H, I, block, hf, hq, hs);
+      w2_row(hq, hs, w2[e], w2_s[e], H, I, block, y);
+      const float wj = topk_weights[t * k + j];
+      for (int64_t n = 0; n < H; ++n) o[n] = o[n] + (wj * y[n]);
+    }
+    free(aq);
+    free(as);
+    free(hf);
+    free(hq);
+    free(hs);
+    free(y);
+  }
+}
