@@ -1,0 +1,256 @@
+"""Benchmark of the W8A8 INT8 fused-MoE layer on one MI355X.
+
+One step = one pass of the whole layer over one batch of synthetic input:
+top-k routing, per-token activation quantization, align by expert, the grouped
+INT8 gate+up GEMM with SiLU and requantization, the grouped INT8 down GEMM with
+the top-k weighted combine.  Inputs (activations, gate logits, int8 expert
+weights and scales) are resident in HBM before timing starts.
+
+Prints one JSON line.  value = tokens/s of the DeepSeek-V3 decode layer
+(T=128, hidden 7168, intermediate 2048, 256 experts, top-8); the same line
+carries the T=8192 prefill layer's figures under "prefill", the roofline of the
+dominant kernel (the gate+up GEMM, weight-streaming and so HBM-bound at T=128)
+and the CPU oracle timed on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s + int8 TOPS at T=128/8192; % of INT8 MFMA or HBM peak"
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
+INT8_PEAK_TOPS = 5000.0    # MI355X dense INT8 MFMA
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="decode")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the T=8192 prefill figures")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=16, help="tokens in the CPU oracle sample")
+    return ap.parse_args()
+
+
+class Stages:
+    """Device buffers and the stage-by-stage calls of one layer pass (all on torch's current stream)."""
+
+    def __init__(self, layer, block_m=0):
+        import torch
+
+        import w8a8_int8_quantized_quant_amd as w8
+
+        self.w8 = w8
+        self.L = layer
+        c = layer.cfg
+        T = layer.x.shape[0]
+        self.T = T
+        self.block = c.scale_mode == "block"
+        self.bm = block_m or w8.w8a8_moe_pick_block_m(T, c.k, c.E)
+        dev = layer.x.device
+        R = w8.w8a8_moe_max_rows(T, c.k, c.E, self.bm)
+        i32, f32 = torch.int32, torch.float32
+        self.ids = torch.empty((T, c.k), dtype=i32, device=dev)
+        self.tw = torch.empty((T, c.k), dtype=f32, device=dev)
+        self.a_q = torch.empty((T, c.H), dtype=torch.int8, device=dev)
+        self.a_s = torch.empty((T, c.H // 128) if self.block else (T,), dtype=f32, device=dev)
+        self.counts = torch.empty(c.E, dtype=i32, device=dev)
+        self.offsets = torch.empty(c.E + 1, dtype=i32, device=dev)
+        self.padded = torch.empty(c.E + 1, dtype=i32, device=dev)
+        self.sorted = torch.empty(max(R, 1), dtype=i32, device=dev)
+        self.tile_expert = torch.empty(max(R // self.bm, 1), dtype=i32, device=dev)
+        self.num_tiles = torch.empty(1, dtype=i32, device=dev)
+        self.h_q = torch.empty((max(R, 1), c.I), dtype=torch.int8, device=dev)
+        self.h_s = torch.empty((max(R, 1), c.I // 128) if self.block else (max(R, 1),), dtype=f32, device=dev)
+        self.out = torch.empty((T, c.H), dtype=f32, device=dev)
+        mode = w8.SCALE_BLOCK128 if self.block else w8.SCALE_CHANNEL
+        self.ws_align = torch.empty(max(w8.moe_align_workspace_bytes(T, c.k, c.E), 256), dtype=torch.uint8, device=dev)
+        gws = max(w8.w8a8_w13_workspace_bytes(T, c.k, c.E, c.H, c.I, self.bm, mode),
+                  w8.w8a8_w2_workspace_bytes(T, c.k, c.E, c.H, c.I, self.bm, mode))
+        self.ws_gemm = torch.empty(gws, dtype=torch.uint8, device=dev)
+
+    def route(self):
+        c = self.L.cfg
+        self.w8.moe_topk_route(self.L.logits, c.k, self.L.score_fn, c.n_group, c.topk_group, c.renormalize,
+                               c.routed_scaling, None, self.ids, self.tw)
+
+    def quant(self):
+        self.w8.w8a8_quant_per_token(self.L.x, 128 if self.block else 0, self.a_q, self.a_s)
+
+    def align(self):
+        self.w8.moe_align_by_expert(self.ids, self.L.cfg.E, self.bm, self.counts, self.offsets, self.padded,
+                                    self.sorted, self.tile_expert, self.num_tiles, self.ws_align)
+
+    def w13(self):
+        fn = self.w8.w8a8_block_grouped_gemm_w13_silu if self.block else self.w8.w8a8_grouped_gemm_w13_silu
+        fn(self.a_q, self.a_s, self.L.w13, self.L.w13_scale, self.sorted, self.padded, self.tile_expert,
+           self.num_tiles, self.T, self.L.cfg.k, self.bm, self.h_q, self.h_s, self.ws_gemm)
+
+    def w2(self):
+        fn = self.w8.w8a8_block_grouped_gemm_w2_combine if self.block else self.w8.w8a8_grouped_gemm_w2_combine
+        fn(self.h_q, self.h_s, self.L.w2, self.L.w2_scale, self.sorted, self.padded, self.tile_expert,
+           self.num_tiles, self.tw, self.T, self.L.cfg.k, self.bm, self.out, self.ws_gemm)
+
+    NAMES = ("route", "quant", "align", "w13", "w2")
+
+    def step(self, events=None):
+        for i, name in enumerate(self.NAMES):
+            if events is not None:
+                events[i].record()
+            getattr(self, name)()
+        if events is not None:
+            events[len(self.NAMES)].record()
+
+
+def measure(layer, steps, warmup):
+    """Whole-step wall time (synchronised on both sides) and per-stage event times."""
+    import torch
+
+    st = Stages(layer)
+    for _ in range(warmup):
+        st.step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(Stages.NAMES) + 1)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        st.step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    stage_ms = {name: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps for j, name in enumerate(Stages.NAMES)}
+    counts = st.counts.cpu().numpy()
+    return (t1 - t0) * 1000.0 / steps, stage_ms, st, counts
+
+
+def layer_figures(cfg, T, ms, counts):
+    P = T * cfg.k
+    ops = 2.0 * P * (2 * cfg.I * cfg.H + cfg.H * cfg.I)
+    active = int((counts > 0).sum())
+    nsh = cfg.I // 128 if cfg.scale_mode == "block" else 1
+    nsw13 = (2 * cfg.I // 128) * (cfg.H // 128) if cfg.scale_mode == "block" else 2 * cfg.I
+    nsw2 = (cfg.H // 128) * (cfg.I // 128) if cfg.scale_mode == "block" else cfg.H
+    nsa = cfg.H // 128 if cfg.scale_mode == "block" else 1
+    w_bytes = active * (2 * cfg.I * cfg.H + cfg.H * cfg.I + 4 * (nsw13 + nsw2))
+    x_bytes = T * cfg.H * (2 if cfg.x_dtype else 4)
+    other = (T * cfg.E * 4 + x_bytes + 2 * (T * cfg.H + 4 * T * nsa) + 2 * (P * cfg.I + 4 * P * nsh)
+             + T * cfg.H * 4 + P * 8)
+    total_bytes = w_bytes + other
+    return dict(tokens_per_s=T / (ms / 1000.0), ms_per_step=ms, int8_tops=ops / (ms / 1000.0) / 1e12,
+                frac_int8_peak=ops / (ms / 1000.0) / 1e12 / INT8_PEAK_TOPS, hbm_gbs=total_bytes / (ms / 1000.0) / 1e9,
+                frac_hbm_peak=total_bytes / (ms / 1000.0) / 1e9 / HBM_PEAK_GBS, active_experts=active,
+                algorithmic_bytes=total_bytes, algorithmic_ops=ops)
+
+
+def w13_algorithmic_bytes(cfg, T, counts):
+    """Bytes the gate+up GEMM stage must move: int8 weights and scales of the active experts,
+    the int8 token rows and their scales, and the int8 intermediate with its scales."""
+    P = T * cfg.k
+    active = int((counts > 0).sum())
+    nsw = (2 * cfg.I // 128) * (cfg.H // 128) if cfg.scale_mode == "block" else 2 * cfg.I
+    nsa = cfg.H // 128 if cfg.scale_mode == "block" else 1
+    nsh = cfg.I // 128 if cfg.scale_mode == "block" else 1
+    return active * (2 * cfg.I * cfg.H + 4 * nsw) + T * (cfg.H + 4 * nsa) + P * (cfg.I + 4 * nsh)
+
+
+def cpu_baseline(cfg, ntok):
+    """The CPU oracle, unchanged, on the first `ntok` tokens of the workload: routing from
+    the logits, then the dense per-token layer.  Oracle-side expert weights are drawn by the
+    shared generator's device fill (bit-identical to its host fill) and quantized by the
+    oracle before the clock starts."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import synth
+
+    lg = synth.logits(cfg, slice(0, ntok))
+    x = oracle.activations_f32(cfg, slice(0, ntok))
+    ids, _ = oracle.route_cfg(cfg, lg)
+    experts = np.unique(ids)
+    w13q, w13s, w2q, w2s = [None] * cfg.E, [None] * cfg.E, [None] * cfg.E, [None] * cfg.E
+    hs = torch.cuda.current_stream().cuda_stream
+    buf = torch.empty(2 * cfg.I * cfg.H, dtype=torch.float32, device="cuda")
+    for e in experts:
+        n13, n2 = 2 * cfg.I * cfg.H, cfg.H * cfg.I
+        synth.dev_normal(buf.data_ptr(), n13, cfg.seed, synth.STREAM_W13, int(e) * n13, cfg.w_sigma, hs)
+        w13q[e], w13s[e] = oracle.quant_weight(buf[:n13].cpu().numpy().reshape(2 * cfg.I, cfg.H), cfg.scale_mode)
+        synth.dev_normal(buf.data_ptr(), n2, cfg.seed, synth.STREAM_W2, int(e) * n2, cfg.w_sigma, hs)
+        w2q[e], w2s[e] = oracle.quant_weight(buf[:n2].cpu().numpy().reshape(cfg.H, cfg.I), cfg.scale_mode)
+    del buf
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    t0 = time.perf_counter()
+    ids, tw = oracle.route_cfg(cfg, lg)
+    oracle.moe_tokens(x, ids, tw, w13q, w13s, w2q, w2s, I=cfg.I, block=cfg.scale_mode == "block")
+    dt = time.perf_counter() - t0
+    return {"value": ntok / dt, "unit": "tokens/s", "cores": min(threads, ntok), "kind": "oracle",
+            "sample": f"first {ntok} of the {cfg.T} tokens of the same layer (routing + dense per-token "
+                      f"quantized MoE, OpenMP over tokens), {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the layer runs unsharded on a "
+              f"single MI355X.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import synth
+    from w8a8_int8_quantized_quant_amd import workload
+
+    cfg = synth.CONFIGS[args.config]
+    print(f"[bench] drawing {cfg.note}", file=sys.stderr, flush=True)
+    layer = workload.make_layer(cfg)
+    ms, stage_ms, st, counts = measure(layer, args.steps, args.warmup)
+    fig = layer_figures(cfg, cfg.T, ms, counts)
+    print(f"[bench] {cfg.name}: {ms:.3f} ms/step, stages {stage_ms}", file=sys.stderr, flush=True)
+    w13_bytes = w13_algorithmic_bytes(cfg, cfg.T, counts)
+    achieved = w13_bytes / (stage_ms["w13"] / 1000.0) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "gate+up grouped GEMM stage (w8a8_grouped_gemm_w13_silu)",
+                "kernel_ms": round(stage_ms["w13"], 4), "algorithmic_bytes": w13_bytes}
+    del st, layer
+    torch.cuda.empty_cache()
+
+    prefill = None
+    if not args.no_prefill and args.config == "decode":
+        pc = synth.CONFIGS["prefill"]
+        print(f"[bench] drawing {pc.note}", file=sys.stderr, flush=True)
+        pl = workload.make_layer(pc)
+        pms, pstage, pst, pcounts = measure(pl, max(3, args.steps // 4), args.warmup)
+        pf = layer_figures(pc, pc.T, pms, pcounts)
+        print(f"[bench] prefill: {pms:.3f} ms/step, stages {pstage}", file=sys.stderr, flush=True)
+        prefill = {"T": pc.T, "ms_per_step": round(pms, 4), "tokens_per_s": round(pf["tokens_per_s"], 1),
+                   "int8_tops": round(pf["int8_tops"], 2), "frac_int8_peak": round(pf["frac_int8_peak"], 4),
+                   "hbm_gbs": round(pf["hbm_gbs"], 1), "stage_ms": {k: round(v, 4) for k, v in pstage.items()}}
+        del pst, pl
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print(f"[bench] CPU oracle baseline on {args.cpu_tokens} tokens", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(cfg, args.cpu_tokens)
+
+    line = {
+        "metric": METRIC, "value": round(fig["tokens_per_s"], 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+        "config": {"workload": f"{cfg.note}: hidden {cfg.H}, intermediate {cfg.I}, {cfg.E} experts, top-{cfg.k}, "
+                               f"{cfg.scale_mode}-wise W8A8 INT8", "T": cfg.T, "H": cfg.H, "I": cfg.I, "E": cfg.E,
+                   "k": cfg.k, "scale": cfg.scale_mode, "active_experts": fig["active_experts"]},
+        "int8_tops": round(fig["int8_tops"], 3), "frac_int8_peak": round(fig["frac_int8_peak"], 4),
+        "hbm_gbs": round(fig["hbm_gbs"], 1), "frac_hbm_peak": round(fig["frac_hbm_peak"], 4),
+        "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "roofline": roofline, "prefill": prefill, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -41,7 +41,7 @@ def _load():
         lib.oracle_w13_silu.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp, i64,
                                         vp, vp]
         lib.oracle_w2_combine.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, vp, i64, i64, i64, i64, i32,
-                                          vp]
+                                          vp, i64, vp]
         lib.oracle_moe_tokens.argtypes = [vp, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, i32, vp]
         for name in ("oracle_quant_blocks", "oracle_route", "oracle_align", "oracle_grouped_gemm_i32",
                      "oracle_w13_silu", "oracle_w2_combine", "oracle_moe_tokens"):
@@ -193,16 +193,20 @@ def w13_silu(a_q: np.ndarray, a_s: np.ndarray, w13, w13_s, al: Dict[str, np.ndar
 
 
 def w2_combine(h_q: np.ndarray, h_s: np.ndarray, w2, w2_s, al: Dict[str, np.ndarray], block_m: int,
-               topk_weights: np.ndarray, T: int, k: int, H: int, I: int, block: bool) -> np.ndarray:
+               topk_weights: np.ndarray, T: int, k: int, H: int, I: int, block: bool,
+               tokens: Optional[Iterable[int]] = None) -> np.ndarray:
+    """Combined output rows: [T, H], or [len(tokens), H] for the listed tokens."""
     h_q = _c(h_q, np.int8)
     h_s = _c(h_s, np.float32)
     wq = _experts(w2, np.int8)
     wsc = _experts(w2_s, np.float32)
     tw = _c(topk_weights, np.float32)
-    out = np.empty((T, H), dtype=np.float32)
+    tk = None if tokens is None else np.ascontiguousarray(np.fromiter(tokens, dtype=np.int64))
+    ntok = T if tk is None else len(tk)
+    out = np.empty((ntok, H), dtype=np.float32)
     _load().oracle_w2_combine(_p(h_q), _p(h_s), _ptr_array(wq), _ptr_array(wsc), _p(al["sorted_pair_ids"]),
                               _p(al["tile_expert"]), int(al["num_tiles"][0]), block_m, _p(tw), T, k, H, I,
-                              int(block), _p(out))
+                              int(block), _p(tk), ntok, _p(out))
     return out
 
 

@@ -338,13 +338,14 @@ ORACLE_EXPORT void oracle_w13_silu(const int8_t* a_q, const float* a_s, const in
   }
 }
 
-/* Second GEMM + top-k weighted combine: out [T, H] fp32, fully overwritten.
- * pair_row is built here from sorted_pair_ids (the inverse map). */
+/* Second GEMM + top-k weighted combine.  out has one fp32 row of H per listed
+ * token (tokens = NULL: all T tokens in order), fully overwritten.  pair_row is
+ * built here from sorted_pair_ids (the inverse map). */
 ORACLE_EXPORT void oracle_w2_combine(const int8_t* h_q, const float* h_s, const int8_t* const* w2,
                                      const float* const* w2_s, const int32_t* sorted_pair_ids,
                                      const int32_t* tile_expert, int32_t num_tiles, int64_t block_m,
                                      const float* topk_weights, int64_t T, int64_t k, int64_t H, int64_t I,
-                                     int32_t block, float* out) {
+                                     int32_t block, const int64_t* tokens, int64_t ntok, float* out) {
   const int64_t P = T * k, R = (int64_t)num_tiles * block_m;
   const int64_t nsh = block ? I / 128 : 1;
   int64_t* pair_row = (int64_t*)malloc(sizeof(int64_t) * (P > 0 ? P : 1));
@@ -352,9 +353,10 @@ ORACLE_EXPORT void oracle_w2_combine(const int8_t* h_q, const float* h_s, const 
   for (int64_t r = 0; r < R; ++r)
     if (sorted_pair_ids[r] < P) pair_row[sorted_pair_ids[r]] = r;
 #pragma omp parallel for schedule(dynamic, 1)
-  for (int64_t t = 0; t < T; ++t) {
+  for (int64_t i = 0; i < ntok; ++i) {
+    const int64_t t = tokens ? tokens[i] : i;
     float* y = (float*)malloc(sizeof(float) * H);
-    float* o = out + t * H;
+    float* o = out + i * H;
     for (int64_t n = 0; n < H; ++n) o[n] = 0.0f;
     for (int64_t j = 0; j < k; ++j) {
       const int64_t r = pair_row[t * k + j];

@@ -256,3 +256,16 @@ def dev_activations(out_ptr: int, cfg: MoEConfig, hip_stream: int, T: Optional[i
     _check(_load_dev().synth_dev_fill_activation(out_ptr, cfg.x_dtype, T, cfg.H, cfg.seed, cfg.x_sigma,
                                                  cfg.outlier_threshold, cfg.outlier_mult, row_start,
                                                  hip_stream), "synth_dev_fill_activation")
+
+
+def int8_matrix(rows: int, cols: int, seed: int, start: int = 0) -> np.ndarray:
+    """Uniform int8 in [-127, 127] (for raw GEMM inputs), from the MISC stream."""
+    w = words(rows * cols, seed, STREAM_MISC, start)
+    return ((w % np.uint64(255)).astype(np.int16) - 127).astype(np.int8).reshape(rows, cols)
+
+
+def positive_scales(n: int, seed: int, lo: float, hi: float, start: int = 0) -> np.ndarray:
+    """Uniform fp32 scales in [lo, hi) (for raw GEMM inputs), from the MISC stream."""
+    w = words(n, seed + 7919, STREAM_MISC, start)
+    u = (w >> np.uint64(40)).astype(np.float64) / float(1 << 24)
+    return (lo + (hi - lo) * u).astype(np.float32)

@@ -1,0 +1,590 @@
+"""GPU parity: every stage of the HIP path against the CPU oracle, through the C ABI.
+
+Bars (stated once, used below):
+  - bit-exact: activation quantization (a_q, a_s), weight quantization, align
+    outputs, raw int32 accumulators, the second GEMM + combine when fed the same
+    intermediate (same fp32 operations in the same order on both sides);
+  - routing: expert ids equal except near-ties, where the oracle's score gap
+    between swapped experts is within 5e-7 relative (libm and device expf
+    differ in the last bits); weights within 8 ulp;
+  - first GEMM epilogue (uses expf): h_scale within 4 ulp, at most 0.1% of
+    h_q entries off by one, none by more;
+  - whole layer: max|err| <= 5e-3 * max|ref| over the checked tokens.
+Full-size workloads are checked on sampled rows / tokens, which the oracle
+computes one by one from its own quantized copies of the experts they touch.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import w8a8_int8_quantized_quant_amd as w8  # noqa: E402
+from w8a8_int8_quantized_quant_amd import workload  # noqa: E402
+
+DEV = "cuda"
+FULL = ["decode", "prefill", "skew", "block"]
+ULP = 2.0 ** -23
+
+
+def small_cfg(name="ds-small", index=20, T=300, H=512, I=256, E=16, k=4, route="sigmoid", n_group=4, topk_group=2,
+              scaling=2.5, mode="channel", x_dtype=synth.DTYPE_BF16):
+    return synth.MoEConfig(name=name, index=index, T=T, H=H, I=I, E=E, k=k, route=route, n_group=n_group,
+                           topk_group=topk_group, routed_scaling=scaling, renormalize=True, x_dtype=x_dtype,
+                           x_sigma=1.0, outlier_threshold=synth.OUTLIER_THRESHOLD, outlier_mult=20.0,
+                           w_sigma=0.006, scale_mode=mode)
+
+
+SMALL = {
+    "tiny": synth.CONFIGS["tiny"],
+    "ds-small": small_cfg(),
+    "ds-small-block": small_cfg(name="ds-small-block", index=21, mode="block", T=257),
+}
+
+
+def cfg_of(name):
+    return synth.CONFIGS.get(name) or SMALL[name]
+
+
+def dt(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+# ------------------------------------------------------------------ caches (one device layer at a time)
+
+_layer = {}
+_oracle_w = {}
+
+
+def layer_of(name):
+    if name not in _layer:
+        _layer.clear()
+        torch.cuda.empty_cache()
+        say(f"[layer] drawing {name} on the device")
+        _layer[name] = workload.make_layer(cfg_of(name), device=DEV)
+    return _layer[name]
+
+
+def oracle_weights(name, experts):
+    """Oracle-side quantized weights (own draw + own quantization), cached per workload."""
+    cfg = cfg_of(name)
+    cache = _oracle_w.setdefault(name, [[None] * cfg.E for _ in range(4)])
+    todo = sorted({int(e) for e in experts if cache[0][int(e)] is None})
+    if todo:
+        w = oracle.expert_weights(cfg, todo)
+        for i in range(4):
+            for e in todo:
+                cache[i][e] = w[i][e]
+    return cache
+
+
+def sample(n, count, seed):
+    rng = np.random.default_rng(seed)
+    return np.sort(rng.choice(n, size=min(n, count), replace=False))
+
+
+def route_host(cfg):
+    return oracle.route_cfg(cfg, synth.logits(cfg))
+
+
+def block_m_of(cfg):
+    return w8.w8a8_moe_pick_block_m(cfg.T, cfg.k, cfg.E)
+
+
+def dev_align(ids_np, E, bm):
+    T, k = ids_np.shape
+    R = max(w8.w8a8_moe_max_rows(T, k, E, bm), 1)
+    o = dict(counts=torch.empty(E, dtype=torch.int32, device=DEV),
+             offsets=torch.empty(E + 1, dtype=torch.int32, device=DEV),
+             padded_offsets=torch.empty(E + 1, dtype=torch.int32, device=DEV),
+             sorted_pair_ids=torch.full((R,), -7, dtype=torch.int32, device=DEV),
+             tile_expert=torch.full((max(R // bm, 1),), -7, dtype=torch.int32, device=DEV),
+             num_tiles=torch.empty(1, dtype=torch.int32, device=DEV))
+    ws = torch.empty(max(w8.moe_align_workspace_bytes(T, k, E), 256), dtype=torch.uint8, device=DEV)
+    w8.moe_align_by_expert(dt(ids_np), E, bm, o["counts"], o["offsets"], o["padded_offsets"], o["sorted_pair_ids"],
+                           o["tile_expert"], o["num_tiles"], ws)
+    return o
+
+
+def oracle_align_dev(ids_np, E, bm):
+    """The oracle's align outputs, uploaded (stage inputs for the GEMM tests)."""
+    al = oracle.align(ids_np, E, bm)
+    d = {key: dt(v) for key, v in al.items()}
+    return al, d
+
+
+# ------------------------------------------------------------------ generator
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "skew"])
+def test_device_generator_matches_host(name):
+    cfg = cfg_of(name)
+    hs = torch.cuda.current_stream().cuda_stream
+    x = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16 if cfg.x_dtype else torch.float32, device=DEV)
+    synth.dev_activations(x.data_ptr(), cfg, hs)
+    xh = synth.activations(cfg)
+    got = host(x.view(torch.int16) if cfg.x_dtype else x)
+    assert np.array_equal(got.view(xh.dtype), xh)
+    lg = torch.empty((cfg.T, cfg.E), dtype=torch.float32, device=DEV)
+    bias = synth.zipf_bias(cfg)
+    bt = None if bias is None else dt(bias)
+    synth.dev_logits(lg.data_ptr(), cfg, None if bt is None else bt.data_ptr(), hs)
+    assert np.array_equal(host(lg), synth.logits(cfg))
+    n = 2 * cfg.I * cfg.H
+    buf = torch.empty(100_000, dtype=torch.float32, device=DEV)
+    for start in (0, (cfg.E - 1) * n + n - 100_000):
+        synth.dev_normal(buf.data_ptr(), 100_000, cfg.seed, synth.STREAM_W13, start, cfg.w_sigma, hs)
+        assert np.array_equal(host(buf), synth.normal(100_000, cfg.seed, synth.STREAM_W13, start, cfg.w_sigma))
+
+
+# ------------------------------------------------------------------ step 1: quantization
+
+@pytest.mark.parametrize("name", ["tiny", "ds-small", "decode", "prefill", "skew", "block"])
+def test_activation_quant_bit_exact(name):
+    cfg = cfg_of(name)
+    group = 128 if cfg.scale_mode == "block" else 0
+    say(f"[quant] {name} T={cfg.T} H={cfg.H} group={group}")
+    xh = synth.activations(cfg)
+    x = dt(xh.view(np.int16)).view(torch.bfloat16) if cfg.x_dtype else dt(xh)
+    q = torch.empty((cfg.T, cfg.H), dtype=torch.int8, device=DEV)
+    s = torch.empty((cfg.T, cfg.H // 128) if group else (cfg.T,), dtype=torch.float32, device=DEV)
+    w8.w8a8_quant_per_token(x, group, q, s)
+    rq, rs = oracle.quant_per_token(oracle.activations_f32(cfg), group)
+    assert np.array_equal(host(q), rq)
+    assert np.array_equal(host(s), rs)
+
+
+@pytest.mark.parametrize("rows,cols,group,dtype", [(1, 24, 0, "f32"), (7, 100, 0, "f32"), (5, 96, 32, "bf16"),
+                                                   (33, 7168, 128, "f32"), (3, 40, 40, "bf16"),
+                                                   (2, 1024, 0, "bf16")])
+def test_activation_quant_ragged_and_degenerate(rows, cols, group, dtype):
+    z = synth.normal(rows * cols, 3, synth.STREAM_MISC, 0).reshape(rows, cols)
+    z[0, :] = 0.0                      # all-zero row: scale floor, q = 0
+    if rows > 2:
+        z[1, :] = 3e-9                 # tiny row: scale floor
+        z[2, ::3] = 0.5                # exact halves
+    if dtype == "bf16":
+        zb = torch.from_numpy(z).to(torch.bfloat16)
+        x = zb.to(DEV)
+        zf = zb.to(torch.float32).numpy()
+    else:
+        x = dt(z)
+        zf = z
+    q = torch.empty((rows, cols), dtype=torch.int8, device=DEV)
+    s = torch.empty((rows, cols // group) if group else (rows,), dtype=torch.float32, device=DEV)
+    w8.w8a8_quant_per_token(x, group, q, s)
+    rq, rs = oracle.quant_per_token(zf, group)
+    assert np.array_equal(host(q), rq)
+    assert np.array_equal(host(s), rs)
+    assert np.all(host(q)[0] == 0)
+
+
+@pytest.mark.parametrize("shape,block", [((300, 384), (128, 128)), ((256, 7168), (1, 7168)), ((129, 257), (128, 128)),
+                                         ((64, 130), (1, 130))])
+def test_weight_quant_blocks_bit_exact(shape, block):
+    z = synth.normal(shape[0] * shape[1], 4, synth.STREAM_MISC, 0, 0.006).reshape(shape)
+    q = torch.empty(shape, dtype=torch.int8, device=DEV)
+    nb = ((shape[0] + block[0] - 1) // block[0], (shape[1] + block[1] - 1) // block[1])
+    s = torch.empty(nb, dtype=torch.float32, device=DEV)
+    w8.w8a8_quant_blocks(dt(z), block[0], block[1], q, s)
+    rq, rs = oracle.quant_blocks(z, *block)
+    assert np.array_equal(host(q), rq)
+    assert np.array_equal(host(s), rs)
+
+
+@pytest.mark.parametrize("name", ["decode", "block"])
+def test_layer_weights_bit_exact(name):
+    """Expert weights drawn and quantized on the device equal the oracle's own draw + quantization."""
+    cfg = cfg_of(name)
+    L = layer_of(name)
+    experts = [0, 97, cfg.E - 1]
+    w = oracle_weights(name, experts)
+    for e in experts:
+        assert np.array_equal(host(L.w13[e]), w[0][e])
+        assert np.array_equal(host(L.w13_scale[e]), w[1][e])
+        assert np.array_equal(host(L.w2[e]), w[2][e])
+        assert np.array_equal(host(L.w2_scale[e]), w[3][e])
+
+
+# ------------------------------------------------------------------ step 2: routing
+
+def check_routing(cfg, logits, ids_g, w_g, ids_o, w_o):
+    fn = oracle.SOFTMAX if cfg.route == "softmax" else oracle.SIGMOID
+    score = logits.astype(np.float64) if fn == oracle.SOFTMAX else 1.0 / (1.0 + np.exp(-logits.astype(np.float64)))
+    bad = 0
+    same = np.all(ids_g == ids_o, axis=1)
+    for t in np.nonzero(~same)[0]:
+        A, B = set(ids_o[t]), set(ids_g[t])
+        if A == B:
+            # same set, slots swapped: only a near-tie can do that
+            j = np.nonzero(ids_g[t] != ids_o[t])[0]
+            gap = np.abs(score[t, ids_o[t, j]] - score[t, ids_g[t, j]]).max()
+        else:
+            gap = abs(score[t, list(A)].sum() - score[t, list(B)].sum())
+        if gap > 5e-7 * np.abs(score[t]).max():
+            bad += 1
+    assert bad == 0, f"{bad} tokens differ beyond a near-tie"
+    assert (~same).sum() <= max(1, cfg.T // 100)
+    rel = np.abs(w_g[same] - w_o[same]) / np.abs(w_o[same])
+    assert rel.max() <= 8 * ULP, rel.max()
+
+
+@pytest.mark.parametrize("name", ["tiny", "ds-small", "decode", "prefill", "skew", "block"])
+def test_routing(name):
+    cfg = cfg_of(name)
+    say(f"[route] {name}")
+    lg = synth.logits(cfg)
+    ids = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=DEV)
+    tw = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=DEV)
+    fn = w8.SCORE_SOFTMAX if cfg.route == "softmax" else w8.SCORE_SIGMOID
+    w8.moe_topk_route(dt(lg), cfg.k, fn, cfg.n_group, cfg.topk_group, cfg.renormalize, cfg.routed_scaling, None,
+                      ids, tw)
+    ids_o, w_o = route_host(cfg)
+    check_routing(cfg, lg, host(ids), host(tw), ids_o, w_o)
+
+
+@pytest.mark.parametrize("E,k,ng,tg,fn,renorm,bias", [(8, 8, 1, 1, 0, True, False), (64, 6, 1, 1, 0, False, False),
+                                                      (1, 1, 1, 1, 0, True, False), (1024, 8, 16, 4, 1, True, True),
+                                                      (72, 5, 1, 1, 1, False, False), (256, 8, 8, 4, 1, True, True)])
+def test_routing_variants(E, k, ng, tg, fn, renorm, bias):
+    T = 77
+    lg = synth.normal(T * E, 5, synth.STREAM_MISC, 0).reshape(T, E)
+    b = synth.normal(E, 6, synth.STREAM_MISC, 0, 0.1) if bias else None
+    ids = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    tw = torch.empty((T, k), dtype=torch.float32, device=DEV)
+    w8.moe_topk_route(dt(lg), k, fn, ng, tg, renorm, 1.5, None if b is None else dt(b), ids, tw)
+    ids_o, w_o = oracle.route(lg, k, fn, ng, tg, renorm, 1.5, b)
+    cfg = small_cfg(T=T, E=E, k=k, route="softmax" if fn == 0 else "sigmoid")
+    if b is None:
+        check_routing(cfg, lg, host(ids), host(tw), ids_o, w_o)
+    else:
+        assert np.mean(np.all(host(ids) == ids_o, axis=1)) >= 0.98
+        same = np.all(host(ids) == ids_o, axis=1)
+        assert (np.abs(host(tw)[same] - w_o[same]) / w_o[same]).max() <= 8 * ULP
+
+
+# ------------------------------------------------------------------ step 3: align
+
+def check_align_equal(d, al):
+    nt = int(al["num_tiles"][0])
+    assert int(host(d["num_tiles"])[0]) == nt
+    for key in ("counts", "offsets", "padded_offsets"):
+        assert np.array_equal(host(d[key]), al[key]), key
+    R = int(al["padded_offsets"][-1])
+    assert np.array_equal(host(d["sorted_pair_ids"])[:R], al["sorted_pair_ids"][:R])
+    assert np.array_equal(host(d["tile_expert"])[:nt], al["tile_expert"][:nt])
+
+
+@pytest.mark.parametrize("name", ["tiny", "ds-small", "decode", "prefill", "skew", "block"])
+@pytest.mark.parametrize("bm", [16, 32, 64, 128])
+def test_align_bit_exact(name, bm):
+    cfg = cfg_of(name)
+    ids, _ = route_host(cfg)
+    check_align_equal(dev_align(ids, cfg.E, bm), oracle.align(ids, cfg.E, bm))
+
+
+def test_align_edge_cases():
+    rng = np.random.default_rng(3)
+    cases = [
+        (np.full((5000, 1), 3, np.int32), 8),                      # every pair on one expert
+        (np.tile(np.arange(8, dtype=np.int32), (300, 1)), 8),       # k = E
+        (np.zeros((1, 1), np.int32), 1),                            # one pair, one expert
+        (np.zeros((70000, 1), np.int32), 1),                        # E = 1, many chunks
+        (rng.integers(0, 1024, size=(3000, 8)).astype(np.int32), 1024),
+        (np.minimum(rng.zipf(1.3, size=(2049, 8)) - 1, 255).astype(np.int32), 256),
+    ]
+    for ids, E in cases:
+        for bm in (16, 128):
+            check_align_equal(dev_align(ids, E, bm), oracle.align(ids, E, bm))
+    # no tokens: counts and offsets zero, no tiles
+    d = dev_align(np.zeros((0, 8), np.int32), 256, 16)
+    assert int(host(d["num_tiles"])[0]) == 0 and not host(d["counts"]).any() and not host(d["offsets"]).any()
+
+
+def test_align_drops_out_of_range_ids():
+    ids = np.array([[0, 5], [9, 2], [-1, 5], [3, 3]], np.int32)
+    d = dev_align(ids, 8, 16)
+    valid = ids.reshape(-1)[(ids.reshape(-1) >= 0) & (ids.reshape(-1) < 8)]
+    assert np.array_equal(host(d["counts"]), np.bincount(valid, minlength=8))
+    srt = host(d["sorted_pair_ids"])[: int(host(d["padded_offsets"])[-1])]
+    assert sorted(srt[srt < 8].tolist()) == [0, 1, 3, 5, 6, 7]
+
+
+def test_align_is_deterministic():
+    ids, _ = route_host(cfg_of("prefill"))
+    a = dev_align(ids, 256, 64)
+    b = dev_align(ids, 256, 64)
+    for key in a:
+        assert torch.equal(a[key], b[key])
+
+
+# ------------------------------------------------------------------ steps 4-5: grouped GEMMs
+
+def stage_rows(al, bm, P, name, nsample, seed):
+    """Non-pad sorted rows to check: all of them for small workloads; else, for three
+    experts (most loaded, least loaded non-empty, median), the first and last rows of
+    their segments (tile edges and the ragged tail) plus a random sample."""
+    R = int(al["num_tiles"][0]) * bm
+    real = np.nonzero(al["sorted_pair_ids"][:R] < P)[0]
+    if name in SMALL:
+        return real
+    counts = al["counts"]
+    order = np.argsort(counts, kind="stable")
+    nonempty = order[counts[order] > 0]
+    picks = [nonempty[-1], nonempty[0], nonempty[len(nonempty) // 2]]
+    rows = []
+    rng = np.random.default_rng(seed)
+    for e in picks:
+        r0, n = int(al["padded_offsets"][e]), int(counts[e])
+        seg = np.arange(r0, r0 + n)
+        rows += list(seg[:6]) + list(seg[-6:]) + list(rng.choice(seg, size=min(n, nsample // 3), replace=False))
+    return np.unique(np.array(rows, dtype=np.int64))
+
+
+def experts_of_rows(al, bm, rows):
+    return sorted({int(al["tile_expert"][r // bm]) for r in rows})
+
+
+@pytest.mark.parametrize("name", ["tiny", "ds-small", "decode", "prefill", "skew", "block"])
+def test_gemm_i32_bit_exact(name):
+    cfg = cfg_of(name)
+    bm = block_m_of(cfg)
+    say(f"[gemm_i32] {name} block_m={bm}")
+    L = layer_of(name)
+    ids, _ = route_host(cfg)
+    P = cfg.T * cfg.k
+    al, d = oracle_align_dev(ids, cfg.E, bm)
+    group = 128 if cfg.scale_mode == "block" else 0
+    a_q, _ = oracle.quant_per_token(oracle.activations_f32(cfg), group)
+    R = w8.w8a8_moe_max_rows(cfg.T, cfg.k, cfg.E, bm)
+    rows = stage_rows(al, bm, P, name, 48, 1)
+    w = oracle_weights(name, experts_of_rows(al, bm, rows))
+    # first GEMM: gathered token rows x w13
+    out = torch.empty((R, 2 * cfg.I), dtype=torch.int32, device=DEV)
+    w8.w8a8_grouped_gemm_i32(dt(a_q), True, L.w13, d["sorted_pair_ids"], d["tile_expert"], d["num_tiles"], cfg.T,
+                             cfg.k, bm, out)
+    ref = oracle.grouped_gemm_i32(a_q, True, w[0], al, bm, P, cfg.k, rows)
+    got = host(out)
+    assert np.array_equal(got[rows], ref[rows])
+    # second GEMM form: sorted rows of an int8 intermediate x w2
+    h = synth.int8_matrix(R, cfg.I, cfg.seed)
+    out2 = torch.empty((R, cfg.H), dtype=torch.int32, device=DEV)
+    w8.w8a8_grouped_gemm_i32(dt(h), False, L.w2, d["sorted_pair_ids"], d["tile_expert"], d["num_tiles"], cfg.T,
+                             cfg.k, bm, out2)
+    ref2 = oracle.grouped_gemm_i32(h, False, w[2], al, bm, P, cfg.k, rows)
+    assert np.array_equal(host(out2)[rows], ref2[rows])
+
+
+@pytest.mark.parametrize("name", ["tiny", "ds-small", "ds-small-block", "decode", "prefill", "skew", "block"])
+def test_first_gemm_silu_requant(name):
+    cfg = cfg_of(name)
+    block = cfg.scale_mode == "block"
+    bm = block_m_of(cfg)
+    say(f"[w13] {name} block_m={bm}")
+    L = layer_of(name)
+    ids, _ = route_host(cfg)
+    P = cfg.T * cfg.k
+    al, d = oracle_align_dev(ids, cfg.E, bm)
+    a_q, a_s = oracle.quant_per_token(oracle.activations_f32(cfg), 128 if block else 0)
+    R = w8.w8a8_moe_max_rows(cfg.T, cfg.k, cfg.E, bm)
+    h_q = torch.empty((R, cfg.I), dtype=torch.int8, device=DEV)
+    h_s = torch.empty((R, cfg.I // 128) if block else (R,), dtype=torch.float32, device=DEV)
+    mode = w8.SCALE_BLOCK128 if block else w8.SCALE_CHANNEL
+    ws = torch.empty(max(w8.w8a8_w13_workspace_bytes(cfg.T, cfg.k, cfg.E, cfg.H, cfg.I, bm, mode), 256),
+                     dtype=torch.uint8, device=DEV)
+    fn = w8.w8a8_block_grouped_gemm_w13_silu if block else w8.w8a8_grouped_gemm_w13_silu
+    fn(dt(a_q), dt(a_s), L.w13, L.w13_scale, d["sorted_pair_ids"], d["padded_offsets"], d["tile_expert"],
+       d["num_tiles"], cfg.T, cfg.k, bm, h_q, h_s, ws)
+    rows = stage_rows(al, bm, P, name, 48, 2)
+    w = oracle_weights(name, experts_of_rows(al, bm, rows))
+    rq, rs = oracle.w13_silu(a_q, a_s, w[0], w[1], al, bm, cfg.T, cfg.k, cfg.H, cfg.I, block, rows)
+    gq, gs = host(h_q)[rows], host(h_s)[rows]
+    rq, rs = rq[rows], rs[rows]
+    assert np.all(np.abs(gs - rs) <= 4 * ULP * rs), np.abs(gs / rs - 1).max()
+    diff = np.abs(gq.astype(np.int32) - rq.astype(np.int32))
+    assert diff.max() <= 1
+    assert np.mean(diff > 0) <= 1e-3, np.mean(diff > 0)
+
+
+@pytest.mark.parametrize("name", ["tiny", "ds-small", "ds-small-block", "decode", "prefill", "skew", "block"])
+def test_second_gemm_combine_bit_exact(name):
+    """Fed the same intermediate, the second GEMM + combine performs the oracle's fp32
+    operations in the oracle's order, so the output matches bit for bit."""
+    cfg = cfg_of(name)
+    block = cfg.scale_mode == "block"
+    bm = block_m_of(cfg)
+    say(f"[w2] {name} block_m={bm}")
+    L = layer_of(name)
+    ids, tw = route_host(cfg)
+    P = cfg.T * cfg.k
+    al, d = oracle_align_dev(ids, cfg.E, bm)
+    R = w8.w8a8_moe_max_rows(cfg.T, cfg.k, cfg.E, bm)
+    h_q = synth.int8_matrix(R, cfg.I, cfg.seed + 100)
+    h_s = synth.positive_scales(R * (cfg.I // 128 if block else 1), cfg.seed, 1e-3, 3e-2)
+    h_s = h_s.reshape(R, cfg.I // 128) if block else h_s
+    out = torch.full((cfg.T, cfg.H), float("nan"), dtype=torch.float32, device=DEV)
+    mode = w8.SCALE_BLOCK128 if block else w8.SCALE_CHANNEL
+    ws = torch.empty(max(w8.w8a8_w2_workspace_bytes(cfg.T, cfg.k, cfg.E, cfg.H, cfg.I, bm, mode), 256),
+                     dtype=torch.uint8, device=DEV)
+    fn = w8.w8a8_block_grouped_gemm_w2_combine if block else w8.w8a8_grouped_gemm_w2_combine
+    fn(dt(h_q), dt(h_s), L.w2, L.w2_scale, d["sorted_pair_ids"], d["padded_offsets"], d["tile_expert"],
+       d["num_tiles"], dt(tw), cfg.T, cfg.k, bm, out, ws)
+    tokens = np.arange(cfg.T) if name in SMALL else sample(cfg.T, 3, 3)
+    w = oracle_weights(name, np.unique(ids[tokens]))
+    ref = oracle.w2_combine(h_q, h_s, w[2], w[3], al, bm, tw, cfg.T, cfg.k, cfg.H, cfg.I, block, tokens)
+    got = host(out)
+    assert np.array_equal(got[tokens], ref)
+    assert np.isfinite(got).all()
+
+
+# ------------------------------------------------------------------ the whole layer
+
+@pytest.mark.parametrize("name", ["tiny", "ds-small", "ds-small-block", "decode", "prefill", "skew", "block"])
+def test_forward_matches_oracle(name):
+    cfg = cfg_of(name)
+    say(f"[forward] {name}")
+    L = layer_of(name)
+    out = torch.empty((cfg.T, cfg.H), dtype=torch.float32, device=DEV)
+    ids = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=DEV)
+    tw = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=DEV)
+    ws = workload.forward_workspace(L)
+    workload.forward(L, out, ws, topk_ids=ids, topk_weights=tw)
+    got, gids = host(out), host(ids)
+    tokens = np.arange(cfg.T) if name in SMALL else sample(cfg.T, 3, 4)
+    lg = synth.logits(cfg, slice(0, cfg.T))[tokens]
+    ids_o, tw_o = oracle.route_cfg(cfg, lg)
+    keep = np.all(gids[tokens] == ids_o, axis=1)
+    assert keep.mean() >= 0.95
+    tokens, ids_o, tw_o = tokens[keep], ids_o[keep], tw_o[keep]
+    w = oracle_weights(name, np.unique(ids_o))
+    x = oracle.activations_f32(cfg)[tokens]
+    ref = oracle.moe_tokens(x, ids_o, tw_o, *w, I=cfg.I, block=cfg.scale_mode == "block")
+    err = np.abs(got[tokens] - ref).max()
+    assert err <= 5e-3 * np.abs(ref).max(), (err, np.abs(ref).max())
+
+
+@pytest.mark.parametrize("bm", [16, 32, 64, 128])
+@pytest.mark.parametrize("name", ["ds-small", "ds-small-block"])
+def test_forward_every_block_m(name, bm):
+    cfg = cfg_of(name)
+    L = layer_of(name)
+    out = torch.empty((cfg.T, cfg.H), dtype=torch.float32, device=DEV)
+    ws = workload.forward_workspace(L, bm)
+    workload.forward(L, out, ws, block_m=bm)
+    ids_o, tw_o = route_host(cfg)
+    w = oracle_weights(name, range(cfg.E))
+    ref = oracle.moe_tokens(oracle.activations_f32(cfg), ids_o, tw_o, *w, I=cfg.I, block=cfg.scale_mode == "block")
+    assert np.abs(host(out) - ref).max() <= 5e-3 * np.abs(ref).max()
+
+
+def test_forward_is_deterministic():
+    L = layer_of("ds-small")
+    cfg = L.cfg
+    a = torch.empty((cfg.T, cfg.H), dtype=torch.float32, device=DEV)
+    b = torch.empty_like(a)
+    ws = workload.forward_workspace(L)
+    workload.forward(L, a, ws)
+    workload.forward(L, b, ws)
+    assert torch.equal(a, b)
+
+
+def _dense_check(cfg, x_np, logits_np, L, out):
+    ids_o, tw_o = oracle.route_cfg(cfg, logits_np)
+    w = oracle_weights_custom(cfg, np.unique(ids_o))
+    ref = oracle.moe_tokens(x_np, ids_o, tw_o, *w, I=cfg.I, block=cfg.scale_mode == "block")
+    err = np.abs(host(out) - ref).max()
+    assert err <= 5e-3 * max(np.abs(ref).max(), 1e-30), err
+
+
+_custom_w = {}
+
+
+def oracle_weights_custom(cfg, experts):
+    key = cfg.name
+    if key not in _custom_w:
+        _custom_w[key] = oracle.expert_weights(cfg, range(cfg.E))
+    return _custom_w[key]
+
+
+@pytest.mark.parametrize("case", ["one_token", "all_to_one_expert", "k_equals_E", "single_expert", "no_tokens"])
+def test_forward_edge_cases(case):
+    if case == "one_token":
+        cfg = small_cfg(name="one", index=30, T=1)
+    elif case == "all_to_one_expert":
+        cfg = small_cfg(name="skewone", index=31, T=200, k=1, route="softmax", n_group=1, topk_group=1, scaling=1.0)
+    elif case == "k_equals_E":
+        cfg = small_cfg(name="kE", index=32, T=40, E=8, k=8, route="softmax", n_group=1, topk_group=1, scaling=1.0)
+    elif case == "single_expert":
+        cfg = small_cfg(name="E1", index=33, T=50, E=1, k=1, route="softmax", n_group=1, topk_group=1, scaling=1.0)
+    else:
+        cfg = small_cfg(name="empty", index=34, T=0)
+    L = workload.make_layer(cfg, device=DEV)
+    if case == "all_to_one_expert":
+        L.logits[:, 5] += 100.0
+    out = torch.full((max(cfg.T, 1), cfg.H), 7.0, dtype=torch.float32, device=DEV)
+    ws = workload.forward_workspace(L)
+    workload.forward(L, out[: cfg.T], ws)
+    if cfg.T == 0:
+        assert torch.all(out == 7.0)
+        return
+    lg = host(L.logits)
+    _dense_check(cfg, oracle.activations_f32(cfg), lg, L, out)
+
+
+def test_outputs_do_not_spill_past_their_buffers():
+    """Guard words after every output buffer stay untouched."""
+    cfg = cfg_of("ds-small")
+    L = layer_of("ds-small")
+    G = 4096
+    bm = 16
+    R = w8.w8a8_moe_max_rows(cfg.T, cfg.k, cfg.E, bm)
+    ids, tw = route_host(cfg)
+
+    def guarded(n, dtype):
+        t = torch.full((n + G,), 0x5A if dtype == torch.int8 else 12345, dtype=dtype, device=DEV)
+        return t, t[:n]
+
+    cnt_g, cnt = guarded(cfg.E, torch.int32)
+    off_g, off = guarded(cfg.E + 1, torch.int32)
+    pad_g, pad = guarded(cfg.E + 1, torch.int32)
+    srt_g, srt = guarded(R, torch.int32)
+    te_g, te = guarded(R // bm, torch.int32)
+    nt_g, nt = guarded(1, torch.int32)
+    ws = torch.empty(w8.moe_align_workspace_bytes(cfg.T, cfg.k, cfg.E), dtype=torch.uint8, device=DEV)
+    w8.moe_align_by_expert(dt(ids), cfg.E, bm, cnt, off, pad, srt, te, nt, ws)
+    for full, n in ((cnt_g, cfg.E), (off_g, cfg.E + 1), (pad_g, cfg.E + 1), (srt_g, R), (te_g, R // bm), (nt_g, 1)):
+        assert torch.all(full[n:] == 12345)
+    hq_g, hq = guarded(R * cfg.I, torch.int8)
+    hs_g, hs = guarded(R, torch.float32)
+    a_q, a_s = oracle.quant_per_token(oracle.activations_f32(cfg))
+    ws1 = torch.empty(w8.w8a8_w13_workspace_bytes(cfg.T, cfg.k, cfg.E, cfg.H, cfg.I, bm), dtype=torch.uint8,
+                      device=DEV)
+    w8.w8a8_grouped_gemm_w13_silu(dt(a_q), dt(a_s), L.w13, L.w13_scale, srt, pad, te, nt, cfg.T, cfg.k, bm,
+                                  hq.view(R, cfg.I), hs, ws1)
+    out_g, out = guarded(cfg.T * cfg.H, torch.float32)
+    ws2 = torch.empty(w8.w8a8_w2_workspace_bytes(cfg.T, cfg.k, cfg.E, cfg.H, cfg.I, bm), dtype=torch.uint8,
+                      device=DEV)
+    w8.w8a8_grouped_gemm_w2_combine(hq.view(R, cfg.I), hs, L.w2, L.w2_scale, srt, pad, te, nt, dt(tw), cfg.T,
+                                    cfg.k, bm, out.view(cfg.T, cfg.H), ws2)
+    assert torch.all(hq_g[R * cfg.I:] == 0x5A)
+    assert torch.all(hs_g[R:] == 12345)
+    assert torch.all(out_g[cfg.T * cfg.H:] == 12345)

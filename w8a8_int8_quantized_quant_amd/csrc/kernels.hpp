@@ -1,0 +1,43 @@
+// kernels.hpp -- internal launchers behind the C ABI (arguments already validated).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace w8a8 {
+
+// quant.hip
+hipError_t quant_blocks(const void* x, int32_t dtype, int64_t rows, int64_t cols, int64_t br, int64_t bc,
+                        int8_t* q, float* scale, hipStream_t stream);
+
+// route.hip
+hipError_t topk_route(const float* logits, int64_t T, int64_t E, int64_t k, int32_t score_fn, int64_t n_group,
+                      int64_t topk_group, int32_t renormalize, float routed_scaling, const float* bias,
+                      int32_t* ids, float* weights, hipStream_t stream);
+
+// align.hip
+constexpr int64_t kAlignChunk = 1024;  // pairs per histogram chunk
+size_t align_ws_bytes(int64_t P, int64_t E);
+hipError_t align_by_expert(const int32_t* ids, int64_t P, int64_t E, int64_t block_m, int32_t* counts,
+                           int32_t* offsets, int32_t* padded_offsets, int32_t* sorted, int32_t* tile_expert,
+                           int32_t* num_tiles, int64_t max_tiles, void* ws, hipStream_t stream);
+
+// gemm.hip
+struct GroupedShape {
+  int64_t T, k, E, H, I, block_m;
+  int64_t max_rows;  // capacity of the sorted-row buffers
+};
+size_t w13_ws_bytes(const GroupedShape& s, int32_t scale_mode);
+size_t w2_ws_bytes(const GroupedShape& s, int32_t scale_mode);
+hipError_t gemm_i32(const int8_t* a, int32_t gather, const int8_t* w, int64_t N, int64_t K, const int32_t* sorted,
+                    const int32_t* tile_expert, const int32_t* num_tiles, int64_t P, int64_t k, int64_t block_m,
+                    int64_t max_rows, int32_t* out, hipStream_t stream);
+hipError_t w13_silu(const GroupedShape& s, int32_t scale_mode, const int8_t* a_q, const float* a_s,
+                    const int8_t* w13, const float* w13_s, const int32_t* sorted, const int32_t* tile_expert,
+                    const int32_t* num_tiles, int8_t* h_q, float* h_s, void* ws, hipStream_t stream);
+hipError_t w2_combine(const GroupedShape& s, int32_t scale_mode, const int8_t* h_q, const float* h_s,
+                      const int8_t* w2, const float* w2_s, const int32_t* sorted, const int32_t* tile_expert,
+                      const int32_t* num_tiles, const float* topk_w, float* out, void* ws, hipStream_t stream);
+
+}  // namespace w8a8

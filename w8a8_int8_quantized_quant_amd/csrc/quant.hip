@@ -1,0 +1,152 @@
+// quant.hip -- symmetric INT8 quantization kernels (gfx950).
+//
+// Online activation quantization, one scale per token or per token-group
+// (jiqizhixin article on Meituan's INT8 DeepSeek R1, "Quantization
+// exploration"), and the offline weight quantization with one scale per
+// output channel or per 128 x 128 block.  Rule: scale = max(max|x|/127, 1e-8),
+// q = clamp(rne(x / scale)).  The max is order-independent and the division is
+// IEEE, so results are bit-exact regardless of how lanes split the work.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace w8a8 {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ float block_max(float v, float* red) {
+  v = wave_max(v);
+  const int w = threadIdx.x / kWave;
+  if (lane_id() == 0) red[w] = v;
+  __syncthreads();
+  float m = red[0];
+#pragma unroll
+  for (int i = 1; i < kThreads / kWave; ++i) m = fmaxf(m, red[i]);
+  return m;
+}
+
+// Eight consecutive inputs as fp32.
+template <typename T>
+__device__ __forceinline__ void load8(const T* p, float (&v)[8]);
+template <>
+__device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, float (&v)[8]) {
+  uint4 u = *reinterpret_cast<const uint4*>(p);
+  uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float (&v)[8]) {
+  float4 a = *reinterpret_cast<const float4*>(p);
+  float4 b = *reinterpret_cast<const float4*>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+// One workgroup per row; cols % 8 == 0 and 16-byte aligned rows: 16-byte loads, 8-byte stores.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void quant_rows_vec_kernel(const T* __restrict__ x, int64_t cols,
+                                                                  int8_t* __restrict__ q,
+                                                                  float* __restrict__ scale) {
+  __shared__ float red[kThreads / kWave];
+  const int64_t row = blockIdx.x;
+  const T* xr = x + row * cols;
+  int8_t* qr = q + row * cols;
+  const int64_t nchunk = cols / 8;
+  float amax = 0.0f;
+  for (int64_t c = threadIdx.x; c < nchunk; c += kThreads) {
+    float v[8];
+    load8(xr + c * 8, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  }
+  const float s = quant_scale(block_max(amax, red));
+  if (threadIdx.x == 0) scale[row] = s;
+  for (int64_t c = threadIdx.x; c < nchunk; c += kThreads) {
+    float v[8];
+    load8(xr + c * 8, v);
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lo |= (uint32_t)(uint8_t)quant_value(v[i], s) << (8 * i);
+      hi |= (uint32_t)(uint8_t)quant_value(v[4 + i], s) << (8 * i);
+    }
+    *reinterpret_cast<uint2*>(qr + c * 8) = make_uint2(lo, hi);
+  }
+}
+
+// One wave per (row, group) for groups of up to a few hundred columns.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void quant_groups_kernel(const T* __restrict__ x, int64_t rows,
+                                                                int64_t cols, int64_t group,
+                                                                int8_t* __restrict__ q,
+                                                                float* __restrict__ scale) {
+  const int64_t ngroups = cols / group;
+  const int64_t gid = (int64_t)blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave;
+  if (gid >= rows * ngroups) return;
+  const int64_t row = gid / ngroups, g = gid % ngroups;
+  const int64_t base = row * cols + g * group;
+  float amax = 0.0f;
+  for (int64_t c = lane_id(); c < group; c += kWave) amax = fmaxf(amax, fabsf(load_as_f32(x, base + c)));
+  const float s = quant_scale(wave_max(amax));
+  if (lane_id() == 0) scale[gid] = s;
+  for (int64_t c = lane_id(); c < group; c += kWave) q[base + c] = quant_value(load_as_f32(x, base + c), s);
+}
+
+// General case: one workgroup per br x bc block (edge blocks may be partial).
+template <typename T>
+__global__ __launch_bounds__(kThreads) void quant_blocks_kernel(const T* __restrict__ x, int64_t rows,
+                                                                int64_t cols, int64_t br, int64_t bc,
+                                                                int8_t* __restrict__ q,
+                                                                float* __restrict__ scale) {
+  __shared__ float red[kThreads / kWave];
+  const int64_t nbc = (cols + bc - 1) / bc;
+  const int64_t bi = blockIdx.x / nbc, bj = blockIdx.x % nbc;
+  const int64_t r0 = bi * br, r1 = min(r0 + br, rows);
+  const int64_t c0 = bj * bc, c1 = min(c0 + bc, cols);
+  const int64_t w = c1 - c0, n = (r1 - r0) * w;
+  float amax = 0.0f;
+  for (int64_t i = threadIdx.x; i < n; i += kThreads)
+    amax = fmaxf(amax, fabsf(load_as_f32(x, (r0 + i / w) * cols + c0 + i % w)));
+  const float s = quant_scale(block_max(amax, red));
+  if (threadIdx.x == 0) scale[blockIdx.x] = s;
+  for (int64_t i = threadIdx.x; i < n; i += kThreads) {
+    const int64_t off = (r0 + i / w) * cols + c0 + i % w;
+    q[off] = quant_value(load_as_f32(x, off), s);
+  }
+}
+
+template <typename T>
+hipError_t launch_quant(const void* xv, int64_t rows, int64_t cols, int64_t br, int64_t bc, int8_t* q,
+                        float* scale, hipStream_t stream) {
+  const T* x = static_cast<const T*>(xv);
+  const bool aligned = (reinterpret_cast<uintptr_t>(x) % 16 == 0) && (reinterpret_cast<uintptr_t>(q) % 8 == 0);
+  if (br == 1 && bc == cols && cols % 8 == 0 && aligned) {
+    hipLaunchKernelGGL(quant_rows_vec_kernel<T>, dim3((uint32_t)rows), dim3(kThreads), 0, stream, x, cols, q,
+                       scale);
+  } else if (br == 1 && bc <= 512 && cols % bc == 0) {
+    const int64_t waves = rows * (cols / bc);
+    const int64_t blocks = (waves + kThreads / kWave - 1) / (kThreads / kWave);
+    hipLaunchKernelGGL(quant_groups_kernel<T>, dim3((uint32_t)blocks), dim3(kThreads), 0, stream, x, rows,
+                       cols, bc, q, scale);
+  } else {
+    const int64_t nb = ((rows + br - 1) / br) * ((cols + bc - 1) / bc);
+    hipLaunchKernelGGL(quant_blocks_kernel<T>, dim3((uint32_t)nb), dim3(kThreads), 0, stream, x, rows, cols,
+                       br, bc, q, scale);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t quant_blocks(const void* x, int32_t dtype, int64_t rows, int64_t cols, int64_t br, int64_t bc,
+                        int8_t* q, float* scale, hipStream_t stream) {
+  if (rows == 0 || cols == 0) return hipSuccess;
+  if (dtype == 1) return launch_quant<uint16_t>(x, rows, cols, br, bc, q, scale, stream);
+  return launch_quant<float>(x, rows, cols, br, bc, q, scale, stream);
+}
+
+}  // namespace w8a8
