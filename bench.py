@@ -34,8 +34,22 @@ def parse():
     ap.add_argument("--config", default="decode")
     ap.add_argument("--no-prefill", action="store_true", help="skip the T=8192 prefill figures")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=16, help="tokens in the CPU oracle sample")
+    ap.add_argument("--cpu-tokens", type=int, default=128, help="tokens in the CPU oracle sample")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy kernel 3 times (counter calibration)")
     return ap.parse_args()
+
+
+def copy_probe():
+    """A plain copy of known size: 1 GiB read + 1 GiB written per launch, for scaling HBM counters."""
+    import torch
+
+    a = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": a.numel() * 4, "copy_probe_bytes_written": b.numel() * 4}))
 
 
 class Stages:
@@ -189,7 +203,8 @@ def cpu_baseline(cfg, ntok):
     dt = time.perf_counter() - t0
     return {"value": ntok / dt, "unit": "tokens/s", "cores": min(threads, ntok), "kind": "oracle",
             "sample": f"first {ntok} of the {cfg.T} tokens of the same layer (routing + dense per-token "
-                      f"quantized MoE, OpenMP over tokens), {dt:.1f} s"}
+                      f"quantized MoE over {len(experts)} experts, OpenMP over tokens), {dt:.2f} s wall, "
+                      f"host has {os.cpu_count()} logical CPUs"}
 
 
 def main():
@@ -198,6 +213,9 @@ def main():
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the layer runs unsharded on a "
               f"single MI355X.", file=sys.stderr)
         sys.exit(2)
+    if args.copy_probe:
+        copy_probe()
+        return
     import torch
 
     import synth
@@ -235,7 +253,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         print(f"[bench] CPU oracle baseline on {args.cpu_tokens} tokens", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(cfg, args.cpu_tokens)
+        cpu = cpu_baseline(cfg, min(args.cpu_tokens, cfg.T))
 
     line = {
         "metric": METRIC, "value": round(fig["tokens_per_s"], 1), "unit": "tokens/s", "n_gpus": 1,

@@ -55,6 +55,14 @@ struct Params {
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return (g / (1.0f + expf(-g))) * u; }
 
+// B-tile row of fragment fn of wavefront column wn: plain tiles split BN evenly over the WN
+// wavefronts; split tiles give each wavefront FN/2 gate fragments and the matching up fragments.
+template <int BN, int WN, int FN, BMap MAP>
+__device__ __forceinline__ int brow_of(int wn, int fn) {
+  if (MAP == BMap::Plain) return wn * (BN / WN) + fn * 16;
+  return (fn < FN / 2 ? 0 : BN / 2) + wn * (BN / 2 / WN) + (fn % (FN / 2)) * 16;
+}
+
 template <int BM, int BN, int WM, int WN, BMap MAP, Epi EPI>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const Params p) {
   constexpr int FM = BM / WM / 16;
@@ -110,31 +118,25 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const Params p) 
     b_src[c] = wexp + wrow * p.K + part * 16;
   }
 
-  uint4 ra[A_CH], rb[B_CH];
-  auto gload = [&](int64_t k0) {
-#pragma unroll
-    for (int c = 0; c < A_CH; ++c)
-      ra[c] = a_ok[c] ? *reinterpret_cast<const uint4*>(a_src[c] + k0) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int c = 0; c < B_CH; ++c) rb[c] = *reinterpret_cast<const uint4*>(b_src[c] + k0);
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int c = 0; c < A_CH; ++c) {
-      const int idx = tid + c * kThreads;
-      if (idx < BM * 8) *reinterpret_cast<uint4*>(&lds[buf][(idx / 8) * kLdsStride + (idx % 8) * 16]) = ra[c];
-    }
-#pragma unroll
-    for (int c = 0; c < B_CH; ++c) {
-      const int idx = tid + c * kThreads;
-      *reinterpret_cast<uint4*>(&lds[buf][(BM + idx / 8) * kLdsStride + (idx % 8) * 16]) = rb[c];
-    }
-  };
-  // B-tile row of fragment fn of this wavefront.
-  auto brow = [&](int fn) -> int {
-    if (MAP == BMap::Plain) return wn * (BN / WN) + fn * 16;
-    return (fn < FNH ? 0 : BN / 2) + wn * (BN / 2 / WN) + (fn % FNH) * 16;
-  };
+  i32x4 ra[A_CH], rb[B_CH];  // native vectors: HIP's uint4 struct would be copied through scratch
+// Global -> registers for the K-stage at byte offset k0, and registers -> LDS buffer `buf`.
+#define W8A8_GLOAD(k0)                                                                                         \
+  do {                                                                                                         \
+    _Pragma("unroll") for (int c = 0; c < A_CH; ++c) ra[c] =                                                   \
+        a_ok[c] ? *reinterpret_cast<const i32x4*>(a_src[c] + (k0)) : i32x4{0, 0, 0, 0};                       \
+    _Pragma("unroll") for (int c = 0; c < B_CH; ++c) rb[c] = *reinterpret_cast<const i32x4*>(b_src[c] + (k0)); \
+  } while (0)
+#define W8A8_SSTORE(buf)                                                                                       \
+  do {                                                                                                         \
+    _Pragma("unroll") for (int c = 0; c < A_CH; ++c) {                                                         \
+      const int idx = tid + c * kThreads;                                                                      \
+      if (idx < BM * 8) *reinterpret_cast<i32x4*>(&lds[buf][(idx / 8) * kLdsStride + (idx % 8) * 16]) = ra[c]; \
+    }                                                                                                          \
+    _Pragma("unroll") for (int c = 0; c < B_CH; ++c) {                                                         \
+      const int idx = tid + c * kThreads;                                                                      \
+      *reinterpret_cast<i32x4*>(&lds[buf][(BM + idx / 8) * kLdsStride + (idx % 8) * 16]) = rb[c];              \
+    }                                                                                                          \
+  } while (0)
 
   i32x4 acc[FM][FN];
   float accf[kBlock ? FM : 1][kBlock ? FN : 1][4];
@@ -153,12 +155,12 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const Params p) 
 
   const int64_t KT = p.K / kBK;
   const int64_t nkb = p.K / 128;  // block-wise scale columns
-  gload(0);
-  sstore(0);
+  W8A8_GLOAD(0);
+  W8A8_SSTORE(0);
   __syncthreads();
   for (int64_t kt = 0; kt < KT; ++kt) {
     const int buf = (int)(kt & 1);
-    if (kt + 1 < KT) gload((kt + 1) * kBK);
+    if (kt + 1 < KT) W8A8_GLOAD((kt + 1) * kBK);
 #pragma unroll
     for (int kk = 0; kk < kBK / 64; ++kk) {
       i32x4 af[FM], bf[FN];
@@ -169,7 +171,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const Params p) 
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn)
         bf[fn] = *reinterpret_cast<const i32x4*>(
-            &lds[buf][(BM + brow(fn) + (l % 16)) * kLdsStride + kk * 64 + (l / 16) * 16]);
+            &lds[buf][(BM + brow_of<BN, WN, FN, MAP>(wn, fn) + (l % 16)) * kLdsStride + kk * 64 + (l / 16) * 16]);
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
@@ -189,7 +191,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const Params p) 
             as = EPI == Epi::W13Block ? p.a_s[(int64_t)(pid / p.k) * nkb + kt] : p.a_s[(row0 + trow) * nkb + kt];
 #pragma unroll
           for (int fn = 0; fn < FN; ++fn) {
-            const int br = brow(fn);
+            const int br = brow_of<BN, WN, FN, MAP>(wn, fn);
             int64_t wrow;
             if (MAP == BMap::Plain)
               wrow = nt * BN + br;
@@ -205,13 +207,13 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const Params p) 
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = i32x4{0, 0, 0, 0};
     }
-    if (kt + 1 < KT) sstore(buf ^ 1);
+    if (kt + 1 < KT) W8A8_SSTORE(buf ^ 1);
     __syncthreads();
   }
 
   // ---------------------------------------------------------------- epilogues
   // Accumulator element r of fragment (fm, fn) sits at tile row
-  // wm*(BM/WM) + fm*16 + (l/16)*4 + r and tile column brow(fn) + l%16.
+  // wm*(BM/WM) + fm*16 + (l/16)*4 + r and tile column brow_of<BN, WN, FN, MAP>(wn, fn) + l%16.
   if constexpr (EPI == Epi::I32) {
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm)
@@ -221,7 +223,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const Params p) 
         if (sh_pid[trow] >= p.P) continue;
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn)
-          p.out_i32[(row0 + trow) * p.N + nt * BN + brow(fn) + (l % 16)] = acc[fm][fn][r];
+          p.out_i32[(row0 + trow) * p.N + nt * BN + brow_of<BN, WN, FN, MAP>(wn, fn) + (l % 16)] = acc[fm][fn][r];
       }
   } else if constexpr (EPI == Epi::W2Channel || EPI == Epi::W2Block) {
 #pragma unroll
@@ -234,7 +236,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const Params p) 
         const float hs = kBlock ? 0.0f : p.a_s[grow];
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
-          const int64_t n = nt * BN + brow(fn) + (l % 16);
+          const int64_t n = nt * BN + brow_of<BN, WN, FN, MAP>(wn, fn) + (l % 16);
           float y;
           if constexpr (kBlock)
             y = accf[fm][fn][r];
@@ -259,7 +261,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const Params p) 
         rmax[fm][r] = 0.0f;
 #pragma unroll
         for (int f = 0; f < FNH; ++f) {
-          const int64_t n = nt * (BN / 2) + brow(f) + (l % 16);
+          const int64_t n = nt * (BN / 2) + brow_of<BN, WN, FN, MAP>(wn, f) + (l % 16);
           float g, u;
           if constexpr (kBlock) {
             g = accf[fm][f][r];
@@ -294,7 +296,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const Params p) 
           if (sh_pid[trow] >= p.P) continue;
 #pragma unroll
           for (int f = 0; f < FNH; ++f)
-            p.out_f32[(row0 + trow) * I + nt * (BN / 2) + brow(f) + (l % 16)] = hf[fm][f][r];
+            p.out_f32[(row0 + trow) * I + nt * (BN / 2) + brow_of<BN, WN, FN, MAP>(wn, f) + (l % 16)] = hf[fm][f][r];
         }
       for (int i = tid; i < BM; i += kThreads) {
         if (sh_pid[i] >= p.P) continue;
@@ -319,11 +321,14 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const Params p) 
           if (wn == 0 && (l % 16) == 0) p.h_s[grow * (I / 128) + nt] = s;
 #pragma unroll
           for (int f = 0; f < FNH; ++f)
-            p.h_q[grow * I + nt * (BN / 2) + brow(f) + (l % 16)] = quant_value(hf[fm][f][r], s);
+            p.h_q[grow * I + nt * (BN / 2) + brow_of<BN, WN, FN, MAP>(wn, f) + (l % 16)] = quant_value(hf[fm][f][r], s);
         }
     }
   }
 }
+
+#undef W8A8_GLOAD
+#undef W8A8_SSTORE
 
 // Channel-wise requantization of the first GEMM's rows: one wavefront per row.
 __global__ __launch_bounds__(kThreads) void requant_rows_kernel(const float* __restrict__ hf,
