@@ -198,8 +198,8 @@ static int32_t w13_entry(int32_t mode, const int8_t* a_q, const float* a_scale, 
   const size_t need = w8a8::w13_ws_bytes(s, mode);
   if (ws_bytes < need) return W8A8_WORKSPACE_TOO_SMALL;
   if (!aligned(ws, 256)) return W8A8_INVALID_ARGUMENT;
-  return hip_status(w8a8::w13_silu(s, mode, a_q, a_scale, w13, w13_scale, sorted, tile_expert, num_tiles, h_q,
-                                   h_scale, ws, stream));
+  return hip_status(w8a8::w13_silu(s, mode, a_q, a_scale, w13, w13_scale, sorted, padded_offsets, tile_expert,
+                                   num_tiles, h_q, h_scale, ws, stream));
 }
 
 static int32_t w2_entry(int32_t mode, const int8_t* h_q, const float* h_scale, const int8_t* w2,
@@ -216,8 +216,8 @@ static int32_t w2_entry(int32_t mode, const int8_t* h_q, const float* h_scale, c
   const size_t need = w8a8::w2_ws_bytes(s, mode);
   if (ws_bytes < need) return W8A8_WORKSPACE_TOO_SMALL;
   if (!aligned(ws, 256)) return W8A8_INVALID_ARGUMENT;
-  return hip_status(w8a8::w2_combine(s, mode, h_q, h_scale, w2, w2_scale, sorted, tile_expert, num_tiles,
-                                     topk_weights, out, ws, stream));
+  return hip_status(w8a8::w2_combine(s, mode, h_q, h_scale, w2, w2_scale, sorted, padded_offsets, tile_expert,
+                                     num_tiles, topk_weights, out, ws, stream));
 }
 
 int32_t w8a8_grouped_gemm_w13_silu(const int8_t* a_q, const float* a_scale, const int8_t* w13,
@@ -367,11 +367,11 @@ int32_t w8a8_moe_forward(const struct w8a8_moe_args* a, void* ws, size_t ws_byte
     e = w8a8::align_by_expert(ids, a->T * a->k, a->E, bm, counts, offsets, padded, sorted, tile_expert, num_tiles,
                               L.max_rows / bm, base + L.align_ws, stream);
   if (e == hipSuccess)
-    e = w8a8::w13_silu(s, a->scale_mode, a_q, a_s, a->w13, a->w13_scale, sorted, tile_expert, num_tiles, h_q, h_s,
-                       gws, stream);
+    e = w8a8::w13_silu(s, a->scale_mode, a_q, a_s, a->w13, a->w13_scale, sorted, padded, tile_expert, num_tiles,
+                       h_q, h_s, gws, stream);
   if (e == hipSuccess)
-    e = w8a8::w2_combine(s, a->scale_mode, h_q, h_s, a->w2, a->w2_scale, sorted, tile_expert, num_tiles, tw,
-                         a->out, gws, stream);
+    e = w8a8::w2_combine(s, a->scale_mode, h_q, h_s, a->w2, a->w2_scale, sorted, padded, tile_expert, num_tiles,
+                         tw, a->out, gws, stream);
   return hip_status(e);
 }
 

@@ -13,13 +13,26 @@
 // scales): int32 partial per 128-wide K-block, acc += ((float)part * a_s) * w_s
 // in ascending K-block order, requantization per (row, 128-group).
 //
-// Tiling: one workgroup = 4 wavefronts computes a BM x BN tile of one expert;
-// K advances 128 bytes per stage through a double-buffered LDS tile (A: the
-// tile's token rows gathered through the sorted pair list; B: BN weight rows),
-// each wavefront issuing v_mfma_i32_16x16x64_i8 on 16 x 16 sub-tiles.  In the
-// first GEMM the B tile holds BN/2 gate rows and the matching BN/2 up rows, so
-// every lane owns both operands of SiLU(gate) * up.  The grid covers the
-// worst-case tile count; workgroups past the device-side tile count exit at once.
+// Two tile engines share the epilogues.  Both issue v_mfma_i32_16x16x64_i8 on
+// 16 x 16 sub-tiles; accumulator element r of a fragment sits at fragment row
+// (lane/16)*4 + r and fragment column lane%16.  In the first GEMM a B tile holds
+// BN/2 gate rows and the matching BN/2 up rows, so the lane that owns gate
+// column n also owns up column n and forms SiLU(gate) * up in registers.
+//  - Staged engine (few rows per expert, weight streaming): tiles of block_m
+//    rows from the align step, K advances 128 bytes per stage through a double
+//    buffered LDS tile loaded via registers.  Many small workgroups keep many
+//    weight bytes in flight.
+//  - DMA engine (many rows per expert, MFMA-bound): 128 x 256 tiles of real rows
+//    only (a device-built work list, so align padding costs no MFMA work), a
+//    3-stage LDS ring of 128-byte K-slices (whole L2 lines) filled by global_load_lds_dwordx4,
+//    XOR-swizzled 16-byte chunks so fragment reads are conflict-free, explicit
+//    vmcnt waits so three stages stay in flight, and an XCD-aware order in
+//    which each XCD walks a contiguous stretch of (tile, N-tile) work so the
+//    A rows and the expert's weights are reused from its own L2.
+// Grids cover the worst case; workgroups past the device-side tile count exit
+// at once (no host read, graph-capturable).
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -29,11 +42,14 @@ namespace {
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
-constexpr int kBK = 128;                // K bytes per stage (= one block-wise K-block)
-constexpr int kLdsStride = kBK + 16;    // padded LDS row (bytes)
 
 enum class BMap { Plain, Split };
 enum class Epi { I32, W13Channel, W2Channel, W13Block, W2Block };
+
+template <Epi EPI>
+constexpr bool is_block() {
+  return EPI == Epi::W13Block || EPI == Epi::W2Block;
+}
 
 struct Params {
   const int8_t* a;
@@ -47,8 +63,8 @@ struct Params {
   const float* a_s;    // activation / intermediate scales
   const float* w_s;    // weight scales
   int32_t* out_i32;
-  float* out_f32;      // hf (first GEMM, channel) or y (second GEMM)
-  float* part_amax;    // [rows, n_tiles] per-tile row maxima (first GEMM, channel)
+  float* out_f32;      // fp32 h (first GEMM, channel) or y (second GEMM)
+  float* part_amax;    // [rows, n_tiles] per-tile row maxima of |h| (first GEMM, channel)
   int8_t* h_q;
   float* h_s;
 };
@@ -63,14 +79,187 @@ __device__ __forceinline__ int brow_of(int wn, int fn) {
   return (fn < FN / 2 ? 0 : BN / 2) + wn * (BN / 2 / WN) + (fn % (FN / 2)) * 16;
 }
 
+// Weight row of B-tile row br in N-tile nt.
+template <int BN, BMap MAP>
+__device__ __forceinline__ int64_t wrow_of(int64_t nt, int br, int64_t I) {
+  if (MAP == BMap::Plain) return nt * BN + br;
+  return br < BN / 2 ? nt * (BN / 2) + br : I + nt * (BN / 2) + (br - BN / 2);
+}
+
+// Block-wise: fold the int32 partials of K-block kb into the fp32 sums, in the
+// written order acc_f = acc_f + (((float)part * a_s) * w_s), and clear them.
+template <int BM, int BN, int WM, int WN, int FM, int FN, BMap MAP, Epi EPI>
+__device__ __forceinline__ void block_flush(const Params& p, i32x4 (&acc)[FM][FN], float (&accf)[FM][FN][4],
+                                            const int32_t* sh_pid, int64_t row0, int64_t nt, int64_t e, int wm,
+                                            int wn, int l, int64_t kb, int64_t nkb) {
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int trow = wm * (BM / WM) + fm * 16 + (l / 16) * 4 + r;
+      const int32_t pid = sh_pid[trow];
+      float as = 0.0f;
+      if (pid < p.P)
+        as = EPI == Epi::W13Block ? p.a_s[(int64_t)(pid / p.k) * nkb + kb] : p.a_s[(row0 + trow) * nkb + kb];
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        const int64_t wrow = wrow_of<BN, MAP>(nt, brow_of<BN, WN, FN, MAP>(wn, fn), p.I);
+        const float ws = p.w_s[(e * (p.N / 128) + wrow / 128) * nkb + kb];
+        accf[fm][fn][r] = accf[fm][fn][r] + (((float)acc[fm][fn][r] * as) * ws);
+      }
+    }
+  }
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = i32x4{0, 0, 0, 0};
+}
+
+// Epilogues.  Rows whose sh_pid is the sentinel (>= P) are skipped.
+template <int BM, int BN, int WM, int WN, int FM, int FN, BMap MAP, Epi EPI>
+__device__ __forceinline__ void epilogue(const Params& p, const i32x4 (&acc)[FM][FN], const float (&accf)[FM][FN][4],
+                                         const int32_t* sh_pid, float (*sh_red)[BM], int64_t row0, int64_t nt,
+                                         int64_t e, int wm, int wn, int l, int tid) {
+  constexpr int FNH = FN / 2;
+  constexpr bool kBlock = is_block<EPI>();
+  if constexpr (EPI == Epi::I32) {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int trow = wm * (BM / WM) + fm * 16 + (l / 16) * 4 + r;
+        if (sh_pid[trow] >= p.P) continue;
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+          p.out_i32[(row0 + trow) * p.N + nt * BN + brow_of<BN, WN, FN, MAP>(wn, fn) + (l % 16)] = acc[fm][fn][r];
+      }
+  } else if constexpr (EPI == Epi::W2Channel || EPI == Epi::W2Block) {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int trow = wm * (BM / WM) + fm * 16 + (l / 16) * 4 + r;
+        if (sh_pid[trow] >= p.P) continue;
+        const int64_t grow = row0 + trow;
+        const float hs = kBlock ? 0.0f : p.a_s[grow];
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+          const int64_t n = nt * BN + brow_of<BN, WN, FN, MAP>(wn, fn) + (l % 16);
+          float y;
+          if constexpr (kBlock)
+            y = accf[fm][fn][r];
+          else
+            y = ((float)acc[fm][fn][r] * hs) * p.w_s[e * p.N + n];
+          p.out_f32[grow * p.N + n] = y;
+        }
+      }
+  } else if constexpr (EPI == Epi::W13Channel) {
+    // First GEMM, channel-wise: SiLU(gate) * up stored as fp32 h, one fragment row at a time
+    // (few live registers), plus this tile's per-row maxima of |h|; the requant pass finishes
+    // each row once all its N-tiles are in.
+    const int64_t I = p.I;
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      float rmax[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int trow = wm * (BM / WM) + fm * 16 + (l / 16) * 4 + r;
+        const int32_t pid = sh_pid[trow];
+        const bool valid = pid < p.P;
+        const float as = valid ? p.a_s[pid / p.k] : 0.0f;
+        rmax[r] = 0.0f;
+#pragma unroll
+        for (int f = 0; f < FNH; ++f) {
+          const int64_t n = nt * (BN / 2) + brow_of<BN, WN, FN, MAP>(wn, f) + (l % 16);
+          const float g = ((float)acc[fm][f][r] * as) * p.w_s[e * 2 * I + n];
+          const float u = ((float)acc[fm][f + FNH][r] * as) * p.w_s[e * 2 * I + I + n];
+          const float h = silu_mul(g, u);
+          if (valid) {
+            p.out_f32[(row0 + trow) * I + n] = h;
+            rmax[r] = fmaxf(rmax[r], fabsf(h));
+          }
+        }
+      }
+      // reduce over the 16 lanes that share a row
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float m = rmax[r];
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+        if ((l % 16) == 0) sh_red[wn][wm * (BM / WM) + fm * 16 + (l / 16) * 4 + r] = m;
+      }
+    }
+    __syncthreads();
+    for (int i = tid; i < BM; i += kThreads) {
+      if (sh_pid[i] >= p.P) continue;
+      float m = sh_red[0][i];
+#pragma unroll
+      for (int w = 1; w < WN; ++w) m = fmaxf(m, sh_red[w][i]);
+      p.part_amax[(row0 + i) * p.n_tiles + nt] = m;
+    }
+  } else {
+    // First GEMM, block-wise: SiLU(gate) * up, then requantization in the tile, whose BN/2 = 128
+    // gate columns are exactly one 128-wide requant group.
+    const int64_t I = p.I;
+    float hf[FM][FNH][4];
+    float rmax[FM][4];
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int trow = wm * (BM / WM) + fm * 16 + (l / 16) * 4 + r;
+        const bool valid = sh_pid[trow] < p.P;
+        rmax[fm][r] = 0.0f;
+#pragma unroll
+        for (int f = 0; f < FNH; ++f) {
+          const float h = silu_mul(accf[fm][f][r], accf[fm][f + FNH][r]);
+          hf[fm][f][r] = h;
+          if (valid) rmax[fm][r] = fmaxf(rmax[fm][r], fabsf(h));
+        }
+      }
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float m = rmax[fm][r];
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+        if ((l % 16) == 0) sh_red[wn][wm * (BM / WM) + fm * 16 + (l / 16) * 4 + r] = m;
+      }
+    __syncthreads();
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int trow = wm * (BM / WM) + fm * 16 + (l / 16) * 4 + r;
+        if (sh_pid[trow] >= p.P) continue;
+        float m = sh_red[0][trow];
+#pragma unroll
+        for (int w = 1; w < WN; ++w) m = fmaxf(m, sh_red[w][trow]);
+        const float s = quant_scale(m);
+        const int64_t grow = row0 + trow;
+        if (wn == 0 && (l % 16) == 0) p.h_s[grow * (I / 128) + nt] = s;
+#pragma unroll
+        for (int f = 0; f < FNH; ++f)
+          p.h_q[grow * I + nt * (BN / 2) + brow_of<BN, WN, FN, MAP>(wn, f) + (l % 16)] = quant_value(hf[fm][f][r], s);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Staged engine: tiles of BM rows (BM divides block_m), BK = 128 bytes per stage, register-staged
+// global loads into a double-buffered, padded LDS tile.
+
+constexpr int kBK = 128;
+constexpr int kLdsStride = kBK + 16;  // padded LDS row (bytes)
+
 template <int BM, int BN, int WM, int WN, BMap MAP, Epi EPI>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const Params p) {
   constexpr int FM = BM / WM / 16;
   constexpr int FN = BN / WN / 16;
-  constexpr int FNH = FN / 2;
   constexpr int A_CH = (BM * 8 + kThreads - 1) / kThreads;
   constexpr int B_CH = BN * 8 / kThreads;
-  constexpr bool kBlock = EPI == Epi::W13Block || EPI == Epi::W2Block;
+  constexpr bool kBlock = is_block<EPI>();
   static_assert(WM * WN == kThreads / kWave, "4 wavefronts");
   static_assert(FM >= 1 && FN >= 1 && B_CH >= 1, "tile too small");
   static_assert(MAP == BMap::Plain || FN % 2 == 0, "split tiles need gate and up fragments");
@@ -110,12 +299,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const Params p) 
 #pragma unroll
   for (int c = 0; c < B_CH; ++c) {
     const int idx = tid + c * kThreads, j = idx / 8, part = idx % 8;
-    int64_t wrow;
-    if (MAP == BMap::Plain)
-      wrow = nt * BN + j;
-    else
-      wrow = j < BN / 2 ? nt * (BN / 2) + j : p.I + nt * (BN / 2) + (j - BN / 2);
-    b_src[c] = wexp + wrow * p.K + part * 16;
+    b_src[c] = wexp + wrow_of<BN, MAP>(nt, j, p.I) * p.K + part * 16;
   }
 
   i32x4 ra[A_CH], rb[B_CH];  // native vectors: HIP's uint4 struct would be copied through scratch
@@ -139,19 +323,15 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const Params p) 
   } while (0)
 
   i32x4 acc[FM][FN];
-  float accf[kBlock ? FM : 1][kBlock ? FN : 1][4];
+  float accf[FM][FN][4];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
-  if (kBlock) {
+    for (int j = 0; j < FN; ++j) {
+      acc[i][j] = i32x4{0, 0, 0, 0};
 #pragma unroll
-    for (int i = 0; i < (kBlock ? FM : 1); ++i)
-#pragma unroll
-      for (int j = 0; j < (kBlock ? FN : 1); ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) accf[i][j][r] = 0.0f;
-  }
+      for (int r = 0; r < 4; ++r) accf[i][j][r] = 0.0f;
+    }
 
   const int64_t KT = p.K / kBK;
   const int64_t nkb = p.K / 128;  // block-wise scale columns
@@ -178,158 +358,268 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const Params p) 
         for (int fn = 0; fn < FN; ++fn)
           acc[fm][fn] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[fm], bf[fn], acc[fm][fn], 0, 0, 0);
     }
-    if constexpr (kBlock) {
-      // Dequantize this K-block's integer partials and fold them into the fp32 sums.
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int trow = wm * (BM / WM) + fm * 16 + (l / 16) * 4 + r;
-          const int32_t pid = sh_pid[trow];
-          float as = 0.0f;
-          if (pid < p.P)
-            as = EPI == Epi::W13Block ? p.a_s[(int64_t)(pid / p.k) * nkb + kt] : p.a_s[(row0 + trow) * nkb + kt];
-#pragma unroll
-          for (int fn = 0; fn < FN; ++fn) {
-            const int br = brow_of<BN, WN, FN, MAP>(wn, fn);
-            int64_t wrow;
-            if (MAP == BMap::Plain)
-              wrow = nt * BN + br;
-            else
-              wrow = br < BN / 2 ? nt * (BN / 2) + br : p.I + nt * (BN / 2) + (br - BN / 2);
-            const float ws = p.w_s[(e * (p.N / 128) + wrow / 128) * nkb + kt];
-            accf[fm][fn][r] = accf[fm][fn][r] + (((float)acc[fm][fn][r] * as) * ws);
-          }
-        }
-      }
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = i32x4{0, 0, 0, 0};
-    }
+    if constexpr (kBlock)
+      block_flush<BM, BN, WM, WN, FM, FN, MAP, EPI>(p, acc, accf, sh_pid, row0, nt, e, wm, wn, l, kt, nkb);
     if (kt + 1 < KT) W8A8_SSTORE(buf ^ 1);
     __syncthreads();
   }
+#undef W8A8_GLOAD
+#undef W8A8_SSTORE
+  epilogue<BM, BN, WM, WN, FM, FN, MAP, EPI>(p, acc, accf, sh_pid, sh_red, row0, nt, e, wm, wn, l, tid);
+}
 
-  // ---------------------------------------------------------------- epilogues
-  // Accumulator element r of fragment (fm, fn) sits at tile row
-  // wm*(BM/WM) + fm*16 + (l/16)*4 + r and tile column brow_of<BN, WN, FN, MAP>(wn, fn) + l%16.
-  if constexpr (EPI == Epi::I32) {
+// ---------------------------------------------------------------------------------------------
+// DMA engine.
+
+constexpr int kWorkFields = 5;  // ints per work-list tile
+constexpr int kDmaBK = 128;  // K bytes per LDS stage: two MFMA K-steps, whole 128-byte L2 lines
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// s_waitcnt immediate (gfx9 encoding) waiting until at most n vector-memory operations of this
+// wavefront are outstanding, without waiting on LDS or export counters.
+template <int n>
+constexpr int vmcnt_imm() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14);
+}
+constexpr int kLgkm0Imm = 15 | (7 << 4) | (0 << 8) | (3 << 14);  // lgkmcnt(0) only
+
+// Workgroup barrier without a memory fence: LDS data written by the DMA is published by the
+// explicit vmcnt wait that precedes it, and a fence would drain every stage still in flight.
+// The "memory" clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
+
+// One 16-byte-per-lane DMA (global_load_lds_dwordx4): lane i's 16 bytes land at lds + 16 i.
+// (A plain device function: calling the builtin directly inside the kernel template kept the
+// host compiler from emitting the kernel's launch stub.)
+__device__ __forceinline__ void dma16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds, 16, 0, 0);
+}
+
+// 16-byte chunk swizzle of a 128-byte LDS row: chunk c of row r sits in slot c ^ ((r >> 1) & 7).
+// Sixteen consecutive rows reading the same chunk then hit sixteen different 16-byte bank groups
+// of a 256-byte window.
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+
+// LDS byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) void*)p);
+}
+
+// One stage (128 bytes of K = two MFMA K-steps) of the DMA engine: fragment reads, then
+// 2 x FM x FN MFMAs.  The rows of a fragment are 16-aligned, so swz(row) = swz(fr): each fragment
+// of a lane sits at a fixed offset from the lane's fragment-0 address.
+template <int BM, int BN, int FM, int FN, BMap MAP>
+__device__ __forceinline__ void dma_mfma_stage(const int8_t* stage, i32x4 (&acc)[FM][FN], int wn, int g, int fr) {
+  constexpr int WN = 4;
+#pragma unroll
+  for (int kk = 0; kk < kDmaBK / 64; ++kk) {
+    const int lane = fr * kDmaBK + (((kk * 4 + g) ^ swz(fr)) << 4);
+    const int8_t* As = stage + lane;
+    const int8_t* Bs = stage + BM * kDmaBK + lane;
+    i32x4 af[FM], bf[FN];
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) af[fm] = *reinterpret_cast<const i32x4*>(As + fm * 16 * kDmaBK);
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+      bf[fn] = *reinterpret_cast<const i32x4*>(Bs + brow_of<BN, WN, FN, MAP>(wn, fn) * kDmaBK);
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int trow = wm * (BM / WM) + fm * 16 + (l / 16) * 4 + r;
-        if (sh_pid[trow] >= p.P) continue;
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
-          p.out_i32[(row0 + trow) * p.N + nt * BN + brow_of<BN, WN, FN, MAP>(wn, fn) + (l % 16)] = acc[fm][fn][r];
-      }
-  } else if constexpr (EPI == Epi::W2Channel || EPI == Epi::W2Block) {
-#pragma unroll
-    for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int trow = wm * (BM / WM) + fm * 16 + (l / 16) * 4 + r;
-        if (sh_pid[trow] >= p.P) continue;
-        const int64_t grow = row0 + trow;
-        const float hs = kBlock ? 0.0f : p.a_s[grow];
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn) {
-          const int64_t n = nt * BN + brow_of<BN, WN, FN, MAP>(wn, fn) + (l % 16);
-          float y;
-          if constexpr (kBlock)
-            y = accf[fm][fn][r];
-          else
-            y = ((float)acc[fm][fn][r] * hs) * p.w_s[e * p.N + n];
-          p.out_f32[grow * p.N + n] = y;
-        }
-      }
-  } else {
-    // First GEMM: SiLU(gate) * up, then the row maxima of |h|.
-    const int64_t I = p.I;
-    float hf[FM][FNH][4];
-    float rmax[FM][4];
-#pragma unroll
-    for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int trow = wm * (BM / WM) + fm * 16 + (l / 16) * 4 + r;
-        const int32_t pid = sh_pid[trow];
-        const bool valid = pid < p.P;
-        const float as = (!kBlock && valid) ? p.a_s[pid / p.k] : 0.0f;
-        rmax[fm][r] = 0.0f;
-#pragma unroll
-        for (int f = 0; f < FNH; ++f) {
-          const int64_t n = nt * (BN / 2) + brow_of<BN, WN, FN, MAP>(wn, f) + (l % 16);
-          float g, u;
-          if constexpr (kBlock) {
-            g = accf[fm][f][r];
-            u = accf[fm][f + FNH][r];
-          } else {
-            g = ((float)acc[fm][f][r] * as) * p.w_s[e * 2 * I + n];
-            u = ((float)acc[fm][f + FNH][r] * as) * p.w_s[e * 2 * I + I + n];
-          }
-          const float h = silu_mul(g, u);
-          hf[fm][f][r] = h;
-          if (valid) rmax[fm][r] = fmaxf(rmax[fm][r], fabsf(h));
-        }
-      }
-    // reduce over the 16 lanes that share a row, then over the WN wavefronts
-#pragma unroll
-    for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float m = rmax[fm][r];
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
-        if ((l % 16) == 0) sh_red[wn][wm * (BM / WM) + fm * 16 + (l / 16) * 4 + r] = m;
-      }
-    __syncthreads();
-    if constexpr (EPI == Epi::W13Channel) {
-      // write h (fp32) and this tile's row maxima; the requant pass finishes the row
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int trow = wm * (BM / WM) + fm * 16 + (l / 16) * 4 + r;
-          if (sh_pid[trow] >= p.P) continue;
-#pragma unroll
-          for (int f = 0; f < FNH; ++f)
-            p.out_f32[(row0 + trow) * I + nt * (BN / 2) + brow_of<BN, WN, FN, MAP>(wn, f) + (l % 16)] = hf[fm][f][r];
-        }
-      for (int i = tid; i < BM; i += kThreads) {
-        if (sh_pid[i] >= p.P) continue;
-        float m = sh_red[0][i];
-#pragma unroll
-        for (int w = 1; w < WN; ++w) m = fmaxf(m, sh_red[w][i]);
-        p.part_amax[(row0 + i) * p.n_tiles + nt] = m;
-      }
-    } else {
-      // block-wise: this tile's BN/2 = 128 gate columns are exactly one requant group
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int trow = wm * (BM / WM) + fm * 16 + (l / 16) * 4 + r;
-          if (sh_pid[trow] >= p.P) continue;
-          float m = sh_red[0][trow];
-#pragma unroll
-          for (int w = 1; w < WN; ++w) m = fmaxf(m, sh_red[w][trow]);
-          const float s = quant_scale(m);
-          const int64_t grow = row0 + trow;
-          if (wn == 0 && (l % 16) == 0) p.h_s[grow * (I / 128) + nt] = s;
-#pragma unroll
-          for (int f = 0; f < FNH; ++f)
-            p.h_q[grow * I + nt * (BN / 2) + brow_of<BN, WN, FN, MAP>(wn, f) + (l % 16)] = quant_value(hf[fm][f][r], s);
-        }
-    }
+      for (int fn = 0; fn < FN; ++fn)
+        acc[fm][fn] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[fm], bf[fn], acc[fm][fn], 0, 0, 0);
   }
 }
 
-#undef W8A8_GLOAD
-#undef W8A8_SSTORE
+// S stages, each its own LDS array, and the K loop (KT steps, a compile-time count) fully
+// unrolled: with every stage index known the compiler tells the buffer being read from the S - 1
+// buffers the DMA is still filling, adds no drain of its own and interleaves the fragment reads
+// with the MFMAs.
+template <int BM, int BN, int KT, int S, BMap MAP, Epi EPI>
+__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(const Params p,
+                                                                      const int32_t* __restrict__ work) {
+  constexpr int WM = 1, WN = 4;
+  constexpr int FM = BM / 16;
+  constexpr int FN = BN / WN / 16;
+  constexpr int CPR = kDmaBK / 16;          // 16-byte chunks per row and stage
+  constexpr int A_LD = BM * CPR / kThreads;  // DMA instructions per thread per stage (A tile)
+  constexpr int B_LD = BN * CPR / kThreads;  // (B tile)
+  constexpr int LD = A_LD + B_LD;
+  constexpr int STAGE = (BM + BN) * kDmaBK;
+  constexpr bool kBlock = is_block<EPI>();
+  static_assert(A_LD >= 1 && B_LD >= 1 && (BM * CPR) % kThreads == 0 && (BN * CPR) % kThreads == 0, "tile shape");
+  static_assert(S >= 3 && S <= 6 && (S - 2) * LD < 64, "stages");
+  static_assert(KT >= S, "K steps");
+  static_assert(MAP == BMap::Plain || FN % 2 == 0, "split tiles need gate and up fragments");
 
+  __shared__ __attribute__((aligned(1024))) int8_t st0[STAGE];
+  __shared__ __attribute__((aligned(1024))) int8_t st1[STAGE];
+  __shared__ __attribute__((aligned(1024))) int8_t st2[STAGE];
+  __shared__ __attribute__((aligned(1024))) int8_t st3[S > 3 ? STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) int8_t st4[S > 4 ? STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) int8_t st5[S > 5 ? STAGE : 16];
+  __shared__ int32_t sh_pid[BM];
+  __shared__ float sh_red[WN][BM];
+
+  // Work order: expert-major, then N-tile, then the expert's row tiles, so the row tiles that share
+  // a weight tile run side by side and the weights come from HBM once.  XCD-aware: workgroups are
+  // dispatched round-robin over the 8 XCDs; each XCD gets a contiguous stretch of that order.
+  const int64_t total = (int64_t)work[0] * p.n_tiles;
+  const int64_t per = (total + 7) / 8;
+  const int64_t v = blockIdx.x;
+  if (v >= 8 * per) return;
+  const int64_t logical = (v % 8) * per + v / 8;
+  if (logical >= total) return;
+  const int32_t* any = work + 1 + kWorkFields * (logical / p.n_tiles);  // a tile of the same expert
+  const int64_t first = any[3], count = any[4];
+  const int64_t local = logical - p.n_tiles * first;
+  const int64_t nt = local / count, ti = first + local % count;
+  const int64_t e = work[1 + kWorkFields * ti];
+  const int64_t row0 = work[2 + kWorkFields * ti];
+  const int nrows = work[3 + kWorkFields * ti];
+  const int8_t* wexp = p.w + e * p.N * p.K;
+
+  const int tid = threadIdx.x, l = lane_id(), wn = tid / kWave;
+  for (int i = tid; i < BM; i += kThreads) sh_pid[i] = i < nrows ? p.sorted[row0 + i] : (int32_t)p.P;
+
+  // Sources of this thread's DMA chunks: stage region chunk q holds row q/CPR, K-chunk (q%CPR)^swz(row).
+  const int8_t* a_src[A_LD];
+  const int8_t* b_src[B_LD];
+#pragma unroll
+  for (int c = 0; c < A_LD; ++c) {
+    const int q = (wn * A_LD + c) * kWave + l, r = q / CPR, kc = (q % CPR) ^ swz(r);
+    const int8_t* row = p.a;  // rows past the tile read row 0 (their results are never stored)
+    if (r < nrows) {
+      const int32_t pid = p.sorted[row0 + r];
+      row = p.gather ? p.a + (int64_t)(pid / p.k) * p.K : p.a + (row0 + r) * p.K;
+    }
+    a_src[c] = row + kc * 16;
+  }
+#pragma unroll
+  for (int c = 0; c < B_LD; ++c) {
+    const int q = (wn * B_LD + c) * kWave + l, j = q / CPR, kc = (q % CPR) ^ swz(j);
+    b_src[c] = wexp + wrow_of<BN, MAP>(nt, j, p.I) * p.K + kc * 16;
+  }
+
+  i32x4 acc[FM][FN];
+  float accf[FM][FN][4];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      acc[i][j] = i32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) accf[i][j][r] = 0.0f;
+    }
+
+  const int64_t nkb = p.K / 128;
+  const int g = l >> 4, fr = l & 15;
+
+#define W8A8_STAGE(j) \
+  ((j) == 0 ? st0 : (j) == 1 ? st1 : (j) == 2 ? st2 : (j) == 3 ? st3 : (j) == 4 ? st4 : st5)
+#define W8A8_DMA(st, j)                                                                                        \
+  do {                                                                                                         \
+    int8_t* base_ = W8A8_STAGE(j);                                                                             \
+    _Pragma("unroll") for (int c = 0; c < A_LD; ++c)                                                           \
+        dma16(a_src[c] + (int64_t)(st) * kDmaBK, base_ + (wn * A_LD + c) * 1024);                              \
+    _Pragma("unroll") for (int c = 0; c < B_LD; ++c)                                                           \
+        dma16(b_src[c] + (int64_t)(st) * kDmaBK, base_ + BM * kDmaBK + (wn * B_LD + c) * 1024);                \
+  } while (0)
+
+  // Prologue: stages 0 .. S-2 in flight, then wait for stage 0.
+#pragma unroll
+  for (int st = 0; st < S - 1; ++st) W8A8_DMA(st, st);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm<(S - 2) * LD>());
+
+  // K-step kt reads stage buffer kt % S (landed) and refills the buffer of step kt - 1 with step
+  // kt + S - 1; at its end it waits until step kt + 1 has landed (stages issued after it may stay
+  // in flight).  All indices are compile-time after unrolling.
+#pragma clang loop unroll(full)
+  for (int kt = 0; kt < KT; ++kt) {
+    __builtin_amdgcn_s_waitcnt(kLgkm0Imm);
+    barrier_no_fence();
+    if (kt + S - 1 < KT) W8A8_DMA(kt + S - 1, (kt + S - 1) % S);
+    dma_mfma_stage<BM, BN, FM, FN, MAP>(W8A8_STAGE(kt % S), acc, wn, g, fr);
+    if constexpr (kBlock)
+      block_flush<BM, BN, WM, WN, FM, FN, MAP, EPI>(p, acc, accf, sh_pid, row0, nt, e, 0, wn, l, kt, nkb);
+    const int ahead = (KT - 1 < kt + S - 1 ? KT - 1 : kt + S - 1) - (kt + 1);  // stages issued after kt + 1
+    if (ahead >= 4)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm<(S - 2 >= 4 ? 4 : 0) * LD>());
+    else if (ahead == 3)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm<3 * LD>());
+    else if (ahead == 2)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm<2 * LD>());
+    else if (ahead == 1)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm<LD>());
+    else if (ahead == 0)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
+  }
+#undef W8A8_DMA
+#undef W8A8_STAGE
+  __syncthreads();
+  epilogue<BM, BN, WM, WN, FM, FN, MAP, EPI>(p, acc, accf, sh_pid, sh_red, row0, nt, e, 0, wn, l, tid);
+}
+
+// Work list of the DMA engine: per expert, tiles of up to bmk real rows of its sorted segment.
+// work[0] = number of tiles; tile i = (expert, first sorted row, rows, index of the expert's
+// first tile, number of the expert's tiles) at work[1 + kWorkFields * i].
+constexpr int kListThreads = 1024;
+
+__device__ int list_exclusive_scan(int v, int* wsum, int& total) {
+  const int l = lane_id(), w = threadIdx.x / kWave;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(x, o, kWave);
+    if (l >= o) x += y;
+  }
+  if (l == kWave - 1) wsum[w] = x;
+  __syncthreads();
+  int before = 0;
+  total = 0;
+  for (int i = 0; i < kListThreads / kWave; ++i) {
+    if (i < w) before += wsum[i];
+    total += wsum[i];
+  }
+  __syncthreads();
+  return before + x - v;
+}
+
+__global__ __launch_bounds__(kListThreads) void build_tiles_kernel(const int32_t* __restrict__ sorted,
+                                                                   const int32_t* __restrict__ padded_offsets, int E,
+                                                                   int32_t P, int bmk, int32_t* __restrict__ work) {
+  __shared__ int wsum[kListThreads / kWave];
+  const int e = threadIdx.x;
+  int cnt = 0, seg = 0;
+  if (e < E) {
+    // real rows are the prefix of the segment below the sentinel P
+    seg = padded_offsets[e];
+    int lo = seg, hi = padded_offsets[e + 1];
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (sorted[mid] < P)
+        lo = mid + 1;
+      else
+        hi = mid;
+    }
+    cnt = lo - seg;
+  }
+  const int tiles = (cnt + bmk - 1) / bmk;
+  int total;
+  const int off = list_exclusive_scan(tiles, wsum, total);
+  for (int i = 0; i < tiles; ++i) {
+    int32_t* t = work + 1 + kWorkFields * (off + i);
+    t[0] = e;
+    t[1] = seg + i * bmk;
+    t[2] = min(bmk, cnt - i * bmk);
+    t[3] = off;
+    t[4] = tiles;
+  }
+  if (e == 0) work[0] = total;
+}
+
+// ---------------------------------------------------------------------------------------------
 // Channel-wise requantization of the first GEMM's rows: one wavefront per row.
 __global__ __launch_bounds__(kThreads) void requant_rows_kernel(const float* __restrict__ hf,
                                                                 const float* __restrict__ part_amax,
@@ -393,42 +683,81 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float* __restri
 
 size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 
+// ---------------------------------------------------------------------------------------------
+// Engine choice and launches.
+
+constexpr int kBNStaged = 128;   // staged engine: 64 gate + 64 up rows, or 128 output columns
+constexpr int kBNBlock13 = 256;  // staged block-wise first GEMM: 128 gate + 128 up rows (one requant group)
+constexpr int kDmaBM = 128;
+constexpr int kDmaBN = 256;      // DMA engine: 128 gate + 128 up rows, or 256 output columns
+constexpr int kDmaStages = 3;    // LDS ring depth: 2 stages of 48 KB in flight
+
+// The DMA engine pays off once experts hold several MFMA tiles of rows.  Its K loop is unrolled
+// for a compile-time K: instantiated for hidden 7168 and intermediate 2048 (the DeepSeek-V3 layer);
+// other shapes run on the staged engine.
+constexpr int kDmaH = 7168, kDmaI = 2048;
+bool use_dma(const GroupedShape& s) { return s.T * s.k >= 64 * s.E && s.H == kDmaH && s.I == kDmaI; }
+
+int64_t dma_max_tiles(const GroupedShape& s) {
+  const int64_t P = s.T * s.k;
+  return (P + kDmaBM - 1) / kDmaBM + std::min<int64_t>(s.E, P);
+}
+
+size_t work_bytes(const GroupedShape& s) {
+  return round256(sizeof(int32_t) * (size_t)(1 + kWorkFields * dma_max_tiles(s)));
+}
+
+// N-tiles of the first GEMM (one row maximum each per row).
+int64_t w13_n_tiles(const GroupedShape& s, int32_t scale_mode) {
+  if (scale_mode == 1) return s.I / (kBNBlock13 / 2);
+  return use_dma(s) ? s.I / (kDmaBN / 2) : s.I / (kBNStaged / 2);
+}
+
 template <int BM, int BN, int WM, int WN, BMap MAP, Epi EPI>
-hipError_t launch(const Params& prm, int64_t max_rows, hipStream_t stream) {
-  const int64_t mtiles = max_rows / BM;
-  const int64_t grid = mtiles * prm.n_tiles;
+hipError_t launch_staged(const Params& prm, int64_t max_rows, hipStream_t stream) {
+  const int64_t grid = (max_rows / BM) * prm.n_tiles;
   if (grid == 0) return hipSuccess;
   hipLaunchKernelGGL((grouped_gemm_kernel<BM, BN, WM, WN, MAP, EPI>), dim3((uint32_t)grid), dim3(kThreads), 0,
                      stream, prm);
   return hipGetLastError();
 }
 
-// Tile height of the kernel for a given align block_m (a divisor of block_m).
+// Staged engine, tile height = block_m (64 for the block-wise first GEMM's 128-row tiles).
 template <BMap MAP, Epi EPI, int BN>
 hipError_t launch_bm(Params prm, int64_t max_rows, hipStream_t stream) {
   prm.n_tiles = MAP == BMap::Plain ? prm.N / BN : prm.I / (BN / 2);
   switch (prm.block_m) {
-    case 16: return launch<16, BN, 1, 4, MAP, EPI>(prm, max_rows, stream);
-    case 32: return launch<32, BN, 1, 4, MAP, EPI>(prm, max_rows, stream);
-    case 64: return launch<64, BN, 2, 2, MAP, EPI>(prm, max_rows, stream);
-    default: return launch<(EPI == Epi::W13Block ? 64 : 128), BN, 2, 2, MAP, EPI>(prm, max_rows, stream);
+    case 16: return launch_staged<16, BN, 1, 4, MAP, EPI>(prm, max_rows, stream);
+    case 32: return launch_staged<32, BN, 1, 4, MAP, EPI>(prm, max_rows, stream);
+    case 64: return launch_staged<64, BN, 2, 2, MAP, EPI>(prm, max_rows, stream);
+    default: return launch_staged<(EPI == Epi::W13Block ? 64 : 128), BN, 2, 2, MAP, EPI>(prm, max_rows, stream);
   }
 }
 
-constexpr int kBNChannel = 128;  // first GEMM: 64 gate + 64 up rows; second GEMM: 128 output columns
-constexpr int kBNBlock13 = 256;  // block-wise first GEMM: 128 gate + 128 up rows (one requant group)
+template <BMap MAP, Epi EPI, int K>
+hipError_t launch_dma(Params prm, const GroupedShape& s, const int32_t* padded_offsets, int32_t* work,
+                      hipStream_t stream) {
+  prm.n_tiles = MAP == BMap::Plain ? prm.N / kDmaBN : prm.I / (kDmaBN / 2);
+  hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(kListThreads), 0, stream, prm.sorted, padded_offsets,
+                     (int)s.E, (int32_t)prm.P, kDmaBM, work);
+  const int64_t grid = (dma_max_tiles(s) * prm.n_tiles + 7) / 8 * 8;
+  hipLaunchKernelGGL((grouped_gemm_dma_kernel<kDmaBM, kDmaBN, K / kDmaBK, kDmaStages, MAP, EPI>), dim3((uint32_t)grid),
+                     dim3(kThreads), 0, stream, prm, (const int32_t*)work);
+  return hipGetLastError();
+}
 
 }  // namespace
 
 size_t w13_ws_bytes(const GroupedShape& s, int32_t scale_mode) {
   if (scale_mode == 1) return 256;
-  const int64_t n_tiles = s.I / (kBNChannel / 2);
-  return round256(sizeof(float) * (size_t)(s.max_rows * s.I)) + round256(sizeof(float) * (size_t)(s.max_rows * n_tiles));
+  return round256(sizeof(float) * (size_t)(s.max_rows * s.I)) +
+         round256(sizeof(float) * (size_t)(s.max_rows * w13_n_tiles(s, scale_mode))) + work_bytes(s);
 }
 
 size_t w2_ws_bytes(const GroupedShape& s, int32_t scale_mode) {
   (void)scale_mode;
-  return round256(sizeof(float) * (size_t)(s.max_rows * s.H)) + round256(sizeof(int32_t) * (size_t)(s.T * s.k));
+  return round256(sizeof(float) * (size_t)(s.max_rows * s.H)) + round256(sizeof(int32_t) * (size_t)(s.T * s.k)) +
+         work_bytes(s);
 }
 
 hipError_t gemm_i32(const int8_t* a, int32_t gather, const int8_t* w, int64_t N, int64_t K, const int32_t* sorted,
@@ -447,12 +776,13 @@ hipError_t gemm_i32(const int8_t* a, int32_t gather, const int8_t* w, int64_t N,
   prm.k = k;
   prm.block_m = block_m;
   prm.out_i32 = out;
-  return launch_bm<BMap::Plain, Epi::I32, kBNChannel>(prm, max_rows, stream);
+  return launch_bm<BMap::Plain, Epi::I32, kBNStaged>(prm, max_rows, stream);
 }
 
 hipError_t w13_silu(const GroupedShape& s, int32_t scale_mode, const int8_t* a_q, const float* a_s,
-                    const int8_t* w13, const float* w13_s, const int32_t* sorted, const int32_t* tile_expert,
-                    const int32_t* num_tiles, int8_t* h_q, float* h_s, void* ws, hipStream_t stream) {
+                    const int8_t* w13, const float* w13_s, const int32_t* sorted, const int32_t* padded_offsets,
+                    const int32_t* tile_expert, const int32_t* num_tiles, int8_t* h_q, float* h_s, void* ws,
+                    hipStream_t stream) {
   Params prm{};
   prm.a = a_q;
   prm.gather = 1;
@@ -471,13 +801,17 @@ hipError_t w13_silu(const GroupedShape& s, int32_t scale_mode, const int8_t* a_q
   prm.h_q = h_q;
   prm.h_s = h_s;
   if (scale_mode == 1) return launch_bm<BMap::Split, Epi::W13Block, kBNBlock13>(prm, s.max_rows, stream);
-  float* hf = static_cast<float*>(ws);
-  float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + round256(sizeof(float) * (size_t)(s.max_rows * s.I)));
+  char* base = static_cast<char*>(ws);
+  const int64_t n_tiles = w13_n_tiles(s, scale_mode);
+  float* hf = reinterpret_cast<float*>(base);
+  float* part = reinterpret_cast<float*>(base + round256(sizeof(float) * (size_t)(s.max_rows * s.I)));
+  int32_t* work = reinterpret_cast<int32_t*>(base + round256(sizeof(float) * (size_t)(s.max_rows * s.I)) +
+                                             round256(sizeof(float) * (size_t)(s.max_rows * n_tiles)));
   prm.out_f32 = hf;
   prm.part_amax = part;
-  hipError_t err = launch_bm<BMap::Split, Epi::W13Channel, kBNChannel>(prm, s.max_rows, stream);
+  hipError_t err = use_dma(s) ? launch_dma<BMap::Split, Epi::W13Channel, kDmaH>(prm, s, padded_offsets, work, stream)
+                              : launch_bm<BMap::Split, Epi::W13Channel, kBNStaged>(prm, s.max_rows, stream);
   if (err != hipSuccess) return err;
-  const int64_t n_tiles = s.I / (kBNChannel / 2);
   const int64_t blocks = (s.max_rows + kThreads / kWave - 1) / (kThreads / kWave);
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL(requant_rows_kernel, dim3((uint32_t)blocks), dim3(kThreads), 0, stream, hf, part, sorted,
@@ -486,13 +820,16 @@ hipError_t w13_silu(const GroupedShape& s, int32_t scale_mode, const int8_t* a_q
 }
 
 hipError_t w2_combine(const GroupedShape& s, int32_t scale_mode, const int8_t* h_q, const float* h_s,
-                      const int8_t* w2, const float* w2_s, const int32_t* sorted, const int32_t* tile_expert,
-                      const int32_t* num_tiles, const float* topk_w, float* out, void* ws, hipStream_t stream) {
+                      const int8_t* w2, const float* w2_s, const int32_t* sorted, const int32_t* padded_offsets,
+                      const int32_t* tile_expert, const int32_t* num_tiles, const float* topk_w, float* out,
+                      void* ws, hipStream_t stream) {
   if (s.T == 0) return hipSuccess;
   const int64_t P = s.T * s.k;
-  float* y = static_cast<float*>(ws);
-  int32_t* pair_row =
-      reinterpret_cast<int32_t*>(static_cast<char*>(ws) + round256(sizeof(float) * (size_t)(s.max_rows * s.H)));
+  char* base = static_cast<char*>(ws);
+  float* y = reinterpret_cast<float*>(base);
+  int32_t* pair_row = reinterpret_cast<int32_t*>(base + round256(sizeof(float) * (size_t)(s.max_rows * s.H)));
+  int32_t* work = reinterpret_cast<int32_t*>(base + round256(sizeof(float) * (size_t)(s.max_rows * s.H)) +
+                                             round256(sizeof(int32_t) * (size_t)P));
   Params prm{};
   prm.a = h_q;
   prm.gather = 0;
@@ -508,8 +845,13 @@ hipError_t w2_combine(const GroupedShape& s, int32_t scale_mode, const int8_t* h
   prm.a_s = h_s;
   prm.w_s = w2_s;
   prm.out_f32 = y;
-  hipError_t err = scale_mode == 1 ? launch_bm<BMap::Plain, Epi::W2Block, kBNChannel>(prm, s.max_rows, stream)
-                                   : launch_bm<BMap::Plain, Epi::W2Channel, kBNChannel>(prm, s.max_rows, stream);
+  hipError_t err;
+  if (scale_mode == 1)
+    err = launch_bm<BMap::Plain, Epi::W2Block, kBNStaged>(prm, s.max_rows, stream);
+  else if (use_dma(s))
+    err = launch_dma<BMap::Plain, Epi::W2Channel, kDmaI>(prm, s, padded_offsets, work, stream);
+  else
+    err = launch_bm<BMap::Plain, Epi::W2Channel, kBNStaged>(prm, s.max_rows, stream);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(fill_i32_kernel, dim3((uint32_t)((P + kThreads - 1) / kThreads)), dim3(kThreads), 0, stream,
                      pair_row, P, -1);

@@ -34,10 +34,12 @@ hipError_t gemm_i32(const int8_t* a, int32_t gather, const int8_t* w, int64_t N,
                     const int32_t* tile_expert, const int32_t* num_tiles, int64_t P, int64_t k, int64_t block_m,
                     int64_t max_rows, int32_t* out, hipStream_t stream);
 hipError_t w13_silu(const GroupedShape& s, int32_t scale_mode, const int8_t* a_q, const float* a_s,
-                    const int8_t* w13, const float* w13_s, const int32_t* sorted, const int32_t* tile_expert,
-                    const int32_t* num_tiles, int8_t* h_q, float* h_s, void* ws, hipStream_t stream);
+                    const int8_t* w13, const float* w13_s, const int32_t* sorted, const int32_t* padded_offsets,
+                    const int32_t* tile_expert, const int32_t* num_tiles, int8_t* h_q, float* h_s, void* ws,
+                    hipStream_t stream);
 hipError_t w2_combine(const GroupedShape& s, int32_t scale_mode, const int8_t* h_q, const float* h_s,
-                      const int8_t* w2, const float* w2_s, const int32_t* sorted, const int32_t* tile_expert,
-                      const int32_t* num_tiles, const float* topk_w, float* out, void* ws, hipStream_t stream);
+                      const int8_t* w2, const float* w2_s, const int32_t* sorted, const int32_t* padded_offsets,
+                      const int32_t* tile_expert, const int32_t* num_tiles, const float* topk_w, float* out,
+                      void* ws, hipStream_t stream);
 
 }  // namespace w8a8
