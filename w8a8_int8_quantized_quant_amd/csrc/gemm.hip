@@ -190,7 +190,7 @@ __device__ __forceinline__ void epilogue(const Params& p, const i32x4 (&acc)[FM]
       }
     }
     __syncthreads();
-    for (int i = tid; i < BM; i += kThreads) {
+    for (int i = tid; i < BM; i += WM * WN * kWave) {
       if (sh_pid[i] >= p.P) continue;
       float m = sh_red[0][i];
 #pragma unroll
@@ -407,58 +407,65 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) void*)p);
 }
 
-// One stage (128 bytes of K = two MFMA K-steps) of the DMA engine: fragment reads, then
-// 2 x FM x FN MFMAs.  The rows of a fragment are 16-aligned, so swz(row) = swz(fr): each fragment
-// of a lane sits at a fixed offset from the lane's fragment-0 address.
-template <int BM, int BN, int FM, int FN, BMap MAP>
-__device__ __forceinline__ void dma_mfma_stage(const int8_t* stage, i32x4 (&acc)[FM][FN], int wn, int g, int fr) {
-  constexpr int WN = 4;
+// The DMA engine's K loop.  Each stage holds 128 bytes of K (two MFMA K-steps) for BM A rows and
+// BN B rows.  A wavefront works through its stage in groups (K-step kk, fragment row fm) of FN
+// MFMAs and issues the next stage's DMA instructions between the groups, one per STRIDE groups, so
+// the memory pipe is fed for the whole stage instead of in a burst that stalls the MFMAs behind
+// it.  Scheduling barriers keep the compiler from regrouping them.
+template <int BM, int BN, int WM, int WN, int LD, BMap MAP>
+__device__ __forceinline__ void dma_stage(const int8_t* stage, int8_t* next, const int8_t* const (&src)[LD],
+                                          const int (&dst)[LD], int64_t next_off, bool prefetch,
+                                          i32x4 (&acc)[BM / WM / 16][BN / WN / 16], int wm, int wn, int g,
+                                          int fr, int rows) {
+  constexpr int FM = BM / WM / 16, FN = BN / WN / 16;
+  constexpr int GROUPS = (kDmaBK / 64) * FM;
+  constexpr int STRIDE = GROUPS / LD;
+  static_assert(STRIDE >= 1 && GROUPS % LD == 0, "DMA slots");
 #pragma unroll
   for (int kk = 0; kk < kDmaBK / 64; ++kk) {
     const int lane = fr * kDmaBK + (((kk * 4 + g) ^ swz(fr)) << 4);
-    const int8_t* As = stage + lane;
-    const int8_t* Bs = stage + BM * kDmaBK + lane;
     i32x4 af[FM], bf[FN];
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm) af[fm] = *reinterpret_cast<const i32x4*>(As + fm * 16 * kDmaBK);
+    for (int fm = 0; fm < FM; ++fm)
+      af[fm] = *reinterpret_cast<const i32x4*>(stage + lane + (wm * FM + fm) * 16 * kDmaBK);
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn)
-      bf[fn] = *reinterpret_cast<const i32x4*>(Bs + brow_of<BN, WN, FN, MAP>(wn, fn) * kDmaBK);
+      bf[fn] = *reinterpret_cast<const i32x4*>(stage + BM * kDmaBK + lane + brow_of<BN, WN, FN, MAP>(wn, fn) * kDmaBK);
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm)
+    for (int fm = 0; fm < FM; ++fm) {
+      const int grp = kk * FM + fm;
+      if (grp % STRIDE == 0 && prefetch) dma16(src[grp / STRIDE] + next_off, next + dst[grp / STRIDE]);
+      if (fm * 16 < rows) {  // fragment rows past the tile's real rows are never stored
 #pragma unroll
-      for (int fn = 0; fn < FN; ++fn)
-        acc[fm][fn] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[fm], bf[fn], acc[fm][fn], 0, 0, 0);
+        for (int fn = 0; fn < FN; ++fn)
+          acc[fm][fn] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[fm], bf[fn], acc[fm][fn], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 }
 
-// S stages, each its own LDS array, and the K loop (KT steps, a compile-time count) fully
-// unrolled: with every stage index known the compiler tells the buffer being read from the S - 1
-// buffers the DMA is still filling, adds no drain of its own and interleaves the fragment reads
-// with the MFMAs.
-template <int BM, int BN, int KT, int S, BMap MAP, Epi EPI>
-__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(const Params p,
-                                                                      const int32_t* __restrict__ work) {
-  constexpr int WM = 1, WN = 4;
-  constexpr int FM = BM / 16;
+// BM x BN tiles on WM x WN wavefronts (two per SIMD), two LDS stages: while the MFMAs read one,
+// the DMA fills the other.  The K loop (KT steps, a compile-time count) is fully unrolled so every
+// stage index is known and the compiler tells the buffer being read from the one being filled.
+template <int BM, int BN, int WM, int WN, int KT, BMap MAP, Epi EPI>
+__global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_dma_kernel(const Params p,
+                                                                             const int32_t* __restrict__ work) {
+  constexpr int NT = WM * WN * kWave;
+  constexpr int FM = BM / WM / 16;
   constexpr int FN = BN / WN / 16;
-  constexpr int CPR = kDmaBK / 16;          // 16-byte chunks per row and stage
-  constexpr int A_LD = BM * CPR / kThreads;  // DMA instructions per thread per stage (A tile)
-  constexpr int B_LD = BN * CPR / kThreads;  // (B tile)
+  constexpr int CPR = kDmaBK / 16;    // 16-byte chunks per row and stage
+  constexpr int A_LD = BM * CPR / NT;  // DMA instructions per thread per stage (A tile)
+  constexpr int B_LD = BN * CPR / NT;  // (B tile)
   constexpr int LD = A_LD + B_LD;
   constexpr int STAGE = (BM + BN) * kDmaBK;
-  constexpr bool kBlock = is_block<EPI>();
-  static_assert(A_LD >= 1 && B_LD >= 1 && (BM * CPR) % kThreads == 0 && (BN * CPR) % kThreads == 0, "tile shape");
-  static_assert(S >= 3 && S <= 6 && (S - 2) * LD < 64, "stages");
-  static_assert(KT >= S, "K steps");
+  static_assert(!is_block<EPI>(), "channel-wise epilogues only");
+  static_assert(A_LD >= 1 && B_LD >= 1 && (BM * CPR) % NT == 0 && (BN * CPR) % NT == 0, "tile shape");
+  static_assert(KT >= 2, "K steps");
   static_assert(MAP == BMap::Plain || FN % 2 == 0, "split tiles need gate and up fragments");
 
   __shared__ __attribute__((aligned(1024))) int8_t st0[STAGE];
   __shared__ __attribute__((aligned(1024))) int8_t st1[STAGE];
-  __shared__ __attribute__((aligned(1024))) int8_t st2[STAGE];
-  __shared__ __attribute__((aligned(1024))) int8_t st3[S > 3 ? STAGE : 16];
-  __shared__ __attribute__((aligned(1024))) int8_t st4[S > 4 ? STAGE : 16];
-  __shared__ __attribute__((aligned(1024))) int8_t st5[S > 5 ? STAGE : 16];
   __shared__ int32_t sh_pid[BM];
   __shared__ float sh_red[WN][BM];
 
@@ -480,26 +487,29 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(const Par
   const int nrows = work[3 + kWorkFields * ti];
   const int8_t* wexp = p.w + e * p.N * p.K;
 
-  const int tid = threadIdx.x, l = lane_id(), wn = tid / kWave;
-  for (int i = tid; i < BM; i += kThreads) sh_pid[i] = i < nrows ? p.sorted[row0 + i] : (int32_t)p.P;
+  const int tid = threadIdx.x, l = lane_id(), wv = tid / kWave, wm = wv / WN, wn = wv % WN;
+  for (int i = tid; i < BM; i += NT) sh_pid[i] = i < nrows ? p.sorted[row0 + i] : (int32_t)p.P;
 
-  // Sources of this thread's DMA chunks: stage region chunk q holds row q/CPR, K-chunk (q%CPR)^swz(row).
-  const int8_t* a_src[A_LD];
-  const int8_t* b_src[B_LD];
+  // This thread's DMA chunks: stage chunk q holds row q / CPR, K-chunk (q % CPR) ^ swz(row); lane i
+  // of an instruction lands 16 i bytes after the instruction's 1 KB slot.
+  const int8_t* src[LD];
+  int dst[LD];
 #pragma unroll
   for (int c = 0; c < A_LD; ++c) {
-    const int q = (wn * A_LD + c) * kWave + l, r = q / CPR, kc = (q % CPR) ^ swz(r);
+    const int q = (wv * A_LD + c) * kWave + l, r = q / CPR, kc = (q % CPR) ^ swz(r);
     const int8_t* row = p.a;  // rows past the tile read row 0 (their results are never stored)
     if (r < nrows) {
       const int32_t pid = p.sorted[row0 + r];
       row = p.gather ? p.a + (int64_t)(pid / p.k) * p.K : p.a + (row0 + r) * p.K;
     }
-    a_src[c] = row + kc * 16;
+    src[c] = row + kc * 16;
+    dst[c] = (wv * A_LD + c) * 1024;
   }
 #pragma unroll
   for (int c = 0; c < B_LD; ++c) {
-    const int q = (wn * B_LD + c) * kWave + l, j = q / CPR, kc = (q % CPR) ^ swz(j);
-    b_src[c] = wexp + wrow_of<BN, MAP>(nt, j, p.I) * p.K + kc * 16;
+    const int q = (wv * B_LD + c) * kWave + l, j = q / CPR, kc = (q % CPR) ^ swz(j);
+    src[A_LD + c] = wexp + wrow_of<BN, MAP>(nt, j, p.I) * p.K + kc * 16;
+    dst[A_LD + c] = BM * kDmaBK + (wv * B_LD + c) * 1024;
   }
 
   i32x4 acc[FM][FN];
@@ -507,58 +517,28 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_dma_kernel(const Par
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      acc[i][j] = i32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int r = 0; r < 4; ++r) accf[i][j][r] = 0.0f;
-    }
-
-  const int64_t nkb = p.K / 128;
+    for (int j = 0; j < FN; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
   const int g = l >> 4, fr = l & 15;
+  const int wrows = nrows - wm * (BM / WM);  // real rows in this wavefront's fragment rows
 
-#define W8A8_STAGE(j) \
-  ((j) == 0 ? st0 : (j) == 1 ? st1 : (j) == 2 ? st2 : (j) == 3 ? st3 : (j) == 4 ? st4 : st5)
-#define W8A8_DMA(st, j)                                                                                        \
-  do {                                                                                                         \
-    int8_t* base_ = W8A8_STAGE(j);                                                                             \
-    _Pragma("unroll") for (int c = 0; c < A_LD; ++c)                                                           \
-        dma16(a_src[c] + (int64_t)(st) * kDmaBK, base_ + (wn * A_LD + c) * 1024);                              \
-    _Pragma("unroll") for (int c = 0; c < B_LD; ++c)                                                           \
-        dma16(b_src[c] + (int64_t)(st) * kDmaBK, base_ + BM * kDmaBK + (wn * B_LD + c) * 1024);                \
-  } while (0)
-
-  // Prologue: stages 0 .. S-2 in flight, then wait for stage 0.
+  // Prologue: stage 0 lands before the loop.
 #pragma unroll
-  for (int st = 0; st < S - 1; ++st) W8A8_DMA(st, st);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm<(S - 2) * LD>());
+  for (int c = 0; c < LD; ++c) dma16(src[c], st0 + dst[c]);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
 
-  // K-step kt reads stage buffer kt % S (landed) and refills the buffer of step kt - 1 with step
-  // kt + S - 1; at its end it waits until step kt + 1 has landed (stages issued after it may stay
-  // in flight).  All indices are compile-time after unrolling.
+  // Step kt: every wavefront is done with step kt - 1 (barrier), so the other buffer is free; the
+  // MFMAs read stage kt while the DMA of step kt + 1 goes out between them; then wait until it
+  // has landed.
 #pragma clang loop unroll(full)
   for (int kt = 0; kt < KT; ++kt) {
     __builtin_amdgcn_s_waitcnt(kLgkm0Imm);
     barrier_no_fence();
-    if (kt + S - 1 < KT) W8A8_DMA(kt + S - 1, (kt + S - 1) % S);
-    dma_mfma_stage<BM, BN, FM, FN, MAP>(W8A8_STAGE(kt % S), acc, wn, g, fr);
-    if constexpr (kBlock)
-      block_flush<BM, BN, WM, WN, FM, FN, MAP, EPI>(p, acc, accf, sh_pid, row0, nt, e, 0, wn, l, kt, nkb);
-    const int ahead = (KT - 1 < kt + S - 1 ? KT - 1 : kt + S - 1) - (kt + 1);  // stages issued after kt + 1
-    if (ahead >= 4)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm<(S - 2 >= 4 ? 4 : 0) * LD>());
-    else if (ahead == 3)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm<3 * LD>());
-    else if (ahead == 2)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm<2 * LD>());
-    else if (ahead == 1)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm<LD>());
-    else if (ahead == 0)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
+    dma_stage<BM, BN, WM, WN, LD, MAP>(kt % 2 == 0 ? st0 : st1, kt % 2 == 0 ? st1 : st0, src, dst,
+                                       (int64_t)(kt + 1) * kDmaBK, kt + 1 < KT, acc, wm, wn, g, fr, wrows);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
   }
-#undef W8A8_DMA
-#undef W8A8_STAGE
   __syncthreads();
-  epilogue<BM, BN, WM, WN, FM, FN, MAP, EPI>(p, acc, accf, sh_pid, sh_red, row0, nt, e, 0, wn, l, tid);
+  epilogue<BM, BN, WM, WN, FM, FN, MAP, EPI>(p, acc, accf, sh_pid, sh_red, row0, nt, e, wm, wn, l, tid);
 }
 
 // Work list of the DMA engine: per expert, tiles of up to bmk real rows of its sorted segment.
@@ -688,9 +668,9 @@ size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 
 constexpr int kBNStaged = 128;   // staged engine: 64 gate + 64 up rows, or 128 output columns
 constexpr int kBNBlock13 = 256;  // staged block-wise first GEMM: 128 gate + 128 up rows (one requant group)
-constexpr int kDmaBM = 128;
-constexpr int kDmaBN = 256;      // DMA engine: 128 gate + 128 up rows, or 256 output columns
-constexpr int kDmaStages = 3;    // LDS ring depth: 2 stages of 48 KB in flight
+constexpr int kDmaBM = 256;      // DMA engine: 256 x 256 tiles on 2 x 4 wavefronts of 128 x 64
+constexpr int kDmaBN = 256;      // 128 gate + 128 up rows, or 256 output columns
+constexpr int kDmaWM = 2, kDmaWN = 4;
 
 // The DMA engine pays off once experts hold several MFMA tiles of rows.  Its K loop is unrolled
 // for a compile-time K: instantiated for hidden 7168 and intermediate 2048 (the DeepSeek-V3 layer);
@@ -741,8 +721,8 @@ hipError_t launch_dma(Params prm, const GroupedShape& s, const int32_t* padded_o
   hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(kListThreads), 0, stream, prm.sorted, padded_offsets,
                      (int)s.E, (int32_t)prm.P, kDmaBM, work);
   const int64_t grid = (dma_max_tiles(s) * prm.n_tiles + 7) / 8 * 8;
-  hipLaunchKernelGGL((grouped_gemm_dma_kernel<kDmaBM, kDmaBN, K / kDmaBK, kDmaStages, MAP, EPI>), dim3((uint32_t)grid),
-                     dim3(kThreads), 0, stream, prm, (const int32_t*)work);
+  hipLaunchKernelGGL((grouped_gemm_dma_kernel<kDmaBM, kDmaBN, kDmaWM, kDmaWN, K / kDmaBK, MAP, EPI>),
+                     dim3((uint32_t)grid), dim3(kDmaWM * kDmaWN * kWave), 0, stream, prm, (const int32_t*)work);
   return hipGetLastError();
 }
 
