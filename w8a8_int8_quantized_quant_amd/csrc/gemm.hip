@@ -409,7 +409,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 
 // The DMA engine's K loop.  Each stage holds 128 bytes of K (two MFMA K-steps) for BM A rows and
 // BN B rows.  A wavefront works through its stage in groups (K-step kk, fragment row fm) of FN
-// MFMAs and issues the next stage's DMA instructions between the groups, one per STRIDE groups, so
+// MFMAs and issues the next stage's DMA instructions between the groups, spread evenly, so
 // the memory pipe is fed for the whole stage instead of in a burst that stalls the MFMAs behind
 // it.  Scheduling barriers keep the compiler from regrouping them.
 template <int BM, int BN, int WM, int WN, int LD, BMap MAP>
@@ -419,8 +419,7 @@ __device__ __forceinline__ void dma_stage(const int8_t* stage, int8_t* next, con
                                           int fr, int rows) {
   constexpr int FM = BM / WM / 16, FN = BN / WN / 16;
   constexpr int GROUPS = (kDmaBK / 64) * FM;
-  constexpr int STRIDE = GROUPS / LD;
-  static_assert(STRIDE >= 1 && GROUPS % LD == 0, "DMA slots");
+  static_assert(GROUPS >= LD, "DMA slots");  // DMA c goes out before group (c * GROUPS) / LD
 #pragma unroll
   for (int kk = 0; kk < kDmaBK / 64; ++kk) {
     const int lane = fr * kDmaBK + (((kk * 4 + g) ^ swz(fr)) << 4);
@@ -434,7 +433,9 @@ __device__ __forceinline__ void dma_stage(const int8_t* stage, int8_t* next, con
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
       const int grp = kk * FM + fm;
-      if (grp % STRIDE == 0 && prefetch) dma16(src[grp / STRIDE] + next_off, next + dst[grp / STRIDE]);
+#pragma unroll
+      for (int c = 0; c < LD; ++c)
+        if ((c * GROUPS) / LD == grp && prefetch) dma16(src[c] + next_off, next + dst[c]);
       if (fm * 16 < rows) {  // fragment rows past the tile's real rows are never stored
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn)
@@ -668,7 +669,7 @@ size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 
 constexpr int kBNStaged = 128;   // staged engine: 64 gate + 64 up rows, or 128 output columns
 constexpr int kBNBlock13 = 256;  // staged block-wise first GEMM: 128 gate + 128 up rows (one requant group)
-constexpr int kDmaBM = 256;      // DMA engine: 256 x 256 tiles on 2 x 4 wavefronts of 128 x 64
+constexpr int kDmaBM = 320;      // DMA engine: 320 x 256 tiles on 2 x 4 wavefronts of 160 x 64
 constexpr int kDmaBN = 256;      // 128 gate + 128 up rows, or 256 output columns
 constexpr int kDmaWM = 2, kDmaWN = 4;
 
