@@ -639,27 +639,45 @@ __global__ void pair_row_kernel(const int32_t* __restrict__ sorted, const int32_
   if (pid >= 0 && pid < P) pair_row[pid] = (int32_t)r;
 }
 
-// out[t, n] = 0 + w[t,0] * y0 + w[t,1] * y1 + ... in slot order; 4 columns per thread.
+// out[t, n] = 0 + w[t,0] * y0 + w[t,1] * y1 + ... in slot order.  One token per workgroup row
+// (its slot rows and weights are uniform, so they come through scalar loads); each thread sums
+// kCombineVec float4 columns, all of a slot's loads in flight together.
+constexpr int kCombineVec = 4;
 __global__ __launch_bounds__(kThreads) void combine_kernel(const float* __restrict__ y,
                                                            const int32_t* __restrict__ pair_row,
-                                                           const float* __restrict__ topk_w, int64_t T, int64_t k,
-                                                           int64_t H, float* __restrict__ out) {
-  const int64_t q = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+                                                           const float* __restrict__ topk_w, int64_t k, int64_t H,
+                                                           float* __restrict__ out) {
+  const int64_t t = blockIdx.x;
   const int64_t H4 = H / 4;
-  if (q >= T * H4) return;
-  const int64_t t = q / H4, c = q % H4;
-  float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  const int64_t c0 = (int64_t)blockIdx.y * kThreads * kCombineVec + threadIdx.x;
+  float4 o[kCombineVec];
+#pragma unroll
+  for (int i = 0; i < kCombineVec; ++i) o[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   for (int64_t j = 0; j < k; ++j) {
     const int32_t r = pair_row[t * k + j];
     if (r < 0) continue;
     const float wj = topk_w[t * k + j];
-    const float4 v = reinterpret_cast<const float4*>(y + (int64_t)r * H)[c];
-    o.x = o.x + wj * v.x;
-    o.y = o.y + wj * v.y;
-    o.z = o.z + wj * v.z;
-    o.w = o.w + wj * v.w;
+    const float4* src = reinterpret_cast<const float4*>(y + (int64_t)r * H);
+    float4 v[kCombineVec];
+#pragma unroll
+    for (int i = 0; i < kCombineVec; ++i) {
+      const int64_t c = c0 + i * kThreads;
+      v[i] = c < H4 ? src[c] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+#pragma unroll
+    for (int i = 0; i < kCombineVec; ++i) {
+      o[i].x = o[i].x + wj * v[i].x;
+      o[i].y = o[i].y + wj * v[i].y;
+      o[i].z = o[i].z + wj * v[i].z;
+      o[i].w = o[i].w + wj * v[i].w;
+    }
   }
-  reinterpret_cast<float4*>(out + t * H)[c] = o;
+  float4* dst = reinterpret_cast<float4*>(out + t * H);
+#pragma unroll
+  for (int i = 0; i < kCombineVec; ++i) {
+    const int64_t c = c0 + i * kThreads;
+    if (c < H4) dst[c] = o[i];
+  }
 }
 
 size_t round256(size_t b) { return (b + 255) / 256 * 256; }
@@ -839,9 +857,9 @@ hipError_t w2_combine(const GroupedShape& s, int32_t scale_mode, const int8_t* h
   if (s.max_rows > 0)
     hipLaunchKernelGGL(pair_row_kernel, dim3((uint32_t)((s.max_rows + kThreads - 1) / kThreads)), dim3(kThreads), 0,
                        stream, sorted, num_tiles, s.block_m, P, pair_row, s.max_rows);
-  const int64_t q = s.T * (s.H / 4);
-  hipLaunchKernelGGL(combine_kernel, dim3((uint32_t)((q + kThreads - 1) / kThreads)), dim3(kThreads), 0, stream, y,
-                     pair_row, topk_w, s.T, s.k, s.H, out);
+  const int64_t col_blocks = (s.H / 4 + kThreads * kCombineVec - 1) / (kThreads * kCombineVec);
+  hipLaunchKernelGGL(combine_kernel, dim3((uint32_t)s.T, (uint32_t)col_blocks), dim3(kThreads), 0, stream, y, pair_row,
+                     topk_w, s.k, s.H, out);
   return hipGetLastError();
 }
 
