@@ -49,6 +49,9 @@ SMALL = {
     "tiny": synth.CONFIGS["tiny"],
     "ds-small": small_cfg(),
     "ds-small-block": small_cfg(name="ds-small-block", index=21, mode="block", T=257),
+    # DeepSeek-V3 expert shapes with few experts: the large-batch GEMM engine at the real K sizes.
+    "dsv3-e8": small_cfg(name="dsv3-e8", index=40, T=1000, H=7168, I=2048, E=8, k=2, route="softmax", n_group=1,
+                         topk_group=1, scaling=1.0),
 }
 
 
@@ -451,6 +454,85 @@ def test_second_gemm_combine_bit_exact(name):
     tokens = np.arange(cfg.T) if name in SMALL else sample(cfg.T, 3, 3)
     w = oracle_weights(name, np.unique(ids[tokens]))
     ref = oracle.w2_combine(h_q, h_s, w[2], w[3], al, bm, tw, cfg.T, cfg.k, cfg.H, cfg.I, block, tokens)
+    got = host(out)
+    assert np.array_equal(got[tokens], ref)
+    assert np.isfinite(got).all()
+
+
+# Rows per expert for the tile-edge cases: empty, one row, a ragged fragment, exactly one 320-row
+# tile, one row past it, several tiles, and ragged multi-tile counts.
+EDGE_COUNTS = [0, 1, 17, 320, 321, 650, 330, 361]
+
+
+def edge_routing(cfg):
+    """Top-2 ids with the counts above (two distinct experts per token: no expert holds more than
+    T rows, so a sorted run never meets itself T places later), tokens shuffled so each expert's
+    rows gather scattered token rows."""
+    flat = np.repeat(np.arange(cfg.E, dtype=np.int32), EDGE_COUNTS)
+    T = len(flat) // 2
+    assert T == cfg.T and cfg.k == 2 and max(EDGE_COUNTS) <= T
+    ids = np.stack([flat[:T], flat[T:]], axis=1)
+    assert np.all(ids[:, 0] != ids[:, 1])
+    ids = ids[np.random.default_rng(40).permutation(T)]
+    tw = synth.positive_scales(T * 2, cfg.seed, 0.05, 1.0).reshape(T, 2)
+    return np.ascontiguousarray(ids), np.ascontiguousarray(tw)
+
+
+def edge_rows(al, counts):
+    """Sorted rows at every 16/64/128/256/320-row boundary of each expert's segment, its first and
+    last rows and the edges of its last 16-row fragment."""
+    rows = set()
+    for e, n in enumerate(counts):
+        r0 = int(al["padded_offsets"][e])
+        js = {0, 1, 15, 16, 17, n - 2, n - 1, (n // 16) * 16 - 1, (n // 16) * 16}
+        for b in (64, 128, 256, 320):
+            for m in range(1, n // b + 1):
+                js |= {m * b - 1, m * b}
+        rows |= {r0 + j for j in js if 0 <= j < n}
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def test_large_batch_engine_tile_edges():
+    """Both GEMM stages at the DeepSeek-V3 expert shapes with constructed routing whose expert
+    row counts straddle every tile and fragment boundary: bit-exact second GEMM + combine and the
+    first GEMM's requantized intermediate, at the rows on those boundaries."""
+    name = "dsv3-e8"
+    cfg = cfg_of(name)
+    bm = block_m_of(cfg)
+    say(f"[edges] {name} block_m={bm}")
+    L = layer_of(name)
+    ids, tw = edge_routing(cfg)
+    P = cfg.T * cfg.k
+    al, d = oracle_align_dev(ids, cfg.E, bm)
+    assert list(al["counts"]) == EDGE_COUNTS
+    rows = edge_rows(al, EDGE_COUNTS)
+    R = w8.w8a8_moe_max_rows(cfg.T, cfg.k, cfg.E, bm)
+    w = oracle_weights(name, [e for e, n in enumerate(EDGE_COUNTS) if n])
+
+    a_q, a_s = oracle.quant_per_token(oracle.activations_f32(cfg), 0)
+    h_q = torch.empty((R, cfg.I), dtype=torch.int8, device=DEV)
+    h_s = torch.empty((R,), dtype=torch.float32, device=DEV)
+    ws = torch.empty(max(w8.w8a8_w13_workspace_bytes(cfg.T, cfg.k, cfg.E, cfg.H, cfg.I, bm), 256),
+                     dtype=torch.uint8, device=DEV)
+    w8.w8a8_grouped_gemm_w13_silu(dt(a_q), dt(a_s), L.w13, L.w13_scale, d["sorted_pair_ids"], d["padded_offsets"],
+                                  d["tile_expert"], d["num_tiles"], cfg.T, cfg.k, bm, h_q, h_s, ws)
+    rq, rs = oracle.w13_silu(a_q, a_s, w[0], w[1], al, bm, cfg.T, cfg.k, cfg.H, cfg.I, False, rows)
+    gq, gs = host(h_q)[rows], host(h_s)[rows]
+    rq, rs = rq[rows], rs[rows]
+    assert np.all(np.abs(gs - rs) <= 4 * ULP * rs), np.abs(gs / rs - 1).max()
+    diff = np.abs(gq.astype(np.int32) - rq.astype(np.int32))
+    assert diff.max() <= 1
+    assert np.mean(diff > 0) <= 1e-3, np.mean(diff > 0)
+
+    hq2 = synth.int8_matrix(R, cfg.I, cfg.seed + 100)
+    hs2 = synth.positive_scales(R, cfg.seed, 1e-3, 3e-2)
+    out = torch.full((cfg.T, cfg.H), float("nan"), dtype=torch.float32, device=DEV)
+    ws2 = torch.empty(max(w8.w8a8_w2_workspace_bytes(cfg.T, cfg.k, cfg.E, cfg.H, cfg.I, bm), 256),
+                      dtype=torch.uint8, device=DEV)
+    w8.w8a8_grouped_gemm_w2_combine(dt(hq2), dt(hs2), L.w2, L.w2_scale, d["sorted_pair_ids"], d["padded_offsets"],
+                                    d["tile_expert"], d["num_tiles"], dt(tw), cfg.T, cfg.k, bm, out, ws2)
+    tokens = np.unique(al["sorted_pair_ids"][rows] // cfg.k)
+    ref = oracle.w2_combine(hq2, hs2, w[2], w[3], al, bm, tw, cfg.T, cfg.k, cfg.H, cfg.I, False, tokens)
     got = host(out)
     assert np.array_equal(got[tokens], ref)
     assert np.isfinite(got).all()
