@@ -303,12 +303,15 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const Params p) 
   }
 
   i32x4 ra[A_CH], rb[B_CH];  // native vectors: HIP's uint4 struct would be copied through scratch
-// Global -> registers for the K-stage at byte offset k0, and registers -> LDS buffer `buf`.
+// Global -> registers for the K-stage at byte offset k0, and registers -> LDS buffer `buf`.  The
+// weights stream through with non-temporal loads (each weight tile is read by few workgroups; the
+// streaming hint measured about 15% more read bandwidth than plain loads on a pure read stream).
 #define W8A8_GLOAD(k0)                                                                                         \
   do {                                                                                                         \
     _Pragma("unroll") for (int c = 0; c < A_CH; ++c) ra[c] =                                                   \
         a_ok[c] ? *reinterpret_cast<const i32x4*>(a_src[c] + (k0)) : i32x4{0, 0, 0, 0};                       \
-    _Pragma("unroll") for (int c = 0; c < B_CH; ++c) rb[c] = *reinterpret_cast<const i32x4*>(b_src[c] + (k0)); \
+    _Pragma("unroll") for (int c = 0; c < B_CH; ++c) rb[c] =                                                   \
+        __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(b_src[c] + (k0)));                           \
   } while (0)
 #define W8A8_SSTORE(buf)                                                                                       \
   do {                                                                                                         \
@@ -396,6 +399,12 @@ __device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::
 __device__ __forceinline__ void dma16(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds, 16, 0, 0);
 }
+// The same with the non-temporal (streaming) cache policy, for the weights: each weight tile is
+// read by the few row tiles of its expert, side by side.
+constexpr int kCachePolicyNT = 2;
+__device__ __forceinline__ void dma16_nt(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds, 16, 0, kCachePolicyNT);
+}
 
 // 16-byte chunk swizzle of a 128-byte LDS row: chunk c of row r sits in slot c ^ ((r >> 1) & 7).
 // Sixteen consecutive rows reading the same chunk then hit sixteen different 16-byte bank groups
@@ -412,7 +421,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // MFMAs and issues the next stage's DMA instructions between the groups, spread evenly, so
 // the memory pipe is fed for the whole stage instead of in a burst that stalls the MFMAs behind
 // it.  Scheduling barriers keep the compiler from regrouping them.
-template <int BM, int BN, int WM, int WN, int LD, BMap MAP>
+template <int BM, int BN, int WM, int WN, int A_LD, int LD, BMap MAP>
 __device__ __forceinline__ void dma_stage(const int8_t* stage, int8_t* next, const int8_t* const (&src)[LD],
                                           const int (&dst)[LD], int64_t next_off, bool prefetch,
                                           i32x4 (&acc)[BM / WM / 16][BN / WN / 16], int wm, int wn, int g,
@@ -435,7 +444,12 @@ __device__ __forceinline__ void dma_stage(const int8_t* stage, int8_t* next, con
       const int grp = kk * FM + fm;
 #pragma unroll
       for (int c = 0; c < LD; ++c)
-        if ((c * GROUPS) / LD == grp && prefetch) dma16(src[c] + next_off, next + dst[c]);
+        if ((c * GROUPS) / LD == grp && prefetch) {
+          if (c < A_LD)
+            dma16(src[c] + next_off, next + dst[c]);
+          else
+            dma16_nt(src[c] + next_off, next + dst[c]);
+        }
       if (fm * 16 < rows) {  // fragment rows past the tile's real rows are never stored
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn)
@@ -524,7 +538,12 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_dma_kernel(co
 
   // Prologue: stage 0 lands before the loop.
 #pragma unroll
-  for (int c = 0; c < LD; ++c) dma16(src[c], st0 + dst[c]);
+  for (int c = 0; c < LD; ++c) {
+    if (c < A_LD)
+      dma16(src[c], st0 + dst[c]);
+    else
+      dma16_nt(src[c], st0 + dst[c]);
+  }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
 
   // Step kt: every wavefront is done with step kt - 1 (barrier), so the other buffer is free; the
@@ -534,7 +553,7 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_dma_kernel(co
   for (int kt = 0; kt < KT; ++kt) {
     __builtin_amdgcn_s_waitcnt(kLgkm0Imm);
     barrier_no_fence();
-    dma_stage<BM, BN, WM, WN, LD, MAP>(kt % 2 == 0 ? st0 : st1, kt % 2 == 0 ? st1 : st0, src, dst,
+    dma_stage<BM, BN, WM, WN, A_LD, LD, MAP>(kt % 2 == 0 ? st0 : st1, kt % 2 == 0 ? st1 : st0, src, dst,
                                        (int64_t)(kt + 1) * kDmaBK, kt + 1 < KT, acc, wm, wn, g, fr, wrows);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
   }
