@@ -460,6 +460,94 @@ __device__ __forceinline__ void dma_stage(const int8_t* stage, int8_t* next, con
   }
 }
 
+// Channel-wise epilogues of the DMA engine, staged through the (then idle) stage buffers: each
+// pass turns the accumulators of a band of fragment rows into fp32 values in LDS (wavefront-half
+// wm in buffer wm), then whole rows leave as contiguous float4 stores.  Second GEMM: y rows of BN
+// columns.  First GEMM: SiLU(gate) * up rows of BN / 2 columns, plus the row maximum of |h| over
+// them, which a half wavefront reduces while it stores the row.
+template <int BM, int BN, int WM, int WN, int STAGE_BYTES, BMap MAP, Epi EPI>
+__device__ __forceinline__ void dma_epilogue(const Params& p, const i32x4 (&acc)[BM / WM / 16][BN / WN / 16],
+                                             const int32_t* sh_pid, int8_t* buf0, int8_t* buf1, int64_t row0,
+                                             int64_t nt, int64_t e, int wm, int wn, int wv, int l) {
+  constexpr int FM = BM / WM / 16, FN = BN / WN / 16, FNH = FN / 2;
+  constexpr int NW = WM * WN;
+  constexpr bool kW13 = EPI == Epi::W13Channel;
+  static_assert(WM == 2 && (EPI == Epi::W2Channel || EPI == Epi::W13Channel), "two LDS halves, channel-wise");
+  constexpr int COLS = kW13 ? BN / 2 : BN;  // fp32 columns per row
+  constexpr int STRIDE = COLS * 4 + 16;     // padded LDS row: the 4 row groups of a store hit distinct banks
+  constexpr int F = STAGE_BYTES / (16 * STRIDE) < FM ? STAGE_BYTES / (16 * STRIDE) : FM;  // fragment rows per pass
+  static_assert(F >= 1, "an LDS half holds at least one fragment row of values");
+  int8_t* half = wm == 0 ? buf0 : buf1;
+  const int64_t I = p.I;
+#pragma unroll
+  for (int f0 = 0; f0 < FM; f0 += F) {
+    // accumulators -> LDS
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      if (fm < f0 || fm >= f0 + F) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int trow = wm * (BM / WM) + fm * 16 + (l / 16) * 4 + r;
+        const int32_t pid = sh_pid[trow];
+        float* dst = reinterpret_cast<float*>(half + ((fm - f0) * 16 + (l / 16) * 4 + r) * STRIDE);
+        if constexpr (kW13) {
+          const float as = pid < p.P ? p.a_s[pid / p.k] : 0.0f;
+#pragma unroll
+          for (int f = 0; f < FNH; ++f) {
+            const int col = brow_of<BN, WN, FN, MAP>(wn, f) + (l % 16);
+            const int64_t n = nt * (BN / 2) + col;
+            const float g = ((float)acc[fm][f][r] * as) * p.w_s[e * 2 * I + n];
+            const float u = ((float)acc[fm][f + FNH][r] * as) * p.w_s[e * 2 * I + I + n];
+            dst[col] = silu_mul(g, u);
+          }
+        } else {
+          const float hs = pid < p.P ? p.a_s[row0 + trow] : 0.0f;
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn) {
+            const int col = brow_of<BN, WN, FN, MAP>(wn, fn) + (l % 16);
+            dst[col] = ((float)acc[fm][fn][r] * hs) * p.w_s[e * p.N + nt * BN + col];
+          }
+        }
+      }
+    }
+    __syncthreads();
+    // LDS -> global, whole rows
+    const int rows = 2 * F * 16;
+    if constexpr (kW13) {
+      // a half wavefront per row: 32 lanes x float4 = 128 columns
+      const int hl = l % 32;
+      for (int idx = wv * 2 + l / 32; idx < rows; idx += NW * 2) {
+        const int hf = idx / (F * 16), lr = idx % (F * 16);
+        const bool in = f0 * 16 + lr < FM * 16;  // the last pass may hold fewer fragment rows
+        const int trow = hf * (BM / WM) + f0 * 16 + (in ? lr : 0);
+        const int32_t pid = in ? sh_pid[trow] : (int32_t)p.P;
+        float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if (in) v = *reinterpret_cast<const float4*>((hf == 0 ? buf0 : buf1) + lr * STRIDE + hl * 16);
+        float m = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));  // within the half wavefront
+        if (pid < p.P) {
+          reinterpret_cast<float4*>(p.out_f32 + (row0 + trow) * I + nt * (BN / 2))[hl] = v;
+          if (hl == 0) p.part_amax[(row0 + trow) * p.n_tiles + nt] = m;
+        }
+      }
+    } else {
+      // a wavefront per row: 64 lanes x float4 = 256 columns
+      for (int idx = wv; idx < rows; idx += NW) {
+        const int hf = idx / (F * 16), lr = idx % (F * 16);
+        const int trow = hf * (BM / WM) + f0 * 16 + lr;
+        if (f0 * 16 + lr >= FM * 16) continue;
+        if (sh_pid[trow] >= p.P) continue;
+#pragma unroll
+        for (int c = l; c < COLS / 4; c += kWave)
+          reinterpret_cast<float4*>(p.out_f32 + (row0 + trow) * p.N + nt * BN)[c] =
+              *reinterpret_cast<const float4*>((hf == 0 ? buf0 : buf1) + lr * STRIDE + c * 16);
+      }
+    }
+    __syncthreads();
+  }
+}
+
 // BM x BN tiles on WM x WN wavefronts (two per SIMD), two LDS stages: while the MFMAs read one,
 // the DMA fills the other.  The K loop (KT steps, a compile-time count) is fully unrolled so every
 // stage index is known and the compiler tells the buffer being read from the one being filled.
@@ -482,7 +570,6 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_dma_kernel(co
   __shared__ __attribute__((aligned(1024))) int8_t st0[STAGE];
   __shared__ __attribute__((aligned(1024))) int8_t st1[STAGE];
   __shared__ int32_t sh_pid[BM];
-  __shared__ float sh_red[WN][BM];
 
   // Work order: expert-major, then N-tile, then the expert's row tiles, so the row tiles that share
   // a weight tile run side by side and the weights come from HBM once.  XCD-aware: workgroups are
@@ -528,7 +615,6 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_dma_kernel(co
   }
 
   i32x4 acc[FM][FN];
-  float accf[FM][FN][4];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -558,7 +644,7 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_dma_kernel(co
     __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
   }
   __syncthreads();
-  epilogue<BM, BN, WM, WN, FM, FN, MAP, EPI>(p, acc, accf, sh_pid, sh_red, row0, nt, e, wm, wn, l, tid);
+  dma_epilogue<BM, BN, WM, WN, STAGE, MAP, EPI>(p, acc, sh_pid, st0, st1, row0, nt, e, wm, wn, wv, l);
 }
 
 // Work list of the DMA engine: per expert, tiles of up to bmk real rows of its sorted segment.
