@@ -40,6 +40,7 @@ namespace w8a8 {
 namespace {
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));  // native vector: the non-temporal builtins take it
 
 constexpr int kThreads = 256;
 
@@ -724,7 +725,7 @@ __global__ __launch_bounds__(kThreads) void requant_rows_kernel(const float* __r
   const float4* src = reinterpret_cast<const float4*>(hf + r * I);
   uint32_t* dst = reinterpret_cast<uint32_t*>(h_q + r * I);
   for (int64_t c = l; c < I / 4; c += kWave) {
-    const float4 v = src[c];
+    const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src) + c);
     dst[c] = (uint32_t)(uint8_t)quant_value(v.x, s) | ((uint32_t)(uint8_t)quant_value(v.y, s) << 8) |
              ((uint32_t)(uint8_t)quant_value(v.z, s) << 16) | ((uint32_t)(uint8_t)quant_value(v.w, s) << 24);
   }
@@ -767,7 +768,12 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float* __restri
 #pragma unroll
     for (int i = 0; i < kCombineVec; ++i) {
       const int64_t c = c0 + i * kThreads;
-      v[i] = c < H4 ? src[c] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      if (c < H4) {
+        const f32x4 q = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src) + c);
+        v[i] = make_float4(q.x, q.y, q.z, q.w);
+      } else {
+        v[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      }
     }
 #pragma unroll
     for (int i = 0; i < kCombineVec; ++i) {
