@@ -87,29 +87,38 @@ __device__ __forceinline__ int64_t wrow_of(int64_t nt, int br, int64_t I) {
   return br < BN / 2 ? nt * (BN / 2) + br : I + nt * (BN / 2) + (br - BN / 2);
 }
 
-// Block-wise: fold the int32 partials of K-block kb into the fp32 sums, in the
-// written order acc_f = acc_f + (((float)part * a_s) * w_s), and clear them.
-template <int BM, int BN, int WM, int WN, int FM, int FN, BMap MAP, Epi EPI>
-__device__ __forceinline__ void block_flush(const Params& p, i32x4 (&acc)[FM][FN], float (&accf)[FM][FN][4],
-                                            const int32_t* sh_pid, int64_t row0, int64_t nt, int64_t e, int wm,
-                                            int wn, int l, int64_t kb, int64_t nkb) {
+// Block-wise scales of K-block kb for this lane's accumulators: the activation (or intermediate)
+// scale of each of its rows (sh_arow: the row's index into the scale matrix, -1 past the real
+// rows) and the weight scale of each of its fragments' 128-row weight block.
+template <int BM, int BN, int WM, int WN, int FM, int FN, BMap MAP>
+__device__ __forceinline__ void block_scales(const Params& p, const int32_t* sh_arow, int64_t nt, int64_t e, int wm,
+                                             int wn, int l, int64_t kb, int64_t nkb, float (&as)[FM][4],
+                                             float (&ws)[FN]) {
 #pragma unroll
-  for (int fm = 0; fm < FM; ++fm) {
+  for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int trow = wm * (BM / WM) + fm * 16 + (l / 16) * 4 + r;
-      const int32_t pid = sh_pid[trow];
-      float as = 0.0f;
-      if (pid < p.P)
-        as = EPI == Epi::W13Block ? p.a_s[(int64_t)(pid / p.k) * nkb + kb] : p.a_s[(row0 + trow) * nkb + kb];
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn) {
-        const int64_t wrow = wrow_of<BN, MAP>(nt, brow_of<BN, WN, FN, MAP>(wn, fn), p.I);
-        const float ws = p.w_s[(e * (p.N / 128) + wrow / 128) * nkb + kb];
-        accf[fm][fn][r] = accf[fm][fn][r] + (((float)acc[fm][fn][r] * as) * ws);
-      }
+      const int32_t ar = sh_arow[wm * (BM / WM) + fm * 16 + (l / 16) * 4 + r];
+      as[fm][r] = ar >= 0 ? p.a_s[(int64_t)ar * nkb + kb] : 0.0f;
     }
+#pragma unroll
+  for (int fn = 0; fn < FN; ++fn) {
+    const int64_t wrow = wrow_of<BN, MAP>(nt, brow_of<BN, WN, FN, MAP>(wn, fn), p.I);
+    ws[fn] = p.w_s[(e * (p.N / 128) + wrow / 128) * nkb + kb];
   }
+}
+
+// Block-wise: fold the int32 partials of one K-block into the fp32 sums, in the written order
+// acc_f = acc_f + (((float)part * a_s) * w_s), and clear them.
+template <int FM, int FN>
+__device__ __forceinline__ void block_flush(i32x4 (&acc)[FM][FN], float (&accf)[FM][FN][4], const float (&as)[FM][4],
+                                            const float (&ws)[FN]) {
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) accf[fm][fn][r] = accf[fm][fn][r] + (((float)acc[fm][fn][r] * as[fm][r]) * ws[fn]);
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
@@ -267,6 +276,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const Params p) 
 
   __shared__ __attribute__((aligned(16))) int8_t lds[2][(BM + BN) * kLdsStride];
   __shared__ int32_t sh_pid[BM];
+  __shared__ int32_t sh_arow[kBlock ? BM : 1];  // block-wise: row index into the activation scales
   __shared__ float sh_red[WN][BM];
 
   const int64_t mt = blockIdx.x / p.n_tiles, nt = blockIdx.x % p.n_tiles;
@@ -278,7 +288,11 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const Params p) 
   const int tid = threadIdx.x, l = lane_id(), wv = tid / kWave;
   const int wm = wv / WN, wn = wv % WN;
 
-  for (int i = tid; i < BM; i += kThreads) sh_pid[i] = p.sorted[row0 + i];
+  for (int i = tid; i < BM; i += kThreads) {
+    const int32_t pid = p.sorted[row0 + i];
+    sh_pid[i] = pid;
+    if constexpr (kBlock) sh_arow[i] = pid < p.P ? (p.gather ? (int32_t)(pid / p.k) : (int32_t)(row0 + i)) : -1;
+  }
 
   // Global sources of this thread's 16-byte chunks (row-major chunks of 8 per 128-byte row).
   const int8_t* a_src[A_CH];
@@ -342,9 +356,17 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const Params p) 
   W8A8_GLOAD(0);
   W8A8_SSTORE(0);
   __syncthreads();
-  for (int64_t kt = 0; kt < KT; ++kt) {
+  // Block-wise: the scales of K-block kt + 1 are loaded during step kt, a full step ahead of use,
+  // into the other of two register sets (the loop is unrolled by two, so no copy waits on them).
+  float sa0[kBlock ? FM : 1][4], sw0[kBlock ? FN : 1], sa1[kBlock ? FM : 1][4], sw1[kBlock ? FN : 1];
+  if constexpr (kBlock) block_scales<BM, BN, WM, WN, FM, FN, MAP>(p, sh_arow, nt, e, wm, wn, l, 0, nkb, sa0, sw0);
+  auto step = [&](int64_t kt, float (&as_c)[kBlock ? FM : 1][4], float (&ws_c)[kBlock ? FN : 1],
+                  float (&as_n)[kBlock ? FM : 1][4], float (&ws_n)[kBlock ? FN : 1]) {
     const int buf = (int)(kt & 1);
     if (kt + 1 < KT) W8A8_GLOAD((kt + 1) * kBK);
+    if constexpr (kBlock) {
+      if (kt + 1 < KT) block_scales<BM, BN, WM, WN, FM, FN, MAP>(p, sh_arow, nt, e, wm, wn, l, kt + 1, nkb, as_n, ws_n);
+    }
 #pragma unroll
     for (int kk = 0; kk < kBK / 64; ++kk) {
       i32x4 af[FM], bf[FN];
@@ -362,10 +384,17 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const Params p) 
         for (int fn = 0; fn < FN; ++fn)
           acc[fm][fn] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[fm], bf[fn], acc[fm][fn], 0, 0, 0);
     }
-    if constexpr (kBlock)
-      block_flush<BM, BN, WM, WN, FM, FN, MAP, EPI>(p, acc, accf, sh_pid, row0, nt, e, wm, wn, l, kt, nkb);
+    if constexpr (kBlock) block_flush<FM, FN>(acc, accf, as_c, ws_c);
     if (kt + 1 < KT) W8A8_SSTORE(buf ^ 1);
     __syncthreads();
+  };
+  if constexpr (kBlock) {
+    for (int64_t kt = 0; kt < KT; kt += 2) {
+      step(kt, sa0, sw0, sa1, sw1);
+      if (kt + 1 < KT) step(kt + 1, sa1, sw1, sa0, sw0);
+    }
+  } else {
+    for (int64_t kt = 0; kt < KT; ++kt) step(kt, sa0, sw0, sa1, sw1);
   }
 #undef W8A8_GLOAD
 #undef W8A8_SSTORE
