@@ -171,6 +171,27 @@ def w13_algorithmic_bytes(cfg, T, counts):
     return active * (2 * cfg.I * cfg.H + 4 * nsw) + T * (cfg.H + 4 * nsa) + P * (cfg.I + 4 * nsh)
 
 
+def measured_traffic(workload):
+    """HBM bytes per launch of the roofline kernel from the committed rocprofv3 counter summary, or
+    None once the kernel source has changed since the counters were taken (the summary records the
+    SHA-256 of gemm.hip it was measured with)."""
+    import hashlib
+
+    summary = os.path.join(ROOT, "profiles", "moe_layer_hbm_counters.txt")
+    src = os.path.join(ROOT, "w8a8_int8_quantized_quant_amd", "csrc", "gemm.hip")
+    try:
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        for line in open(summary):
+            f = line.split()
+            if len(f) == 4 and f[0] == "bench-traffic" and f[1] == workload:
+                fields = dict(x.split("=", 1) for x in f[2:])
+                if fields.get("gemm_sha256") == sha:
+                    return int(fields["bytes"])
+    except (OSError, ValueError, KeyError):
+        return None
+    return None
+
+
 def cpu_baseline(cfg, ntok):
     """The CPU oracle, unchanged, on the first `ntok` tokens of the workload: routing from
     the logits, then the dense per-token layer.  Oracle-side expert weights are drawn by the
@@ -230,7 +251,8 @@ def main():
     w13_bytes = w13_algorithmic_bytes(cfg, cfg.T, counts)
     achieved = w13_bytes / (stage_ms["w13"] / 1000.0) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic("decode-w13-stage") if args.config == "decode" else None,
                 "kernel": "gate+up grouped GEMM stage (w8a8_grouped_gemm_w13_silu)",
                 "kernel_ms": round(stage_ms["w13"], 4), "algorithmic_bytes": w13_bytes}
     del st, layer
