@@ -8,9 +8,11 @@ weights and scales) are resident in HBM before timing starts.
 
 Prints one JSON line.  value = tokens/s of the DeepSeek-V3 decode layer
 (T=128, hidden 7168, intermediate 2048, 256 experts, top-8); the same line
-carries the T=8192 prefill layer's figures under "prefill", the roofline of the
-dominant kernel (the gate+up GEMM, weight-streaming and so HBM-bound at T=128)
-and the CPU oracle timed on a bounded sample of the same workload.
+carries the T=8192 prefill layer's figures under "prefill", the tiny (T=16), skewed
+(T=4096) and block-wise (T=2048) layers under "configs", the roofline of the
+dominant kernel (the gate+up GEMM, weight-streaming and so HBM-bound at T=128),
+the device's measured read / copy / INT8-MFMA rates under "peaks_measured", and
+the CPU oracle timed on a bounded sample of the same workload.
 """
 import argparse
 import json
@@ -35,6 +37,8 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true", help="skip the T=8192 prefill figures")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=128, help="tokens in the CPU oracle sample")
+    ap.add_argument("--no-configs", action="store_true", help="skip the tiny / skew / block workloads")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured-peak probes")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy kernel 3 times (counter calibration)")
     return ap.parse_args()
@@ -171,6 +175,56 @@ def w13_algorithmic_bytes(cfg, T, counts):
     return active * (2 * cfg.I * cfg.H + 4 * nsw) + T * (cfg.H + 4 * nsa) + P * (cfg.I + 4 * nsh)
 
 
+def measured_peaks():
+    """Rates of the probe kernels (include/w8a8probe.h) on this device: a 4 GiB non-temporal read
+    stream, a 2 GiB non-temporal copy, and an INT8 MFMA loop on pseudo-random operands."""
+    import ctypes
+
+    import torch
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "w8a8_int8_quantized_quant_amd", "libw8a8probe.so"))
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    lib.w8a8_probe_read.argtypes = [vp, i64, vp, vp]
+    lib.w8a8_probe_copy.argtypes = [vp, vp, i64, vp]
+    lib.w8a8_probe_mfma_i8.argtypes = [i64, i32, vp, vp]
+    lib.w8a8_probe_mfma_i8_ops.argtypes = [i64, i32]
+    for f in (lib.w8a8_probe_read, lib.w8a8_probe_copy, lib.w8a8_probe_mfma_i8):
+        f.restype = i32
+    lib.w8a8_probe_mfma_i8_ops.restype = i64
+    stream = torch.cuda.current_stream()
+    hs = stream.cuda_stream
+
+    def timed(fn, reps=5):
+        for _ in range(2):
+            if fn() != 0:
+                raise RuntimeError("probe launch failed")
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps / 1000.0
+
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    t_read = timed(lambda: lib.w8a8_probe_read(buf.data_ptr(), nbytes, sink.data_ptr(), hs))
+    half = nbytes // 2
+    t_copy = timed(lambda: lib.w8a8_probe_copy(buf.data_ptr(), buf.data_ptr() + half, half, hs))
+    del buf
+    torch.cuda.empty_cache()
+    iters, wgs = 4096, 2048
+    t_mfma = timed(lambda: lib.w8a8_probe_mfma_i8(iters, wgs, sink.data_ptr(), hs))
+    ops = lib.w8a8_probe_mfma_i8_ops(iters, wgs)
+    return {"hbm_read_gbs": round(nbytes / t_read / 1e9, 1), "hbm_copy_gbs": round(2 * half / t_copy / 1e9, 1),
+            "int8_mfma_tops": round(ops / t_mfma / 1e12, 1),
+            "note": "probe kernels of libw8a8probe.so: non-temporal 16-byte read stream over 4 GiB; "
+                    "non-temporal copy of 2 GiB (read + written bytes); 8 independent "
+                    "v_mfma_i32_16x16x64_i8 chains per wavefront on pseudo-random operands, 8 workgroups "
+                    "of 4 wavefronts per CU"}
+
+
 def measured_traffic(workload):
     """HBM bytes per launch of the roofline kernel from the committed rocprofv3 counter summary, or
     None once the kernel source has changed since the counters were taken (the summary records the
@@ -272,6 +326,42 @@ def main():
         del pst, pl
         torch.cuda.empty_cache()
 
+    configs = None
+    if not args.no_configs and args.config == "decode":
+        configs = {}
+        for name in ("tiny", "skew", "block"):
+            oc = synth.CONFIGS[name]
+            print(f"[bench] drawing {oc.note}", file=sys.stderr, flush=True)
+            ol = workload.make_layer(oc)
+            oms, ostage, ost, ocounts = measure(ol, max(3, args.steps // 2), args.warmup)
+            of = layer_figures(oc, oc.T, oms, ocounts)
+            print(f"[bench] {name}: {oms:.3f} ms/step, stages {ostage}", file=sys.stderr, flush=True)
+            entry = {"T": oc.T, "ms_per_step": round(oms, 4), "tokens_per_s": round(of["tokens_per_s"], 1),
+                     "int8_tops": round(of["int8_tops"], 3), "frac_int8_peak": round(of["frac_int8_peak"], 4),
+                     "hbm_gbs": round(of["hbm_gbs"], 1), "frac_hbm_peak": round(of["frac_hbm_peak"], 4),
+                     "active_experts": of["active_experts"], "scale": oc.scale_mode,
+                     "stage_ms": {k: round(v, 4) for k, v in ostage.items()}}
+            if name == "skew":
+                import numpy as np
+
+                c = np.sort(ocounts)[::-1]
+                entry["top8_share"] = round(float(c[:8].sum() / max(c.sum(), 1)), 4)
+                entry["empty_experts"] = int((ocounts == 0).sum())
+            configs[name] = entry
+            del ost, ol
+            torch.cuda.empty_cache()
+
+    peaks = None
+    if not args.no_peaks:
+        print("[bench] measured peaks (probe kernels)", file=sys.stderr, flush=True)
+        peaks = measured_peaks()
+        roofline["frac_of_measured_read"] = round(achieved / peaks["hbm_read_gbs"], 4)
+        if prefill is not None:
+            prefill["frac_of_measured_mfma"] = round(prefill["int8_tops"] / peaks["int8_mfma_tops"], 4)
+        for entry in (configs or {}).values():
+            entry["frac_of_measured_mfma"] = round(entry["int8_tops"] / peaks["int8_mfma_tops"], 4)
+            entry["frac_of_measured_read"] = round(entry["hbm_gbs"] / peaks["hbm_read_gbs"], 4)
+
     cpu = None
     if not args.no_cpu_baseline:
         print(f"[bench] CPU oracle baseline on {args.cpu_tokens} tokens", file=sys.stderr, flush=True)
@@ -287,7 +377,8 @@ def main():
         "int8_tops": round(fig["int8_tops"], 3), "frac_int8_peak": round(fig["frac_int8_peak"], 4),
         "hbm_gbs": round(fig["hbm_gbs"], 1), "frac_hbm_peak": round(fig["frac_hbm_peak"], 4),
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
-        "roofline": roofline, "prefill": prefill, "cpu_baseline": cpu,
+        "roofline": roofline, "prefill": prefill, "configs": configs, "peaks_measured": peaks,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 

@@ -1,0 +1,38 @@
+/* w8a8probe.h -- measured peaks of the device, for the benchmark's report (libw8a8probe.so).
+ *
+ * Not part of the MoE layer: three small kernels whose rates are the "measured on this chip"
+ * counterparts of the published peaks the layer's figures are quoted against.  All calls are
+ * asynchronous on `stream` (NULL = default stream); the caller times them (HIP events) and
+ * owns every buffer.  Return 0 on success, 1 for a bad argument (null pointer, size not a
+ * positive multiple of 16, non-positive count), 5 when the launch fails.
+ */
+#ifndef W8A8PROBE_H
+#define W8A8PROBE_H
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Reads `bytes` of device memory at `buf` once (16-byte non-temporal loads); writes to the
+ * device int32 `sink` only in a case that does not occur in practice. */
+int32_t w8a8_probe_read(const void* buf, int64_t bytes, int32_t* sink, hipStream_t stream);
+
+/* Copies `bytes` from device `src` to device `dst` (non-overlapping), 16-byte non-temporal
+ * loads and stores. */
+int32_t w8a8_probe_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream);
+
+/* `workgroups` workgroups of 4 wavefronts, each wavefront issuing `iters` rounds of 8
+ * independent v_mfma_i32_16x16x64_i8 on pseudo-random operands; `sink` as above. */
+int32_t w8a8_probe_mfma_i8(int64_t iters, int32_t workgroups, int32_t* sink, hipStream_t stream);
+
+/* Integer operations (2 per multiply-add) of one w8a8_probe_mfma_i8 launch. */
+int64_t w8a8_probe_mfma_i8_ops(int64_t iters, int32_t workgroups);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W8A8PROBE_H */

@@ -17,8 +17,8 @@ OK, INV, SHAPE, WS, DT = (w8.W8A8_OK, w8.W8A8_INVALID_ARGUMENT, w8.W8A8_UNSUPPOR
 P16 = 1 << 20  # a fake, 256-byte aligned device address: these calls must fail validation first
 
 
-def header_functions():
-    text = open(HEADER).read()
+def header_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
 
@@ -30,6 +30,31 @@ def test_every_declared_symbol_is_exported():
     missing = [n for n in names if not hasattr(L, n)]
     assert not missing, missing
     assert sorted(w8.EXPORTS) == names
+
+
+def test_probe_library_exports_its_header_and_validates():
+    """The benchmark's measured-peak probes (libw8a8probe.so): every declared symbol exported,
+    invalid arguments rejected without a GPU, and the MFMA op count of a launch."""
+    import ctypes
+
+    names = header_functions(os.path.join(ROOT, "include", "w8a8probe.h"))
+    assert names == ["w8a8_probe_copy", "w8a8_probe_mfma_i8", "w8a8_probe_mfma_i8_ops", "w8a8_probe_read"]
+    L = ctypes.CDLL(os.path.join(ROOT, "w8a8_int8_quantized_quant_amd", "libw8a8probe.so"))
+    for n in names:
+        assert hasattr(L, n), n
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    L.w8a8_probe_read.argtypes = [vp, i64, vp, vp]
+    L.w8a8_probe_copy.argtypes = [vp, vp, i64, vp]
+    L.w8a8_probe_mfma_i8.argtypes = [i64, i32, vp, vp]
+    L.w8a8_probe_mfma_i8_ops.argtypes = [i64, i32]
+    L.w8a8_probe_mfma_i8_ops.restype = i64
+    assert L.w8a8_probe_read(None, 1024, P16, None) == 1
+    assert L.w8a8_probe_read(P16, 1000, P16, None) == 1
+    assert L.w8a8_probe_copy(P16, P16, 0, None) == 1
+    assert L.w8a8_probe_mfma_i8(0, 8, P16, None) == 1
+    assert L.w8a8_probe_mfma_i8(1, 8, None, None) == 1
+    # 2 workgroups x 4 wavefronts x 3 rounds x 8 MFMAs x (16*16*64 multiply-adds x 2)
+    assert L.w8a8_probe_mfma_i8_ops(3, 2) == 2 * 4 * 3 * 8 * 2 * 16 * 16 * 64
 
 
 def test_status_strings():

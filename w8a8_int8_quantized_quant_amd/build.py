@@ -13,6 +13,9 @@ CSRC = os.path.join(HERE, "csrc")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["api.cpp", "quant.hip", "route.hip", "align.hip", "gemm.hip"]
 LIB = os.path.join(HERE, "libw8a8moe.so")
+# measured-peak probes for the benchmark (include/w8a8probe.h), a library of their own
+PROBE_SOURCES = ["probe.hip"]
+PROBE_LIB = os.path.join(HERE, "libw8a8probe.so")
 
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-fno-fast-math",
              "-fhip-fp32-correctly-rounded-divide-sqrt", "-Xclang", "-target-feature", "-Xclang",
@@ -20,11 +23,17 @@ HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contra
 
 
 def build(verbose: bool = False, jobs: int = 8) -> str:
+    _build(SOURCES, LIB, verbose, jobs)
+    _build(PROBE_SOURCES, PROBE_LIB, verbose, jobs)
+    return LIB
+
+
+def _build(sources, lib, verbose: bool, jobs: int) -> str:
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
     procs = []
     objs = []
-    for src in SOURCES:
+    for src in sources:
         obj = os.path.join(objdir, src + ".o")
         objs.append(obj)
         lang = ["-x", "hip"] if src.endswith(".cpp") else []
@@ -44,12 +53,12 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
             failed.append(src)
     if failed:
         raise RuntimeError(f"hipcc failed for {failed}")
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", LIB + ".tmp"]
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", lib + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(lib + ".tmp", lib)
+    return lib
 
 
 if __name__ == "__main__":

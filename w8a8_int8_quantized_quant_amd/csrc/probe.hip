@@ -1,0 +1,110 @@
+// probe.hip -- measured peaks of the chip the layer runs on, for the benchmark's report: a
+// streaming HBM read, a streaming HBM copy and an INT8 MFMA loop.  Not part of the layer.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/w8a8probe.h"
+
+namespace {
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 8;  // 16-byte loads in flight per thread
+
+// Every thread reads kUnroll 16-byte chunks per round, non-temporal (the weights of the layer are
+// streamed the same way); the XOR of everything read decides a store that never happens in
+// practice, so the loads cannot be dropped.
+__global__ __launch_bounds__(kThreads) void read_kernel(const i32x4* __restrict__ p, int64_t n,
+                                                        int32_t* __restrict__ sink) {
+  i32x4 acc = {0, 0, 0, 0};
+  const int64_t stride = (int64_t)gridDim.x * kThreads * kUnroll;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads * kUnroll + threadIdx.x; i < n; i += stride) {
+    i32x4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t j = i + (int64_t)u * kThreads;
+      v[u] = j < n ? __builtin_nontemporal_load(p + j) : i32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) acc ^= v[u];
+  }
+  if ((acc[0] ^ acc[1] ^ acc[2] ^ acc[3]) == 0x7f3a5c11) sink[0] = 1;
+}
+
+__global__ __launch_bounds__(kThreads) void copy_kernel(const i32x4* __restrict__ src, i32x4* __restrict__ dst,
+                                                        int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads * kUnroll;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads * kUnroll + threadIdx.x; i < n; i += stride) {
+    i32x4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t j = i + (int64_t)u * kThreads;
+      v[u] = j < n ? __builtin_nontemporal_load(src + j) : i32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t j = i + (int64_t)u * kThreads;
+      if (j < n) __builtin_nontemporal_store(v[u], dst + j);
+    }
+  }
+}
+
+// Each wavefront keeps kChains independent accumulators busy with v_mfma_i32_16x16x64_i8 on
+// operands of pseudo-random bytes (a multiply-xorshift of the lane id: all-equal operands would
+// draw less power and clock higher than real data).
+constexpr int kChains = 8;
+__global__ __launch_bounds__(kThreads) void mfma_kernel(int64_t iters, int32_t* __restrict__ sink) {
+  const uint32_t l = threadIdx.x + blockIdx.x * kThreads;
+  auto mix = [](uint32_t x) {
+    x ^= x >> 16;
+    x *= 0x7feb352du;
+    x ^= x >> 15;
+    x *= 0x846ca68bu;
+    return x ^ (x >> 16);
+  };
+  i32x4 a = {(int32_t)mix(l), (int32_t)mix(l + 1u), (int32_t)mix(l + 2u), (int32_t)mix(l + 3u)};
+  i32x4 b = {(int32_t)mix(~l), (int32_t)mix(~l + 7u), (int32_t)mix(~l + 9u), (int32_t)mix(~l + 11u)};
+  i32x4 acc[kChains];
+#pragma unroll
+  for (int c = 0; c < kChains; ++c) acc[c] = i32x4{0, 0, 0, 0};
+  for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int c = 0; c < kChains; ++c) acc[c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[c], 0, 0, 0);
+  }
+  int32_t s = 0;
+#pragma unroll
+  for (int c = 0; c < kChains; ++c) s ^= acc[c][0] ^ acc[c][1] ^ acc[c][2] ^ acc[c][3];
+  if (s == 0x13572468) sink[0] = s;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t w8a8_probe_read(const void* buf, int64_t bytes, int32_t* sink, hipStream_t stream) {
+  if (!buf || !sink || bytes < 16 || bytes % 16) return 1;
+  hipLaunchKernelGGL(read_kernel, dim3(4096), dim3(kThreads), 0, stream, static_cast<const i32x4*>(buf), bytes / 16,
+                     sink);
+  return hipGetLastError() == hipSuccess ? 0 : 5;
+}
+
+int32_t w8a8_probe_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream) {
+  if (!src || !dst || bytes < 16 || bytes % 16) return 1;
+  hipLaunchKernelGGL(copy_kernel, dim3(4096), dim3(kThreads), 0, stream, static_cast<const i32x4*>(src),
+                     static_cast<i32x4*>(dst), bytes / 16);
+  return hipGetLastError() == hipSuccess ? 0 : 5;
+}
+
+int32_t w8a8_probe_mfma_i8(int64_t iters, int32_t workgroups, int32_t* sink, hipStream_t stream) {
+  if (!sink || iters < 1 || workgroups < 1) return 1;
+  hipLaunchKernelGGL(mfma_kernel, dim3((uint32_t)workgroups), dim3(kThreads), 0, stream, iters, sink);
+  return hipGetLastError() == hipSuccess ? 0 : 5;
+}
+
+int64_t w8a8_probe_mfma_i8_ops(int64_t iters, int32_t workgroups) {
+  // per wavefront and iteration: kChains MFMAs of 16 x 16 x 64 multiply-adds
+  return (int64_t)workgroups * (kThreads / 64) * iters * kChains * 2 * 16 * 16 * 64;
+}
+
+}  // extern "C"
