@@ -452,10 +452,10 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // the memory pipe is fed for the whole stage instead of in a burst that stalls the MFMAs behind
 // it.  Scheduling barriers keep the compiler from regrouping them.
 template <int BM, int BN, int WM, int WN, int A_LD, int LD, BMap MAP>
-__device__ __forceinline__ void dma_stage(const int8_t* stage, int8_t* next, const int8_t* const (&src)[LD],
-                                          const int (&dst)[LD], int64_t next_off, bool prefetch,
-                                          i32x4 (&acc)[BM / WM / 16][BN / WN / 16], int wm, int wn, int g,
-                                          int fr, int rows) {
+__device__ __forceinline__ void dma_stage(const int8_t* stage, int8_t* next, const int8_t* a_base,
+                                          const int8_t* b_base, const uint32_t (&off)[LD], int a_dst, int b_dst,
+                                          uint32_t next_off, bool prefetch, i32x4 (&acc)[BM / WM / 16][BN / WN / 16],
+                                          int wm, int wn, int g, int fr, int rows) {
   constexpr int FM = BM / WM / 16, FN = BN / WN / 16;
   constexpr int GROUPS = (kDmaBK / 64) * FM;
   static_assert(GROUPS >= LD, "DMA slots");  // DMA c goes out before group (c * GROUPS) / LD
@@ -476,9 +476,9 @@ __device__ __forceinline__ void dma_stage(const int8_t* stage, int8_t* next, con
       for (int c = 0; c < LD; ++c)
         if ((c * GROUPS) / LD == grp && prefetch) {
           if (c < A_LD)
-            dma16(src[c] + next_off, next + dst[c]);
+            dma16(a_base + (off[c] + next_off), next + a_dst + c * 1024);
           else
-            dma16_nt(src[c] + next_off, next + dst[c]);
+            dma16_nt(b_base + (off[c] + next_off), next + b_dst + (c - A_LD) * 1024);
         }
       if (fm * 16 < rows) {  // fragment rows past the tile's real rows are never stored
 #pragma unroll
@@ -579,9 +579,11 @@ __device__ __forceinline__ void dma_epilogue(const Params& p, const i32x4 (&acc)
 }
 
 // BM x BN tiles on WM x WN wavefronts (two per SIMD), two LDS stages: while the MFMAs read one,
-// the DMA fills the other.  The K loop (KT steps, a compile-time count) is fully unrolled so every
-// stage index is known and the compiler tells the buffer being read from the one being filled.
-template <int BM, int BN, int WM, int WN, int KT, BMap MAP, Epi EPI>
+// the DMA fills the other.  The K loop runs two steps per iteration, one per stage buffer, so every
+// stage index is known at compile time and the compiler tells the buffer being read from the one
+// being filled; every step ends with all its DMA landed, so nothing is in flight across the loop's
+// back edge.  K is a multiple of 256 (an even number of 128-byte steps).
+template <int BM, int BN, int WM, int WN, BMap MAP, Epi EPI>
 __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_dma_kernel(const Params p,
                                                                              const int32_t* __restrict__ work) {
   constexpr int NT = WM * WN * kWave;
@@ -594,7 +596,6 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_dma_kernel(co
   constexpr int STAGE = (BM + BN) * kDmaBK;
   static_assert(!is_block<EPI>(), "channel-wise epilogues only");
   static_assert(A_LD >= 1 && B_LD >= 1 && (BM * CPR) % NT == 0 && (BN * CPR) % NT == 0, "tile shape");
-  static_assert(KT >= 2, "K steps");
   static_assert(MAP == BMap::Plain || FN % 2 == 0, "split tiles need gate and up fragments");
 
   __shared__ __attribute__((aligned(1024))) int8_t st0[STAGE];
@@ -619,30 +620,31 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_dma_kernel(co
   const int nrows = work[3 + kWorkFields * ti];
   const int8_t* wexp = p.w + e * p.N * p.K;
 
-  const int tid = threadIdx.x, l = lane_id(), wv = tid / kWave, wm = wv / WN, wn = wv % WN;
+  const int tid = threadIdx.x, l = lane_id();
+  const int wv = __builtin_amdgcn_readfirstlane(tid / kWave), wm = wv / WN, wn = wv % WN;
   for (int i = tid; i < BM; i += NT) sh_pid[i] = i < nrows ? p.sorted[row0 + i] : (int32_t)p.P;
 
   // This thread's DMA chunks: stage chunk q holds row q / CPR, K-chunk (q % CPR) ^ swz(row); lane i
-  // of an instruction lands 16 i bytes after the instruction's 1 KB slot.
-  const int8_t* src[LD];
-  int dst[LD];
+  // of an instruction lands 16 i bytes after the instruction's 1 KB slot.  Sources are 32-bit
+  // offsets from the A matrix and from the expert's weights (the host checks they fit).  Rows past
+  // the tile read row 0 (their results are never stored).
+  uint32_t off[LD];
 #pragma unroll
   for (int c = 0; c < A_LD; ++c) {
     const int q = (wv * A_LD + c) * kWave + l, r = q / CPR, kc = (q % CPR) ^ swz(r);
-    const int8_t* row = p.a;  // rows past the tile read row 0 (their results are never stored)
+    int64_t row = 0;
     if (r < nrows) {
       const int32_t pid = p.sorted[row0 + r];
-      row = p.gather ? p.a + (int64_t)(pid / p.k) * p.K : p.a + (row0 + r) * p.K;
+      row = p.gather ? (int64_t)(pid / p.k) : row0 + r;
     }
-    src[c] = row + kc * 16;
-    dst[c] = (wv * A_LD + c) * 1024;
+    off[c] = (uint32_t)(row * p.K + kc * 16);
   }
 #pragma unroll
   for (int c = 0; c < B_LD; ++c) {
     const int q = (wv * B_LD + c) * kWave + l, j = q / CPR, kc = (q % CPR) ^ swz(j);
-    src[A_LD + c] = wexp + wrow_of<BN, MAP>(nt, j, p.I) * p.K + kc * 16;
-    dst[A_LD + c] = BM * kDmaBK + (wv * B_LD + c) * 1024;
+    off[A_LD + c] = (uint32_t)(wrow_of<BN, MAP>(nt, j, p.I) * p.K + kc * 16);
   }
+  const int a_dst = wv * A_LD * 1024, b_dst = BM * kDmaBK + wv * B_LD * 1024;
 
   i32x4 acc[FM][FN];
 #pragma unroll
@@ -656,21 +658,26 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_dma_kernel(co
 #pragma unroll
   for (int c = 0; c < LD; ++c) {
     if (c < A_LD)
-      dma16(src[c], st0 + dst[c]);
+      dma16(p.a + off[c], st0 + a_dst + c * 1024);
     else
-      dma16_nt(src[c], st0 + dst[c]);
+      dma16_nt(wexp + off[c], st0 + b_dst + (c - A_LD) * 1024);
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
 
   // Step kt: every wavefront is done with step kt - 1 (barrier), so the other buffer is free; the
   // MFMAs read stage kt while the DMA of step kt + 1 goes out between them; then wait until it
   // has landed.
-#pragma clang loop unroll(full)
-  for (int kt = 0; kt < KT; ++kt) {
+  const int64_t KT = p.K / kDmaBK;
+  for (int64_t kt = 0; kt < KT; kt += 2) {
     __builtin_amdgcn_s_waitcnt(kLgkm0Imm);
     barrier_no_fence();
-    dma_stage<BM, BN, WM, WN, A_LD, LD, MAP>(kt % 2 == 0 ? st0 : st1, kt % 2 == 0 ? st1 : st0, src, dst,
-                                       (int64_t)(kt + 1) * kDmaBK, kt + 1 < KT, acc, wm, wn, g, fr, wrows);
+    dma_stage<BM, BN, WM, WN, A_LD, LD, MAP>(st0, st1, p.a, wexp, off, a_dst, b_dst, (uint32_t)(kt + 1) * kDmaBK, true,
+                                             acc, wm, wn, g, fr, wrows);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
+    __builtin_amdgcn_s_waitcnt(kLgkm0Imm);
+    barrier_no_fence();
+    dma_stage<BM, BN, WM, WN, A_LD, LD, MAP>(st1, st0, p.a, wexp, off, a_dst, b_dst, (uint32_t)(kt + 2) * kDmaBK,
+                                             kt + 2 < KT, acc, wm, wn, g, fr, wrows);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
   }
   __syncthreads();
@@ -831,11 +838,14 @@ constexpr int kDmaBM = 320;      // DMA engine: 320 x 256 tiles on 2 x 4 wavefro
 constexpr int kDmaBN = 256;      // 128 gate + 128 up rows, or 256 output columns
 constexpr int kDmaWM = 2, kDmaWN = 4;
 
-// The DMA engine pays off once experts hold several MFMA tiles of rows.  Its K loop is unrolled
-// for a compile-time K: instantiated for hidden 7168 and intermediate 2048 (the DeepSeek-V3 layer);
-// other shapes run on the staged engine.
-constexpr int kDmaH = 7168, kDmaI = 2048;
-bool use_dma(const GroupedShape& s) { return s.T * s.k >= 64 * s.E && s.H == kDmaH && s.I == kDmaI; }
+// The DMA engine pays off once experts hold tens of rows (on average 64 or more here); its K steps
+// go in pairs and its down GEMM's N-tiles are 256 wide, so hidden and intermediate sizes must be
+// multiples of 256; other shapes run on the staged engine.
+// Its DMA sources are 32-bit offsets into the activation or intermediate matrix and into one expert.
+bool use_dma(const GroupedShape& s) {
+  return s.T * s.k >= 64 * s.E && s.H % 256 == 0 && s.I % 256 == 0 && (uint64_t)s.T * s.H < (1ull << 32) &&
+         (uint64_t)s.max_rows * s.I < (1ull << 32) && (uint64_t)2 * s.I * s.H < (1ull << 32);
+}
 
 int64_t dma_max_tiles(const GroupedShape& s) {
   const int64_t P = s.T * s.k;
@@ -873,14 +883,14 @@ hipError_t launch_bm(Params prm, int64_t max_rows, hipStream_t stream) {
   }
 }
 
-template <BMap MAP, Epi EPI, int K>
+template <BMap MAP, Epi EPI>
 hipError_t launch_dma(Params prm, const GroupedShape& s, const int32_t* padded_offsets, int32_t* work,
                       hipStream_t stream) {
   prm.n_tiles = MAP == BMap::Plain ? prm.N / kDmaBN : prm.I / (kDmaBN / 2);
   hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(kListThreads), 0, stream, prm.sorted, padded_offsets,
                      (int)s.E, (int32_t)prm.P, kDmaBM, work);
   const int64_t grid = (dma_max_tiles(s) * prm.n_tiles + 7) / 8 * 8;
-  hipLaunchKernelGGL((grouped_gemm_dma_kernel<kDmaBM, kDmaBN, kDmaWM, kDmaWN, K / kDmaBK, MAP, EPI>),
+  hipLaunchKernelGGL((grouped_gemm_dma_kernel<kDmaBM, kDmaBN, kDmaWM, kDmaWN, MAP, EPI>),
                      dim3((uint32_t)grid), dim3(kDmaWM * kDmaWN * kWave), 0, stream, prm, (const int32_t*)work);
   return hipGetLastError();
 }
@@ -948,7 +958,7 @@ hipError_t w13_silu(const GroupedShape& s, int32_t scale_mode, const int8_t* a_q
                                              round256(sizeof(float) * (size_t)(s.max_rows * n_tiles)));
   prm.out_f32 = hf;
   prm.part_amax = part;
-  hipError_t err = use_dma(s) ? launch_dma<BMap::Split, Epi::W13Channel, kDmaH>(prm, s, padded_offsets, work, stream)
+  hipError_t err = use_dma(s) ? launch_dma<BMap::Split, Epi::W13Channel>(prm, s, padded_offsets, work, stream)
                               : launch_bm<BMap::Split, Epi::W13Channel, kBNStaged>(prm, s.max_rows, stream);
   if (err != hipSuccess) return err;
   const int64_t blocks = (s.max_rows + kThreads / kWave - 1) / (kThreads / kWave);
@@ -988,7 +998,7 @@ hipError_t w2_combine(const GroupedShape& s, int32_t scale_mode, const int8_t* h
   if (scale_mode == 1)
     err = launch_bm<BMap::Plain, Epi::W2Block, kBNStaged>(prm, s.max_rows, stream);
   else if (use_dma(s))
-    err = launch_dma<BMap::Plain, Epi::W2Channel, kDmaI>(prm, s, padded_offsets, work, stream);
+    err = launch_dma<BMap::Plain, Epi::W2Channel>(prm, s, padded_offsets, work, stream);
   else
     err = launch_bm<BMap::Plain, Epi::W2Channel, kBNStaged>(prm, s.max_rows, stream);
   if (err != hipSuccess) return err;
