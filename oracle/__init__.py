@@ -43,8 +43,9 @@ def _load():
         lib.oracle_w2_combine.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, vp, i64, i64, i64, i64, i32,
                                           vp, i64, vp]
         lib.oracle_moe_tokens.argtypes = [vp, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, i32, vp]
+        lib.oracle_linear.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, i64, vp]
         for name in ("oracle_quant_blocks", "oracle_route", "oracle_align", "oracle_grouped_gemm_i32",
-                     "oracle_w13_silu", "oracle_w2_combine", "oracle_moe_tokens"):
+                     "oracle_w13_silu", "oracle_w2_combine", "oracle_moe_tokens", "oracle_linear"):
             getattr(lib, name).restype = None
         _lib = lib
     return _lib
@@ -207,6 +208,24 @@ def w2_combine(h_q: np.ndarray, h_s: np.ndarray, w2, w2_s, al: Dict[str, np.ndar
     _load().oracle_w2_combine(_p(h_q), _p(h_s), _ptr_array(wq), _ptr_array(wsc), _p(al["sorted_pair_ids"]),
                               _p(al["tile_expert"]), int(al["num_tiles"][0]), block_m, _p(tw), T, k, H, I,
                               int(block), _p(tk), ntok, _p(out))
+    return out
+
+
+def linear(a_q: np.ndarray, a_s: np.ndarray, w: np.ndarray, w_s: np.ndarray,
+           rows: Optional[Iterable[int]] = None) -> np.ndarray:
+    """Dense W8A8 linear: out [M, N] fp32 = ((float)(a_q . w) * a_s[m]) * w_s[n]; with `rows`, only
+    those rows are computed (the others are zero)."""
+    a_q = _c(a_q, np.int8)
+    w = _c(w, np.int8)
+    a_s = _c(a_s, np.float32)
+    w_s = _c(w_s, np.float32)
+    M, K = a_q.shape
+    N = w.shape[0]
+    assert w.shape[1] == K and a_s.shape == (M,) and w_s.shape == (N,)
+    out = np.zeros((M, N), dtype=np.float32)
+    r = None if rows is None else _c(np.asarray(list(rows), dtype=np.int64), np.int64)
+    _load().oracle_linear(_p(a_q), _p(a_s), _p(w), _p(w_s), M, N, K, None if r is None else _p(r),
+                          0 if r is None else len(r), _p(out))
     return out
 
 

@@ -413,3 +413,24 @@ ORACLE_EXPORT void oracle_moe_tokens(const float* x, int64_t ntok, int64_t H, in
     free(y);
   }
 }
+
+/* ------------------------------------------------------------------ dense linear
+ *
+ * The model's non-MoE projections in W8A8 INT8 (PR #3888 Modifications, "Norm Linear"; article,
+ * "Quantization exploration": per-token activation scales, per-channel weight scales, one
+ * dequantization after the INT8 matmul):
+ *   out[m][n] = ((float)(a_q[m] . w[n]) * a_s[m]) * w_s[n]
+ * a_q [M, K] int8, a_s [M], w [N, K] int8, w_s [N], out [M, N] fp32; `rows` / `nrows` select the
+ * rows m to compute (NULL = all). */
+ORACLE_EXPORT void oracle_linear(const int8_t* a_q, const float* a_s, const int8_t* w, const float* w_s, int64_t M,
+                                 int64_t N, int64_t K, const int64_t* rows, int64_t nrows, float* out) {
+  if (!rows) nrows = M;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t i = 0; i < nrows; ++i) {
+    const int64_t m = row_at(rows, i);
+    for (int64_t n = 0; n < N; ++n) {
+      const int32_t acc = dot_i8(a_q + m * K, w + n * K, K);
+      out[m * N + n] = ((float)acc * a_s[m]) * w_s[n];
+    }
+  }
+}

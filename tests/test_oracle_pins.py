@@ -471,3 +471,72 @@ def test_quantized_layer_tracks_fp64_layer():
             ref[t] += float(tw[t, j]) * (w2 @ (g / (1 + np.exp(-g)) * u))
     cos = (out.astype(np.float64) * ref).sum() / np.linalg.norm(out) / np.linalg.norm(ref)
     assert cos >= 0.99, cos
+
+
+# ---------------------------------------------------------------- dense W8A8 linear
+
+def linear_inputs(M, N, K, seed):
+    a_q = synth.int8_matrix(M, K, seed)
+    w = synth.int8_matrix(N, K, seed + 1)
+    a_s = synth.positive_scales(M, seed + 2, 1e-3, 3e-2)
+    w_s = synth.positive_scales(N, seed + 3, 1e-3, 3e-2)
+    return a_q, a_s, w, w_s
+
+
+def test_linear_equals_the_moe_second_gemm_with_one_expert():
+    """A dense linear is the grouped second GEMM + combine with one expert, top-1 and combine
+    weight 1.0 (0 + 1.0 * y == y): the oracle's other code path (align, sorted rows, combine)
+    must give the same bits."""
+    M, N, K = 37, 256, 384
+    a_q, a_s, w, w_s = linear_inputs(M, N, K, 71)
+    got = oracle.linear(a_q, a_s, w, w_s)
+    ids = np.zeros((M, 1), dtype=np.int32)
+    for bm in (16, 64):
+        al = oracle.align(ids, 1, bm)
+        R = int(al["num_tiles"][0]) * bm
+        h_q = np.zeros((R, K), dtype=np.int8)
+        h_s = np.ones(R, dtype=np.float32)
+        real = al["sorted_pair_ids"][:R] < M
+        h_q[real] = a_q[al["sorted_pair_ids"][:R][real]]
+        h_s[real] = a_s[al["sorted_pair_ids"][:R][real]]
+        ref = oracle.w2_combine(h_q, h_s, w[None], w_s[None], al, bm, np.ones((M, 1), np.float32), M, 1, N, K,
+                                False)
+        assert np.array_equal(got, ref)
+
+
+def test_linear_within_two_roundings_of_fp64():
+    """|acc| < 2^24, so (float)acc is exact and the two fp32 products round once each."""
+    M, N, K = 9, 256, 256
+    a_q, a_s, w, w_s = linear_inputs(M, N, K, 73)
+    got = oracle.linear(a_q, a_s, w, w_s).astype(np.float64)
+    exact = (a_q.astype(np.float64) @ w.astype(np.float64).T) * a_s.astype(np.float64)[:, None] \
+        * w_s.astype(np.float64)[None, :]
+    assert np.all(np.abs(got - exact) <= np.abs(exact) * (2.0 ** -23 + 2.0 ** -46))
+
+
+def test_linear_closed_form_and_row_selection():
+    """All-ones operands: out[m, n] = K * a_s[m] * w_s[n] in fp32; a row selection computes only
+    those rows."""
+    M, N, K = 4, 256, 512
+    a_q = np.ones((M, K), np.int8)
+    w = np.ones((N, K), np.int8)
+    a_s = np.array([0.5, 0.25, 2.0, 1.0], np.float32)
+    w_s = np.linspace(0.125, 4.0, N).astype(np.float32)
+    got = oracle.linear(a_q, a_s, w, w_s)
+    assert np.array_equal(got, (np.float32(K) * a_s[:, None]) * w_s[None, :])
+    part = oracle.linear(a_q, a_s, w, w_s, rows=[2])
+    assert np.array_equal(part[2], got[2]) and not part[[0, 1, 3]].any()
+
+
+def test_linear_tracks_the_unquantized_matmul():
+    """Per-token activation and per-channel weight quantization of Gaussian data, then the linear:
+    close to the fp64 x @ W^T (catches a transposed operand or a swapped scale)."""
+    rng_x = synth.normal(64 * 1024, 5, 1, 0).reshape(64, 1024).astype(np.float32)
+    W = (synth.normal(512 * 1024, 5, 2, 0).reshape(512, 1024) * 0.02).astype(np.float32)
+    a_q, a_s = oracle.quant_per_token(rng_x, 0)
+    w_q, w_s = oracle.quant_weight(W, "channel")
+    got = oracle.linear(a_q, a_s, w_q, w_s.reshape(-1)).astype(np.float64)
+    ref = rng_x.astype(np.float64) @ W.astype(np.float64).T
+    cos = (got * ref).sum() / np.linalg.norm(got) / np.linalg.norm(ref)
+    assert cos >= 0.999, cos
+    assert np.abs(got - ref).max() <= 0.05 * np.abs(ref).max()
