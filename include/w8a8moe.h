@@ -220,6 +220,23 @@ int32_t w8a8_block_grouped_gemm_w2_combine(const int8_t* h_q, const float* h_sca
                                            int64_t k, int64_t E, int64_t H, int64_t I, int64_t block_m,
                                            float* out, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------ dense linear
+ * W8A8 INT8 linear for the model's non-MoE projections (PR #3888 Modifications, "Norm Linear": the
+ * dense layers run as w8a8 int8 GEMMs; article, "Quantization exploration": channel-wise weights
+ * with online per-token activation scales, one dequantization after the INT8 matmul):
+ *   out[m, n] = ((float)(a_q[m] . w[n]) * a_scale[m]) * w_scale[n]   (int32 dot product, fp32 out)
+ *   a_q      device, [M, K] int8 (quantize with w8a8_quant_per_token, group 0)
+ *   a_scale  device, [M] fp32
+ *   w        device, [N, K] int8, K-contiguous;  w_scale device, [N] fp32
+ *   out      device, [M, N] fp32 (output, fully overwritten)
+ *   ws       device workspace of w8a8_linear_workspace_bytes(M) bytes (a tile list)
+ * Shapes: K and N multiples of 256, M*K and N*K below 2^32; M = 0 is a no-op.  a_q and w 16-byte
+ * aligned.  Returns W8A8_UNSUPPORTED_SHAPE for other shapes, W8A8_WORKSPACE_TOO_SMALL for a short
+ * workspace.  Deterministic: every output is one fixed sequence of operations. */
+size_t w8a8_linear_workspace_bytes(int64_t M);
+int32_t w8a8_linear(const int8_t* a_q, const float* a_scale, const int8_t* w, const float* w_scale, int64_t M,
+                    int64_t N, int64_t K, float* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------------ the whole layer
  * Steps 2, 1, 3, 4, 5 on one stream, intermediates carved from `ws`.
  * block_m = 0 picks a tile height from the average rows per expert. */

@@ -57,6 +57,24 @@ def test_probe_library_exports_its_header_and_validates():
     assert L.w8a8_probe_mfma_i8_ops(3, 2) == 2 * 4 * 3 * 8 * 2 * 16 * 16 * 64
 
 
+def test_linear_validation():
+    """w8a8_linear rejects bad calls on the host: sizes, shapes outside the engine, a short
+    workspace, missing pointers."""
+    L = w8.lib()
+    ws = w8.w8a8_linear_workspace_bytes(1000)
+    assert ws >= 4 * (1 + 5 * 4) and w8.w8a8_linear_workspace_bytes(0) >= 4
+    call = lambda M, N, K, wsb=ws, a=P16, w=P16, out=P16: L.w8a8_linear(a, P16, w, P16, M, N, K, out, P16, wsb, None)
+    assert call(-1, 256, 256) == INV
+    assert call(4, 576, 256) == SHAPE  # N not a multiple of 256
+    assert call(4, 256, 384) == SHAPE  # K not a multiple of 256
+    assert call(4, 256, 0) == SHAPE
+    assert call(1 << 17, 256, 1 << 16) == SHAPE  # M*K beyond 32-bit offsets
+    assert call(1000, 256, 256, wsb=ws - 1) == WS
+    assert call(4, 256, 256, a=None) == INV
+    assert call(4, 256, 256, w=P16 + 4) == INV  # weights not 16-byte aligned
+    assert call(0, 256, 256, a=None, w=None, out=None) == OK  # no rows: nothing to do
+
+
 def test_status_strings():
     assert w8.status_string(0) == "W8A8_OK"
     assert w8.status_string(3) == "W8A8_WORKSPACE_TOO_SMALL"

@@ -34,7 +34,7 @@ EXPORTS = (
     "moe_align_workspace_bytes", "moe_align_by_expert", "w8a8_grouped_gemm_i32", "w8a8_w13_workspace_bytes",
     "w8a8_grouped_gemm_w13_silu", "w8a8_w2_workspace_bytes", "w8a8_grouped_gemm_w2_combine",
     "w8a8_block_grouped_gemm_w13_silu", "w8a8_block_grouped_gemm_w2_combine", "w8a8_moe_pick_block_m",
-    "w8a8_moe_workspace_bytes", "w8a8_moe_forward",
+    "w8a8_moe_workspace_bytes", "w8a8_moe_forward", "w8a8_linear_workspace_bytes", "w8a8_linear",
 )
 
 
@@ -92,6 +92,8 @@ def lib() -> ctypes.CDLL:
             "w8a8_moe_pick_block_m": (i64, [i64, i64, i64]),
             "w8a8_moe_workspace_bytes": (sz, [i64, i64, i64, i64, i64, i64, i32]),
             "w8a8_moe_forward": (i32, [ctypes.POINTER(MoEArgs), vp, sz, vp]),
+            "w8a8_linear_workspace_bytes": (sz, [i64]),
+            "w8a8_linear": (i32, [vp, vp, vp, vp, i64, i64, i64, vp, vp, sz, vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -236,6 +238,18 @@ def w8a8_block_grouped_gemm_w2_combine(h_q, h_scale, w2, w2_scale, sorted_pair_i
                                        num_tiles, topk_weights, T, k, block_m, out, ws, stream=None) -> None:
     _w2("w8a8_block_grouped_gemm_w2_combine", h_q, h_scale, w2, w2_scale, sorted_pair_ids, padded_offsets,
         tile_expert, num_tiles, topk_weights, T, k, block_m, out, ws, stream)
+
+
+def w8a8_linear_workspace_bytes(M: int) -> int:
+    return lib().w8a8_linear_workspace_bytes(M)
+
+
+def w8a8_linear(a_q, a_scale, w, w_scale, out, ws, stream=None) -> None:
+    """out[M, N] fp32 = ((float)(a_q . w) * a_scale[m]) * w_scale[n]; a_q [M, K] int8, w [N, K] int8."""
+    M, K = a_q.shape
+    N = w.shape[0]
+    _call("w8a8_linear", _ptr(a_q), _ptr(a_scale), _ptr(w), _ptr(w_scale), M, N, K, _ptr(out), _ptr(ws),
+          _nbytes(ws), _stream(stream))
 
 
 def w8a8_moe_pick_block_m(T: int, k: int, E: int) -> int:

@@ -57,7 +57,7 @@ struct Params {
   int32_t gather;
   const int8_t* w;
   int64_t N, K;
-  const int32_t* sorted;
+  const int32_t* sorted;  // null: rows in their own order (the dense linear), row r = pair r
   const int32_t* tile_expert;
   const int32_t* num_tiles;
   int64_t P, k, block_m, n_tiles, I;
@@ -622,7 +622,8 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_dma_kernel(co
 
   const int tid = threadIdx.x, l = lane_id();
   const int wv = __builtin_amdgcn_readfirstlane(tid / kWave), wm = wv / WN, wn = wv % WN;
-  for (int i = tid; i < BM; i += NT) sh_pid[i] = i < nrows ? p.sorted[row0 + i] : (int32_t)p.P;
+  for (int i = tid; i < BM; i += NT)
+    sh_pid[i] = i < nrows ? (p.sorted ? p.sorted[row0 + i] : (int32_t)(row0 + i)) : (int32_t)p.P;
 
   // This thread's DMA chunks: stage chunk q holds row q / CPR, K-chunk (q % CPR) ^ swz(row); lane i
   // of an instruction lands 16 i bytes after the instruction's 1 KB slot.  Sources are 32-bit
@@ -633,10 +634,7 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_dma_kernel(co
   for (int c = 0; c < A_LD; ++c) {
     const int q = (wv * A_LD + c) * kWave + l, r = q / CPR, kc = (q % CPR) ^ swz(r);
     int64_t row = 0;
-    if (r < nrows) {
-      const int32_t pid = p.sorted[row0 + r];
-      row = p.gather ? (int64_t)(pid / p.k) : row0 + r;
-    }
+    if (r < nrows) row = p.gather ? (int64_t)(p.sorted[row0 + r] / p.k) : row0 + r;
     off[c] = (uint32_t)(row * p.K + kc * 16);
   }
 #pragma unroll
@@ -829,6 +827,20 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float* __restri
 
 size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 
+// Work list of the dense linear: one "expert", rows in their own order, tiles of bmk rows.
+__global__ void linear_tiles_kernel(int64_t M, int bmk, int32_t* __restrict__ work) {
+  const int64_t tiles = (M + bmk - 1) / bmk;
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i == 0) work[0] = (int32_t)tiles;
+  if (i >= tiles) return;
+  int32_t* t = work + 1 + kWorkFields * i;
+  t[0] = 0;
+  t[1] = (int32_t)(i * bmk);
+  t[2] = (int32_t)(M - i * bmk < bmk ? M - i * bmk : bmk);
+  t[3] = 0;
+  t[4] = (int32_t)tiles;
+}
+
 // ---------------------------------------------------------------------------------------------
 // Engine choice and launches.
 
@@ -1010,6 +1022,41 @@ hipError_t w2_combine(const GroupedShape& s, int32_t scale_mode, const int8_t* h
   const int64_t col_blocks = (s.H / 4 + kThreads * kCombineVec - 1) / (kThreads * kCombineVec);
   hipLaunchKernelGGL(combine_kernel, dim3((uint32_t)s.T, (uint32_t)col_blocks), dim3(kThreads), 0, stream, y, pair_row,
                      topk_w, s.k, s.H, out);
+  return hipGetLastError();
+}
+
+// Dense W8A8 linear: the DMA engine on one weight matrix, rows in their own order.
+size_t linear_ws_bytes(int64_t M) {
+  return round256(sizeof(int32_t) * (size_t)(1 + kWorkFields * ((M + kDmaBM - 1) / kDmaBM)));
+}
+
+bool linear_supported(int64_t M, int64_t N, int64_t K) {
+  return K % 256 == 0 && N % kDmaBN == 0 && (uint64_t)M * K < (1ull << 32) && (uint64_t)N * K < (1ull << 32);
+}
+
+hipError_t linear(const int8_t* a_q, const float* a_s, const int8_t* w, const float* w_s, int64_t M, int64_t N,
+                  int64_t K, float* out, void* ws, hipStream_t stream) {
+  if (M == 0) return hipSuccess;
+  Params prm{};
+  prm.a = a_q;
+  prm.gather = 0;
+  prm.w = w;
+  prm.N = N;
+  prm.K = K;
+  prm.sorted = nullptr;
+  prm.P = M;
+  prm.k = 1;
+  prm.a_s = a_s;
+  prm.w_s = w_s;
+  prm.out_f32 = out;
+  prm.n_tiles = N / kDmaBN;
+  int32_t* work = static_cast<int32_t*>(ws);
+  const int64_t tiles = (M + kDmaBM - 1) / kDmaBM;
+  hipLaunchKernelGGL(linear_tiles_kernel, dim3((uint32_t)((tiles + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                     stream, M, kDmaBM, work);
+  const int64_t grid = (tiles * prm.n_tiles + 7) / 8 * 8;
+  hipLaunchKernelGGL((grouped_gemm_dma_kernel<kDmaBM, kDmaBN, kDmaWM, kDmaWN, BMap::Plain, Epi::W2Channel>),
+                     dim3((uint32_t)grid), dim3(kDmaWM * kDmaWN * kWave), 0, stream, prm, (const int32_t*)work);
   return hipGetLastError();
 }
 
