@@ -9,7 +9,8 @@ weights and scales) are resident in HBM before timing starts.
 Prints one JSON line.  value = tokens/s of the DeepSeek-V3 decode layer
 (T=128, hidden 7168, intermediate 2048, 256 experts, top-8); the same line
 carries the T=8192 prefill layer's figures under "prefill", the tiny (T=16), skewed
-(T=4096) and block-wise (T=2048) layers under "configs", the roofline of the
+(T=4096) and block-wise (T=2048) layers under "configs", the dense W8A8 linear
+under "linear", the roofline of the
 dominant kernel (the gate+up GEMM, weight-streaming and so HBM-bound at T=128),
 the device's measured read / copy / INT8-MFMA rates under "peaks_measured", and
 the CPU oracle timed on a bounded sample of the same workload.
@@ -225,6 +226,51 @@ def measured_peaks():
                     "of 4 wavefronts per CU"}
 
 
+def linear_figures(steps, warmup):
+    """The dense W8A8 linear (w8a8_linear) on DeepSeek-V3's attention output projection (N = 7168,
+    K = 16384) at 128 and 8192 tokens, seeded uniform int8 operands; hipBLASLt's int8 GEMM
+    (torch._int_mm, int32 out, no dequantization) on the same operands as a reference point."""
+    import torch
+
+    import w8a8_int8_quantized_quant_amd as w8
+
+    out = {}
+    g = torch.Generator(device="cuda")
+    g.manual_seed(16384)
+    stream = torch.cuda.current_stream()
+    for name, M, N, K in (("decode", 128, 7168, 16384), ("prefill", 8192, 7168, 16384)):
+        a_q = torch.randint(-127, 128, (M, K), dtype=torch.int8, device="cuda", generator=g)
+        w = torch.randint(-127, 128, (N, K), dtype=torch.int8, device="cuda", generator=g)
+        a_s = torch.rand(M, device="cuda", generator=g) * 1e-2 + 1e-3
+        w_s = torch.rand(N, device="cuda", generator=g) * 1e-2 + 1e-3
+        y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        ws = torch.empty(max(w8.w8a8_linear_workspace_bytes(M, N, K), 256), dtype=torch.uint8, device="cuda")
+
+        def timed(fn):
+            for _ in range(warmup):
+                fn()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(steps):
+                fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) / steps
+
+        ms = timed(lambda: w8.w8a8_linear(a_q, a_s, w, w_s, y, ws))
+        wt = w.t()
+        ref_ms = timed(lambda: torch._int_mm(a_q, wt))
+        ops = 2.0 * M * N * K
+        nbytes = M * K + N * K + 4 * (M + N) + 4 * M * N
+        out[name] = {"M": M, "N": N, "K": K, "ms": round(ms, 4), "int8_tops": round(ops / ms / 1e9, 1),
+                     "frac_int8_peak": round(ops / ms / 1e9 / INT8_PEAK_TOPS, 4),
+                     "hbm_gbs": round(nbytes / ms / 1e6, 1), "frac_hbm_peak": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4),
+                     "hipblaslt_int_mm_ms": round(ref_ms, 4)}
+        del a_q, w, y, ws, wt
+    torch.cuda.empty_cache()
+    return out
+
+
 def measured_traffic(workload):
     """HBM bytes per launch of the roofline kernel from the committed rocprofv3 counter summary, or
     None once the kernel source has changed since the counters were taken (the summary records the
@@ -351,6 +397,12 @@ def main():
             del ost, ol
             torch.cuda.empty_cache()
 
+    linear = None
+    if not args.no_configs and args.config == "decode":
+        print("[bench] dense W8A8 linear", file=sys.stderr, flush=True)
+        linear = linear_figures(max(5, args.steps // 2), args.warmup)
+        print(f"[bench] linear: {linear}", file=sys.stderr, flush=True)
+
     peaks = None
     if not args.no_peaks:
         print("[bench] measured peaks (probe kernels)", file=sys.stderr, flush=True)
@@ -358,6 +410,9 @@ def main():
         roofline["frac_of_measured_read"] = round(achieved / peaks["hbm_read_gbs"], 4)
         if prefill is not None:
             prefill["frac_of_measured_mfma"] = round(prefill["int8_tops"] / peaks["int8_mfma_tops"], 4)
+        for entry in (linear or {}).values():
+            entry["frac_of_measured_mfma"] = round(entry["int8_tops"] / peaks["int8_mfma_tops"], 4)
+            entry["frac_of_measured_read"] = round(entry["hbm_gbs"] / peaks["hbm_read_gbs"], 4)
         for entry in (configs or {}).values():
             entry["frac_of_measured_mfma"] = round(entry["int8_tops"] / peaks["int8_mfma_tops"], 4)
             entry["frac_of_measured_read"] = round(entry["hbm_gbs"] / peaks["hbm_read_gbs"], 4)
@@ -377,7 +432,7 @@ def main():
         "int8_tops": round(fig["int8_tops"], 3), "frac_int8_peak": round(fig["frac_int8_peak"], 4),
         "hbm_gbs": round(fig["hbm_gbs"], 1), "frac_hbm_peak": round(fig["frac_hbm_peak"], 4),
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
-        "roofline": roofline, "prefill": prefill, "configs": configs, "peaks_measured": peaks,
+        "roofline": roofline, "prefill": prefill, "configs": configs, "linear": linear, "peaks_measured": peaks,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -229,11 +229,12 @@ int32_t w8a8_block_grouped_gemm_w2_combine(const int8_t* h_q, const float* h_sca
  *   a_scale  device, [M] fp32
  *   w        device, [N, K] int8, K-contiguous;  w_scale device, [N] fp32
  *   out      device, [M, N] fp32 (output, fully overwritten)
- *   ws       device workspace of w8a8_linear_workspace_bytes(M) bytes (a tile list)
+ *   ws       device workspace of w8a8_linear_workspace_bytes(M, N, K) bytes: a tile list and, when
+ *            few rows leave CUs idle, int32 partial sums of K slices (added exactly, in slice order)
  * Shapes: K and N multiples of 256, M*K and N*K below 2^32; M = 0 is a no-op.  a_q and w 16-byte
  * aligned.  Returns W8A8_UNSUPPORTED_SHAPE for other shapes, W8A8_WORKSPACE_TOO_SMALL for a short
  * workspace.  Deterministic: every output is one fixed sequence of operations. */
-size_t w8a8_linear_workspace_bytes(int64_t M);
+size_t w8a8_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);  /* 0 for an unsupported shape */
 int32_t w8a8_linear(const int8_t* a_q, const float* a_scale, const int8_t* w, const float* w_scale, int64_t M,
                     int64_t N, int64_t K, float* out, void* ws, size_t ws_bytes, hipStream_t stream);
 

@@ -61,8 +61,11 @@ def test_linear_validation():
     """w8a8_linear rejects bad calls on the host: sizes, shapes outside the engine, a short
     workspace, missing pointers."""
     L = w8.lib()
-    ws = w8.w8a8_linear_workspace_bytes(1000)
-    assert ws >= 4 * (1 + 5 * 4) and w8.w8a8_linear_workspace_bytes(0) >= 4
+    ws = w8.w8a8_linear_workspace_bytes(1000, 256, 256)
+    assert ws >= 4 * (1 + 5 * 4) and w8.w8a8_linear_workspace_bytes(0, 256, 256) >= 4
+    assert w8.w8a8_linear_workspace_bytes(4, 576, 256) == 0  # unsupported shape
+    # few rows: K slices, their int32 partials in the workspace (128 x 7168 outputs, K = 16384)
+    assert w8.w8a8_linear_workspace_bytes(128, 7168, 16384) >= 2 * 4 * 128 * 7168
     call = lambda M, N, K, wsb=ws, a=P16, w=P16, out=P16: L.w8a8_linear(a, P16, w, P16, M, N, K, out, P16, wsb, None)
     assert call(-1, 256, 256) == INV
     assert call(4, 576, 256) == SHAPE  # N not a multiple of 256
@@ -70,6 +73,7 @@ def test_linear_validation():
     assert call(4, 256, 0) == SHAPE
     assert call(1 << 17, 256, 1 << 16) == SHAPE  # M*K beyond 32-bit offsets
     assert call(1000, 256, 256, wsb=ws - 1) == WS
+    assert call(128, 7168, 16384, wsb=ws) == WS  # needs room for its K-slice partials
     assert call(4, 256, 256, a=None) == INV
     assert call(4, 256, 256, w=P16 + 4) == INV  # weights not 16-byte aligned
     assert call(0, 256, 256, a=None, w=None, out=None) == OK  # no rows: nothing to do

@@ -39,13 +39,14 @@ def run(a_q, a_s, w, w_s, guard=0):
     M, N = a_q.shape[0], w.shape[0]
     d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
     out = torch.full((M * N + guard,), float("nan"), dtype=torch.float32, device=DEV)
-    ws = torch.empty(max(w8.w8a8_linear_workspace_bytes(M), 256), dtype=torch.uint8, device=DEV)
+    N, K = w.shape
+    ws = torch.empty(max(w8.w8a8_linear_workspace_bytes(M, N, K), 256), dtype=torch.uint8, device=DEV)
     w8.w8a8_linear(d(a_q), d(a_s), d(w), d(w_s), out[: M * N].view(M, N), ws)
     torch.cuda.synchronize()
     return out.cpu().numpy()
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 256, 256), (37, 512, 768), (333, 768, 1024), (640, 256, 512),
+@pytest.mark.parametrize("M,N,K", [(1, 256, 256), (5, 256, 4096), (37, 512, 768), (333, 768, 1024), (640, 256, 512),
                                    (1000, 1536, 7168)])
 def test_linear_bit_exact(M, N, K):
     say(f"[linear] M={M} N={N} K={K}")

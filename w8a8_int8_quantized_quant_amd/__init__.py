@@ -92,7 +92,7 @@ def lib() -> ctypes.CDLL:
             "w8a8_moe_pick_block_m": (i64, [i64, i64, i64]),
             "w8a8_moe_workspace_bytes": (sz, [i64, i64, i64, i64, i64, i64, i32]),
             "w8a8_moe_forward": (i32, [ctypes.POINTER(MoEArgs), vp, sz, vp]),
-            "w8a8_linear_workspace_bytes": (sz, [i64]),
+            "w8a8_linear_workspace_bytes": (sz, [i64, i64, i64]),
             "w8a8_linear": (i32, [vp, vp, vp, vp, i64, i64, i64, vp, vp, sz, vp]),
         }
         for name, (res, args) in sig.items():
@@ -240,8 +240,8 @@ def w8a8_block_grouped_gemm_w2_combine(h_q, h_scale, w2, w2_scale, sorted_pair_i
         tile_expert, num_tiles, topk_weights, T, k, block_m, out, ws, stream)
 
 
-def w8a8_linear_workspace_bytes(M: int) -> int:
-    return lib().w8a8_linear_workspace_bytes(M)
+def w8a8_linear_workspace_bytes(M: int, N: int, K: int) -> int:
+    return lib().w8a8_linear_workspace_bytes(M, N, K)
 
 
 def w8a8_linear(a_q, a_scale, w, w_scale, out, ws, stream=None) -> None:

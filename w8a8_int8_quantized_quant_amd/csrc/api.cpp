@@ -262,9 +262,10 @@ int32_t w8a8_block_grouped_gemm_w2_combine(const int8_t* h_q, const float* h_sca
 
 // ---------------------------------------------------------------------------------------- composite
 
-size_t w8a8_linear_workspace_bytes(int64_t M) {
-  if (M < 0) return 0;
-  return w8a8::linear_ws_bytes(M);
+size_t w8a8_linear_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N < 1 || K < 1 || N > kMaxPairs || K > kMaxDim || M > kMaxPairs || !w8a8::linear_supported(M, N, K))
+    return 0;
+  return w8a8::linear_ws_bytes(M, N, K);
 }
 
 int32_t w8a8_linear(const int8_t* a_q, const float* a_scale, const int8_t* w, const float* w_scale, int64_t M,
@@ -275,7 +276,7 @@ int32_t w8a8_linear(const int8_t* a_q, const float* a_scale, const int8_t* w, co
   if (M == 0) return W8A8_OK;
   if (!ok16(a_q) || !ok4(a_scale) || !ok16(w) || !ok4(w_scale) || !ok16(out) || !aligned(ws, 4))
     return W8A8_INVALID_ARGUMENT;
-  if (ws_bytes < w8a8::linear_ws_bytes(M)) return W8A8_WORKSPACE_TOO_SMALL;
+  if (ws_bytes < w8a8::linear_ws_bytes(M, N, K)) return W8A8_WORKSPACE_TOO_SMALL;
   return hip_status(w8a8::linear(a_q, a_scale, w, w_scale, M, N, K, out, ws, stream));
 }
 

@@ -68,6 +68,7 @@ struct Params {
   float* part_amax;    // [rows, n_tiles] per-tile row maxima of |h| (first GEMM, channel)
   int8_t* h_q;
   float* h_s;
+  int64_t ksplit;  // DMA engine, Epi::I32: K slices per tile (1 = none); slice s writes out_i32 + s*P*N
 };
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return (g / (1.0f + expf(-g))) * u; }
@@ -498,11 +499,13 @@ __device__ __forceinline__ void dma_stage(const int8_t* stage, int8_t* next, con
 template <int BM, int BN, int WM, int WN, int STAGE_BYTES, BMap MAP, Epi EPI>
 __device__ __forceinline__ void dma_epilogue(const Params& p, const i32x4 (&acc)[BM / WM / 16][BN / WN / 16],
                                              const int32_t* sh_pid, int8_t* buf0, int8_t* buf1, int64_t row0,
-                                             int64_t nt, int64_t e, int wm, int wn, int wv, int l) {
+                                             int64_t nt, int64_t e, int wm, int wn, int wv, int l,
+                                             int64_t i32_off) {
   constexpr int FM = BM / WM / 16, FN = BN / WN / 16, FNH = FN / 2;
   constexpr int NW = WM * WN;
   constexpr bool kW13 = EPI == Epi::W13Channel;
-  static_assert(WM == 2 && (EPI == Epi::W2Channel || EPI == Epi::W13Channel), "two LDS halves, channel-wise");
+  static_assert(WM == 2 && (EPI == Epi::W2Channel || EPI == Epi::W13Channel || EPI == Epi::I32),
+                "two LDS halves, channel-wise or raw int32");
   constexpr int COLS = kW13 ? BN / 2 : BN;  // fp32 columns per row
   constexpr int STRIDE = COLS * 4 + 16;     // padded LDS row: the 4 row groups of a store hit distinct banks
   constexpr int F = STAGE_BYTES / (16 * STRIDE) < FM ? STAGE_BYTES / (16 * STRIDE) : FM;  // fragment rows per pass
@@ -529,6 +532,12 @@ __device__ __forceinline__ void dma_epilogue(const Params& p, const i32x4 (&acc)
             const float g = ((float)acc[fm][f][r] * as) * p.w_s[e * 2 * I + n];
             const float u = ((float)acc[fm][f + FNH][r] * as) * p.w_s[e * 2 * I + I + n];
             dst[col] = silu_mul(g, u);
+          }
+        } else if constexpr (EPI == Epi::I32) {
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn) {
+            const int col = brow_of<BN, WN, FN, MAP>(wn, fn) + (l % 16);
+            reinterpret_cast<int32_t*>(dst)[col] = acc[fm][fn][r];
           }
         } else {
           const float hs = pid < p.P ? p.a_s[row0 + trow] : 0.0f;
@@ -569,9 +578,13 @@ __device__ __forceinline__ void dma_epilogue(const Params& p, const i32x4 (&acc)
         if (f0 * 16 + lr >= FM * 16) continue;
         if (sh_pid[trow] >= p.P) continue;
 #pragma unroll
-        for (int c = l; c < COLS / 4; c += kWave)
-          reinterpret_cast<float4*>(p.out_f32 + (row0 + trow) * p.N + nt * BN)[c] =
-              *reinterpret_cast<const float4*>((hf == 0 ? buf0 : buf1) + lr * STRIDE + c * 16);
+        for (int c = l; c < COLS / 4; c += kWave) {
+          const float4 v = *reinterpret_cast<const float4*>((hf == 0 ? buf0 : buf1) + lr * STRIDE + c * 16);
+          if constexpr (EPI == Epi::I32)
+            reinterpret_cast<float4*>(p.out_i32 + i32_off + (row0 + trow) * p.N + nt * BN)[c] = v;  // int32 bits
+          else
+            reinterpret_cast<float4*>(p.out_f32 + (row0 + trow) * p.N + nt * BN)[c] = v;
+        }
       }
     }
     __syncthreads();
@@ -605,12 +618,14 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_dma_kernel(co
   // Work order: expert-major, then N-tile, then the expert's row tiles, so the row tiles that share
   // a weight tile run side by side and the weights come from HBM once.  XCD-aware: workgroups are
   // dispatched round-robin over the 8 XCDs; each XCD gets a contiguous stretch of that order.
-  const int64_t total = (int64_t)work[0] * p.n_tiles;
+  const int64_t total = (int64_t)work[0] * p.n_tiles * p.ksplit;
   const int64_t per = (total + 7) / 8;
   const int64_t v = blockIdx.x;
   if (v >= 8 * per) return;
-  const int64_t logical = (v % 8) * per + v / 8;
-  if (logical >= total) return;
+  const int64_t item = (v % 8) * per + v / 8;
+  if (item >= total) return;
+  const int64_t ks = item % p.ksplit, logical = item / p.ksplit;  // K slice, then the (tile, N-tile) item
+  const int64_t kslice = p.K / p.ksplit;                           // bytes of K per slice
   const int32_t* any = work + 1 + kWorkFields * (logical / p.n_tiles);  // a tile of the same expert
   const int64_t first = any[3], count = any[4];
   const int64_t local = logical - p.n_tiles * first;
@@ -635,12 +650,12 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_dma_kernel(co
     const int q = (wv * A_LD + c) * kWave + l, r = q / CPR, kc = (q % CPR) ^ swz(r);
     int64_t row = 0;
     if (r < nrows) row = p.gather ? (int64_t)(p.sorted[row0 + r] / p.k) : row0 + r;
-    off[c] = (uint32_t)(row * p.K + kc * 16);
+    off[c] = (uint32_t)(row * p.K + ks * kslice + kc * 16);
   }
 #pragma unroll
   for (int c = 0; c < B_LD; ++c) {
     const int q = (wv * B_LD + c) * kWave + l, j = q / CPR, kc = (q % CPR) ^ swz(j);
-    off[A_LD + c] = (uint32_t)(wrow_of<BN, MAP>(nt, j, p.I) * p.K + kc * 16);
+    off[A_LD + c] = (uint32_t)(wrow_of<BN, MAP>(nt, j, p.I) * p.K + ks * kslice + kc * 16);
   }
   const int a_dst = wv * A_LD * 1024, b_dst = BM * kDmaBK + wv * B_LD * 1024;
 
@@ -665,7 +680,7 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_dma_kernel(co
   // Step kt: every wavefront is done with step kt - 1 (barrier), so the other buffer is free; the
   // MFMAs read stage kt while the DMA of step kt + 1 goes out between them; then wait until it
   // has landed.
-  const int64_t KT = p.K / kDmaBK;
+  const int64_t KT = kslice / kDmaBK;
   for (int64_t kt = 0; kt < KT; kt += 2) {
     __builtin_amdgcn_s_waitcnt(kLgkm0Imm);
     barrier_no_fence();
@@ -679,7 +694,8 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_dma_kernel(co
     __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
   }
   __syncthreads();
-  dma_epilogue<BM, BN, WM, WN, STAGE, MAP, EPI>(p, acc, sh_pid, st0, st1, row0, nt, e, wm, wn, wv, l);
+  dma_epilogue<BM, BN, WM, WN, STAGE, MAP, EPI>(p, acc, sh_pid, st0, st1, row0, nt, e, wm, wn, wv, l,
+                                                ks * p.P * p.N);
 }
 
 // Work list of the DMA engine: per expert, tiles of up to bmk real rows of its sorted segment.
@@ -899,6 +915,7 @@ template <BMap MAP, Epi EPI>
 hipError_t launch_dma(Params prm, const GroupedShape& s, const int32_t* padded_offsets, int32_t* work,
                       hipStream_t stream) {
   prm.n_tiles = MAP == BMap::Plain ? prm.N / kDmaBN : prm.I / (kDmaBN / 2);
+  prm.ksplit = 1;
   hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(kListThreads), 0, stream, prm.sorted, padded_offsets,
                      (int)s.E, (int32_t)prm.P, kDmaBM, work);
   const int64_t grid = (dma_max_tiles(s) * prm.n_tiles + 7) / 8 * 8;
@@ -1025,9 +1042,54 @@ hipError_t w2_combine(const GroupedShape& s, int32_t scale_mode, const int8_t* h
   return hipGetLastError();
 }
 
-// Dense W8A8 linear: the DMA engine on one weight matrix, rows in their own order.
-size_t linear_ws_bytes(int64_t M) {
-  return round256(sizeof(int32_t) * (size_t)(1 + kWorkFields * ((M + kDmaBM - 1) / kDmaBM)));
+// Dense W8A8 linear: the DMA engine on one weight matrix, rows in their own order.  When the
+// (row tile, N-tile) items are fewer than the CUs (few rows), K is split into slices whose int32
+// partial sums go to the workspace; a second pass adds them in slice order (exact: integers) and
+// dequantizes once, so the result does not depend on the split.
+__global__ __launch_bounds__(kThreads) void linear_reduce_kernel(const int32_t* __restrict__ part, int64_t ksplit,
+                                                                 int64_t M, int64_t N, const float* __restrict__ a_s,
+                                                                 const float* __restrict__ w_s,
+                                                                 float* __restrict__ out) {
+  const int64_t q = (int64_t)blockIdx.x * kThreads + threadIdx.x;  // 4 outputs per thread
+  if (q >= M * N / 4) return;
+  const int64_t m = (4 * q) / N, n = (4 * q) % N;
+  i32x4 acc = reinterpret_cast<const i32x4*>(part)[q];
+  for (int64_t s = 1; s < ksplit; ++s) acc += reinterpret_cast<const i32x4*>(part + s * M * N)[q];
+  const float as = a_s[m];
+  float4 o;
+  o.x = ((float)acc[0] * as) * w_s[n];
+  o.y = ((float)acc[1] * as) * w_s[n + 1];
+  o.z = ((float)acc[2] * as) * w_s[n + 2];
+  o.w = ((float)acc[3] * as) * w_s[n + 3];
+  reinterpret_cast<float4*>(out)[q] = o;
+}
+
+// K slices for a linear of this shape, planned for the MI355X's 256 CUs (a fixed count, so the
+// workspace size is a function of the shape alone; the result does not depend on it).  Only when
+// the unsplit items leave CUs idle (few rows): then the power of two s minimising rounds / s, where
+// rounds = ceil(items * s / 256) and every slice keeps an even number of at least 8 K-steps; ties go
+// to the smaller s (less int32 partial traffic).
+constexpr int64_t kLinearCUs = 256;
+int64_t linear_ksplit(int64_t M, int64_t N, int64_t K) {
+  const int64_t items = (M + kDmaBM - 1) / kDmaBM * (N / kDmaBN);
+  const int64_t steps = K / kDmaBK;
+  if (items >= kLinearCUs) return 1;
+  int64_t best = 1;
+  double best_cost = (double)((items + kLinearCUs - 1) / kLinearCUs);
+  for (int64_t s = 2; steps % (2 * s) == 0 && steps / s >= 8; s *= 2) {
+    const double cost = (double)((items * s + kLinearCUs - 1) / kLinearCUs) / (double)s;
+    if (cost < best_cost) {
+      best = s;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
+size_t linear_ws_bytes(int64_t M, int64_t N, int64_t K) {
+  const size_t list = round256(sizeof(int32_t) * (size_t)(1 + kWorkFields * ((M + kDmaBM - 1) / kDmaBM)));
+  const int64_t s = linear_ksplit(M, N, K);
+  return list + (s > 1 ? round256(sizeof(int32_t) * (size_t)(s * M * N)) : 0);
 }
 
 bool linear_supported(int64_t M, int64_t N, int64_t K) {
@@ -1037,6 +1099,7 @@ bool linear_supported(int64_t M, int64_t N, int64_t K) {
 hipError_t linear(const int8_t* a_q, const float* a_s, const int8_t* w, const float* w_s, int64_t M, int64_t N,
                   int64_t K, float* out, void* ws, hipStream_t stream) {
   if (M == 0) return hipSuccess;
+  const int64_t ksplit = linear_ksplit(M, N, K);
   Params prm{};
   prm.a = a_q;
   prm.gather = 0;
@@ -1050,13 +1113,25 @@ hipError_t linear(const int8_t* a_q, const float* a_s, const int8_t* w, const fl
   prm.w_s = w_s;
   prm.out_f32 = out;
   prm.n_tiles = N / kDmaBN;
-  int32_t* work = static_cast<int32_t*>(ws);
+  prm.ksplit = ksplit;
+  char* base = static_cast<char*>(ws);
+  int32_t* work = reinterpret_cast<int32_t*>(base);
   const int64_t tiles = (M + kDmaBM - 1) / kDmaBM;
   hipLaunchKernelGGL(linear_tiles_kernel, dim3((uint32_t)((tiles + kThreads - 1) / kThreads)), dim3(kThreads), 0,
                      stream, M, kDmaBM, work);
-  const int64_t grid = (tiles * prm.n_tiles + 7) / 8 * 8;
-  hipLaunchKernelGGL((grouped_gemm_dma_kernel<kDmaBM, kDmaBN, kDmaWM, kDmaWN, BMap::Plain, Epi::W2Channel>),
+  const int64_t grid = (tiles * prm.n_tiles * ksplit + 7) / 8 * 8;
+  if (ksplit == 1) {
+    hipLaunchKernelGGL((grouped_gemm_dma_kernel<kDmaBM, kDmaBN, kDmaWM, kDmaWN, BMap::Plain, Epi::W2Channel>),
+                       dim3((uint32_t)grid), dim3(kDmaWM * kDmaWN * kWave), 0, stream, prm, (const int32_t*)work);
+    return hipGetLastError();
+  }
+  int32_t* part = reinterpret_cast<int32_t*>(base + round256(sizeof(int32_t) * (size_t)(1 + kWorkFields * tiles)));
+  prm.out_i32 = part;
+  hipLaunchKernelGGL((grouped_gemm_dma_kernel<kDmaBM, kDmaBN, kDmaWM, kDmaWN, BMap::Plain, Epi::I32>),
                      dim3((uint32_t)grid), dim3(kDmaWM * kDmaWN * kWave), 0, stream, prm, (const int32_t*)work);
+  const int64_t q = M * N / 4;
+  hipLaunchKernelGGL(linear_reduce_kernel, dim3((uint32_t)((q + kThreads - 1) / kThreads)), dim3(kThreads), 0, stream,
+                     part, ksplit, M, N, a_s, w_s, out);
   return hipGetLastError();
 }
 

@@ -42,7 +42,7 @@ hipError_t w2_combine(const GroupedShape& s, int32_t scale_mode, const int8_t* h
                       const int32_t* tile_expert, const int32_t* num_tiles, const float* topk_w, float* out,
                       void* ws, hipStream_t stream);
 
-size_t linear_ws_bytes(int64_t M);
+size_t linear_ws_bytes(int64_t M, int64_t N, int64_t K);
 bool linear_supported(int64_t M, int64_t N, int64_t K);
 hipError_t linear(const int8_t* a_q, const float* a_s, const int8_t* w, const float* w_s, int64_t M, int64_t N,
                   int64_t K, float* out, void* ws, hipStream_t stream);
