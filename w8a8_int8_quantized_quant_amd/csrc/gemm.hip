@@ -406,6 +406,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const Params p) 
 // DMA engine.
 
 constexpr int kWorkFields = 5;  // ints per work-list tile
+constexpr int64_t kSuperRows = 4;  // row tiles per super-row of the DMA engine's work order
 constexpr int kDmaBK = 128;  // K bytes per LDS stage: two MFMA K-steps, whole 128-byte L2 lines
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -615,8 +616,8 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_dma_kernel(co
   __shared__ __attribute__((aligned(1024))) int8_t st1[STAGE];
   __shared__ int32_t sh_pid[BM];
 
-  // Work order: expert-major, then N-tile, then the expert's row tiles, so the row tiles that share
-  // a weight tile run side by side and the weights come from HBM once.  XCD-aware: workgroups are
+  // Work order: expert-major, then (super-row, N-tile, row tile), so the row tiles that share a
+  // weight tile run side by side and the weights come from HBM once.  XCD-aware: workgroups are
   // dispatched round-robin over the 8 XCDs; each XCD gets a contiguous stretch of that order.
   const int64_t total = (int64_t)work[0] * p.n_tiles * p.ksplit;
   const int64_t per = (total + 7) / 8;
@@ -628,8 +629,14 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_dma_kernel(co
   const int64_t kslice = p.K / p.ksplit;                           // bytes of K per slice
   const int32_t* any = work + 1 + kWorkFields * (logical / p.n_tiles);  // a tile of the same expert
   const int64_t first = any[3], count = any[4];
+  // Within the expert: super-rows of up to kSuperRows row tiles, N-tile-major inside each, so the
+  // workgroups running together share a few row tiles and a few weight tiles (an expert with at
+  // most kSuperRows row tiles is one super-row: all its row tiles of an N-tile side by side).
   const int64_t local = logical - p.n_tiles * first;
-  const int64_t nt = local / count, ti = first + local % count;
+  const int64_t sr = local / (kSuperRows * p.n_tiles);
+  const int64_t in_sr = count - sr * kSuperRows < kSuperRows ? count - sr * kSuperRows : kSuperRows;
+  const int64_t rem = local - sr * kSuperRows * p.n_tiles;
+  const int64_t nt = rem / in_sr, ti = first + sr * kSuperRows + rem % in_sr;
   const int64_t e = work[1 + kWorkFields * ti];
   const int64_t row0 = work[2 + kWorkFields * ti];
   const int nrows = work[3 + kWorkFields * ti];
