@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=128, help="tokens in the CPU oracle sample")
     ap.add_argument("--no-configs", action="store_true", help="skip the tiny / skew / block workloads")
     ap.add_argument("--no-peaks", action="store_true", help="skip the measured-peak probes")
+    ap.add_argument("--linear-only", action="store_true",
+                    help="only time the dense W8A8 linear shapes and print their figures (profiling)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy kernel 3 times (counter calibration)")
     return ap.parse_args()
@@ -336,6 +338,9 @@ def main():
         sys.exit(2)
     if args.copy_probe:
         copy_probe()
+        return
+    if args.linear_only:
+        print(json.dumps({"linear": linear_figures(args.steps, args.warmup)}), flush=True)
         return
     import torch
 
