@@ -52,6 +52,8 @@ SMALL = {
     # DeepSeek-V3 expert shapes with few experts: the large-batch GEMM engine at the real K sizes.
     "dsv3-e8": small_cfg(name="dsv3-e8", index=40, T=1000, H=7168, I=2048, E=8, k=2, route="softmax", n_group=1,
                          topk_group=1, scaling=1.0),
+    "dsv3-e8-block": small_cfg(name="dsv3-e8-block", index=41, T=1000, H=7168, I=2048, E=8, k=2, route="softmax",
+                               n_group=1, topk_group=1, scaling=1.0, mode="block"),
 }
 
 
@@ -492,12 +494,15 @@ def edge_rows(al, counts):
     return np.array(sorted(rows), dtype=np.int64)
 
 
-def test_large_batch_engine_tile_edges():
-    """Both GEMM stages at the DeepSeek-V3 expert shapes with constructed routing whose expert
-    row counts straddle every tile and fragment boundary: bit-exact second GEMM + combine and the
-    first GEMM's requantized intermediate, at the rows on those boundaries."""
-    name = "dsv3-e8"
+@pytest.mark.parametrize("name", ["dsv3-e8", "dsv3-e8-block"])
+def test_large_batch_engine_tile_edges(name):
+    """Both GEMM stages at the DeepSeek-V3 expert shapes (channel-wise and block-wise) with
+    constructed routing whose expert row counts straddle every tile and fragment boundary:
+    bit-exact second GEMM + combine and the first GEMM's requantized intermediate, at the rows on
+    those boundaries."""
     cfg = cfg_of(name)
+    block = cfg.scale_mode == "block"
+    mode = w8.SCALE_BLOCK128 if block else w8.SCALE_CHANNEL
     bm = block_m_of(cfg)
     say(f"[edges] {name} block_m={bm}")
     L = layer_of(name)
@@ -509,14 +514,15 @@ def test_large_batch_engine_tile_edges():
     R = w8.w8a8_moe_max_rows(cfg.T, cfg.k, cfg.E, bm)
     w = oracle_weights(name, [e for e, n in enumerate(EDGE_COUNTS) if n])
 
-    a_q, a_s = oracle.quant_per_token(oracle.activations_f32(cfg), 0)
+    a_q, a_s = oracle.quant_per_token(oracle.activations_f32(cfg), 128 if block else 0)
     h_q = torch.empty((R, cfg.I), dtype=torch.int8, device=DEV)
-    h_s = torch.empty((R,), dtype=torch.float32, device=DEV)
-    ws = torch.empty(max(w8.w8a8_w13_workspace_bytes(cfg.T, cfg.k, cfg.E, cfg.H, cfg.I, bm), 256),
+    h_s = torch.empty((R, cfg.I // 128) if block else (R,), dtype=torch.float32, device=DEV)
+    ws = torch.empty(max(w8.w8a8_w13_workspace_bytes(cfg.T, cfg.k, cfg.E, cfg.H, cfg.I, bm, mode), 256),
                      dtype=torch.uint8, device=DEV)
-    w8.w8a8_grouped_gemm_w13_silu(dt(a_q), dt(a_s), L.w13, L.w13_scale, d["sorted_pair_ids"], d["padded_offsets"],
-                                  d["tile_expert"], d["num_tiles"], cfg.T, cfg.k, bm, h_q, h_s, ws)
-    rq, rs = oracle.w13_silu(a_q, a_s, w[0], w[1], al, bm, cfg.T, cfg.k, cfg.H, cfg.I, False, rows)
+    fn = w8.w8a8_block_grouped_gemm_w13_silu if block else w8.w8a8_grouped_gemm_w13_silu
+    fn(dt(a_q), dt(a_s), L.w13, L.w13_scale, d["sorted_pair_ids"], d["padded_offsets"], d["tile_expert"],
+       d["num_tiles"], cfg.T, cfg.k, bm, h_q, h_s, ws)
+    rq, rs = oracle.w13_silu(a_q, a_s, w[0], w[1], al, bm, cfg.T, cfg.k, cfg.H, cfg.I, block, rows)
     gq, gs = host(h_q)[rows], host(h_s)[rows]
     rq, rs = rq[rows], rs[rows]
     assert np.all(np.abs(gs - rs) <= 4 * ULP * rs), np.abs(gs / rs - 1).max()
@@ -525,14 +531,16 @@ def test_large_batch_engine_tile_edges():
     assert np.mean(diff > 0) <= 1e-3, np.mean(diff > 0)
 
     hq2 = synth.int8_matrix(R, cfg.I, cfg.seed + 100)
-    hs2 = synth.positive_scales(R, cfg.seed, 1e-3, 3e-2)
+    hs2 = synth.positive_scales(R * (cfg.I // 128 if block else 1), cfg.seed, 1e-3, 3e-2)
+    hs2 = hs2.reshape(R, cfg.I // 128) if block else hs2
     out = torch.full((cfg.T, cfg.H), float("nan"), dtype=torch.float32, device=DEV)
-    ws2 = torch.empty(max(w8.w8a8_w2_workspace_bytes(cfg.T, cfg.k, cfg.E, cfg.H, cfg.I, bm), 256),
+    ws2 = torch.empty(max(w8.w8a8_w2_workspace_bytes(cfg.T, cfg.k, cfg.E, cfg.H, cfg.I, bm, mode), 256),
                       dtype=torch.uint8, device=DEV)
-    w8.w8a8_grouped_gemm_w2_combine(dt(hq2), dt(hs2), L.w2, L.w2_scale, d["sorted_pair_ids"], d["padded_offsets"],
-                                    d["tile_expert"], d["num_tiles"], dt(tw), cfg.T, cfg.k, bm, out, ws2)
+    fn = w8.w8a8_block_grouped_gemm_w2_combine if block else w8.w8a8_grouped_gemm_w2_combine
+    fn(dt(hq2), dt(hs2), L.w2, L.w2_scale, d["sorted_pair_ids"], d["padded_offsets"], d["tile_expert"],
+       d["num_tiles"], dt(tw), cfg.T, cfg.k, bm, out, ws2)
     tokens = np.unique(al["sorted_pair_ids"][rows] // cfg.k)
-    ref = oracle.w2_combine(hq2, hs2, w[2], w[3], al, bm, tw, cfg.T, cfg.k, cfg.H, cfg.I, False, tokens)
+    ref = oracle.w2_combine(hq2, hs2, w[2], w[3], al, bm, tw, cfg.T, cfg.k, cfg.H, cfg.I, block, tokens)
     got = host(out)
     assert np.array_equal(got[tokens], ref)
     assert np.isfinite(got).all()

@@ -705,6 +705,170 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_dma_kernel(co
                                                 ks * p.P * p.N);
 }
 
+// One 4-byte-per-lane DMA (global_load_lds_dword): lane i's value lands at lds + 4 i.
+__device__ __forceinline__ void dma4(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds, 4, 0, 0);
+}
+
+// Block-wise DMA engine.  Each 128-byte K-step is one 128-wide scale block: the MFMAs of a step
+// form int32 partials that are folded into the fp32 sums with that block's scales before the next
+// step.  A 3-stage LDS ring (the tile is 128 rows x 256 columns, 48 KB a stage): step kt reads
+// stage kt, the DMA of stage kt + 2 goes out between its MFMA groups, and at its end only stage
+// kt + 1 must have landed, so two stages stay in flight.  The K loop (KT steps, a compile-time
+// count) is fully unrolled: every stage index and wait count is known, so the compiler tells the
+// buffer being read from the two being filled, and no loop back edge joins in-flight DMA.
+// Scales: the tile's activation scales travel by DMA too, four K-blocks at a time next to the
+// data stage of their first block (each wavefront brings 16 rows x 4 blocks into one of two
+// buffers), so the data waits cover them; the weight scales of the tile's two 128-row weight
+// blocks (every K-block) are read into LDS once, before the loop.
+template <int BM, int BN, int WM, int WN, int KT, BMap MAP, Epi EPI>
+__global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_dma_block_kernel(const Params p,
+                                                                                   const int32_t* __restrict__ work) {
+  constexpr int NT = WM * WN * kWave;
+  constexpr int NW = WM * WN;
+  constexpr int FM = BM / WM / 16;
+  constexpr int FN = BN / WN / 16;
+  constexpr int CPR = kDmaBK / 16;
+  constexpr int A_LD = BM * CPR / NT;
+  constexpr int B_LD = BN * CPR / NT;
+  constexpr int LD = A_LD + B_LD;
+  constexpr int STAGE = (BM + BN) * kDmaBK;
+  constexpr int SG = 4;  // K-blocks per activation-scale DMA
+  static_assert(is_block<EPI>(), "block-wise epilogues only");
+  static_assert(A_LD >= 1 && B_LD >= 1 && (BM * CPR) % NT == 0 && (BN * CPR) % NT == 0, "tile shape");
+  static_assert(KT >= 2 && KT % SG == 0 && LD + 1 < 64, "K steps");
+  static_assert(NW * 16 == BM && kWave == 16 * SG, "one scale DMA per wavefront covers 16 rows x SG blocks");
+  static_assert(BN == 256, "two 128-row weight-scale blocks per tile");
+  static_assert(MAP == BMap::Plain || FN % 2 == 0, "split tiles need gate and up fragments");
+
+  __shared__ __attribute__((aligned(1024))) int8_t st0[STAGE];
+  __shared__ __attribute__((aligned(1024))) int8_t st1[STAGE];
+  __shared__ __attribute__((aligned(1024))) int8_t st2[STAGE];
+  __shared__ __attribute__((aligned(16))) float sas0[NW * kWave];  // activation scales, even groups
+  __shared__ __attribute__((aligned(16))) float sas1[NW * kWave];  // odd groups
+  __shared__ float sh_ws[2][KT];
+  __shared__ int32_t sh_pid[BM];
+  __shared__ float sh_red[WN][BM];
+
+  const int64_t total = (int64_t)work[0] * p.n_tiles;
+  const int64_t per = (total + 7) / 8;
+  const int64_t v = blockIdx.x;
+  if (v >= 8 * per) return;
+  const int64_t logical = (v % 8) * per + v / 8;
+  if (logical >= total) return;
+  const int32_t* any = work + 1 + kWorkFields * (logical / p.n_tiles);
+  const int64_t first = any[3], count = any[4];
+  const int64_t local = logical - p.n_tiles * first;
+  const int64_t sr = local / (kSuperRows * p.n_tiles);
+  const int64_t in_sr = count - sr * kSuperRows < kSuperRows ? count - sr * kSuperRows : kSuperRows;
+  const int64_t rem = local - sr * kSuperRows * p.n_tiles;
+  const int64_t nt = rem / in_sr, ti = first + sr * kSuperRows + rem % in_sr;
+  const int64_t e = work[1 + kWorkFields * ti];
+  const int64_t row0 = work[2 + kWorkFields * ti];
+  const int nrows = work[3 + kWorkFields * ti];
+  const int8_t* wexp = p.w + e * p.N * p.K;
+
+  const int tid = threadIdx.x, l = lane_id();
+  const int wv = __builtin_amdgcn_readfirstlane(tid / kWave), wm = wv / WN, wn = wv % WN;
+  const int g = l >> 4, fr = l & 15;
+  for (int i = tid; i < BM; i += NT) sh_pid[i] = i < nrows ? p.sorted[row0 + i] : (int32_t)p.P;
+  for (int i = tid; i < 2 * KT; i += NT) {
+    const int64_t blk = wrow_of<BN, MAP>(nt, (i / KT) * 128, p.I) / 128;
+    sh_ws[i / KT][i % KT] = p.w_s[(e * (p.N / 128) + blk) * KT + i % KT];
+  }
+  // Source row of a tile row; rows past the real ones read the first row (finite values whose
+  // results are never stored).
+  auto src_row = [&](int r) -> int64_t {
+    const int64_t rr = r < nrows ? r : 0;
+    return p.gather ? (int64_t)(p.sorted[row0 + rr] / p.k) : row0 + rr;
+  };
+
+  uint32_t off[LD];
+#pragma unroll
+  for (int c = 0; c < A_LD; ++c) {
+    const int q = (wv * A_LD + c) * kWave + l, r = q / CPR, kc = (q % CPR) ^ swz(r);
+    off[c] = (uint32_t)(src_row(r) * p.K + kc * 16);
+  }
+#pragma unroll
+  for (int c = 0; c < B_LD; ++c) {
+    const int q = (wv * B_LD + c) * kWave + l, j = q / CPR, kc = (q % CPR) ^ swz(j);
+    off[A_LD + c] = (uint32_t)(wrow_of<BN, MAP>(nt, j, p.I) * p.K + kc * 16);
+  }
+  // activation-scale DMA: lane l brings row wv * 16 + (l & 15) of K-block (group * SG + l / 16)
+  const uint32_t s_off = (uint32_t)(src_row(wv * 16 + (l & 15)) * KT + (l >> 4));
+  const int a_dst = wv * A_LD * 1024, b_dst = BM * kDmaBK + wv * B_LD * 1024;
+
+  i32x4 acc[FM][FN];
+  float accf[FM][FN][4];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      acc[i][j] = i32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) accf[i][j][r] = 0.0f;
+    }
+  const int wrows = nrows - wm * (BM / WM);
+
+#define W8A8_BSTG(j) ((j) == 0 ? st0 : (j) == 1 ? st1 : st2)
+#define W8A8_BSAS(q) (((q) & 1) ? sas1 : sas0)
+  __syncthreads();  // sh_pid, sh_ws
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+#pragma unroll
+    for (int c = 0; c < LD; ++c) {
+      if (c < A_LD)
+        dma16(p.a + (off[c] + (uint32_t)(st * kDmaBK)), W8A8_BSTG(st) + a_dst + c * 1024);
+      else
+        dma16_nt(wexp + (off[c] + (uint32_t)(st * kDmaBK)), W8A8_BSTG(st) + b_dst + (c - A_LD) * 1024);
+    }
+    if (st == 0) dma4(p.a_s + s_off, sas0 + wv * kWave);
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm<LD>());  // stage 0 and the first scale group landed
+
+  // Uniform bases of the stage two steps ahead, advanced one step at a time; the empty asm keeps
+  // the compiler from precomputing every step's address up front.
+  const int8_t* a_next = p.a + 2 * kDmaBK;
+  const int8_t* b_next = wexp + 2 * kDmaBK;
+#pragma clang loop unroll(full)
+  for (int kt = 0; kt < KT; ++kt) {
+    __builtin_amdgcn_s_waitcnt(kLgkm0Imm);
+    barrier_no_fence();
+    const bool more = kt + 2 < KT;
+    const bool sdma = more && (kt + 2) % SG == 0;  // scale group of stage kt + 2 goes out now
+    if (sdma) dma4(p.a_s + s_off + (kt + 2), W8A8_BSAS((kt + 2) / SG) + wv * kWave);
+    dma_stage<BM, BN, WM, WN, A_LD, LD, MAP>(W8A8_BSTG(kt % 3), W8A8_BSTG((kt + 2) % 3), a_next, b_next, off, a_dst,
+                                             b_dst, 0u, more, acc, wm, wn, g, fr, wrows);
+    a_next += kDmaBK;
+    b_next += kDmaBK;
+    asm volatile("" : "+s"(a_next), "+s"(b_next));
+    if (wrows > 0) {
+      float as[FM][4], ws[FN];
+      const float* sa = W8A8_BSAS(kt / SG) + (kt % SG) * 16 + (l >> 4) * 4;
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) {
+        const f32x4 s4 = *reinterpret_cast<const f32x4*>(sa + (wm * FM + fm) * kWave);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) as[fm][r] = s4[r];
+      }
+      const float w0 = sh_ws[0][kt], w1 = sh_ws[1][kt];
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) ws[fn] = brow_of<BN, WN, FN, MAP>(wn, fn) >= 128 ? w1 : w0;
+      block_flush<FM, FN>(acc, accf, as, ws);
+    }
+    if (sdma)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm<LD + 1>());
+    else if (more)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm<LD>());
+    else
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
+  }
+#undef W8A8_BSAS
+#undef W8A8_BSTG
+  __syncthreads();
+  epilogue<BM, BN, WM, WN, FM, FN, MAP, EPI>(p, acc, accf, sh_pid, sh_red, row0, nt, e, wm, wn, l, tid);
+}
+
 // Work list of the DMA engine: per expert, tiles of up to bmk real rows of its sorted segment.
 // work[0] = number of tiles; tile i = (expert, first sorted row, rows, index of the expert's
 // first tile, number of the expert's tiles) at work[1 + kWorkFields * i].
@@ -882,13 +1046,23 @@ bool use_dma(const GroupedShape& s) {
          (uint64_t)s.max_rows * s.I < (1ull << 32) && (uint64_t)2 * s.I * s.H < (1ull << 32);
 }
 
-int64_t dma_max_tiles(const GroupedShape& s) {
-  const int64_t P = s.T * s.k;
-  return (P + kDmaBM - 1) / kDmaBM + std::min<int64_t>(s.E, P);
+// Block-wise DMA engine: 128-row tiles, its K loops unrolled for the DeepSeek-V3 layer (hidden 7168,
+// intermediate 2048); experts of 16 rows or more on average.
+constexpr int kDmaBlockBM = 128;
+constexpr int kDmaH = 7168, kDmaI = 2048;
+bool use_dma_block(const GroupedShape& s) {
+  return s.T * s.k >= 16 * s.E && s.H == kDmaH && s.I == kDmaI && (uint64_t)s.T * s.H < (1ull << 32) &&
+         (uint64_t)s.max_rows * s.I < (1ull << 32);
 }
 
+int64_t dma_max_tiles(const GroupedShape& s, int64_t bm = kDmaBM) {
+  const int64_t P = s.T * s.k;
+  return (P + bm - 1) / bm + std::min<int64_t>(s.E, P);
+}
+
+// Tile lists of either DMA engine fit.
 size_t work_bytes(const GroupedShape& s) {
-  return round256(sizeof(int32_t) * (size_t)(1 + kWorkFields * dma_max_tiles(s)));
+  return round256(sizeof(int32_t) * (size_t)(1 + kWorkFields * dma_max_tiles(s, kDmaBlockBM)));
 }
 
 // N-tiles of the first GEMM (one row maximum each per row).
@@ -931,10 +1105,23 @@ hipError_t launch_dma(Params prm, const GroupedShape& s, const int32_t* padded_o
   return hipGetLastError();
 }
 
+template <BMap MAP, Epi EPI, int KT>
+hipError_t launch_dma_block(Params prm, const GroupedShape& s, const int32_t* padded_offsets, int32_t* work,
+                            hipStream_t stream) {
+  prm.n_tiles = MAP == BMap::Plain ? prm.N / kDmaBN : prm.I / (kDmaBN / 2);
+  prm.ksplit = 1;
+  hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(kListThreads), 0, stream, prm.sorted, padded_offsets,
+                     (int)s.E, (int32_t)prm.P, kDmaBlockBM, work);
+  const int64_t grid = (dma_max_tiles(s, kDmaBlockBM) * prm.n_tiles + 7) / 8 * 8;
+  hipLaunchKernelGGL((grouped_gemm_dma_block_kernel<kDmaBlockBM, kDmaBN, kDmaWM, kDmaWN, KT, MAP, EPI>),
+                     dim3((uint32_t)grid), dim3(kDmaWM * kDmaWN * kWave), 0, stream, prm, (const int32_t*)work);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 size_t w13_ws_bytes(const GroupedShape& s, int32_t scale_mode) {
-  if (scale_mode == 1) return 256;
+  if (scale_mode == 1) return use_dma_block(s) ? work_bytes(s) : 256;
   return round256(sizeof(float) * (size_t)(s.max_rows * s.I)) +
          round256(sizeof(float) * (size_t)(s.max_rows * w13_n_tiles(s, scale_mode))) + work_bytes(s);
 }
@@ -985,7 +1172,12 @@ hipError_t w13_silu(const GroupedShape& s, int32_t scale_mode, const int8_t* a_q
   prm.w_s = w13_s;
   prm.h_q = h_q;
   prm.h_s = h_s;
-  if (scale_mode == 1) return launch_bm<BMap::Split, Epi::W13Block, kBNBlock13>(prm, s.max_rows, stream);
+  if (scale_mode == 1) {
+    if (use_dma_block(s))
+      return launch_dma_block<BMap::Split, Epi::W13Block, kDmaH / kDmaBK>(prm, s, padded_offsets,
+                                                                          static_cast<int32_t*>(ws), stream);
+    return launch_bm<BMap::Split, Epi::W13Block, kBNBlock13>(prm, s.max_rows, stream);
+  }
   char* base = static_cast<char*>(ws);
   const int64_t n_tiles = w13_n_tiles(s, scale_mode);
   float* hf = reinterpret_cast<float*>(base);
@@ -1032,7 +1224,9 @@ hipError_t w2_combine(const GroupedShape& s, int32_t scale_mode, const int8_t* h
   prm.out_f32 = y;
   hipError_t err;
   if (scale_mode == 1)
-    err = launch_bm<BMap::Plain, Epi::W2Block, kBNStaged>(prm, s.max_rows, stream);
+    err = use_dma_block(s) ? launch_dma_block<BMap::Plain, Epi::W2Block, kDmaI / kDmaBK>(prm, s, padded_offsets, work,
+                                                                                        stream)
+                           : launch_bm<BMap::Plain, Epi::W2Block, kBNStaged>(prm, s.max_rows, stream);
   else if (use_dma(s))
     err = launch_dma<BMap::Plain, Epi::W2Channel>(prm, s, padded_offsets, work, stream);
   else
