@@ -54,6 +54,9 @@ SMALL = {
                          topk_group=1, scaling=1.0),
     "dsv3-e8-block": small_cfg(name="dsv3-e8-block", index=41, T=1000, H=7168, I=2048, E=8, k=2, route="softmax",
                                n_group=1, topk_group=1, scaling=1.0, mode="block"),
+    # 125 rows per expert on average: the mid-batch (128-row tile) engine, channel-wise
+    "dsv3-e16": small_cfg(name="dsv3-e16", index=42, T=1000, H=7168, I=2048, E=16, k=2, route="softmax", n_group=1,
+                          topk_group=1, scaling=1.0),
 }
 
 
@@ -466,11 +469,15 @@ def test_second_gemm_combine_bit_exact(name):
 EDGE_COUNTS = [0, 1, 17, 320, 321, 650, 330, 361]
 
 
+def edge_counts(cfg):
+    return EDGE_COUNTS + [0] * (cfg.E - len(EDGE_COUNTS))
+
+
 def edge_routing(cfg):
     """Top-2 ids with the counts above (two distinct experts per token: no expert holds more than
     T rows, so a sorted run never meets itself T places later), tokens shuffled so each expert's
     rows gather scattered token rows."""
-    flat = np.repeat(np.arange(cfg.E, dtype=np.int32), EDGE_COUNTS)
+    flat = np.repeat(np.arange(cfg.E, dtype=np.int32), edge_counts(cfg))
     T = len(flat) // 2
     assert T == cfg.T and cfg.k == 2 and max(EDGE_COUNTS) <= T
     ids = np.stack([flat[:T], flat[T:]], axis=1)
@@ -494,7 +501,7 @@ def edge_rows(al, counts):
     return np.array(sorted(rows), dtype=np.int64)
 
 
-@pytest.mark.parametrize("name", ["dsv3-e8", "dsv3-e8-block"])
+@pytest.mark.parametrize("name", ["dsv3-e8", "dsv3-e16", "dsv3-e8-block"])
 def test_large_batch_engine_tile_edges(name):
     """Both GEMM stages at the DeepSeek-V3 expert shapes (channel-wise and block-wise) with
     constructed routing whose expert row counts straddle every tile and fragment boundary:
@@ -509,10 +516,11 @@ def test_large_batch_engine_tile_edges(name):
     ids, tw = edge_routing(cfg)
     P = cfg.T * cfg.k
     al, d = oracle_align_dev(ids, cfg.E, bm)
-    assert list(al["counts"]) == EDGE_COUNTS
-    rows = edge_rows(al, EDGE_COUNTS)
+    counts = edge_counts(cfg)
+    assert list(al["counts"]) == counts
+    rows = edge_rows(al, counts)
     R = w8.w8a8_moe_max_rows(cfg.T, cfg.k, cfg.E, bm)
-    w = oracle_weights(name, [e for e, n in enumerate(EDGE_COUNTS) if n])
+    w = oracle_weights(name, [e for e, n in enumerate(counts) if n])
 
     a_q, a_s = oracle.quant_per_token(oracle.activations_f32(cfg), 128 if block else 0)
     h_q = torch.empty((R, cfg.I), dtype=torch.int8, device=DEV)

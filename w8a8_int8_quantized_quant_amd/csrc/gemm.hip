@@ -13,22 +13,26 @@
 // scales): int32 partial per 128-wide K-block, acc += ((float)part * a_s) * w_s
 // in ascending K-block order, requantization per (row, 128-group).
 //
-// Two tile engines share the epilogues.  Both issue v_mfma_i32_16x16x64_i8 on
-// 16 x 16 sub-tiles; accumulator element r of a fragment sits at fragment row
-// (lane/16)*4 + r and fragment column lane%16.  In the first GEMM a B tile holds
-// BN/2 gate rows and the matching BN/2 up rows, so the lane that owns gate
-// column n also owns up column n and forms SiLU(gate) * up in registers.
+// Three tile engines.  All issue v_mfma_i32_16x16x64_i8 on 16 x 16 sub-tiles;
+// accumulator element r of a fragment sits at fragment row (lane/16)*4 + r and
+// fragment column lane%16.  In the first GEMM a B tile holds BN/2 gate rows and
+// the matching BN/2 up rows, so the lane that owns gate column n also owns up
+// column n and forms SiLU(gate) * up in registers.
 //  - Staged engine (few rows per expert, weight streaming): tiles of block_m
 //    rows from the align step, K advances 128 bytes per stage through a double
 //    buffered LDS tile loaded via registers.  Many small workgroups keep many
 //    weight bytes in flight.
-//  - DMA engine (many rows per expert, MFMA-bound): 128 x 256 tiles of real rows
-//    only (a device-built work list, so align padding costs no MFMA work), a
-//    3-stage LDS ring of 128-byte K-slices (whole L2 lines) filled by global_load_lds_dwordx4,
-//    XOR-swizzled 16-byte chunks so fragment reads are conflict-free, explicit
-//    vmcnt waits so three stages stay in flight, and an XCD-aware order in
-//    which each XCD walks a contiguous stretch of (tile, N-tile) work so the
-//    A rows and the expert's weights are reused from its own L2.
+//  - DMA engine (hundreds of rows per expert, MFMA-bound): 320 x 256 tiles of
+//    real rows only (a device-built work list, so align padding costs no MFMA
+//    work), two LDS stages of 128-byte K-slices (whole L2 lines) filled by
+//    global_load_lds_dwordx4, XOR-swizzled 16-byte chunks so fragment reads are
+//    conflict-free, and an XCD-aware order in which each XCD walks a contiguous
+//    stretch of (tile, N-tile) work so the A rows and the expert's weights are
+//    reused from its own L2.
+//  - Ring engine (tens to a couple of hundred rows per expert, and every
+//    block-wise batch past decode): the DMA engine's work list and order with
+//    128 x 256 tiles and a 3-stage LDS ring whose K loop is unrolled for the
+//    layer's K sizes, so two stages are always in flight.
 // Grids cover the worst case; workgroups past the device-side tile count exit
 // at once (no host read, graph-capturable).
 #include <algorithm>
@@ -710,20 +714,22 @@ __device__ __forceinline__ void dma4(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds, 4, 0, 0);
 }
 
-// Block-wise DMA engine.  Each 128-byte K-step is one 128-wide scale block: the MFMAs of a step
-// form int32 partials that are folded into the fp32 sums with that block's scales before the next
-// step.  A 3-stage LDS ring (the tile is 128 rows x 256 columns, 48 KB a stage): step kt reads
-// stage kt, the DMA of stage kt + 2 goes out between its MFMA groups, and at its end only stage
-// kt + 1 must have landed, so two stages stay in flight.  The K loop (KT steps, a compile-time
-// count) is fully unrolled: every stage index and wait count is known, so the compiler tells the
-// buffer being read from the two being filled, and no loop back edge joins in-flight DMA.
-// Scales: the tile's activation scales travel by DMA too, four K-blocks at a time next to the
-// data stage of their first block (each wavefront brings 16 rows x 4 blocks into one of two
-// buffers), so the data waits cover them; the weight scales of the tile's two 128-row weight
-// blocks (every K-block) are read into LDS once, before the loop.
+// Ring engine: the DMA engine's tiles and work order with a 3-stage LDS ring (the tile is 128 rows
+// x 256 columns, 48 KB a stage).  Step kt reads stage kt, the DMA of stage kt + 2 goes out between
+// its MFMA groups, and at its end only stage kt + 1 must have landed, so two stages stay in flight
+// at all times.  The K loop (KT steps of 128 bytes, a compile-time count) is fully unrolled: every
+// stage index and wait count is known, so the compiler tells the buffer being read from the two
+// being filled, and no loop back edge joins in-flight DMA.
+// Block-wise scales: each step is one 128-wide K-block, whose int32 partials are folded into the
+// fp32 sums at the end of the step.  The tile's activation scales travel by DMA too, four K-blocks
+// at a time next to the data stage of their first block (each wavefront brings 16 rows x 4 blocks
+// into one of two buffers), so the data waits cover them; the weight scales of the tile's two
+// 128-row weight blocks (every K-block) are read into LDS once, before the loop.
+// Channel-wise: int32 sums over all of K, then the DMA engine's LDS-staged epilogue.
 template <int BM, int BN, int WM, int WN, int KT, BMap MAP, Epi EPI>
-__global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_dma_block_kernel(const Params p,
-                                                                                   const int32_t* __restrict__ work) {
+__global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_ring_kernel(const Params p,
+                                                                              const int32_t* __restrict__ work) {
+  constexpr bool kBlock = is_block<EPI>();
   constexpr int NT = WM * WN * kWave;
   constexpr int NW = WM * WN;
   constexpr int FM = BM / WM / 16;
@@ -734,21 +740,21 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_dma_block_ker
   constexpr int LD = A_LD + B_LD;
   constexpr int STAGE = (BM + BN) * kDmaBK;
   constexpr int SG = 4;  // K-blocks per activation-scale DMA
-  static_assert(is_block<EPI>(), "block-wise epilogues only");
+  static_assert(EPI != Epi::I32, "scaled epilogues only");
   static_assert(A_LD >= 1 && B_LD >= 1 && (BM * CPR) % NT == 0 && (BN * CPR) % NT == 0, "tile shape");
   static_assert(KT >= 2 && KT % SG == 0 && LD + 1 < 64, "K steps");
-  static_assert(NW * 16 == BM && kWave == 16 * SG, "one scale DMA per wavefront covers 16 rows x SG blocks");
-  static_assert(BN == 256, "two 128-row weight-scale blocks per tile");
+  static_assert(!kBlock || (NW * 16 == BM && kWave == 16 * SG), "one scale DMA per wavefront: 16 rows x SG blocks");
+  static_assert(!kBlock || BN == 256, "two 128-row weight-scale blocks per tile");
   static_assert(MAP == BMap::Plain || FN % 2 == 0, "split tiles need gate and up fragments");
 
   __shared__ __attribute__((aligned(1024))) int8_t st0[STAGE];
   __shared__ __attribute__((aligned(1024))) int8_t st1[STAGE];
   __shared__ __attribute__((aligned(1024))) int8_t st2[STAGE];
-  __shared__ __attribute__((aligned(16))) float sas0[NW * kWave];  // activation scales, even groups
-  __shared__ __attribute__((aligned(16))) float sas1[NW * kWave];  // odd groups
-  __shared__ float sh_ws[2][KT];
+  __shared__ __attribute__((aligned(16))) float sas0[kBlock ? NW * kWave : 1];  // activation scales, even groups
+  __shared__ __attribute__((aligned(16))) float sas1[kBlock ? NW * kWave : 1];  // odd groups
+  __shared__ float sh_ws[kBlock ? 2 : 1][kBlock ? KT : 1];
   __shared__ int32_t sh_pid[BM];
-  __shared__ float sh_red[WN][BM];
+  __shared__ float sh_red[kBlock ? WN : 1][BM];
 
   const int64_t total = (int64_t)work[0] * p.n_tiles;
   const int64_t per = (total + 7) / 8;
@@ -772,9 +778,11 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_dma_block_ker
   const int wv = __builtin_amdgcn_readfirstlane(tid / kWave), wm = wv / WN, wn = wv % WN;
   const int g = l >> 4, fr = l & 15;
   for (int i = tid; i < BM; i += NT) sh_pid[i] = i < nrows ? p.sorted[row0 + i] : (int32_t)p.P;
-  for (int i = tid; i < 2 * KT; i += NT) {
-    const int64_t blk = wrow_of<BN, MAP>(nt, (i / KT) * 128, p.I) / 128;
-    sh_ws[i / KT][i % KT] = p.w_s[(e * (p.N / 128) + blk) * KT + i % KT];
+  if constexpr (kBlock) {
+    for (int i = tid; i < 2 * KT; i += NT) {
+      const int64_t blk = wrow_of<BN, MAP>(nt, (i / KT) * 128, p.I) / 128;
+      sh_ws[i / KT][i % KT] = p.w_s[(e * (p.N / 128) + blk) * KT + i % KT];
+    }
   }
   // Source row of a tile row; rows past the real ones read the first row (finite values whose
   // results are never stored).
@@ -795,36 +803,36 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_dma_block_ker
     off[A_LD + c] = (uint32_t)(wrow_of<BN, MAP>(nt, j, p.I) * p.K + kc * 16);
   }
   // activation-scale DMA: lane l brings row wv * 16 + (l & 15) of K-block (group * SG + l / 16)
-  const uint32_t s_off = (uint32_t)(src_row(wv * 16 + (l & 15)) * KT + (l >> 4));
+  const uint32_t s_off = kBlock ? (uint32_t)(src_row(wv * 16 + (l & 15)) * KT + (l >> 4)) : 0u;
   const int a_dst = wv * A_LD * 1024, b_dst = BM * kDmaBK + wv * B_LD * 1024;
 
   i32x4 acc[FM][FN];
-  float accf[FM][FN][4];
+  float accf[FM][FN][kBlock ? 4 : 1];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       acc[i][j] = i32x4{0, 0, 0, 0};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) accf[i][j][r] = 0.0f;
+      for (int r = 0; r < (kBlock ? 4 : 1); ++r) accf[i][j][r] = 0.0f;
     }
   const int wrows = nrows - wm * (BM / WM);
 
-#define W8A8_BSTG(j) ((j) == 0 ? st0 : (j) == 1 ? st1 : st2)
-#define W8A8_BSAS(q) (((q) & 1) ? sas1 : sas0)
+#define W8A8_RSTG(j) ((j) == 0 ? st0 : (j) == 1 ? st1 : st2)
+#define W8A8_RSAS(q) (((q) & 1) ? sas1 : sas0)
   __syncthreads();  // sh_pid, sh_ws
 #pragma unroll
   for (int st = 0; st < 2; ++st) {
 #pragma unroll
     for (int c = 0; c < LD; ++c) {
       if (c < A_LD)
-        dma16(p.a + (off[c] + (uint32_t)(st * kDmaBK)), W8A8_BSTG(st) + a_dst + c * 1024);
+        dma16(p.a + (off[c] + (uint32_t)(st * kDmaBK)), W8A8_RSTG(st) + a_dst + c * 1024);
       else
-        dma16_nt(wexp + (off[c] + (uint32_t)(st * kDmaBK)), W8A8_BSTG(st) + b_dst + (c - A_LD) * 1024);
+        dma16_nt(wexp + (off[c] + (uint32_t)(st * kDmaBK)), W8A8_RSTG(st) + b_dst + (c - A_LD) * 1024);
     }
-    if (st == 0) dma4(p.a_s + s_off, sas0 + wv * kWave);
+    if (kBlock && st == 0) dma4(p.a_s + s_off, sas0 + wv * kWave);
   }
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm<LD>());  // stage 0 and the first scale group landed
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm<LD>());  // stage 0 (and the first scale group) landed
 
   // Uniform bases of the stage two steps ahead, advanced one step at a time; the empty asm keeps
   // the compiler from precomputing every step's address up front.
@@ -835,26 +843,28 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_dma_block_ker
     __builtin_amdgcn_s_waitcnt(kLgkm0Imm);
     barrier_no_fence();
     const bool more = kt + 2 < KT;
-    const bool sdma = more && (kt + 2) % SG == 0;  // scale group of stage kt + 2 goes out now
-    if (sdma) dma4(p.a_s + s_off + (kt + 2), W8A8_BSAS((kt + 2) / SG) + wv * kWave);
-    dma_stage<BM, BN, WM, WN, A_LD, LD, MAP>(W8A8_BSTG(kt % 3), W8A8_BSTG((kt + 2) % 3), a_next, b_next, off, a_dst,
+    const bool sdma = kBlock && more && (kt + 2) % SG == 0;  // scale group of stage kt + 2 goes out now
+    if (sdma) dma4(p.a_s + s_off + (kt + 2), W8A8_RSAS((kt + 2) / SG) + wv * kWave);
+    dma_stage<BM, BN, WM, WN, A_LD, LD, MAP>(W8A8_RSTG(kt % 3), W8A8_RSTG((kt + 2) % 3), a_next, b_next, off, a_dst,
                                              b_dst, 0u, more, acc, wm, wn, g, fr, wrows);
     a_next += kDmaBK;
     b_next += kDmaBK;
     asm volatile("" : "+s"(a_next), "+s"(b_next));
-    if (wrows > 0) {
-      float as[FM][4], ws[FN];
-      const float* sa = W8A8_BSAS(kt / SG) + (kt % SG) * 16 + (l >> 4) * 4;
+    if constexpr (kBlock) {
+      if (wrows > 0) {
+        float as[FM][4], ws[FN];
+        const float* sa = W8A8_RSAS(kt / SG) + (kt % SG) * 16 + (l >> 4) * 4;
 #pragma unroll
-      for (int fm = 0; fm < FM; ++fm) {
-        const f32x4 s4 = *reinterpret_cast<const f32x4*>(sa + (wm * FM + fm) * kWave);
+        for (int fm = 0; fm < FM; ++fm) {
+          const f32x4 s4 = *reinterpret_cast<const f32x4*>(sa + (wm * FM + fm) * kWave);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) as[fm][r] = s4[r];
+          for (int r = 0; r < 4; ++r) as[fm][r] = s4[r];
+        }
+        const float w0 = sh_ws[0][kt], w1 = sh_ws[1][kt];
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) ws[fn] = brow_of<BN, WN, FN, MAP>(wn, fn) >= 128 ? w1 : w0;
+        block_flush<FM, FN>(acc, accf, as, ws);
       }
-      const float w0 = sh_ws[0][kt], w1 = sh_ws[1][kt];
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn) ws[fn] = brow_of<BN, WN, FN, MAP>(wn, fn) >= 128 ? w1 : w0;
-      block_flush<FM, FN>(acc, accf, as, ws);
     }
     if (sdma)
       __builtin_amdgcn_s_waitcnt(vmcnt_imm<LD + 1>());
@@ -863,10 +873,13 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_dma_block_ker
     else
       __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
   }
-#undef W8A8_BSAS
-#undef W8A8_BSTG
+#undef W8A8_RSAS
+#undef W8A8_RSTG
   __syncthreads();
-  epilogue<BM, BN, WM, WN, FM, FN, MAP, EPI>(p, acc, accf, sh_pid, sh_red, row0, nt, e, wm, wn, l, tid);
+  if constexpr (kBlock)
+    epilogue<BM, BN, WM, WN, FM, FN, MAP, EPI>(p, acc, accf, sh_pid, sh_red, row0, nt, e, wm, wn, l, tid);
+  else
+    dma_epilogue<BM, BN, WM, WN, STAGE, MAP, EPI>(p, acc, sh_pid, st0, st1, row0, nt, e, wm, wn, wv, l, 0);
 }
 
 // Work list of the DMA engine: per expert, tiles of up to bmk real rows of its sorted segment.
@@ -1046,13 +1059,17 @@ bool use_dma(const GroupedShape& s) {
          (uint64_t)s.max_rows * s.I < (1ull << 32) && (uint64_t)2 * s.I * s.H < (1ull << 32);
 }
 
-// Block-wise DMA engine: 128-row tiles, its K loops unrolled for the DeepSeek-V3 layer (hidden 7168,
-// intermediate 2048); experts of 16 rows or more on average.
-constexpr int kDmaBlockBM = 128;
-constexpr int kDmaH = 7168, kDmaI = 2048;
-bool use_dma_block(const GroupedShape& s) {
-  return s.T * s.k >= 16 * s.E && s.H == kDmaH && s.I == kDmaI && (uint64_t)s.T * s.H < (1ull << 32) &&
-         (uint64_t)s.max_rows * s.I < (1ull << 32);
+// Ring engine: 128-row tiles, its K loops unrolled for the DeepSeek-V3 layer (hidden 7168,
+// intermediate 2048).  Block-wise it takes every batch with 16 or more rows per expert on average;
+// channel-wise the batches between that and kRingMaxAvgRows rows per expert, above which the
+// 320-row tiles of the DMA engine feed the MFMAs with fewer bytes per operation.
+constexpr int kRingBM = 128;
+constexpr int kRingH = 7168, kRingI = 2048;
+constexpr int64_t kRingMinAvgRows = 16, kRingMaxAvgRows = 192;
+bool use_ring(const GroupedShape& s, int32_t scale_mode) {
+  const int64_t P = s.T * s.k;
+  return P >= kRingMinAvgRows * s.E && (scale_mode == 1 || P < kRingMaxAvgRows * s.E) && s.H == kRingH &&
+         s.I == kRingI && (uint64_t)s.T * s.H < (1ull << 32) && (uint64_t)s.max_rows * s.I < (1ull << 32);
 }
 
 int64_t dma_max_tiles(const GroupedShape& s, int64_t bm = kDmaBM) {
@@ -1062,13 +1079,13 @@ int64_t dma_max_tiles(const GroupedShape& s, int64_t bm = kDmaBM) {
 
 // Tile lists of either DMA engine fit.
 size_t work_bytes(const GroupedShape& s) {
-  return round256(sizeof(int32_t) * (size_t)(1 + kWorkFields * dma_max_tiles(s, kDmaBlockBM)));
+  return round256(sizeof(int32_t) * (size_t)(1 + kWorkFields * dma_max_tiles(s, kRingBM)));
 }
 
 // N-tiles of the first GEMM (one row maximum each per row).
 int64_t w13_n_tiles(const GroupedShape& s, int32_t scale_mode) {
   if (scale_mode == 1) return s.I / (kBNBlock13 / 2);
-  return use_dma(s) ? s.I / (kDmaBN / 2) : s.I / (kBNStaged / 2);
+  return use_ring(s, scale_mode) || use_dma(s) ? s.I / (kDmaBN / 2) : s.I / (kBNStaged / 2);
 }
 
 template <int BM, int BN, int WM, int WN, BMap MAP, Epi EPI>
@@ -1106,14 +1123,14 @@ hipError_t launch_dma(Params prm, const GroupedShape& s, const int32_t* padded_o
 }
 
 template <BMap MAP, Epi EPI, int KT>
-hipError_t launch_dma_block(Params prm, const GroupedShape& s, const int32_t* padded_offsets, int32_t* work,
+hipError_t launch_ring(Params prm, const GroupedShape& s, const int32_t* padded_offsets, int32_t* work,
                             hipStream_t stream) {
   prm.n_tiles = MAP == BMap::Plain ? prm.N / kDmaBN : prm.I / (kDmaBN / 2);
   prm.ksplit = 1;
   hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(kListThreads), 0, stream, prm.sorted, padded_offsets,
-                     (int)s.E, (int32_t)prm.P, kDmaBlockBM, work);
-  const int64_t grid = (dma_max_tiles(s, kDmaBlockBM) * prm.n_tiles + 7) / 8 * 8;
-  hipLaunchKernelGGL((grouped_gemm_dma_block_kernel<kDmaBlockBM, kDmaBN, kDmaWM, kDmaWN, KT, MAP, EPI>),
+                     (int)s.E, (int32_t)prm.P, kRingBM, work);
+  const int64_t grid = (dma_max_tiles(s, kRingBM) * prm.n_tiles + 7) / 8 * 8;
+  hipLaunchKernelGGL((grouped_gemm_ring_kernel<kRingBM, kDmaBN, kDmaWM, kDmaWN, KT, MAP, EPI>),
                      dim3((uint32_t)grid), dim3(kDmaWM * kDmaWN * kWave), 0, stream, prm, (const int32_t*)work);
   return hipGetLastError();
 }
@@ -1121,7 +1138,7 @@ hipError_t launch_dma_block(Params prm, const GroupedShape& s, const int32_t* pa
 }  // namespace
 
 size_t w13_ws_bytes(const GroupedShape& s, int32_t scale_mode) {
-  if (scale_mode == 1) return use_dma_block(s) ? work_bytes(s) : 256;
+  if (scale_mode == 1) return use_ring(s, 1) ? work_bytes(s) : 256;
   return round256(sizeof(float) * (size_t)(s.max_rows * s.I)) +
          round256(sizeof(float) * (size_t)(s.max_rows * w13_n_tiles(s, scale_mode))) + work_bytes(s);
 }
@@ -1173,9 +1190,9 @@ hipError_t w13_silu(const GroupedShape& s, int32_t scale_mode, const int8_t* a_q
   prm.h_q = h_q;
   prm.h_s = h_s;
   if (scale_mode == 1) {
-    if (use_dma_block(s))
-      return launch_dma_block<BMap::Split, Epi::W13Block, kDmaH / kDmaBK>(prm, s, padded_offsets,
-                                                                          static_cast<int32_t*>(ws), stream);
+    if (use_ring(s, 1))
+      return launch_ring<BMap::Split, Epi::W13Block, kRingH / kDmaBK>(prm, s, padded_offsets,
+                                                                      static_cast<int32_t*>(ws), stream);
     return launch_bm<BMap::Split, Epi::W13Block, kBNBlock13>(prm, s.max_rows, stream);
   }
   char* base = static_cast<char*>(ws);
@@ -1186,8 +1203,10 @@ hipError_t w13_silu(const GroupedShape& s, int32_t scale_mode, const int8_t* a_q
                                              round256(sizeof(float) * (size_t)(s.max_rows * n_tiles)));
   prm.out_f32 = hf;
   prm.part_amax = part;
-  hipError_t err = use_dma(s) ? launch_dma<BMap::Split, Epi::W13Channel>(prm, s, padded_offsets, work, stream)
-                              : launch_bm<BMap::Split, Epi::W13Channel, kBNStaged>(prm, s.max_rows, stream);
+  hipError_t err = use_ring(s, 0)
+                       ? launch_ring<BMap::Split, Epi::W13Channel, kRingH / kDmaBK>(prm, s, padded_offsets, work, stream)
+                   : use_dma(s) ? launch_dma<BMap::Split, Epi::W13Channel>(prm, s, padded_offsets, work, stream)
+                                : launch_bm<BMap::Split, Epi::W13Channel, kBNStaged>(prm, s.max_rows, stream);
   if (err != hipSuccess) return err;
   const int64_t blocks = (s.max_rows + kThreads / kWave - 1) / (kThreads / kWave);
   if (blocks == 0) return hipSuccess;
@@ -1224,9 +1243,10 @@ hipError_t w2_combine(const GroupedShape& s, int32_t scale_mode, const int8_t* h
   prm.out_f32 = y;
   hipError_t err;
   if (scale_mode == 1)
-    err = use_dma_block(s) ? launch_dma_block<BMap::Plain, Epi::W2Block, kDmaI / kDmaBK>(prm, s, padded_offsets, work,
-                                                                                        stream)
-                           : launch_bm<BMap::Plain, Epi::W2Block, kBNStaged>(prm, s.max_rows, stream);
+    err = use_ring(s, 1) ? launch_ring<BMap::Plain, Epi::W2Block, kRingI / kDmaBK>(prm, s, padded_offsets, work, stream)
+                         : launch_bm<BMap::Plain, Epi::W2Block, kBNStaged>(prm, s.max_rows, stream);
+  else if (use_ring(s, 0))
+    err = launch_ring<BMap::Plain, Epi::W2Channel, kRingI / kDmaBK>(prm, s, padded_offsets, work, stream);
   else if (use_dma(s))
     err = launch_dma<BMap::Plain, Epi::W2Channel>(prm, s, padded_offsets, work, stream);
   else
