@@ -434,3 +434,223 @@ ORACLE_EXPORT void oracle_linear(const int8_t* a_q, const float* a_s, const int8
     }
   }
 }
+
+/* ------------------------------------------------------------------ FP8 block-wise path
+ *
+ * SGLang PR #8273 "support cutlass_moe_fp8 for deepepmoe" (description, "New FP8 MoE Kernel"):
+ * an MoE whose weights are FP8 with one scale per block and whose activations are FP8 with one
+ * scale per token-group, multiplied by a block-scaled grouped GEMM (fp8_blockwise_scaled_grouped_mm
+ * in its review).  The pages name the scheme and no arithmetic; the readings taken here:
+ *  - FP8 is E4M3 as the OCP 8-bit floating-point specification defines it: sign bit, 4 exponent
+ *    bits with bias 7, 3 mantissa bits, subnormals at exponent field 0, largest finite value 448,
+ *    no infinities; codes 0x7F and 0xFF are NaN and are never produced.
+ *  - Scales follow the INT8 rule with 448 (the largest finite E4M3 value) in place of 127:
+ *    scale = max(max|x| / 448, 1e-8); code = the E4M3 value nearest to x / scale, ties to the
+ *    even mantissa, with x / scale clamped to [-448, 448] first; a result of zero keeps the sign
+ *    of x / scale.  Blocks are those of the INT8 block-wise path: 128 x 128 weight blocks and
+ *    (token, 128-column) activation groups; the intermediate is requantized per (row, 128-group).
+ *  - Block-scaled product: for each 128-wide K-block, part = sum of the products of the decoded
+ *    values, computed exactly (every product of two E4M3 values is exact in a double, and 128 of
+ *    them span fewer than 53 bits) and rounded once to fp32; then acc = acc + ((part * a_s) * w_s)
+ *    in fp32, in ascending K-block order.  Everything after the sums is the INT8 block-wise path's
+ *    arithmetic (SiLU(gate) * up, requantization, combine). */
+
+/* Value of an E4M3 code (NaN codes never reach here). */
+static double e4m3_decode(uint8_t c) {
+  const int e = (c >> 3) & 15, m = c & 7;
+  const double v = e == 0 ? ldexp((double)m, -9)      /* m/8 * 2^-6 */
+                          : ldexp((double)(8 + m), e - 10); /* (1 + m/8) * 2^(e-7) */
+  return (c & 0x80) ? -v : v;
+}
+
+/* E4M3 code nearest to x (x finite): clamp to [-448, 448], then the nearest of the 127
+ * non-negative finite codes by magnitude, ties to the even code (consecutive codes alternate
+ * mantissa parity, so the even code is the even mantissa). */
+static uint8_t e4m3_encode(float x) {
+  const int neg = signbit(x) != 0;
+  double a = fabs((double)x);
+  if (a > 448.0) a = 448.0;
+  int lo = 0;
+  for (int c = 0; c <= 0x7E; ++c)
+    if (e4m3_decode((uint8_t)c) <= a) lo = c;
+  int code = lo;
+  if (e4m3_decode((uint8_t)lo) != a) {
+    const int hi = lo + 1; /* a < 448 here, so lo < 0x7E */
+    const double mid = (e4m3_decode((uint8_t)lo) + e4m3_decode((uint8_t)hi)) / 2.0; /* exact */
+    if (a > mid || (a == mid && (hi & 1) == 0)) code = hi;
+  }
+  return (uint8_t)(code | (neg ? 0x80 : 0));
+}
+
+ORACLE_EXPORT void oracle_fp8_decode(const uint8_t* c, int64_t n, float* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = (float)e4m3_decode(c[i]);
+}
+
+ORACLE_EXPORT void oracle_fp8_encode(const float* x, int64_t n, uint8_t* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) out[i] = e4m3_encode(x[i]);
+}
+
+static float fp8_scale(float amax) {
+  float sc = amax / 448.0f;
+  if (sc < 1e-8f) sc = 1e-8f;
+  return sc;
+}
+
+/* FP8 quantization with one scale per br x bc block of a row-major [rows, cols] fp32 matrix
+ * (br=1, bc=128: per-token-group activations; br=bc=128: block-wise weights). */
+ORACLE_EXPORT void oracle_fp8_quant_blocks(const float* x, int64_t rows, int64_t cols, int64_t br, int64_t bc,
+                                           uint8_t* q, float* s) {
+  const int64_t nbr = (rows + br - 1) / br, nbc = (cols + bc - 1) / bc;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t b = 0; b < nbr * nbc; ++b) {
+    const int64_t bi = b / nbc, bj = b % nbc;
+    const int64_t r0 = bi * br, r1 = (r0 + br < rows) ? r0 + br : rows;
+    const int64_t c0 = bj * bc, c1 = (c0 + bc < cols) ? c0 + bc : cols;
+    float amax = 0.0f;
+    for (int64_t r = r0; r < r1; ++r)
+      for (int64_t c = c0; c < c1; ++c) {
+        float a = fabsf(x[r * cols + c]);
+        if (a > amax) amax = a;
+      }
+    const float sc = fp8_scale(amax);
+    s[b] = sc;
+    for (int64_t r = r0; r < r1; ++r)
+      for (int64_t c = c0; c < c1; ++c) q[r * cols + c] = e4m3_encode(x[r * cols + c] / sc);
+  }
+}
+
+/* One K-block's sum of products, exact, rounded once to fp32. */
+static float fp8_part(const uint8_t* a, const uint8_t* b) {
+  double sum = 0.0;
+  for (int i = 0; i < 128; ++i) sum += e4m3_decode(a[i]) * e4m3_decode(b[i]);
+  return (float)sum;
+}
+
+static void fp8_requant_row(const float* hf, int64_t n, uint8_t* q, float* s) {
+  for (int64_t g0 = 0, gi = 0; g0 < n; g0 += 128, ++gi) {
+    float amax = 0.0f;
+    for (int64_t i = g0; i < g0 + 128; ++i) {
+      float a = fabsf(hf[i]);
+      if (a > amax) amax = a;
+    }
+    const float sc = fp8_scale(amax);
+    s[gi] = sc;
+    for (int64_t i = g0; i < g0 + 128; ++i) q[i] = e4m3_encode(hf[i] / sc);
+  }
+}
+
+/* One expert row of the FP8 first GEMM: a [H] codes, a_s [H/128], w13 [2I, H] codes, w_s
+ * [2I/128, H/128]; hf [I] scratch; writes h_q [I] codes and h_s [I/128]. */
+static void fp8_w13_row(const uint8_t* a, const float* a_s, const uint8_t* w13, const float* w_s, int64_t H,
+                        int64_t I, float* hf, uint8_t* h_q, float* h_s) {
+  const int64_t nkb = H / 128;
+  for (int64_t n = 0; n < I; ++n) {
+    float g = 0.0f, u = 0.0f;
+    for (int64_t kb = 0; kb < nkb; ++kb) {
+      const float pg = fp8_part(a + kb * 128, w13 + n * H + kb * 128);
+      const float pu = fp8_part(a + kb * 128, w13 + (n + I) * H + kb * 128);
+      g = g + ((pg * a_s[kb]) * w_s[(n / 128) * nkb + kb]);
+      u = u + ((pu * a_s[kb]) * w_s[((n + I) / 128) * nkb + kb]);
+    }
+    hf[n] = silu_mul(g, u);
+  }
+  fp8_requant_row(hf, I, h_q, h_s);
+}
+
+/* One expert row of the FP8 second GEMM: y [H]. */
+static void fp8_w2_row(const uint8_t* hq, const float* h_s, const uint8_t* w2, const float* w_s, int64_t H,
+                       int64_t I, float* y) {
+  const int64_t nkb = I / 128;
+  for (int64_t n = 0; n < H; ++n) {
+    float acc = 0.0f;
+    for (int64_t kb = 0; kb < nkb; ++kb) {
+      const float part = fp8_part(hq + kb * 128, w2 + n * I + kb * 128);
+      acc = acc + ((part * h_s[kb]) * w_s[(n / 128) * nkb + kb]);
+    }
+    y[n] = acc;
+  }
+}
+
+/* FP8 first GEMM + SiLU(gate)*up + requantization over sorted rows (arguments as
+ * oracle_w13_silu in block mode, codes in place of int8 values). */
+ORACLE_EXPORT void oracle_fp8_w13_silu(const uint8_t* a_q, const float* a_s, const uint8_t* const* w13,
+                                       const float* const* w13_s, const int32_t* sorted_pair_ids,
+                                       const int32_t* tile_expert, int64_t block_m, int64_t T, int64_t k,
+                                       int64_t H, int64_t I, const int64_t* rows, int64_t nrows, uint8_t* h_q,
+                                       float* h_s) {
+  const int64_t P = T * k;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t i = 0; i < nrows; ++i) {
+    const int64_t r = row_at(rows, i);
+    const int64_t p = sorted_pair_ids[r];
+    if (p >= P) continue;
+    const int64_t t = p / k, e = tile_expert[r / block_m];
+    float* hf = (float*)malloc(sizeof(float) * I);
+    fp8_w13_row(a_q + t * H, a_s + t * (H / 128), w13[e], w13_s[e], H, I, hf, h_q + r * I, h_s + r * (I / 128));
+    free(hf);
+  }
+}
+
+/* FP8 second GEMM + top-k weighted combine (arguments as oracle_w2_combine in block mode). */
+ORACLE_EXPORT void oracle_fp8_w2_combine(const uint8_t* h_q, const float* h_s, const uint8_t* const* w2,
+                                         const float* const* w2_s, const int32_t* sorted_pair_ids,
+                                         const int32_t* tile_expert, int32_t num_tiles, int64_t block_m,
+                                         const float* topk_weights, int64_t T, int64_t k, int64_t H, int64_t I,
+                                         const int64_t* tokens, int64_t ntok, float* out) {
+  const int64_t P = T * k, R = (int64_t)num_tiles * block_m;
+  int64_t* pair_row = (int64_t*)malloc(sizeof(int64_t) * (P > 0 ? P : 1));
+  for (int64_t p = 0; p < P; ++p) pair_row[p] = -1;
+  for (int64_t r = 0; r < R; ++r)
+    if (sorted_pair_ids[r] < P) pair_row[sorted_pair_ids[r]] = r;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t i = 0; i < ntok; ++i) {
+    const int64_t t = tokens ? tokens[i] : i;
+    float* y = (float*)malloc(sizeof(float) * H);
+    float* o = out + i * H;
+    for (int64_t n = 0; n < H; ++n) o[n] = 0.0f;
+    for (int64_t j = 0; j < k; ++j) {
+      const int64_t r = pair_row[t * k + j];
+      if (r < 0) continue;
+      const int64_t e = tile_expert[r / block_m];
+      fp8_w2_row(h_q + r * I, h_s + r * (I / 128), w2[e], w2_s[e], H, I, y);
+      const float wj = topk_weights[t * k + j];
+      for (int64_t n = 0; n < H; ++n) o[n] = o[n] + (wj * y[n]);
+    }
+    free(y);
+  }
+  free(pair_row);
+}
+
+/* The whole FP8 layer for a list of tokens, straight from the routing (as oracle_moe_tokens):
+ * FP8 quantization of the token per 128-group, then per slot the expert MLP and the combine. */
+ORACLE_EXPORT void oracle_fp8_moe_tokens(const float* x, int64_t ntok, int64_t H, int64_t I, int64_t k,
+                                         const int32_t* ids, const float* topk_weights,
+                                         const uint8_t* const* w13, const float* const* w13_s,
+                                         const uint8_t* const* w2, const float* const* w2_s, float* out) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t t = 0; t < ntok; ++t) {
+    uint8_t* aq = (uint8_t*)malloc(H);
+    float* as = (float*)malloc(sizeof(float) * (H / 128));
+    float* hf = (float*)malloc(sizeof(float) * I);
+    uint8_t* hq = (uint8_t*)malloc(I);
+    float* hs = (float*)malloc(sizeof(float) * (I / 128));
+    float* y = (float*)malloc(sizeof(float) * H);
+    fp8_requant_row(x + t * H, H, aq, as);
+    float* o = out + t * H;
+    for (int64_t n = 0; n < H; ++n) o[n] = 0.0f;
+    for (int64_t j = 0; j < k; ++j) {
+      const int64_t e = ids[t * k + j];
+      fp8_w13_row(aq, as, w13[e], w13_s[e], H, I, hf, hq, hs);
+      fp8_w2_row(hq, hs, w2[e], w2_s[e], H, I, y);
+      const float wj = topk_weights[t * k + j];
+      for (int64_t n = 0; n < H; ++n) o[n] = o[n] + (wj * y[n]);
+    }
+    free(aq);
+    free(as);
+    free(hf);
+    free(hq);
+    free(hs);
+    free(y);
+  }
+}
