@@ -67,8 +67,9 @@ enum { W8A8_DTYPE_F32 = 0, W8A8_DTYPE_BF16 = 1 };
 /* Routing score functions. */
 enum { W8A8_SCORE_SOFTMAX = 0, W8A8_SCORE_SIGMOID = 1 };
 
-/* Scale layouts. */
-enum { W8A8_SCALE_CHANNEL = 0, W8A8_SCALE_BLOCK128 = 1 };
+/* Scale layouts.  W8A8_SCALE_FP8_BLOCK128: the block-wise layouts with FP8 (E4M3) codes in place
+ * of int8 values (see "FP8 block-wise variant" below). */
+enum { W8A8_SCALE_CHANNEL = 0, W8A8_SCALE_BLOCK128 = 1, W8A8_SCALE_FP8_BLOCK128 = 2 };
 
 /* Name of a status code ("W8A8_OK", ...); never NULL. */
 const char* w8a8_status_string(int32_t status);
@@ -220,6 +221,42 @@ int32_t w8a8_block_grouped_gemm_w2_combine(const int8_t* h_q, const float* h_sca
                                            int64_t k, int64_t E, int64_t H, int64_t I, int64_t block_m,
                                            float* out, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------ FP8 block-wise variant
+ * SGLang PR #8273 (description, "New FP8 MoE Kernel"): an MoE with per-block FP8 weights and
+ * per-token-group FP8 activations, multiplied by a block-scaled grouped GEMM.  FP8 here is E4M3
+ * as the OCP 8-bit floating-point specification defines it (sign, 4 exponent bits with bias 7,
+ * 3 mantissa bits, largest finite value 448, codes 0x7F / 0xFF NaN and never produced); codes are
+ * bytes (uint8_t).  Quantization rule: scale = max(max|x| / 448, 1e-8), code = the E4M3 value
+ * nearest to x / scale (ties to even) after clamping x / scale to [-448, 448].
+ *
+ * w8a8_fp8_quant_blocks: arguments as w8a8_quant_blocks, FP8 codes out (block_rows = 1,
+ * block_cols = 128: per-token-group activations; 128 x 128: weights).
+ *
+ * The GEMMs take the block-wise layouts of the INT8 variants (a_scale [T, H/128], w13_scale
+ * [E, 2I/128, H/128], h_scale [max_rows, I/128], w2_scale [E, H/128, I/128]) and accumulate each
+ * 128-wide K-block's products with the gfx950 FP8 MFMA in fp32, then
+ * acc += (part_kb * a_s[t, kb]) * w_s[e, n/128, kb] in fp32, in ascending K-block order.  The
+ * products are exact; the MFMA's fp32 summation order inside a K-block is the hardware's, so
+ * results agree with an exact per-block sum to within fp32 rounding, not bit for bit.  The first
+ * GEMM requantizes SiLU(gate) * up to FP8 per (row, 128-group).  Workspaces from the size queries
+ * with scale_mode = W8A8_SCALE_FP8_BLOCK128.
+ * Shapes (W8A8_UNSUPPORTED_SHAPE otherwise): H a multiple of 256; H/128 and I/128 each one of
+ * 1, 2, 4, 8, 16, 32, 56; T*H, max_rows*I and 2*I*H below 2^32.  Operand pointers 16-byte aligned. */
+int32_t w8a8_fp8_quant_blocks(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t block_rows,
+                              int64_t block_cols, uint8_t* q, float* scale, hipStream_t stream);
+int32_t w8a8_fp8_grouped_gemm_w13_silu(const uint8_t* a_q, const float* a_scale, const uint8_t* w13,
+                                       const float* w13_scale, const int32_t* sorted_pair_ids,
+                                       const int32_t* padded_offsets, const int32_t* tile_expert,
+                                       const int32_t* num_tiles, int64_t T, int64_t k, int64_t E, int64_t H,
+                                       int64_t I, int64_t block_m, uint8_t* h_q, float* h_scale, void* ws,
+                                       size_t ws_bytes, hipStream_t stream);
+int32_t w8a8_fp8_grouped_gemm_w2_combine(const uint8_t* h_q, const float* h_scale, const uint8_t* w2,
+                                         const float* w2_scale, const int32_t* sorted_pair_ids,
+                                         const int32_t* padded_offsets, const int32_t* tile_expert,
+                                         const int32_t* num_tiles, const float* topk_weights, int64_t T, int64_t k,
+                                         int64_t E, int64_t H, int64_t I, int64_t block_m, float* out, void* ws,
+                                         size_t ws_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------------ dense linear
  * W8A8 INT8 linear for the model's non-MoE projections (PR #3888 Modifications, "Norm Linear": the
  * dense layers run as w8a8 int8 GEMMs; article, "Quantization exploration": channel-wise weights
@@ -240,14 +277,16 @@ int32_t w8a8_linear(const int8_t* a_q, const float* a_scale, const int8_t* w, co
 
 /* ------------------------------------------------------------------ the whole layer
  * Steps 2, 1, 3, 4, 5 on one stream, intermediates carved from `ws`.
- * block_m = 0 picks a tile height from the average rows per expert. */
+ * block_m = 0 picks a tile height from the average rows per expert.  With scale_mode =
+ * W8A8_SCALE_FP8_BLOCK128 the w13 / w2 buffers hold FP8 codes and the activations are quantized
+ * to FP8 per token-group (the FP8 variant's rule and shape limits). */
 struct w8a8_moe_args {
   const void* x;               /* device, [T, H] fp32 or bf16 activations */
   int32_t x_dtype;             /* W8A8_DTYPE_* */
   const float* router_logits;  /* device, [T, E] fp32 */
-  const int8_t* w13;           /* device, [E, 2I, H] int8 */
+  const int8_t* w13;           /* device, [E, 2I, H] int8 (or FP8 codes) */
   const float* w13_scale;      /* device, [E, 2I] or [E, 2I/128, H/128] fp32 */
-  const int8_t* w2;            /* device, [E, H, I] int8 */
+  const int8_t* w2;            /* device, [E, H, I] int8 (or FP8 codes) */
   const float* w2_scale;       /* device, [E, H] or [E, H/128, I/128] fp32 */
   const float* correction_bias;/* device, [E] fp32 or NULL */
   float* out;                  /* device, [T, H] fp32 (output) */

@@ -28,6 +28,14 @@ int32_t w8a8_probe_copy(const void* src, void* dst, int64_t bytes, hipStream_t s
  * independent v_mfma_i32_16x16x64_i8 on pseudo-random operands; `sink` as above. */
 int32_t w8a8_probe_mfma_i8(int64_t iters, int32_t workgroups, int32_t* sink, hipStream_t stream);
 
+/* `blocks` independent products, one wavefront and one FP8 MFMA
+ * (v_mfma_scale_f32_16x16x128_f8f6f4, E4M3 operands, scales 1.0, zero accumulator) each:
+ * c[blk][i][j] = sum over k < 128 of a[blk][i][k] * b[blk][j][k], with a and b device [blocks, 16,
+ * 128] E4M3 codes (32-byte aligned) and c device [blocks, 16, 16] fp32.  The operands are fed
+ * with the layer's FP8 GEMM layout (lane (g, r): bytes [32 g, 32 g + 32) of row r), so the tests
+ * measure the accumulation that GEMM gets. */
+int32_t w8a8_probe_mfma_f8_block(const uint8_t* a, const uint8_t* b, float* c, int32_t blocks, hipStream_t stream);
+
 /* Integer operations (2 per multiply-add) of one w8a8_probe_mfma_i8 launch. */
 int64_t w8a8_probe_mfma_i8_ops(int64_t iters, int32_t workgroups);
 

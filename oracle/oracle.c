@@ -463,6 +463,16 @@ static double e4m3_decode(uint8_t c) {
   return (c & 0x80) ? -v : v;
 }
 
+/* The 256 code values, filled from e4m3_decode before any parallel use (the GEMMs and the
+ * quantization look every code up many times). */
+static double e4m3_table[256];
+static int e4m3_table_ready = 0;
+static void e4m3_table_init(void) {
+  if (e4m3_table_ready) return;
+  for (int c = 0; c < 256; ++c) e4m3_table[c] = e4m3_decode((uint8_t)c);
+  e4m3_table_ready = 1;
+}
+
 /* E4M3 code nearest to x (x finite): clamp to [-448, 448], then the nearest of the 127
  * non-negative finite codes by magnitude, ties to the even code (consecutive codes alternate
  * mantissa parity, so the even code is the even mantissa). */
@@ -472,11 +482,11 @@ static uint8_t e4m3_encode(float x) {
   if (a > 448.0) a = 448.0;
   int lo = 0;
   for (int c = 0; c <= 0x7E; ++c)
-    if (e4m3_decode((uint8_t)c) <= a) lo = c;
+    if (e4m3_table[c] <= a) lo = c;
   int code = lo;
-  if (e4m3_decode((uint8_t)lo) != a) {
+  if (e4m3_table[lo] != a) {
     const int hi = lo + 1; /* a < 448 here, so lo < 0x7E */
-    const double mid = (e4m3_decode((uint8_t)lo) + e4m3_decode((uint8_t)hi)) / 2.0; /* exact */
+    const double mid = (e4m3_table[lo] + e4m3_table[hi]) / 2.0; /* exact */
     if (a > mid || (a == mid && (hi & 1) == 0)) code = hi;
   }
   return (uint8_t)(code | (neg ? 0x80 : 0));
@@ -487,6 +497,7 @@ ORACLE_EXPORT void oracle_fp8_decode(const uint8_t* c, int64_t n, float* out) {
 }
 
 ORACLE_EXPORT void oracle_fp8_encode(const float* x, int64_t n, uint8_t* out) {
+  e4m3_table_init();
 #pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < n; ++i) out[i] = e4m3_encode(x[i]);
 }
@@ -501,6 +512,7 @@ static float fp8_scale(float amax) {
  * (br=1, bc=128: per-token-group activations; br=bc=128: block-wise weights). */
 ORACLE_EXPORT void oracle_fp8_quant_blocks(const float* x, int64_t rows, int64_t cols, int64_t br, int64_t bc,
                                            uint8_t* q, float* s) {
+  e4m3_table_init();
   const int64_t nbr = (rows + br - 1) / br, nbc = (cols + bc - 1) / bc;
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t b = 0; b < nbr * nbc; ++b) {
@@ -523,7 +535,7 @@ ORACLE_EXPORT void oracle_fp8_quant_blocks(const float* x, int64_t rows, int64_t
 /* One K-block's sum of products, exact, rounded once to fp32. */
 static float fp8_part(const uint8_t* a, const uint8_t* b) {
   double sum = 0.0;
-  for (int i = 0; i < 128; ++i) sum += e4m3_decode(a[i]) * e4m3_decode(b[i]);
+  for (int i = 0; i < 128; ++i) sum += e4m3_table[a[i]] * e4m3_table[b[i]];
   return (float)sum;
 }
 
@@ -579,6 +591,7 @@ ORACLE_EXPORT void oracle_fp8_w13_silu(const uint8_t* a_q, const float* a_s, con
                                        const int32_t* tile_expert, int64_t block_m, int64_t T, int64_t k,
                                        int64_t H, int64_t I, const int64_t* rows, int64_t nrows, uint8_t* h_q,
                                        float* h_s) {
+  e4m3_table_init();
   const int64_t P = T * k;
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t i = 0; i < nrows; ++i) {
@@ -598,6 +611,7 @@ ORACLE_EXPORT void oracle_fp8_w2_combine(const uint8_t* h_q, const float* h_s, c
                                          const int32_t* tile_expert, int32_t num_tiles, int64_t block_m,
                                          const float* topk_weights, int64_t T, int64_t k, int64_t H, int64_t I,
                                          const int64_t* tokens, int64_t ntok, float* out) {
+  e4m3_table_init();
   const int64_t P = T * k, R = (int64_t)num_tiles * block_m;
   int64_t* pair_row = (int64_t*)malloc(sizeof(int64_t) * (P > 0 ? P : 1));
   for (int64_t p = 0; p < P; ++p) pair_row[p] = -1;
@@ -628,6 +642,7 @@ ORACLE_EXPORT void oracle_fp8_moe_tokens(const float* x, int64_t ntok, int64_t H
                                          const int32_t* ids, const float* topk_weights,
                                          const uint8_t* const* w13, const float* const* w13_s,
                                          const uint8_t* const* w2, const float* const* w2_s, float* out) {
+  e4m3_table_init();
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t t = 0; t < ntok; ++t) {
     uint8_t* aq = (uint8_t*)malloc(H);

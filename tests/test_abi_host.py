@@ -38,7 +38,8 @@ def test_probe_library_exports_its_header_and_validates():
     import ctypes
 
     names = header_functions(os.path.join(ROOT, "include", "w8a8probe.h"))
-    assert names == ["w8a8_probe_copy", "w8a8_probe_mfma_i8", "w8a8_probe_mfma_i8_ops", "w8a8_probe_read"]
+    assert names == ["w8a8_probe_copy", "w8a8_probe_mfma_f8_block", "w8a8_probe_mfma_i8", "w8a8_probe_mfma_i8_ops",
+                     "w8a8_probe_read"]
     L = ctypes.CDLL(os.path.join(ROOT, "w8a8_int8_quantized_quant_amd", "libw8a8probe.so"))
     for n in names:
         assert hasattr(L, n), n
@@ -53,6 +54,9 @@ def test_probe_library_exports_its_header_and_validates():
     assert L.w8a8_probe_copy(P16, P16, 0, None) == 1
     assert L.w8a8_probe_mfma_i8(0, 8, P16, None) == 1
     assert L.w8a8_probe_mfma_i8(1, 8, None, None) == 1
+    L.w8a8_probe_mfma_f8_block.argtypes = [vp, vp, vp, i32, vp]
+    assert L.w8a8_probe_mfma_f8_block(P16, P16, None, 1, None) == 1
+    assert L.w8a8_probe_mfma_f8_block(P16, P16, P16, 0, None) == 1
     # 2 workgroups x 4 wavefronts x 3 rounds x 8 MFMAs x (16*16*64 multiply-adds x 2)
     assert L.w8a8_probe_mfma_i8_ops(3, 2) == 2 * 4 * 3 * 8 * 2 * 16 * 16 * 64
 

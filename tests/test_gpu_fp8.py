@@ -1,0 +1,470 @@
+"""GPU parity of the FP8 (E4M3) block-wise path against the CPU oracle, through the C ABI.
+
+The FP8 MFMA's sums (measured here by test_fp8_mfma_block_sum_model, through the probe library,
+on the operand layout the GEMM uses): a 128-product K-block is summed as 16 groups of 8 adjacent
+products; inside a group every product is cut (toward zero) to a multiple of 2^-13 times the
+largest power of two not above the group's largest |product|; the exact group sums are then added
+in fp32.  So a K-block sum is off its exact value by at most
+    TAU * S,  TAU = 7 * 2^-13 + gamma_17,  S = sum of |products|,  gamma_n = n u / (1 - n u),
+u = 2^-24, where the oracle rounds the exact sum once (u).  Both sides then run the same fp32
+expression on those sums, so over nkb K-blocks and k slots
+    |got - ref| <= (TAU + u + 2 gamma_(nkb+2) + 2 gamma_(k+1)) * 1.01 * B,
+B being the same computation on magnitudes (codes with the sign cleared, |scales|, |weights|).
+Bars:
+  - quantization (activations per token-group, weights per 128 x 128 block): codes and scales
+    bit-exact, including every tie between neighbouring E4M3 values;
+  - second GEMM + combine fed the oracle's intermediate: the bound above, elementwise;
+  - first GEMM: g and u carry the bound above (without the combine term); SiLU(g) * u carries
+    dh <= 1.1 |u| dg + |silu(g)| du + 1.1 dg du + 16 u |h| (|silu'| <= 1.1, a few fp32 roundings);
+    the requantized value is within half an E4M3 step of the value it rounds; so every
+    dequantized code is checked against the exact fp64 h, and against the oracle's code, with
+    those terms, and every h_scale against max|h| / 448;
+  - whole layer: max|err| <= 2e-2 * max|ref| over the checked tokens (an intermediate code one E4M3
+    step off moves a row's contribution by up to 1/16 of that value).
+"""
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import w8a8_int8_quantized_quant_amd as w8  # noqa: E402
+from w8a8_int8_quantized_quant_amd import workload  # noqa: E402
+
+DEV = "cuda"
+U = 2.0 ** -24
+MODE = w8.SCALE_FP8_BLOCK128
+
+
+def gamma(n):
+    return n * U / (1 - n * U)
+
+
+TAU = 7 * 2.0 ** -13 + gamma(17)  # one FP8 MFMA K-block sum, relative to its sum of |products|
+
+
+def tol_sums(nkb, k=None):
+    """Relative (to the magnitude computation) bound after nkb scaled K-block additions, and
+    the top-k combine when k is given."""
+    t = TAU + U + 2 * gamma(nkb + 2)
+    if k is not None:
+        t += 2 * gamma(k + 1)
+    return t * 1.01
+
+
+def small_cfg(name, index, T, H, I, E, k, route="softmax", n_group=1, topk_group=1, scaling=1.0,
+              x_dtype=synth.DTYPE_BF16, w_sigma=0.006):
+    return synth.MoEConfig(name=name, index=index, T=T, H=H, I=I, E=E, k=k, route=route, n_group=n_group,
+                           topk_group=topk_group, routed_scaling=scaling, renormalize=True, x_dtype=x_dtype,
+                           x_sigma=1.0, outlier_threshold=synth.OUTLIER_THRESHOLD, outlier_mult=20.0,
+                           w_sigma=w_sigma, scale_mode="fp8")
+
+
+CFG = {
+    # K of one and two 128-blocks (the shortest unrolled K loops)
+    "fp8-tiny": small_cfg("fp8-tiny", 60, T=16, H=256, I=128, E=8, k=2, x_dtype=synth.DTYPE_F32, w_sigma=0.02),
+    "fp8-small": small_cfg("fp8-small", 61, T=300, H=512, I=256, E=16, k=4, route="sigmoid", n_group=4,
+                           topk_group=2, scaling=2.5),
+    # DeepSeek-V3 expert shapes, few experts: several 128-row tiles per expert
+    "fp8-dsv3-e8": small_cfg("fp8-dsv3-e8", 62, T=1000, H=7168, I=2048, E=8, k=2),
+    # the block-wise workload's shapes and draws in FP8 (T=2048, 256 experts, top-8)
+    "fp8-block": dataclasses.replace(synth.CONFIGS["block"], name="fp8-block", scale_mode="fp8"),
+    "fp8-decode": dataclasses.replace(synth.CONFIGS["decode"], name="fp8-decode", scale_mode="fp8"),
+}
+SMALL = ("fp8-tiny", "fp8-small")
+
+
+def dt(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+_layer = {}
+_oracle_w = {}
+
+
+def layer_of(name):
+    if name not in _layer:
+        _layer.clear()
+        torch.cuda.empty_cache()
+        say(f"[layer] drawing {name} on the device")
+        _layer[name] = workload.make_layer(CFG[name], device=DEV)
+    return _layer[name]
+
+
+def oracle_weights(name, experts):
+    cfg = CFG[name]
+    cache = _oracle_w.setdefault(name, [[None] * cfg.E for _ in range(4)])
+    todo = sorted({int(e) for e in experts if cache[0][int(e)] is None})
+    if todo:
+        w = oracle.expert_weights(cfg, todo)
+        for i in range(4):
+            for e in todo:
+                cache[i][e] = w[i][e]
+    return cache
+
+
+def block_m_of(cfg):
+    return w8.w8a8_moe_pick_block_m(cfg.T, cfg.k, cfg.E)
+
+
+def route_host(cfg):
+    return oracle.route_cfg(cfg, synth.logits(cfg))
+
+
+def align_dev(ids, E, bm):
+    al = oracle.align(ids, E, bm)
+    return al, {key: dt(v) for key, v in al.items()}
+
+
+def check_rows(al, bm, P, name, nsample=48, seed=2):
+    """All real rows of small workloads; else the first and last rows of the most and least
+    loaded experts' segments plus a random sample."""
+    R = int(al["num_tiles"][0]) * bm
+    real = np.nonzero(al["sorted_pair_ids"][:R] < P)[0]
+    if name in SMALL:
+        return real
+    counts = al["counts"]
+    order = np.argsort(counts, kind="stable")
+    nonempty = order[counts[order] > 0]
+    rows = []
+    for e in (nonempty[-1], nonempty[0]):
+        r0, n = int(al["padded_offsets"][e]), int(counts[e])
+        rows += [r0, r0 + n - 1, r0 + min(n - 1, 127), r0 + min(n - 1, 128)]
+    rng = np.random.default_rng(seed)
+    rows += list(rng.choice(real, size=min(nsample, len(real)), replace=False))
+    return np.unique(np.array(rows, dtype=np.int64))
+
+
+def code_steps(a, b):
+    """Distance in E4M3 steps between codes of the same sign (sign mismatch of nonzero values = inf)."""
+    a = np.asarray(a, dtype=np.int32)
+    b = np.asarray(b, dtype=np.int32)
+    ma, mb = a & 0x7F, b & 0x7F
+    same = ((a ^ b) & 0x80) == 0
+    d = np.abs(ma - mb).astype(np.float64)
+    d[~same & ((ma != 0) | (mb != 0))] = np.inf
+    return d
+
+
+# ------------------------------------------------------------------ the FP8 MFMA's sums
+
+def probe_lib():
+    import ctypes
+    import os
+
+    L = ctypes.CDLL(os.path.join(os.path.dirname(w8.__file__), "libw8a8probe.so"))
+    vp = ctypes.c_void_p
+    L.w8a8_probe_mfma_f8_block.argtypes = [vp, vp, vp, ctypes.c_int32, vp]
+    return L
+
+
+def group_model_bound(a, b):
+    """Bound of the sum model on blocks a, b [n, 16, 128] of decoded values: per (i, j), the sum
+    over the 16 groups of 8 products of 7 * 2^-13 * max|product|, plus gamma_17 * sum |products|."""
+    prod = a[:, :, None, :] * b[:, None, :, :]  # [n, 16, 16, 128]
+    gmax = np.abs(prod).reshape(*prod.shape[:3], 16, 8).max(-1)
+    return 7 * 2.0 ** -13 * gmax.sum(-1) + gamma(17) * np.abs(prod).sum(-1), prod.sum(-1)
+
+
+@pytest.mark.parametrize("kind", ["uniform_codes", "normal_values", "wide_groups"])
+def test_fp8_mfma_block_sum_model(kind):
+    """The FP8 MFMA, fed with the GEMM's operand layout, sums a K-block within the model the
+    tolerances below rest on (and pairs A's and B's K-elements correctly: a wrong pairing would
+    be off by the size of the sums)."""
+    n = 256
+    rng = np.random.default_rng(11)
+    if kind == "uniform_codes":  # every finite code, so products span the whole E4M3 range
+        ac = rng.integers(0, 256, size=(n, 16, 128), dtype=np.uint8)
+        bc = rng.integers(0, 256, size=(n, 16, 128), dtype=np.uint8)
+        ac[(ac & 0x7F) == 0x7F] -= 1
+        bc[(bc & 0x7F) == 0x7F] -= 1
+    elif kind == "normal_values":
+        ac = oracle.fp8_quant_blocks(rng.standard_normal((n * 16, 128)).astype(np.float32), 1, 128)[0]
+        bc = oracle.fp8_quant_blocks(rng.standard_normal((n * 16, 128)).astype(np.float32), 128, 128)[0]
+        ac, bc = ac.reshape(n, 16, 128), bc.reshape(n, 16, 128)
+    else:  # one large product per group of 8 and small ones beside it
+        av = rng.choice([1.0, -1.0], size=(n, 16, 128)) * 2.0 ** rng.integers(-9, -1, size=(n, 16, 128))
+        av[:, :, ::8] = rng.choice([448.0, -448.0, 256.0, 96.0], size=(n, 16, 16))
+        ac = oracle.fp8_encode(av.astype(np.float32))
+        bc = oracle.fp8_encode(rng.uniform(-4, 4, size=(n, 16, 128)).astype(np.float32))
+    a, b = oracle.fp8_decode(ac).astype(np.float64), oracle.fp8_decode(bc).astype(np.float64)
+    c = torch.empty((n, 16, 16), dtype=torch.float32, device=DEV)
+    assert probe_lib().w8a8_probe_mfma_f8_block(dt(ac).data_ptr(), dt(bc).data_ptr(), c.data_ptr(), n,
+                                                 torch.cuda.current_stream().cuda_stream) == 0
+    got = host(c).astype(np.float64)
+    bound, exact = group_model_bound(a, b)
+    err = np.abs(got - exact)
+    say(f"[fp8 mfma] {kind}: exact {np.mean(err == 0):.4f}, max err/bound {np.max(err / np.maximum(bound, 1e-300)):.3f}")
+    assert np.all(err <= bound * 1.001)
+
+
+# ------------------------------------------------------------------ quantization
+
+def tie_matrix():
+    """Rows of 128 values whose largest magnitude is exactly 448 (so the scale is exactly 1): every
+    exact E4M3 value, every midpoint between neighbours, and the fp32 neighbours of each midpoint,
+    with both signs."""
+    c = np.arange(0x7E, dtype=np.uint8)
+    lo, hi = oracle.fp8_decode(c), oracle.fp8_decode(c + 1)
+    mid = ((lo.astype(np.float64) + hi) / 2).astype(np.float32)
+    vals = np.concatenate([lo, mid, np.nextafter(mid, np.float32(np.inf)), np.nextafter(mid, np.float32(0)),
+                           np.array([448.0, 1e-30, 2.0 ** -10, 2.0 ** -11], dtype=np.float32)])
+    vals = np.concatenate([vals, -vals])
+    per = 127
+    rows = (len(vals) + per - 1) // per
+    pad = np.zeros(rows * per, dtype=np.float32)
+    pad[:len(vals)] = vals
+    return np.concatenate([np.full((rows, 1), 448.0, dtype=np.float32), pad.reshape(rows, per)], axis=1)
+
+
+@pytest.mark.parametrize("case", ["ties", "groups_bf16", "blocks_partial", "rows_vec"])
+def test_fp8_quant_bit_exact(case):
+    if case == "ties":
+        x, br, bc = tie_matrix(), 1, 128
+    elif case == "groups_bf16":
+        cfg = CFG["fp8-small"]
+        x, br, bc = synth.activations(cfg), 1, 128
+    elif case == "blocks_partial":
+        x, br, bc = synth.normal(129 * 257, 9, 0, sigma=0.3).reshape(129, 257), 128, 128
+    else:
+        x, br, bc = synth.normal(33 * 7168, 10, 0, sigma=2.0).reshape(33, 7168), 1, 7168
+    say(f"[fp8 quant] {case} {x.shape} {br}x{bc}")
+    xf = oracle.bf16_to_f32(x) if x.dtype == np.uint16 else x
+    rq, rs = oracle.fp8_quant_blocks(xf, br, bc)
+    xd = dt(x.view(np.int16)).view(torch.bfloat16) if x.dtype == np.uint16 else dt(x)
+    q = torch.empty(x.shape, dtype=torch.uint8, device=DEV)
+    s = torch.empty(rs.shape, dtype=torch.float32, device=DEV)
+    w8.w8a8_fp8_quant_blocks(xd, br, bc, q, s)
+    assert np.array_equal(host(s), rs)
+    got = host(q)
+    if case == "ties":
+        assert np.array_equal(got, rq), np.count_nonzero(got != rq)
+    else:
+        assert np.array_equal(got, rq)
+
+
+@pytest.mark.parametrize("name", ["fp8-small", "fp8-block"])
+def test_fp8_layer_weights_bit_exact(name):
+    cfg = CFG[name]
+    L = layer_of(name)
+    experts = [0, cfg.E - 1]
+    w = oracle_weights(name, experts)
+    for e in experts:
+        assert np.array_equal(host(L.w13[e]), w[0][e]) and np.array_equal(host(L.w13_scale[e]), w[1][e])
+        assert np.array_equal(host(L.w2[e]), w[2][e]) and np.array_equal(host(L.w2_scale[e]), w[3][e])
+
+
+# ------------------------------------------------------------------ the grouped GEMMs
+
+def run_w13(name, ids):
+    cfg = CFG[name]
+    bm = block_m_of(cfg)
+    L = layer_of(name)
+    al, d = align_dev(ids, cfg.E, bm)
+    a_q, a_s = oracle.fp8_quant_blocks(oracle.activations_f32(cfg), 1, 128)
+    R = w8.w8a8_moe_max_rows(cfg.T, cfg.k, cfg.E, bm)
+    h_q = torch.empty((R, cfg.I), dtype=torch.uint8, device=DEV)
+    h_s = torch.empty((R, cfg.I // 128), dtype=torch.float32, device=DEV)
+    ws = torch.empty(max(w8.w8a8_w13_workspace_bytes(cfg.T, cfg.k, cfg.E, cfg.H, cfg.I, bm, MODE), 256),
+                     dtype=torch.uint8, device=DEV)
+    w8.w8a8_fp8_grouped_gemm_w13_silu(dt(a_q), dt(a_s), L.w13, L.w13_scale, d["sorted_pair_ids"],
+                                      d["padded_offsets"], d["tile_expert"], d["num_tiles"], cfg.T, cfg.k, bm, h_q,
+                                      h_s, ws)
+    return al, bm, a_q, a_s, host(h_q), host(h_s)
+
+
+_dec = {}
+
+
+def decoded_w13(name, e, w):
+    """fp64 [2I, H] dequantized weights of one expert (codes x block scales) and their magnitudes."""
+    key = (name, e)
+    if key not in _dec:
+        _dec.clear()
+        wd = oracle.fp8_decode(w[0][e]).astype(np.float64)
+        wd *= np.repeat(np.repeat(w[1][e].astype(np.float64), 128, 0), 128, 1)
+        _dec[key] = wd
+    return _dec[key]
+
+
+def check_w13(name, al, bm, a_q, a_s, gq_all, gs_all, rows):
+    cfg = CFG[name]
+    I = cfg.I
+    w = oracle_weights(name, sorted({int(al["tile_expert"][r // bm]) for r in rows}))
+    rq, rs = oracle.fp8_w13_silu(a_q, a_s, w[0], w[1], al, bm, cfg.T, cfg.k, cfg.H, I, rows)
+    tol = tol_sums(cfg.H // 128)
+    worst, off, n = 0.0, 0, 0
+    rows = sorted(rows, key=lambda r: int(al["tile_expert"][r // bm]))
+    for r in rows:
+        p = int(al["sorted_pair_ids"][r])
+        t, e = p // cfg.k, int(al["tile_expert"][r // bm])
+        wd = decoded_w13(name, e, w)
+        a = oracle.fp8_decode(a_q[t]).astype(np.float64) * np.repeat(a_s[t].astype(np.float64), 128)
+        gu, bgu = wd @ a, np.abs(wd) @ np.abs(a)
+        g, u, dg, du = gu[:I], gu[I:], tol * bgu[:I], tol * bgu[I:]
+        sg = g / (1 + np.exp(-g))
+        h = sg * u
+        dh = 1.1 * np.abs(u) * dg + np.abs(sg) * du + 1.1 * dg * du + 16 * U * np.abs(h)
+        # scales: max|h~| / 448 with |h~ - h| <= dh
+        hg, dhg = np.abs(h).reshape(-1, 128), dh.reshape(-1, 128)
+        lo = np.maximum((hg - dhg).max(1) / 448, 1e-8) * (1 - 2 * U)
+        hi = np.maximum((hg + dhg).max(1) / 448, 1e-8) * (1 + 2 * U)
+        gs = gs_all[r].astype(np.float64)
+        assert np.all((gs >= lo) & (gs <= hi)), (r, gs, lo, hi)
+        # codes: within half a step of some value within dh of h
+        sc = np.repeat(gs, 128)
+        deq = oracle.fp8_decode(gq_all[r]).astype(np.float64) * sc
+        half = 2.0 ** -4 * (np.abs(h) + dh) + 2.0 ** -10 * sc
+        assert np.all(np.abs(deq - h) <= (half + dh) * (1 + 1e-6)), r
+        # and against the oracle's own code (which is within half a step of h up to fp32 roundings)
+        rsc = np.repeat(rs[r].astype(np.float64), 128)
+        rdeq = oracle.fp8_decode(rq[r]).astype(np.float64) * rsc
+        rhalf = 2.0 ** -4 * (np.abs(h) + dh) + 2.0 ** -10 * rsc
+        assert np.all(np.abs(deq - rdeq) <= (half + rhalf + 2 * dh) * (1 + 1e-6)), r
+        worst = max(worst, float(np.max(np.abs(gs / rs[r] - 1))))
+        off += int(np.count_nonzero(gq_all[r] != rq[r]))
+        n += I
+    say(f"[fp8 w13] {name}: rows {len(rows)}, h_s max rel vs oracle {worst:.2e}, codes differing from the "
+        f"oracle {off}/{n}")
+
+
+def w13_rows(al, bm, P, name):
+    rows = check_rows(al, bm, P, name)
+    if name not in SMALL and len(rows) > 40:
+        rows = np.sort(np.random.default_rng(7).choice(rows, 40, replace=False))
+    return rows
+
+
+@pytest.mark.parametrize("name", ["fp8-tiny", "fp8-small", "fp8-block"])
+def test_fp8_first_gemm_silu_requant(name):
+    cfg = CFG[name]
+    ids, _ = route_host(cfg)
+    al, bm, a_q, a_s, gq, gs = run_w13(name, ids)
+    check_w13(name, al, bm, a_q, a_s, gq, gs, w13_rows(al, bm, cfg.T * cfg.k, name))
+
+
+def abs_bound(h_q, h_s, w, al, bm, tw, cfg, tokens):
+    """Same computation on magnitudes: B >= sum of |every term| reaching each output."""
+    wa = [None if x is None else oracle.fp8_abs(x) for x in w[2]]
+    sa = [None if x is None else np.abs(x) for x in w[3]]
+    return oracle.fp8_w2_combine(oracle.fp8_abs(h_q), np.abs(h_s), wa, sa, al, bm, np.abs(tw), cfg.T, cfg.k, cfg.H,
+                                 cfg.I, tokens).astype(np.float64)
+
+
+def run_check_w2(name, ids, tw, tokens):
+    cfg = CFG[name]
+    bm = block_m_of(cfg)
+    L = layer_of(name)
+    al, d = align_dev(ids, cfg.E, bm)
+    R = w8.w8a8_moe_max_rows(cfg.T, cfg.k, cfg.E, bm)
+    # an intermediate of uniformly drawn finite FP8 codes (the whole E4M3 range) with scales in
+    # [1e-3, 3e-2]
+    h_q = synth.int8_matrix(R, cfg.I, cfg.seed + 100).view(np.uint8).copy()
+    h_q[(h_q & 0x7F) == 0x7F] -= 1
+    h_s = synth.positive_scales(R * (cfg.I // 128), cfg.seed, 1e-3, 3e-2).reshape(R, cfg.I // 128)
+    out = torch.full((cfg.T, cfg.H), float("nan"), dtype=torch.float32, device=DEV)
+    ws = torch.empty(max(w8.w8a8_w2_workspace_bytes(cfg.T, cfg.k, cfg.E, cfg.H, cfg.I, bm, MODE), 256),
+                     dtype=torch.uint8, device=DEV)
+    w8.w8a8_fp8_grouped_gemm_w2_combine(dt(h_q), dt(h_s), L.w2, L.w2_scale, d["sorted_pair_ids"],
+                                        d["padded_offsets"], d["tile_expert"], d["num_tiles"], dt(tw), cfg.T, cfg.k,
+                                        bm, out, ws)
+    got = host(out)
+    assert np.isfinite(got).all()
+    w = oracle_weights(name, np.unique(ids[tokens]))
+    ref = oracle.fp8_w2_combine(h_q, h_s, w[2], w[3], al, bm, tw, cfg.T, cfg.k, cfg.H, cfg.I, tokens)
+    B = abs_bound(h_q, h_s, w, al, bm, tw, cfg, tokens)
+    tol = tol_sums(cfg.I // 128, cfg.k)
+    err = np.abs(got[tokens].astype(np.float64) - ref)
+    say(f"[fp8 w2] {name}: tokens {len(tokens)}, bit-equal {np.mean(got[tokens] == ref):.6f}, "
+        f"max err/B {np.max(err / np.maximum(B, 1e-30)):.2e} (tol {tol:.2e})")
+    assert np.all(err <= tol * B)
+
+
+@pytest.mark.parametrize("name", ["fp8-tiny", "fp8-small", "fp8-block"])
+def test_fp8_second_gemm_combine(name):
+    cfg = CFG[name]
+    ids, tw = route_host(cfg)
+    tokens = np.arange(cfg.T) if name in SMALL else np.sort(np.random.default_rng(3).choice(cfg.T, 6, replace=False))
+    run_check_w2(name, ids, tw, tokens)
+
+
+EDGE_COUNTS = [0, 1, 17, 128, 129, 650, 330, 745]
+
+
+def test_fp8_tile_edges():
+    """Both FP8 GEMMs at the DeepSeek-V3 expert shapes with routing whose expert row counts
+    straddle the 128-row tile and 16-row fragment boundaries."""
+    name = "fp8-dsv3-e8"
+    cfg = CFG[name]
+    flat = np.repeat(np.arange(cfg.E, dtype=np.int32), EDGE_COUNTS)
+    T = len(flat) // 2
+    assert T == cfg.T and max(EDGE_COUNTS) <= T
+    ids = np.stack([flat[:T], flat[T:]], axis=1)
+    assert np.all(ids[:, 0] != ids[:, 1])
+    ids = np.ascontiguousarray(ids[np.random.default_rng(41).permutation(T)])
+    tw = synth.positive_scales(T * 2, cfg.seed, 0.05, 1.0).reshape(T, 2)
+    al, bm, a_q, a_s, gq, gs = run_w13(name, ids)
+    assert list(al["counts"]) == EDGE_COUNTS
+    rows = set()
+    for e, n in enumerate(EDGE_COUNTS):
+        r0 = int(al["padded_offsets"][e])
+        js = {0, 1, 15, 16, 17, n - 2, n - 1}
+        for m in range(1, n // 128 + 1):
+            js |= {m * 128 - 1, m * 128}
+        rows |= {r0 + j for j in js if 0 <= j < n}
+    rows = np.array(sorted(rows), dtype=np.int64)
+    check_w13(name, al, bm, a_q, a_s, gq, gs, rows)
+    tokens = np.unique(al["sorted_pair_ids"][rows] // cfg.k)
+    run_check_w2(name, ids, tw, tokens)
+
+
+# ------------------------------------------------------------------ the whole layer
+
+@pytest.mark.parametrize("name", ["fp8-tiny", "fp8-small", "fp8-decode", "fp8-block"])
+def test_fp8_forward_matches_oracle(name):
+    cfg = CFG[name]
+    say(f"[fp8 forward] {name}")
+    L = layer_of(name)
+    out = torch.empty((cfg.T, cfg.H), dtype=torch.float32, device=DEV)
+    ids = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=DEV)
+    tw = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=DEV)
+    ws = workload.forward_workspace(L)
+    workload.forward(L, out, ws, topk_ids=ids, topk_weights=tw)
+    got, ids_d, tw_d = host(out), host(ids), host(tw)
+    tokens = np.arange(cfg.T) if name in ("fp8-tiny", "fp8-small") else \
+        np.sort(np.random.default_rng(4).choice(cfg.T, 8, replace=False))
+    x = oracle.activations_f32(cfg)[tokens]
+    w = oracle_weights(name, np.unique(ids_d[tokens]))
+    ref = oracle.fp8_moe_tokens(x, ids_d[tokens], tw_d[tokens], *w, I=cfg.I)
+    err = np.abs(got[tokens] - ref).max()
+    say(f"[fp8 forward] {name}: max err {err:.3e}, max |ref| {np.abs(ref).max():.3e}, "
+        f"bit-equal {np.mean(got[tokens] == ref):.4f}")
+    assert np.isfinite(got).all()
+    assert err <= 2e-2 * np.abs(ref).max()
+
+
+def test_fp8_unsupported_shapes_are_rejected():
+    # H = 384 is not a multiple of 256; I = 384 gives three K-blocks (no unrolled kernel)
+    for H, I in ((384, 256), (512, 384)):
+        assert w8.w8a8_w13_workspace_bytes(64, 2, 8, H, I, 16, MODE) == 0
+        assert w8.w8a8_moe_workspace_bytes(64, 2, 8, H, I, 16, MODE) == 0

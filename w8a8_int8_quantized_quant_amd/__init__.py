@@ -27,6 +27,7 @@ SCORE_SOFTMAX = 0
 SCORE_SIGMOID = 1
 SCALE_CHANNEL = 0
 SCALE_BLOCK128 = 1
+SCALE_FP8_BLOCK128 = 2
 
 # Every symbol the C header declares (checked by the CPU test suite).
 EXPORTS = (
@@ -35,6 +36,7 @@ EXPORTS = (
     "w8a8_grouped_gemm_w13_silu", "w8a8_w2_workspace_bytes", "w8a8_grouped_gemm_w2_combine",
     "w8a8_block_grouped_gemm_w13_silu", "w8a8_block_grouped_gemm_w2_combine", "w8a8_moe_pick_block_m",
     "w8a8_moe_workspace_bytes", "w8a8_moe_forward", "w8a8_linear_workspace_bytes", "w8a8_linear",
+    "w8a8_fp8_quant_blocks", "w8a8_fp8_grouped_gemm_w13_silu", "w8a8_fp8_grouped_gemm_w2_combine",
 )
 
 
@@ -94,6 +96,11 @@ def lib() -> ctypes.CDLL:
             "w8a8_moe_forward": (i32, [ctypes.POINTER(MoEArgs), vp, sz, vp]),
             "w8a8_linear_workspace_bytes": (sz, [i64, i64, i64]),
             "w8a8_linear": (i32, [vp, vp, vp, vp, i64, i64, i64, vp, vp, sz, vp]),
+            "w8a8_fp8_quant_blocks": (i32, [vp, i32, i64, i64, i64, i64, vp, vp, vp]),
+            "w8a8_fp8_grouped_gemm_w13_silu": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                                                     vp, vp, vp, sz, vp]),
+            "w8a8_fp8_grouped_gemm_w2_combine": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                                       i64, vp, vp, sz, vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -155,6 +162,13 @@ def w8a8_quant_per_token(x, group: int, q, scale, stream=None) -> None:
 def w8a8_quant_blocks(x, block_rows: int, block_cols: int, q, scale, stream=None) -> None:
     rows, cols = x.shape
     _call("w8a8_quant_blocks", _ptr(x), _dtype_code(x), rows, cols, block_rows, block_cols, _ptr(q), _ptr(scale),
+          _stream(stream))
+
+
+def w8a8_fp8_quant_blocks(x, block_rows: int, block_cols: int, q, scale, stream=None) -> None:
+    """FP8 (E4M3) codes (uint8 q) with one scale per block_rows x block_cols block."""
+    rows, cols = x.shape
+    _call("w8a8_fp8_quant_blocks", _ptr(x), _dtype_code(x), rows, cols, block_rows, block_cols, _ptr(q), _ptr(scale),
           _stream(stream))
 
 
@@ -237,6 +251,18 @@ def w8a8_grouped_gemm_w2_combine(h_q, h_scale, w2, w2_scale, sorted_pair_ids, pa
 def w8a8_block_grouped_gemm_w2_combine(h_q, h_scale, w2, w2_scale, sorted_pair_ids, padded_offsets, tile_expert,
                                        num_tiles, topk_weights, T, k, block_m, out, ws, stream=None) -> None:
     _w2("w8a8_block_grouped_gemm_w2_combine", h_q, h_scale, w2, w2_scale, sorted_pair_ids, padded_offsets,
+        tile_expert, num_tiles, topk_weights, T, k, block_m, out, ws, stream)
+
+
+def w8a8_fp8_grouped_gemm_w13_silu(a_q, a_scale, w13, w13_scale, sorted_pair_ids, padded_offsets, tile_expert,
+                                   num_tiles, T, k, block_m, h_q, h_scale, ws, stream=None) -> None:
+    _w13("w8a8_fp8_grouped_gemm_w13_silu", a_q, a_scale, w13, w13_scale, sorted_pair_ids, padded_offsets,
+         tile_expert, num_tiles, T, k, block_m, h_q, h_scale, ws, stream)
+
+
+def w8a8_fp8_grouped_gemm_w2_combine(h_q, h_scale, w2, w2_scale, sorted_pair_ids, padded_offsets, tile_expert,
+                                     num_tiles, topk_weights, T, k, block_m, out, ws, stream=None) -> None:
+    _w2("w8a8_fp8_grouped_gemm_w2_combine", h_q, h_scale, w2, w2_scale, sorted_pair_ids, padded_offsets,
         tile_expert, num_tiles, topk_weights, T, k, block_m, out, ws, stream)
 
 

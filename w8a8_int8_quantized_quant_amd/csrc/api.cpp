@@ -27,6 +27,10 @@ bool valid_block_m(int64_t bm) { return bm == 16 || bm == 32 || bm == 64 || bm =
 
 bool valid_dim(int64_t d) { return d >= 128 && d <= kMaxDim && d % 128 == 0; }
 
+bool valid_mode(int32_t m) {
+  return m == W8A8_SCALE_CHANNEL || m == W8A8_SCALE_BLOCK128 || m == W8A8_SCALE_FP8_BLOCK128;
+}
+
 // T, k, E limits shared by every MoE entry point.
 int32_t check_tke(int64_t T, int64_t k, int64_t E) {
   if (T < 0 || k < 0 || E < 0) return W8A8_INVALID_ARGUMENT;
@@ -97,8 +101,8 @@ const char* w8a8_status_string(int32_t status) {
   }
 }
 
-int32_t w8a8_quant_blocks(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t block_rows,
-                          int64_t block_cols, int8_t* q, float* scale, hipStream_t stream) {
+static int32_t quant_entry(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t block_rows,
+                           int64_t block_cols, int8_t* q, float* scale, hipStream_t stream, bool fp8) {
   if (rows < 0 || cols < 0 || block_rows < 1 || block_cols < 1) return W8A8_INVALID_ARGUMENT;
   if (x_dtype != W8A8_DTYPE_F32 && x_dtype != W8A8_DTYPE_BF16) return W8A8_UNSUPPORTED_DTYPE;
   if (rows == 0 || cols == 0) return W8A8_OK;
@@ -106,7 +110,18 @@ int32_t w8a8_quant_blocks(const void* x, int32_t x_dtype, int64_t rows, int64_t 
   const int64_t nb = ((rows + block_rows - 1) / block_rows) * ((cols + block_cols - 1) / block_cols);
   if (rows >= (int64_t(1) << 31) || nb >= (int64_t(1) << 31) || rows * cols >= (int64_t(1) << 40))
     return W8A8_UNSUPPORTED_SHAPE;
-  return hip_status(w8a8::quant_blocks(x, x_dtype, rows, cols, block_rows, block_cols, q, scale, stream));
+  return hip_status(w8a8::quant_blocks(x, x_dtype, rows, cols, block_rows, block_cols, q, scale, stream, fp8));
+}
+
+int32_t w8a8_quant_blocks(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t block_rows,
+                          int64_t block_cols, int8_t* q, float* scale, hipStream_t stream) {
+  return quant_entry(x, x_dtype, rows, cols, block_rows, block_cols, q, scale, stream, false);
+}
+
+int32_t w8a8_fp8_quant_blocks(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t block_rows,
+                              int64_t block_cols, uint8_t* q, float* scale, hipStream_t stream) {
+  return quant_entry(x, x_dtype, rows, cols, block_rows, block_cols, reinterpret_cast<int8_t*>(q), scale, stream,
+                     true);
 }
 
 int32_t w8a8_quant_per_token(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t group, int8_t* q,
@@ -174,14 +189,20 @@ int32_t w8a8_grouped_gemm_i32(const int8_t* a, int32_t gather, const int8_t* w, 
 
 size_t w8a8_w13_workspace_bytes(int64_t T, int64_t k, int64_t E, int64_t H, int64_t I, int64_t block_m,
                                 int32_t scale_mode) {
-  if (check_tke(T, k, E) || !valid_dim(H) || !valid_dim(I) || !valid_block_m(block_m)) return 0;
-  return w8a8::w13_ws_bytes(shape_of(T, k, E, H, I, block_m), scale_mode);
+  if (check_tke(T, k, E) || !valid_dim(H) || !valid_dim(I) || !valid_block_m(block_m) || !valid_mode(scale_mode))
+    return 0;
+  const GroupedShape s = shape_of(T, k, E, H, I, block_m);
+  if (scale_mode == W8A8_SCALE_FP8_BLOCK128 && !w8a8::fp8_supported(s)) return 0;
+  return w8a8::w13_ws_bytes(s, scale_mode);
 }
 
 size_t w8a8_w2_workspace_bytes(int64_t T, int64_t k, int64_t E, int64_t H, int64_t I, int64_t block_m,
                                int32_t scale_mode) {
-  if (check_tke(T, k, E) || !valid_dim(H) || !valid_dim(I) || !valid_block_m(block_m)) return 0;
-  return w8a8::w2_ws_bytes(shape_of(T, k, E, H, I, block_m), scale_mode);
+  if (check_tke(T, k, E) || !valid_dim(H) || !valid_dim(I) || !valid_block_m(block_m) || !valid_mode(scale_mode))
+    return 0;
+  const GroupedShape s = shape_of(T, k, E, H, I, block_m);
+  if (scale_mode == W8A8_SCALE_FP8_BLOCK128 && !w8a8::fp8_supported(s)) return 0;
+  return w8a8::w2_ws_bytes(s, scale_mode);
 }
 
 static int32_t w13_entry(int32_t mode, const int8_t* a_q, const float* a_scale, const int8_t* w13,
@@ -191,10 +212,11 @@ static int32_t w13_entry(int32_t mode, const int8_t* a_q, const float* a_scale, 
                          size_t ws_bytes, hipStream_t stream) {
   int32_t st = check_grouped(sorted, padded_offsets, tile_expert, num_tiles, T, k, E, H, I, block_m);
   if (st) return st;
+  const GroupedShape s = shape_of(T, k, E, H, I, block_m);
+  if (mode == W8A8_SCALE_FP8_BLOCK128 && !w8a8::fp8_supported(s)) return W8A8_UNSUPPORTED_SHAPE;
   if (T == 0) return W8A8_OK;
   if (!ok16(a_q) || !ok4(a_scale) || !ok16(w13) || !ok4(w13_scale) || !ok16(h_q) || !ok4(h_scale))
     return W8A8_INVALID_ARGUMENT;
-  const GroupedShape s = shape_of(T, k, E, H, I, block_m);
   const size_t need = w8a8::w13_ws_bytes(s, mode);
   if (ws_bytes < need) return W8A8_WORKSPACE_TOO_SMALL;
   if (!aligned(ws, 256)) return W8A8_INVALID_ARGUMENT;
@@ -209,10 +231,11 @@ static int32_t w2_entry(int32_t mode, const int8_t* h_q, const float* h_scale, c
                         size_t ws_bytes, hipStream_t stream) {
   int32_t st = check_grouped(sorted, padded_offsets, tile_expert, num_tiles, T, k, E, H, I, block_m);
   if (st) return st;
+  const GroupedShape s = shape_of(T, k, E, H, I, block_m);
+  if (mode == W8A8_SCALE_FP8_BLOCK128 && !w8a8::fp8_supported(s)) return W8A8_UNSUPPORTED_SHAPE;
   if (T == 0) return W8A8_OK;
   if (!ok16(h_q) || !ok4(h_scale) || !ok16(w2) || !ok4(w2_scale) || !ok4(topk_weights) || !ok16(out))
     return W8A8_INVALID_ARGUMENT;
-  const GroupedShape s = shape_of(T, k, E, H, I, block_m);
   const size_t need = w8a8::w2_ws_bytes(s, mode);
   if (ws_bytes < need) return W8A8_WORKSPACE_TOO_SMALL;
   if (!aligned(ws, 256)) return W8A8_INVALID_ARGUMENT;
@@ -260,6 +283,28 @@ int32_t w8a8_block_grouped_gemm_w2_combine(const int8_t* h_q, const float* h_sca
                   num_tiles, topk_weights, T, k, E, H, I, block_m, out, ws, ws_bytes, stream);
 }
 
+int32_t w8a8_fp8_grouped_gemm_w13_silu(const uint8_t* a_q, const float* a_scale, const uint8_t* w13,
+                                       const float* w13_scale, const int32_t* sorted_pair_ids,
+                                       const int32_t* padded_offsets, const int32_t* tile_expert,
+                                       const int32_t* num_tiles, int64_t T, int64_t k, int64_t E, int64_t H,
+                                       int64_t I, int64_t block_m, uint8_t* h_q, float* h_scale, void* ws,
+                                       size_t ws_bytes, hipStream_t stream) {
+  return w13_entry(W8A8_SCALE_FP8_BLOCK128, reinterpret_cast<const int8_t*>(a_q), a_scale,
+                   reinterpret_cast<const int8_t*>(w13), w13_scale, sorted_pair_ids, padded_offsets, tile_expert,
+                   num_tiles, T, k, E, H, I, block_m, reinterpret_cast<int8_t*>(h_q), h_scale, ws, ws_bytes, stream);
+}
+
+int32_t w8a8_fp8_grouped_gemm_w2_combine(const uint8_t* h_q, const float* h_scale, const uint8_t* w2,
+                                         const float* w2_scale, const int32_t* sorted_pair_ids,
+                                         const int32_t* padded_offsets, const int32_t* tile_expert,
+                                         const int32_t* num_tiles, const float* topk_weights, int64_t T, int64_t k,
+                                         int64_t E, int64_t H, int64_t I, int64_t block_m, float* out, void* ws,
+                                         size_t ws_bytes, hipStream_t stream) {
+  return w2_entry(W8A8_SCALE_FP8_BLOCK128, reinterpret_cast<const int8_t*>(h_q), h_scale,
+                  reinterpret_cast<const int8_t*>(w2), w2_scale, sorted_pair_ids, padded_offsets, tile_expert,
+                  num_tiles, topk_weights, T, k, E, H, I, block_m, out, ws, ws_bytes, stream);
+}
+
 // ---------------------------------------------------------------------------------------- composite
 
 size_t w8a8_linear_workspace_bytes(int64_t M, int64_t N, int64_t K) {
@@ -302,7 +347,7 @@ Layout layout_of(int64_t T, int64_t k, int64_t E, int64_t H, int64_t I, int64_t 
   const int64_t P = T * k;
   const GroupedShape s = shape_of(T, k, E, H, I, bm);
   L.max_rows = s.max_rows;
-  const bool block = mode == W8A8_SCALE_BLOCK128;
+  const bool block = mode != W8A8_SCALE_CHANNEL;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t at = off;
@@ -334,7 +379,8 @@ size_t w8a8_moe_workspace_bytes(int64_t T, int64_t k, int64_t E, int64_t H, int6
   if (check_tke(T, k, E) || !valid_dim(H) || !valid_dim(I)) return 0;
   if (block_m == 0) block_m = w8a8_moe_pick_block_m(T, k, E);
   if (!valid_block_m(block_m)) return 0;
-  if (scale_mode != W8A8_SCALE_CHANNEL && scale_mode != W8A8_SCALE_BLOCK128) return 0;
+  if (!valid_mode(scale_mode)) return 0;
+  if (scale_mode == W8A8_SCALE_FP8_BLOCK128 && !w8a8::fp8_supported(shape_of(T, k, E, H, I, block_m))) return 0;
   return layout_of(T, k, E, H, I, block_m, scale_mode).total;
 }
 
@@ -344,10 +390,12 @@ int32_t w8a8_moe_forward(const struct w8a8_moe_args* a, void* ws, size_t ws_byte
   if (st) return st;
   if (a->H < 0 || a->I < 0 || a->block_m < 0) return W8A8_INVALID_ARGUMENT;
   if (!valid_dim(a->H) || !valid_dim(a->I)) return W8A8_UNSUPPORTED_SHAPE;
-  if (a->scale_mode != W8A8_SCALE_CHANNEL && a->scale_mode != W8A8_SCALE_BLOCK128) return W8A8_INVALID_ARGUMENT;
+  if (!valid_mode(a->scale_mode)) return W8A8_INVALID_ARGUMENT;
   if (a->x_dtype != W8A8_DTYPE_F32 && a->x_dtype != W8A8_DTYPE_BF16) return W8A8_UNSUPPORTED_DTYPE;
   const int64_t bm = a->block_m == 0 ? w8a8_moe_pick_block_m(a->T, a->k, a->E) : a->block_m;
   if (!valid_block_m(bm)) return W8A8_UNSUPPORTED_SHAPE;
+  if (a->scale_mode == W8A8_SCALE_FP8_BLOCK128 && !w8a8::fp8_supported(shape_of(a->T, a->k, a->E, a->H, a->I, bm)))
+    return W8A8_UNSUPPORTED_SHAPE;
   if (a->T == 0) return W8A8_OK;
   st = route_check(a->router_logits, a->T, a->E, a->k, a->score_fn, a->n_group, a->topk_group, a->correction_bias,
                    a->topk_ids ? a->topk_ids : reinterpret_cast<int32_t*>(16),
@@ -374,13 +422,14 @@ int32_t w8a8_moe_forward(const struct w8a8_moe_args* a, void* ws, size_t ws_byte
   int8_t* h_q = reinterpret_cast<int8_t*>(base + L.h_q);
   float* h_s = reinterpret_cast<float*>(base + L.h_s);
   void* gws = base + L.gemm_ws;
-  const bool block = a->scale_mode == W8A8_SCALE_BLOCK128;
+  const bool block = a->scale_mode != W8A8_SCALE_CHANNEL;
+  const bool fp8 = a->scale_mode == W8A8_SCALE_FP8_BLOCK128;
   const GroupedShape s = shape_of(a->T, a->k, a->E, a->H, a->I, bm);
 
   hipError_t e = w8a8::topk_route(a->router_logits, a->T, a->E, a->k, a->score_fn, a->n_group, a->topk_group,
                                   a->renormalize, a->routed_scaling, a->correction_bias, ids, tw, stream);
   if (e == hipSuccess)
-    e = w8a8::quant_blocks(a->x, a->x_dtype, a->T, a->H, 1, block ? 128 : a->H, a_q, a_s, stream);
+    e = w8a8::quant_blocks(a->x, a->x_dtype, a->T, a->H, 1, block ? 128 : a->H, a_q, a_s, stream, fp8);
   if (e == hipSuccess)
     e = w8a8::align_by_expert(ids, a->T * a->k, a->E, bm, counts, offsets, padded, sorted, tile_expert, num_tiles,
                               L.max_rows / bm, base + L.align_ws, stream);

@@ -35,6 +35,25 @@ __device__ __forceinline__ int8_t quant_value(float x, float s) {
   return (int8_t)(int)v;
 }
 
+// FP8 rule (E4M3 as the OCP 8-bit floating-point specification defines it: bias 7, 3 mantissa
+// bits, largest finite 448): scale = max(max|x| / 448, 1e-8); code = the E4M3 value nearest to
+// x / scale, ties to even, after clamping x / scale to [-448, 448].  v_cvt_pk_fp8_f32 rounds to
+// nearest even and keeps the sign of a zero result; the clamp keeps it off the NaN encoding.
+__device__ __forceinline__ float fp8_scale(float amax) {
+  float s = amax / 448.0f;
+  return s < 1e-8f ? 1e-8f : s;
+}
+__device__ __forceinline__ float fp8_clamp(float v) { return fminf(fmaxf(v, -448.0f), 448.0f); }
+// Two codes into bytes 0-1 (HI = false) or 2-3 (HI = true) of `old`.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8_pack2(float a, float b, uint32_t old) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fp8_clamp(a), fp8_clamp(b), (int)old, HI);
+}
+__device__ __forceinline__ uint8_t fp8_value(float x, float s) {
+  const float v = x / s;
+  return (uint8_t)(fp8_pack2<false>(v, v, 0u) & 0xFFu);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));

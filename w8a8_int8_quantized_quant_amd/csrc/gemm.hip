@@ -36,6 +36,7 @@
 // Grids cover the worst case; workgroups past the device-side tile count exit
 // at once (no host read, graph-capturable).
 #include <algorithm>
+#include <type_traits>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -45,15 +46,22 @@ namespace {
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));  // native vector: the non-temporal builtins take it
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));  // 32 FP8 codes: one lane's MFMA operand
 
 constexpr int kThreads = 256;
 
 enum class BMap { Plain, Split };
-enum class Epi { I32, W13Channel, W2Channel, W13Block, W2Block };
+// W13Fp8 / W2Fp8: the block-wise epilogues for FP8 (E4M3) operands, whose per-K-block partial
+// sums come from the FP8 MFMA in fp32; the first GEMM requantizes to E4M3.
+enum class Epi { I32, W13Channel, W2Channel, W13Block, W2Block, W13Fp8, W2Fp8 };
 
 template <Epi EPI>
+constexpr bool is_fp8() {
+  return EPI == Epi::W13Fp8 || EPI == Epi::W2Fp8;
+}
+template <Epi EPI>
 constexpr bool is_block() {
-  return EPI == Epi::W13Block || EPI == Epi::W2Block;
+  return EPI == Epi::W13Block || EPI == Epi::W2Block || is_fp8<EPI>();
 }
 
 struct Params {
@@ -115,8 +123,8 @@ __device__ __forceinline__ void block_scales(const Params& p, const int32_t* sh_
 
 // Block-wise: fold the int32 partials of one K-block into the fp32 sums, in the written order
 // acc_f = acc_f + (((float)part * a_s) * w_s), and clear them.
-template <int FM, int FN>
-__device__ __forceinline__ void block_flush(i32x4 (&acc)[FM][FN], float (&accf)[FM][FN][4], const float (&as)[FM][4],
+template <int FM, int FN, typename AccT>
+__device__ __forceinline__ void block_flush(AccT (&acc)[FM][FN], float (&accf)[FM][FN][4], const float (&as)[FM][4],
                                             const float (&ws)[FN]) {
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm)
@@ -127,12 +135,12 @@ __device__ __forceinline__ void block_flush(i32x4 (&acc)[FM][FN], float (&accf)[
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-    for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = i32x4{0, 0, 0, 0};
+    for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = AccT{0, 0, 0, 0};
 }
 
 // Epilogues.  Rows whose sh_pid is the sentinel (>= P) are skipped.
-template <int BM, int BN, int WM, int WN, int FM, int FN, BMap MAP, Epi EPI>
-__device__ __forceinline__ void epilogue(const Params& p, const i32x4 (&acc)[FM][FN], const float (&accf)[FM][FN][4],
+template <int BM, int BN, int WM, int WN, int FM, int FN, BMap MAP, Epi EPI, typename AccT>
+__device__ __forceinline__ void epilogue(const Params& p, const AccT (&acc)[FM][FN], const float (&accf)[FM][FN][4],
                                          const int32_t* sh_pid, float (*sh_red)[BM], int64_t row0, int64_t nt,
                                          int64_t e, int wm, int wn, int l, int tid) {
   constexpr int FNH = FN / 2;
@@ -148,7 +156,7 @@ __device__ __forceinline__ void epilogue(const Params& p, const i32x4 (&acc)[FM]
         for (int fn = 0; fn < FN; ++fn)
           p.out_i32[(row0 + trow) * p.N + nt * BN + brow_of<BN, WN, FN, MAP>(wn, fn) + (l % 16)] = acc[fm][fn][r];
       }
-  } else if constexpr (EPI == Epi::W2Channel || EPI == Epi::W2Block) {
+  } else if constexpr (EPI == Epi::W2Channel || EPI == Epi::W2Block || EPI == Epi::W2Fp8) {
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
@@ -214,7 +222,7 @@ __device__ __forceinline__ void epilogue(const Params& p, const i32x4 (&acc)[FM]
     }
   } else {
     // First GEMM, block-wise: SiLU(gate) * up, then requantization in the tile, whose BN/2 = 128
-    // gate columns are exactly one 128-wide requant group.
+    // gate columns are exactly one 128-wide requant group (INT8, or E4M3 for FP8 operands).
     const int64_t I = p.I;
     float hf[FM][FNH][4];
     float rmax[FM][4];
@@ -251,12 +259,13 @@ __device__ __forceinline__ void epilogue(const Params& p, const i32x4 (&acc)[FM]
         float m = sh_red[0][trow];
 #pragma unroll
         for (int w = 1; w < WN; ++w) m = fmaxf(m, sh_red[w][trow]);
-        const float s = quant_scale(m);
+        const float s = is_fp8<EPI>() ? fp8_scale(m) : quant_scale(m);
         const int64_t grow = row0 + trow;
         if (wn == 0 && (l % 16) == 0) p.h_s[grow * (I / 128) + nt] = s;
 #pragma unroll
         for (int f = 0; f < FNH; ++f)
-          p.h_q[grow * I + nt * (BN / 2) + brow_of<BN, WN, FN, MAP>(wn, f) + (l % 16)] = quant_value(hf[fm][f][r], s);
+          p.h_q[grow * I + nt * (BN / 2) + brow_of<BN, WN, FN, MAP>(wn, f) + (l % 16)] =
+              is_fp8<EPI>() ? (int8_t)fp8_value(hf[fm][f][r], s) : quant_value(hf[fm][f][r], s);
       }
   }
 }
@@ -490,6 +499,56 @@ __device__ __forceinline__ void dma_stage(const int8_t* stage, int8_t* next, con
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn)
           acc[fm][fn] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[fm], bf[fn], acc[fm][fn], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+// The same K loop step for FP8 (E4M3) operands: one v_mfma_scale_f32_16x16x128_f8f6f4 per
+// fragment covers the stage's 128 K-bytes (the scale operands are E8M0 127, i.e. 1.0).  Lane
+// (g, fr) takes the 16-byte chunks 2g and 2g+1 of row fr, and the same chunks of both operands, so
+// A and B hold the same K-elements at the same register positions.  Groups are (fragment row,
+// half of the fragment columns), two MFMAs each, with the next stage's DMA spread between them as
+// in dma_stage.
+template <int BM, int BN, int WM, int WN, int A_LD, int LD, BMap MAP>
+__device__ __forceinline__ void dma_stage_f8(const int8_t* stage, int8_t* next, const int8_t* a_base,
+                                             const int8_t* b_base, const uint32_t (&off)[LD], int a_dst, int b_dst,
+                                             uint32_t next_off, bool prefetch, f32x4 (&acc)[BM / WM / 16][BN / WN / 16],
+                                             int wm, int wn, int g, int fr, int rows) {
+  constexpr int FM = BM / WM / 16, FN = BN / WN / 16, FNH = FN / 2;
+  constexpr int GROUPS = 2 * FM;
+  static_assert(GROUPS >= LD && FN % 2 == 0, "DMA slots");  // DMA c goes out before group (c * GROUPS) / LD
+  constexpr int kScaleOne = 127;                             // E8M0 exponent of 1.0
+  const int c0 = fr * kDmaBK + (((2 * g) ^ swz(fr)) << 4);
+  const int c1 = fr * kDmaBK + (((2 * g + 1) ^ swz(fr)) << 4);
+  auto ld32 = [&](const int8_t* rowbase) {
+    const i32x4 lo = *reinterpret_cast<const i32x4*>(rowbase + c0);
+    const i32x4 hi = *reinterpret_cast<const i32x4*>(rowbase + c1);
+    return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  };
+  i32x8 bf[FN];
+#pragma unroll
+  for (int fn = 0; fn < FN; ++fn) bf[fn] = ld32(stage + BM * kDmaBK + brow_of<BN, WN, FN, MAP>(wn, fn) * kDmaBK);
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) {
+    const i32x8 af = ld32(stage + (wm * FM + fm) * 16 * kDmaBK);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int grp = fm * 2 + h;
+#pragma unroll
+      for (int c = 0; c < LD; ++c)
+        if ((c * GROUPS) / LD == grp && prefetch) {
+          if (c < A_LD)
+            dma16(a_base + (off[c] + next_off), next + a_dst + c * 1024);
+          else
+            dma16_nt(b_base + (off[c] + next_off), next + b_dst + (c - A_LD) * 1024);
+        }
+      if (fm * 16 < rows) {
+#pragma unroll
+        for (int f = 0; f < FNH; ++f)
+          acc[fm][h * FNH + f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              af, bf[h * FNH + f], acc[fm][h * FNH + f], 0, 0, 0, kScaleOne, 0, kScaleOne);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -730,6 +789,8 @@ template <int BM, int BN, int WM, int WN, int KT, BMap MAP, Epi EPI>
 __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_ring_kernel(const Params p,
                                                                               const int32_t* __restrict__ work) {
   constexpr bool kBlock = is_block<EPI>();
+  constexpr bool kFp8 = is_fp8<EPI>();
+  using AccT = typename std::conditional<kFp8, f32x4, i32x4>::type;
   constexpr int NT = WM * WN * kWave;
   constexpr int NW = WM * WN;
   constexpr int FM = BM / WM / 16;
@@ -742,7 +803,7 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_ring_kernel(c
   constexpr int SG = 4;  // K-blocks per activation-scale DMA
   static_assert(EPI != Epi::I32, "scaled epilogues only");
   static_assert(A_LD >= 1 && B_LD >= 1 && (BM * CPR) % NT == 0 && (BN * CPR) % NT == 0, "tile shape");
-  static_assert(KT >= 2 && KT % SG == 0 && LD + 1 < 64, "K steps");
+  static_assert(KT >= 1 && LD + 1 < 64, "K steps");
   static_assert(!kBlock || (NW * 16 == BM && kWave == 16 * SG), "one scale DMA per wavefront: 16 rows x SG blocks");
   static_assert(!kBlock || BN == 256, "two 128-row weight-scale blocks per tile");
   static_assert(MAP == BMap::Plain || FN % 2 == 0, "split tiles need gate and up fragments");
@@ -802,17 +863,19 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_ring_kernel(c
     const int q = (wv * B_LD + c) * kWave + l, j = q / CPR, kc = (q % CPR) ^ swz(j);
     off[A_LD + c] = (uint32_t)(wrow_of<BN, MAP>(nt, j, p.I) * p.K + kc * 16);
   }
-  // activation-scale DMA: lane l brings row wv * 16 + (l & 15) of K-block (group * SG + l / 16)
-  const uint32_t s_off = kBlock ? (uint32_t)(src_row(wv * 16 + (l & 15)) * KT + (l >> 4)) : 0u;
+  // activation-scale DMA: lane l brings row wv * 16 + (l & 15) of K-block group * SG + l / 16
+  // (the last K-block again where a group runs past K)
+  const uint32_t s_off = kBlock ? (uint32_t)(src_row(wv * 16 + (l & 15)) * KT) : 0u;
+  auto s_blk = [&](int q) { return (uint32_t)min(q * SG + (l >> 4), KT - 1); };
   const int a_dst = wv * A_LD * 1024, b_dst = BM * kDmaBK + wv * B_LD * 1024;
 
-  i32x4 acc[FM][FN];
+  AccT acc[FM][FN];
   float accf[FM][FN][kBlock ? 4 : 1];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      acc[i][j] = i32x4{0, 0, 0, 0};
+      acc[i][j] = AccT{0, 0, 0, 0};
 #pragma unroll
       for (int r = 0; r < (kBlock ? 4 : 1); ++r) accf[i][j][r] = 0.0f;
     }
@@ -822,7 +885,7 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_ring_kernel(c
 #define W8A8_RSAS(q) (((q) & 1) ? sas1 : sas0)
   __syncthreads();  // sh_pid, sh_ws
 #pragma unroll
-  for (int st = 0; st < 2; ++st) {
+  for (int st = 0; st < (KT < 2 ? KT : 2); ++st) {
 #pragma unroll
     for (int c = 0; c < LD; ++c) {
       if (c < A_LD)
@@ -830,9 +893,13 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_ring_kernel(c
       else
         dma16_nt(wexp + (off[c] + (uint32_t)(st * kDmaBK)), W8A8_RSTG(st) + b_dst + (c - A_LD) * 1024);
     }
-    if (kBlock && st == 0) dma4(p.a_s + s_off, sas0 + wv * kWave);
+    if (kBlock && st == 0) dma4(p.a_s + (s_off + s_blk(0)), sas0 + wv * kWave);
   }
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm<LD>());  // stage 0 (and the first scale group) landed
+  // stage 0 (and the first scale group) landed
+  if constexpr (KT >= 2)
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm<LD>());
+  else
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
 
   // Uniform bases of the stage two steps ahead, advanced one step at a time; the empty asm keeps
   // the compiler from precomputing every step's address up front.
@@ -844,9 +911,13 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_ring_kernel(c
     barrier_no_fence();
     const bool more = kt + 2 < KT;
     const bool sdma = kBlock && more && (kt + 2) % SG == 0;  // scale group of stage kt + 2 goes out now
-    if (sdma) dma4(p.a_s + s_off + (kt + 2), W8A8_RSAS((kt + 2) / SG) + wv * kWave);
-    dma_stage<BM, BN, WM, WN, A_LD, LD, MAP>(W8A8_RSTG(kt % 3), W8A8_RSTG((kt + 2) % 3), a_next, b_next, off, a_dst,
-                                             b_dst, 0u, more, acc, wm, wn, g, fr, wrows);
+    if (sdma) dma4(p.a_s + (s_off + s_blk((kt + 2) / SG)), W8A8_RSAS((kt + 2) / SG) + wv * kWave);
+    if constexpr (kFp8)
+      dma_stage_f8<BM, BN, WM, WN, A_LD, LD, MAP>(W8A8_RSTG(kt % 3), W8A8_RSTG((kt + 2) % 3), a_next, b_next, off,
+                                                  a_dst, b_dst, 0u, more, acc, wm, wn, g, fr, wrows);
+    else
+      dma_stage<BM, BN, WM, WN, A_LD, LD, MAP>(W8A8_RSTG(kt % 3), W8A8_RSTG((kt + 2) % 3), a_next, b_next, off, a_dst,
+                                               b_dst, 0u, more, acc, wm, wn, g, fr, wrows);
     a_next += kDmaBK;
     b_next += kDmaBK;
     asm volatile("" : "+s"(a_next), "+s"(b_next));
@@ -863,7 +934,7 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_ring_kernel(c
         const float w0 = sh_ws[0][kt], w1 = sh_ws[1][kt];
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) ws[fn] = brow_of<BN, WN, FN, MAP>(wn, fn) >= 128 ? w1 : w0;
-        block_flush<FM, FN>(acc, accf, as, ws);
+        block_flush<FM, FN, AccT>(acc, accf, as, ws);
       }
     }
     if (sdma)
@@ -1135,9 +1206,34 @@ hipError_t launch_ring(Params prm, const GroupedShape& s, const int32_t* padded_
   return hipGetLastError();
 }
 
+// FP8 operands always take the ring engine; K sizes with an instantiated kernel (K / 128).
+bool fp8_kt_ok(int64_t kt) { return kt == 1 || kt == 2 || kt == 4 || kt == 8 || kt == 16 || kt == 32 || kt == 56; }
+
+template <BMap MAP, Epi EPI>
+hipError_t launch_ring_fp8(const Params& prm, const GroupedShape& s, const int32_t* padded_offsets, int32_t* work,
+                           hipStream_t stream) {
+  switch (prm.K / kDmaBK) {
+    case 1: return launch_ring<MAP, EPI, 1>(prm, s, padded_offsets, work, stream);
+    case 2: return launch_ring<MAP, EPI, 2>(prm, s, padded_offsets, work, stream);
+    case 4: return launch_ring<MAP, EPI, 4>(prm, s, padded_offsets, work, stream);
+    case 8: return launch_ring<MAP, EPI, 8>(prm, s, padded_offsets, work, stream);
+    case 16: return launch_ring<MAP, EPI, 16>(prm, s, padded_offsets, work, stream);
+    case 32: return launch_ring<MAP, EPI, 32>(prm, s, padded_offsets, work, stream);
+    case 56: return launch_ring<MAP, EPI, 56>(prm, s, padded_offsets, work, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace
 
+bool fp8_supported(const GroupedShape& s) {
+  return s.H % kDmaBN == 0 && s.I % (kDmaBN / 2) == 0 && fp8_kt_ok(s.H / kDmaBK) && fp8_kt_ok(s.I / kDmaBK) &&
+         (uint64_t)s.T * s.H < (1ull << 32) && (uint64_t)s.max_rows * s.I < (1ull << 32) &&
+         (uint64_t)2 * s.I * s.H < (1ull << 32);
+}
+
 size_t w13_ws_bytes(const GroupedShape& s, int32_t scale_mode) {
+  if (scale_mode == 2) return work_bytes(s);
   if (scale_mode == 1) return use_ring(s, 1) ? work_bytes(s) : 256;
   return round256(sizeof(float) * (size_t)(s.max_rows * s.I)) +
          round256(sizeof(float) * (size_t)(s.max_rows * w13_n_tiles(s, scale_mode))) + work_bytes(s);
@@ -1189,6 +1285,8 @@ hipError_t w13_silu(const GroupedShape& s, int32_t scale_mode, const int8_t* a_q
   prm.w_s = w13_s;
   prm.h_q = h_q;
   prm.h_s = h_s;
+  if (scale_mode == 2)
+    return launch_ring_fp8<BMap::Split, Epi::W13Fp8>(prm, s, padded_offsets, static_cast<int32_t*>(ws), stream);
   if (scale_mode == 1) {
     if (use_ring(s, 1))
       return launch_ring<BMap::Split, Epi::W13Block, kRingH / kDmaBK>(prm, s, padded_offsets,
@@ -1242,7 +1340,9 @@ hipError_t w2_combine(const GroupedShape& s, int32_t scale_mode, const int8_t* h
   prm.w_s = w2_s;
   prm.out_f32 = y;
   hipError_t err;
-  if (scale_mode == 1)
+  if (scale_mode == 2)
+    err = launch_ring_fp8<BMap::Plain, Epi::W2Fp8>(prm, s, padded_offsets, work, stream);
+  else if (scale_mode == 1)
     err = use_ring(s, 1) ? launch_ring<BMap::Plain, Epi::W2Block, kRingI / kDmaBK>(prm, s, padded_offsets, work, stream)
                          : launch_bm<BMap::Plain, Epi::W2Block, kBNStaged>(prm, s.max_rows, stream);
   else if (use_ring(s, 0))

@@ -1,5 +1,6 @@
 // probe.hip -- measured peaks of the chip the layer runs on, for the benchmark's report: a
-// streaming HBM read, a streaming HBM copy and an INT8 MFMA loop.  Not part of the layer.
+// streaming HBM read, a streaming HBM copy and an INT8 MFMA loop; and one FP8 MFMA on given
+// operands, whose sums the tests compare with exact ones.  Not part of the layer.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -78,6 +79,23 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(int64_t iters, int32_t* 
   if (s == 0x13572468) sink[0] = s;
 }
 
+// One v_mfma_scale_f32_16x16x128_f8f6f4 per wavefront (scales 1.0, C = 0) on one [16, 128] A block
+// and one [16, 128] B block of E4M3 codes, K-contiguous rows, with the operand layout of the
+// layer's FP8 GEMM: lane (g, r) holds bytes [32 g, 32 g + 32) of row r of each operand.
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(64) void mfma_f8_block_kernel(const uint8_t* __restrict__ a, const uint8_t* __restrict__ b,
+                                                           float* __restrict__ c) {
+  const int l = threadIdx.x, g = l >> 4, r = l & 15;
+  const int64_t blk = blockIdx.x;
+  const i32x8 av = *reinterpret_cast<const i32x8*>(a + blk * 2048 + r * 128 + g * 32);
+  const i32x8 bv = *reinterpret_cast<const i32x8*>(b + blk * 2048 + r * 128 + g * 32);
+  const f32x4 acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0,
+                                                                      0, 127, 0, 127);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c[blk * 256 + (g * 4 + i) * 16 + r] = acc[i];
+}
+
 }  // namespace
 
 extern "C" {
@@ -99,6 +117,12 @@ int32_t w8a8_probe_copy(const void* src, void* dst, int64_t bytes, hipStream_t s
 int32_t w8a8_probe_mfma_i8(int64_t iters, int32_t workgroups, int32_t* sink, hipStream_t stream) {
   if (!sink || iters < 1 || workgroups < 1) return 1;
   hipLaunchKernelGGL(mfma_kernel, dim3((uint32_t)workgroups), dim3(kThreads), 0, stream, iters, sink);
+  return hipGetLastError() == hipSuccess ? 0 : 5;
+}
+
+int32_t w8a8_probe_mfma_f8_block(const uint8_t* a, const uint8_t* b, float* c, int32_t blocks, hipStream_t stream) {
+  if (!a || !b || !c || blocks < 1) return 1;
+  hipLaunchKernelGGL(mfma_f8_block_kernel, dim3((uint32_t)blocks), dim3(64), 0, stream, a, b, c);
   return hipGetLastError() == hipSuccess ? 0 : 5;
 }
 

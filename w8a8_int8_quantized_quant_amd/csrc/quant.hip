@@ -1,11 +1,14 @@
-// quant.hip -- symmetric INT8 quantization kernels (gfx950).
+// quant.hip -- symmetric INT8 and FP8 (E4M3) quantization kernels (gfx950).
 //
 // Online activation quantization, one scale per token or per token-group
 // (jiqizhixin article on Meituan's INT8 DeepSeek R1, "Quantization
 // exploration"), and the offline weight quantization with one scale per
-// output channel or per 128 x 128 block.  Rule: scale = max(max|x|/127, 1e-8),
-// q = clamp(rne(x / scale)).  The max is order-independent and the division is
-// IEEE, so results are bit-exact regardless of how lanes split the work.
+// output channel or per 128 x 128 block.  INT8 rule: scale = max(max|x|/127,
+// 1e-8), q = clamp(rne(x / scale)).  FP8 (SGLang PR #8273: per-block FP8
+// weights, per-token-group FP8 activations): scale = max(max|x|/448, 1e-8), q =
+// the nearest E4M3 code of x / scale.  The max is order-independent and the
+// division is IEEE, so results are bit-exact regardless of how lanes split the
+// work.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -46,8 +49,28 @@ __device__ __forceinline__ void load8<float>(const float* p, float (&v)[8]) {
   v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
+// The two code formats: scale rule, one code, four codes packed into a word.
+struct Int8Codec {
+  static __device__ __forceinline__ float scale(float amax) { return quant_scale(amax); }
+  static __device__ __forceinline__ int8_t code(float x, float s) { return quant_value(x, s); }
+  static __device__ __forceinline__ uint32_t pack4(const float* v, float s) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w |= (uint32_t)(uint8_t)quant_value(v[i], s) << (8 * i);
+    return w;
+  }
+};
+struct Fp8Codec {
+  static __device__ __forceinline__ float scale(float amax) { return fp8_scale(amax); }
+  static __device__ __forceinline__ int8_t code(float x, float s) { return (int8_t)fp8_value(x, s); }
+  static __device__ __forceinline__ uint32_t pack4(const float* v, float s) {
+    const uint32_t w = fp8_pack2<false>(v[0] / s, v[1] / s, 0u);
+    return fp8_pack2<true>(v[2] / s, v[3] / s, w);
+  }
+};
+
 // One workgroup per row; cols % 8 == 0 and 16-byte aligned rows: 16-byte loads, 8-byte stores.
-template <typename T>
+template <typename T, typename C>
 __global__ __launch_bounds__(kThreads) void quant_rows_vec_kernel(const T* __restrict__ x, int64_t cols,
                                                                   int8_t* __restrict__ q,
                                                                   float* __restrict__ scale) {
@@ -63,23 +86,17 @@ __global__ __launch_bounds__(kThreads) void quant_rows_vec_kernel(const T* __res
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
   }
-  const float s = quant_scale(block_max(amax, red));
+  const float s = C::scale(block_max(amax, red));
   if (threadIdx.x == 0) scale[row] = s;
   for (int64_t c = threadIdx.x; c < nchunk; c += kThreads) {
     float v[8];
     load8(xr + c * 8, v);
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      lo |= (uint32_t)(uint8_t)quant_value(v[i], s) << (8 * i);
-      hi |= (uint32_t)(uint8_t)quant_value(v[4 + i], s) << (8 * i);
-    }
-    *reinterpret_cast<uint2*>(qr + c * 8) = make_uint2(lo, hi);
+    *reinterpret_cast<uint2*>(qr + c * 8) = make_uint2(C::pack4(v, s), C::pack4(v + 4, s));
   }
 }
 
 // One wave per (row, group) for groups of up to a few hundred columns.
-template <typename T>
+template <typename T, typename C>
 __global__ __launch_bounds__(kThreads) void quant_groups_kernel(const T* __restrict__ x, int64_t rows,
                                                                 int64_t cols, int64_t group,
                                                                 int8_t* __restrict__ q,
@@ -91,13 +108,13 @@ __global__ __launch_bounds__(kThreads) void quant_groups_kernel(const T* __restr
   const int64_t base = row * cols + g * group;
   float amax = 0.0f;
   for (int64_t c = lane_id(); c < group; c += kWave) amax = fmaxf(amax, fabsf(load_as_f32(x, base + c)));
-  const float s = quant_scale(wave_max(amax));
+  const float s = C::scale(wave_max(amax));
   if (lane_id() == 0) scale[gid] = s;
-  for (int64_t c = lane_id(); c < group; c += kWave) q[base + c] = quant_value(load_as_f32(x, base + c), s);
+  for (int64_t c = lane_id(); c < group; c += kWave) q[base + c] = C::code(load_as_f32(x, base + c), s);
 }
 
 // General case: one workgroup per br x bc block (edge blocks may be partial).
-template <typename T>
+template <typename T, typename C>
 __global__ __launch_bounds__(kThreads) void quant_blocks_kernel(const T* __restrict__ x, int64_t rows,
                                                                 int64_t cols, int64_t br, int64_t bc,
                                                                 int8_t* __restrict__ q,
@@ -111,30 +128,30 @@ __global__ __launch_bounds__(kThreads) void quant_blocks_kernel(const T* __restr
   float amax = 0.0f;
   for (int64_t i = threadIdx.x; i < n; i += kThreads)
     amax = fmaxf(amax, fabsf(load_as_f32(x, (r0 + i / w) * cols + c0 + i % w)));
-  const float s = quant_scale(block_max(amax, red));
+  const float s = C::scale(block_max(amax, red));
   if (threadIdx.x == 0) scale[blockIdx.x] = s;
   for (int64_t i = threadIdx.x; i < n; i += kThreads) {
     const int64_t off = (r0 + i / w) * cols + c0 + i % w;
-    q[off] = quant_value(load_as_f32(x, off), s);
+    q[off] = C::code(load_as_f32(x, off), s);
   }
 }
 
-template <typename T>
+template <typename T, typename C>
 hipError_t launch_quant(const void* xv, int64_t rows, int64_t cols, int64_t br, int64_t bc, int8_t* q,
                         float* scale, hipStream_t stream) {
   const T* x = static_cast<const T*>(xv);
   const bool aligned = (reinterpret_cast<uintptr_t>(x) % 16 == 0) && (reinterpret_cast<uintptr_t>(q) % 8 == 0);
   if (br == 1 && bc == cols && cols % 8 == 0 && aligned) {
-    hipLaunchKernelGGL(quant_rows_vec_kernel<T>, dim3((uint32_t)rows), dim3(kThreads), 0, stream, x, cols, q,
+    hipLaunchKernelGGL((quant_rows_vec_kernel<T, C>), dim3((uint32_t)rows), dim3(kThreads), 0, stream, x, cols, q,
                        scale);
   } else if (br == 1 && bc <= 512 && cols % bc == 0) {
     const int64_t waves = rows * (cols / bc);
     const int64_t blocks = (waves + kThreads / kWave - 1) / (kThreads / kWave);
-    hipLaunchKernelGGL(quant_groups_kernel<T>, dim3((uint32_t)blocks), dim3(kThreads), 0, stream, x, rows,
+    hipLaunchKernelGGL((quant_groups_kernel<T, C>), dim3((uint32_t)blocks), dim3(kThreads), 0, stream, x, rows,
                        cols, bc, q, scale);
   } else {
     const int64_t nb = ((rows + br - 1) / br) * ((cols + bc - 1) / bc);
-    hipLaunchKernelGGL(quant_blocks_kernel<T>, dim3((uint32_t)nb), dim3(kThreads), 0, stream, x, rows, cols,
+    hipLaunchKernelGGL((quant_blocks_kernel<T, C>), dim3((uint32_t)nb), dim3(kThreads), 0, stream, x, rows, cols,
                        br, bc, q, scale);
   }
   return hipGetLastError();
@@ -143,10 +160,14 @@ hipError_t launch_quant(const void* xv, int64_t rows, int64_t cols, int64_t br, 
 }  // namespace
 
 hipError_t quant_blocks(const void* x, int32_t dtype, int64_t rows, int64_t cols, int64_t br, int64_t bc,
-                        int8_t* q, float* scale, hipStream_t stream) {
+                        int8_t* q, float* scale, hipStream_t stream, bool fp8) {
   if (rows == 0 || cols == 0) return hipSuccess;
-  if (dtype == 1) return launch_quant<uint16_t>(x, rows, cols, br, bc, q, scale, stream);
-  return launch_quant<float>(x, rows, cols, br, bc, q, scale, stream);
+  if (fp8) {
+    if (dtype == 1) return launch_quant<uint16_t, Fp8Codec>(x, rows, cols, br, bc, q, scale, stream);
+    return launch_quant<float, Fp8Codec>(x, rows, cols, br, bc, q, scale, stream);
+  }
+  if (dtype == 1) return launch_quant<uint16_t, Int8Codec>(x, rows, cols, br, bc, q, scale, stream);
+  return launch_quant<float, Int8Codec>(x, rows, cols, br, bc, q, scale, stream);
 }
 
 }  // namespace w8a8

@@ -14,8 +14,8 @@ import torch
 
 import synth
 
-from . import (SCALE_BLOCK128, SCALE_CHANNEL, SCORE_SIGMOID, SCORE_SOFTMAX, w8a8_moe_forward,
-               w8a8_moe_workspace_bytes, w8a8_quant_blocks)
+from . import (SCALE_BLOCK128, SCALE_CHANNEL, SCALE_FP8_BLOCK128, SCORE_SIGMOID, SCORE_SOFTMAX, w8a8_fp8_quant_blocks,
+               w8a8_moe_forward, w8a8_moe_workspace_bytes, w8a8_quant_blocks)
 
 
 @dataclass
@@ -23,23 +23,24 @@ class DeviceLayer:
     cfg: synth.MoEConfig
     x: torch.Tensor            # [T, H] bf16 or fp32
     logits: torch.Tensor       # [T, E] fp32
-    w13: torch.Tensor          # [E, 2I, H] int8
+    w13: torch.Tensor          # [E, 2I, H] int8 (uint8 FP8 codes for "fp8")
     w13_scale: torch.Tensor    # [E, 2I] or [E, 2I/128, H/128]
-    w2: torch.Tensor           # [E, H, I] int8
+    w2: torch.Tensor           # [E, H, I] int8 (uint8 FP8 codes for "fp8")
     w2_scale: torch.Tensor     # [E, H] or [E, H/128, I/128]
 
     @property
     def scale_mode(self) -> int:
-        return SCALE_BLOCK128 if self.cfg.scale_mode == "block" else SCALE_CHANNEL
+        return {"block": SCALE_BLOCK128, "fp8": SCALE_FP8_BLOCK128}.get(self.cfg.scale_mode, SCALE_CHANNEL)
 
     @property
     def score_fn(self) -> int:
         return SCORE_SOFTMAX if self.cfg.route == "softmax" else SCORE_SIGMOID
 
 
-def _quantize_experts(cfg, stream_tag: int, E: int, N: int, K: int, block: bool, device, chunk_bytes: int):
-    """Draw [E, N, K] fp32 weights chunk by chunk and quantize them into int8 + scales."""
-    q = torch.empty((E, N, K), dtype=torch.int8, device=device)
+def _quantize_experts(cfg, stream_tag: int, E: int, N: int, K: int, block: bool, device, chunk_bytes: int,
+                      fp8: bool = False):
+    """Draw [E, N, K] fp32 weights chunk by chunk and quantize them into int8 (or FP8 codes) + scales."""
+    q = torch.empty((E, N, K), dtype=torch.uint8 if fp8 else torch.int8, device=device)
     scale = torch.empty((E, N // 128, K // 128) if block else (E, N), dtype=torch.float32, device=device)
     per_expert = N * K
     chunk = max(1, min(E, chunk_bytes // (4 * per_expert)))
@@ -50,7 +51,10 @@ def _quantize_experts(cfg, stream_tag: int, E: int, N: int, K: int, block: bool,
         buf = scratch[: c * per_expert]
         synth.dev_normal(buf.data_ptr(), c * per_expert, cfg.seed, stream_tag, e0 * per_expert, cfg.w_sigma, hs)
         mat = buf.view(c * N, K)
-        if block:
+        if fp8:
+            w8a8_fp8_quant_blocks(mat, 128, 128, q[e0:e0 + c].view(c * N, K),
+                                  scale[e0:e0 + c].view(c * N // 128, K // 128))
+        elif block:
             w8a8_quant_blocks(mat, 128, 128, q[e0:e0 + c].view(c * N, K), scale[e0:e0 + c].view(c * N // 128, K // 128))
         else:
             w8a8_quant_blocks(mat, 1, K, q[e0:e0 + c].view(c * N, K), scale[e0:e0 + c].view(c * N, 1))
@@ -70,9 +74,10 @@ def make_layer(cfg: synth.MoEConfig, device="cuda", T: Optional[int] = None,
     bias = synth.zipf_bias(cfg)
     bias_t = None if bias is None else torch.from_numpy(bias).to(device)
     synth.dev_logits(logits.data_ptr(), cfg, None if bias_t is None else bias_t.data_ptr(), hs, T=T)
-    block = cfg.scale_mode == "block"
-    w13, w13_s = _quantize_experts(cfg, synth.STREAM_W13, cfg.E, 2 * cfg.I, cfg.H, block, device, chunk_bytes)
-    w2, w2_s = _quantize_experts(cfg, synth.STREAM_W2, cfg.E, cfg.H, cfg.I, block, device, chunk_bytes)
+    fp8 = cfg.scale_mode == "fp8"
+    block = cfg.scale_mode == "block" or fp8
+    w13, w13_s = _quantize_experts(cfg, synth.STREAM_W13, cfg.E, 2 * cfg.I, cfg.H, block, device, chunk_bytes, fp8)
+    w2, w2_s = _quantize_experts(cfg, synth.STREAM_W2, cfg.E, cfg.H, cfg.I, block, device, chunk_bytes, fp8)
     torch.cuda.synchronize(device)
     return DeviceLayer(cfg, x, logits, w13, w13_s, w2, w2_s)
 
