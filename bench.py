@@ -9,7 +9,7 @@ weights and scales) are resident in HBM before timing starts.
 Prints one JSON line.  value = tokens/s of the DeepSeek-V3 decode layer
 (T=128, hidden 7168, intermediate 2048, 256 experts, top-8); the same line
 carries the T=8192 prefill layer's figures under "prefill", the tiny (T=16), skewed
-(T=4096) and block-wise (T=2048) layers under "configs", the dense W8A8 linear
+(T=4096) and block-wise (T=2048, INT8 and FP8) layers under "configs", the dense W8A8 linear
 under "linear", the roofline of the
 dominant kernel (the gate+up GEMM, weight-streaming and so HBM-bound at T=128),
 the device's measured read / copy / INT8-MFMA rates under "peaks_measured", and
@@ -27,6 +27,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer tokens/s + int8 TOPS at T=128/8192; % of INT8 MFMA or HBM peak"
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0    # MI355X dense INT8 MFMA
+FP8_PEAK_TFLOPS = 5000.0   # MI355X dense FP8 MFMA
 
 
 def parse():
@@ -72,14 +73,16 @@ class Stages:
         c = layer.cfg
         T = layer.x.shape[0]
         self.T = T
-        self.block = c.scale_mode == "block"
+        self.fp8 = c.scale_mode == "fp8"
+        self.block = c.scale_mode == "block" or self.fp8
         self.bm = block_m or w8.w8a8_moe_pick_block_m(T, c.k, c.E)
         dev = layer.x.device
         R = w8.w8a8_moe_max_rows(T, c.k, c.E, self.bm)
         i32, f32 = torch.int32, torch.float32
         self.ids = torch.empty((T, c.k), dtype=i32, device=dev)
         self.tw = torch.empty((T, c.k), dtype=f32, device=dev)
-        self.a_q = torch.empty((T, c.H), dtype=torch.int8, device=dev)
+        code = torch.uint8 if self.fp8 else torch.int8
+        self.a_q = torch.empty((T, c.H), dtype=code, device=dev)
         self.a_s = torch.empty((T, c.H // 128) if self.block else (T,), dtype=f32, device=dev)
         self.counts = torch.empty(c.E, dtype=i32, device=dev)
         self.offsets = torch.empty(c.E + 1, dtype=i32, device=dev)
@@ -87,10 +90,10 @@ class Stages:
         self.sorted = torch.empty(max(R, 1), dtype=i32, device=dev)
         self.tile_expert = torch.empty(max(R // self.bm, 1), dtype=i32, device=dev)
         self.num_tiles = torch.empty(1, dtype=i32, device=dev)
-        self.h_q = torch.empty((max(R, 1), c.I), dtype=torch.int8, device=dev)
+        self.h_q = torch.empty((max(R, 1), c.I), dtype=code, device=dev)
         self.h_s = torch.empty((max(R, 1), c.I // 128) if self.block else (max(R, 1),), dtype=f32, device=dev)
         self.out = torch.empty((T, c.H), dtype=f32, device=dev)
-        mode = w8.SCALE_BLOCK128 if self.block else w8.SCALE_CHANNEL
+        mode = w8.SCALE_FP8_BLOCK128 if self.fp8 else w8.SCALE_BLOCK128 if self.block else w8.SCALE_CHANNEL
         self.ws_align = torch.empty(max(w8.moe_align_workspace_bytes(T, c.k, c.E), 256), dtype=torch.uint8, device=dev)
         gws = max(w8.w8a8_w13_workspace_bytes(T, c.k, c.E, c.H, c.I, self.bm, mode),
                   w8.w8a8_w2_workspace_bytes(T, c.k, c.E, c.H, c.I, self.bm, mode))
@@ -102,19 +105,24 @@ class Stages:
                                c.routed_scaling, None, self.ids, self.tw)
 
     def quant(self):
-        self.w8.w8a8_quant_per_token(self.L.x, 128 if self.block else 0, self.a_q, self.a_s)
+        if self.fp8:
+            self.w8.w8a8_fp8_quant_blocks(self.L.x, 1, 128, self.a_q, self.a_s)
+        else:
+            self.w8.w8a8_quant_per_token(self.L.x, 128 if self.block else 0, self.a_q, self.a_s)
 
     def align(self):
         self.w8.moe_align_by_expert(self.ids, self.L.cfg.E, self.bm, self.counts, self.offsets, self.padded,
                                     self.sorted, self.tile_expert, self.num_tiles, self.ws_align)
 
     def w13(self):
-        fn = self.w8.w8a8_block_grouped_gemm_w13_silu if self.block else self.w8.w8a8_grouped_gemm_w13_silu
+        fn = (self.w8.w8a8_fp8_grouped_gemm_w13_silu if self.fp8 else self.w8.w8a8_block_grouped_gemm_w13_silu
+              if self.block else self.w8.w8a8_grouped_gemm_w13_silu)
         fn(self.a_q, self.a_s, self.L.w13, self.L.w13_scale, self.sorted, self.padded, self.tile_expert,
            self.num_tiles, self.T, self.L.cfg.k, self.bm, self.h_q, self.h_s, self.ws_gemm)
 
     def w2(self):
-        fn = self.w8.w8a8_block_grouped_gemm_w2_combine if self.block else self.w8.w8a8_grouped_gemm_w2_combine
+        fn = (self.w8.w8a8_fp8_grouped_gemm_w2_combine if self.fp8 else self.w8.w8a8_block_grouped_gemm_w2_combine
+              if self.block else self.w8.w8a8_grouped_gemm_w2_combine)
         fn(self.h_q, self.h_s, self.L.w2, self.L.w2_scale, self.sorted, self.padded, self.tile_expert,
            self.num_tiles, self.tw, self.T, self.L.cfg.k, self.bm, self.out, self.ws_gemm)
 
@@ -152,10 +160,11 @@ def layer_figures(cfg, T, ms, counts):
     P = T * cfg.k
     ops = 2.0 * P * (2 * cfg.I * cfg.H + cfg.H * cfg.I)
     active = int((counts > 0).sum())
-    nsh = cfg.I // 128 if cfg.scale_mode == "block" else 1
-    nsw13 = (2 * cfg.I // 128) * (cfg.H // 128) if cfg.scale_mode == "block" else 2 * cfg.I
-    nsw2 = (cfg.H // 128) * (cfg.I // 128) if cfg.scale_mode == "block" else cfg.H
-    nsa = cfg.H // 128 if cfg.scale_mode == "block" else 1
+    blk = cfg.scale_mode in ("block", "fp8")
+    nsh = cfg.I // 128 if blk else 1
+    nsw13 = (2 * cfg.I // 128) * (cfg.H // 128) if blk else 2 * cfg.I
+    nsw2 = (cfg.H // 128) * (cfg.I // 128) if blk else cfg.H
+    nsa = cfg.H // 128 if blk else 1
     w_bytes = active * (2 * cfg.I * cfg.H + cfg.H * cfg.I + 4 * (nsw13 + nsw2))
     x_bytes = T * cfg.H * (2 if cfg.x_dtype else 4)
     other = (T * cfg.E * 4 + x_bytes + 2 * (T * cfg.H + 4 * T * nsa) + 2 * (P * cfg.I + 4 * P * nsh)
@@ -380,8 +389,12 @@ def main():
     configs = None
     if not args.no_configs and args.config == "decode":
         configs = {}
-        for name in ("tiny", "skew", "block"):
-            oc = synth.CONFIGS[name]
+        import dataclasses
+
+        fp8_block = dataclasses.replace(synth.CONFIGS["block"], name="fp8-block", scale_mode="fp8",
+                                        note="DeepSeek-V3 shapes, 128x128 block-wise FP8 (E4M3), T=2048")
+        for name in ("tiny", "skew", "block", "fp8-block"):
+            oc = fp8_block if name == "fp8-block" else synth.CONFIGS[name]
             print(f"[bench] drawing {oc.note}", file=sys.stderr, flush=True)
             ol = workload.make_layer(oc)
             oms, ostage, ost, ocounts = measure(ol, max(3, args.steps // 2), args.warmup)
@@ -392,6 +405,11 @@ def main():
                      "hbm_gbs": round(of["hbm_gbs"], 1), "frac_hbm_peak": round(of["frac_hbm_peak"], 4),
                      "active_experts": of["active_experts"], "scale": oc.scale_mode,
                      "stage_ms": {k: round(v, 4) for k, v in ostage.items()}}
+            if name == "fp8-block":  # the same operation count on the FP8 MFMA
+                for key in ("int8_tops", "frac_int8_peak"):
+                    del entry[key]
+                entry["fp8_tflops"] = round(of["int8_tops"], 3)
+                entry["frac_fp8_peak"] = round(of["int8_tops"] / FP8_PEAK_TFLOPS, 4)
             if name == "skew":
                 import numpy as np
 
@@ -419,7 +437,8 @@ def main():
             entry["frac_of_measured_mfma"] = round(entry["int8_tops"] / peaks["int8_mfma_tops"], 4)
             entry["frac_of_measured_read"] = round(entry["hbm_gbs"] / peaks["hbm_read_gbs"], 4)
         for entry in (configs or {}).values():
-            entry["frac_of_measured_mfma"] = round(entry["int8_tops"] / peaks["int8_mfma_tops"], 4)
+            if "int8_tops" in entry:
+                entry["frac_of_measured_mfma"] = round(entry["int8_tops"] / peaks["int8_mfma_tops"], 4)
             entry["frac_of_measured_read"] = round(entry["hbm_gbs"] / peaks["hbm_read_gbs"], 4)
 
     cpu = None
