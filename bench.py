@@ -35,7 +35,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="decode")
+    ap.add_argument("--config", default="decode",
+                    help="decode (the headline), prefill, tiny, skew, block, or fp8-block")
     ap.add_argument("--no-prefill", action="store_true", help="skip the T=8192 prefill figures")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=128, help="tokens in the CPU oracle sample")
@@ -137,6 +138,16 @@ class Stages:
             events[len(self.NAMES)].record()
 
 
+def fp8_block_config():
+    """The block-wise workload (T=2048, DeepSeek-V3 shapes, same draws) with FP8 (E4M3) operands."""
+    import dataclasses
+
+    import synth
+
+    return dataclasses.replace(synth.CONFIGS["block"], name="fp8-block", scale_mode="fp8",
+                               note="DeepSeek-V3 shapes, 128x128 block-wise FP8 (E4M3), T=2048")
+
+
 def measure(layer, steps, warmup):
     """Whole-step wall time (synchronised on both sides) and per-stage event times."""
     import torch
@@ -181,9 +192,10 @@ def w13_algorithmic_bytes(cfg, T, counts):
     the int8 token rows and their scales, and the int8 intermediate with its scales."""
     P = T * cfg.k
     active = int((counts > 0).sum())
-    nsw = (2 * cfg.I // 128) * (cfg.H // 128) if cfg.scale_mode == "block" else 2 * cfg.I
-    nsa = cfg.H // 128 if cfg.scale_mode == "block" else 1
-    nsh = cfg.I // 128 if cfg.scale_mode == "block" else 1
+    blk = cfg.scale_mode in ("block", "fp8")
+    nsw = (2 * cfg.I // 128) * (cfg.H // 128) if blk else 2 * cfg.I
+    nsa = cfg.H // 128 if blk else 1
+    nsh = cfg.I // 128 if blk else 1
     return active * (2 * cfg.I * cfg.H + 4 * nsw) + T * (cfg.H + 4 * nsa) + P * (cfg.I + 4 * nsh)
 
 
@@ -321,17 +333,25 @@ def cpu_baseline(cfg, ntok):
     w13q, w13s, w2q, w2s = [None] * cfg.E, [None] * cfg.E, [None] * cfg.E, [None] * cfg.E
     hs = torch.cuda.current_stream().cuda_stream
     buf = torch.empty(2 * cfg.I * cfg.H, dtype=torch.float32, device="cuda")
+    fp8 = cfg.scale_mode == "fp8"
+
+    def quant(w):
+        return oracle.fp8_quant_blocks(w, 128, 128) if fp8 else oracle.quant_weight(w, cfg.scale_mode)
+
     for e in experts:
         n13, n2 = 2 * cfg.I * cfg.H, cfg.H * cfg.I
         synth.dev_normal(buf.data_ptr(), n13, cfg.seed, synth.STREAM_W13, int(e) * n13, cfg.w_sigma, hs)
-        w13q[e], w13s[e] = oracle.quant_weight(buf[:n13].cpu().numpy().reshape(2 * cfg.I, cfg.H), cfg.scale_mode)
+        w13q[e], w13s[e] = quant(buf[:n13].cpu().numpy().reshape(2 * cfg.I, cfg.H))
         synth.dev_normal(buf.data_ptr(), n2, cfg.seed, synth.STREAM_W2, int(e) * n2, cfg.w_sigma, hs)
-        w2q[e], w2s[e] = oracle.quant_weight(buf[:n2].cpu().numpy().reshape(cfg.H, cfg.I), cfg.scale_mode)
+        w2q[e], w2s[e] = quant(buf[:n2].cpu().numpy().reshape(cfg.H, cfg.I))
     del buf
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     t0 = time.perf_counter()
     ids, tw = oracle.route_cfg(cfg, lg)
-    oracle.moe_tokens(x, ids, tw, w13q, w13s, w2q, w2s, I=cfg.I, block=cfg.scale_mode == "block")
+    if fp8:
+        oracle.fp8_moe_tokens(x, ids, tw, w13q, w13s, w2q, w2s, I=cfg.I)
+    else:
+        oracle.moe_tokens(x, ids, tw, w13q, w13s, w2q, w2s, I=cfg.I, block=cfg.scale_mode == "block")
     dt = time.perf_counter() - t0
     return {"value": ntok / dt, "unit": "tokens/s", "cores": min(threads, ntok), "kind": "oracle",
             "sample": f"first {ntok} of the {cfg.T} tokens of the same layer (routing + dense per-token "
@@ -356,7 +376,7 @@ def main():
     import synth
     from w8a8_int8_quantized_quant_amd import workload
 
-    cfg = synth.CONFIGS[args.config]
+    cfg = fp8_block_config() if args.config == "fp8-block" else synth.CONFIGS[args.config]
     print(f"[bench] drawing {cfg.note}", file=sys.stderr, flush=True)
     layer = workload.make_layer(cfg)
     ms, stage_ms, st, counts = measure(layer, args.steps, args.warmup)
@@ -389,12 +409,8 @@ def main():
     configs = None
     if not args.no_configs and args.config == "decode":
         configs = {}
-        import dataclasses
-
-        fp8_block = dataclasses.replace(synth.CONFIGS["block"], name="fp8-block", scale_mode="fp8",
-                                        note="DeepSeek-V3 shapes, 128x128 block-wise FP8 (E4M3), T=2048")
         for name in ("tiny", "skew", "block", "fp8-block"):
-            oc = fp8_block if name == "fp8-block" else synth.CONFIGS[name]
+            oc = fp8_block_config() if name == "fp8-block" else synth.CONFIGS[name]
             print(f"[bench] drawing {oc.note}", file=sys.stderr, flush=True)
             ol = workload.make_layer(oc)
             oms, ostage, ost, ocounts = measure(ol, max(3, args.steps // 2), args.warmup)
@@ -449,9 +465,11 @@ def main():
     line = {
         "metric": METRIC, "value": round(fig["tokens_per_s"], 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8" if cfg.scale_mode == "fp8" else "int8", "data": "synthetic",
         "config": {"workload": f"{cfg.note}: hidden {cfg.H}, intermediate {cfg.I}, {cfg.E} experts, top-{cfg.k}, "
-                               f"{cfg.scale_mode}-wise W8A8 INT8", "T": cfg.T, "H": cfg.H, "I": cfg.I, "E": cfg.E,
+                               + ("128x128 block-wise FP8 (E4M3)" if cfg.scale_mode == "fp8" else
+                                  f"{cfg.scale_mode}-wise W8A8 INT8"), "T": cfg.T, "H": cfg.H, "I": cfg.I, "E": cfg.E,
                    "k": cfg.k, "scale": cfg.scale_mode, "active_experts": fig["active_experts"]},
         "int8_tops": round(fig["int8_tops"], 3), "frac_int8_peak": round(fig["frac_int8_peak"], 4),
         "hbm_gbs": round(fig["hbm_gbs"], 1), "frac_hbm_peak": round(fig["frac_hbm_peak"], 4),
