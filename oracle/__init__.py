@@ -51,6 +51,14 @@ def _load():
         lib.oracle_fp8_w2_combine.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, vp, i64, i64, i64, i64, vp, i64,
                                               vp]
         lib.oracle_fp8_moe_tokens.argtypes = [vp, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp]
+        lib.oracle_w4_unpack.argtypes = [vp, i64, i64, vp]
+        lib.oracle_w4_quant.argtypes = [vp, i64, i64, vp, vp]
+        lib.oracle_w4_w13_silu.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, i64, vp, vp]
+        lib.oracle_w4_w2_combine.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, vp, i64, i64, i64, i64, vp, i64, vp]
+        lib.oracle_w4_moe_tokens.argtypes = [vp, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp]
+        for name in ("oracle_w4_unpack", "oracle_w4_quant", "oracle_w4_w13_silu", "oracle_w4_w2_combine",
+                     "oracle_w4_moe_tokens"):
+            getattr(lib, name).restype = None
         for name in ("oracle_quant_blocks", "oracle_route", "oracle_align", "oracle_grouped_gemm_i32",
                      "oracle_w13_silu", "oracle_w2_combine", "oracle_moe_tokens", "oracle_linear",
                      "oracle_fp8_decode", "oracle_fp8_encode", "oracle_fp8_quant_blocks", "oracle_fp8_w13_silu",
@@ -338,6 +346,82 @@ def fp8_abs(codes: np.ndarray) -> np.ndarray:
     return np.asarray(codes, dtype=np.uint8) & np.uint8(0x7F)
 
 
+# --------------------------------------------------------------------------- W4A8 path (int4 weights, FP8 activations)
+
+def w4_quant(x: np.ndarray):
+    """Int4 weights, one scale per (row, 128 columns): (packed uint8 [rows, cols/2], s fp32 [rows, cols/128])."""
+    x = _c(x, np.float32)
+    rows, cols = x.shape
+    q = np.empty((rows, cols // 2), dtype=np.uint8)
+    s = np.empty((rows, cols // 128), dtype=np.float32)
+    if rows and cols:
+        _load().oracle_w4_quant(_p(x), rows, cols, _p(q), _p(s))
+    return q, s
+
+
+def w4_unpack(packed: np.ndarray) -> np.ndarray:
+    """Integer values [rows, 2 * bytes] of packed int4 rows."""
+    q = _c(packed, np.uint8)
+    rows, nb = q.shape
+    out = np.empty((rows, 2 * nb), dtype=np.int8)
+    if q.size:
+        _load().oracle_w4_unpack(_p(q), rows, 2 * nb, _p(out))
+    return out
+
+
+def w4_w13_silu(a_q: np.ndarray, a_s: np.ndarray, w13, w13_s, al: Dict[str, np.ndarray], block_m: int, T: int,
+                k: int, H: int, I: int, rows: Optional[Iterable[int]] = None):
+    """W4A8 sorted-row intermediate: h_q [R, I] FP8 codes and h_s [R, I/128]."""
+    a_q = _c(a_q, np.uint8)
+    a_s = _c(a_s, np.float32)
+    nt = int(al["num_tiles"][0])
+    R = nt * block_m
+    r, nr = _rows(rows, nt, block_m)
+    h_q = np.zeros((R, I), dtype=np.uint8)
+    h_s = np.zeros((R, I // 128), dtype=np.float32)
+    _load().oracle_w4_w13_silu(_p(a_q), _p(a_s), _ptr_array(_experts(w13, np.uint8)),
+                               _ptr_array(_experts(w13_s, np.float32)), _p(al["sorted_pair_ids"]),
+                               _p(al["tile_expert"]), block_m, T, k, H, I, _p(r), nr, _p(h_q), _p(h_s))
+    return h_q, h_s
+
+
+def w4_w2_combine(h_q: np.ndarray, h_s: np.ndarray, w2, w2_s, al: Dict[str, np.ndarray], block_m: int,
+                  topk_weights: np.ndarray, T: int, k: int, H: int, I: int,
+                  tokens: Optional[Iterable[int]] = None) -> np.ndarray:
+    """W4A8 second GEMM + combine: [T, H], or [len(tokens), H] for the listed tokens."""
+    h_q = _c(h_q, np.uint8)
+    h_s = _c(h_s, np.float32)
+    tw = _c(topk_weights, np.float32)
+    tk = None if tokens is None else np.ascontiguousarray(np.fromiter(tokens, dtype=np.int64))
+    ntok = T if tk is None else len(tk)
+    out = np.empty((ntok, H), dtype=np.float32)
+    _load().oracle_w4_w2_combine(_p(h_q), _p(h_s), _ptr_array(_experts(w2, np.uint8)),
+                                 _ptr_array(_experts(w2_s, np.float32)), _p(al["sorted_pair_ids"]),
+                                 _p(al["tile_expert"]), int(al["num_tiles"][0]), block_m, _p(tw), T, k, H, I,
+                                 _p(tk), ntok, _p(out))
+    return out
+
+
+def w4_moe_tokens(x: np.ndarray, ids: np.ndarray, topk_weights: np.ndarray, w13, w13_s, w2, w2_s,
+                  I: int) -> np.ndarray:
+    """Dense per-token reference of the whole W4A8 layer for the given token rows (fp32 x)."""
+    x = _c(x, np.float32)
+    ntok, H = x.shape
+    ids = _c(ids, np.int32)
+    k = ids.shape[1]
+    tw = _c(topk_weights, np.float32)
+    out = np.empty((ntok, H), dtype=np.float32)
+    _load().oracle_w4_moe_tokens(_p(x), ntok, H, I, k, _p(ids), _p(tw), _ptr_array(_experts(w13, np.uint8)),
+                                 _ptr_array(_experts(w13_s, np.float32)), _ptr_array(_experts(w2, np.uint8)),
+                                 _ptr_array(_experts(w2_s, np.float32)), _p(out))
+    return out
+
+
+def w4_abs(packed: np.ndarray) -> np.ndarray:
+    """Packed int4 rows of the magnitudes (sign bits cleared)."""
+    return np.asarray(packed, dtype=np.uint8) & np.uint8(0x77)
+
+
 # --------------------------------------------------------------------------- layer construction
 
 def expert_weights(cfg, experts: Iterable[int]):
@@ -353,6 +437,10 @@ def expert_weights(cfg, experts: Iterable[int]):
     w2_q: List[Optional[np.ndarray]] = [None] * E
     w2_s: List[Optional[np.ndarray]] = [None] * E
     for e in sorted(set(int(x) for x in experts)):
+        if mode == "w4a8":
+            w13_q[e], w13_s[e] = w4_quant(synth.w13_f32(cfg, e))
+            w2_q[e], w2_s[e] = w4_quant(synth.w2_f32(cfg, e))
+            continue
         if mode == "fp8":
             w13_q[e], w13_s[e] = fp8_quant_blocks(synth.w13_f32(cfg, e), 128, 128)
             w2_q[e], w2_s[e] = fp8_quant_blocks(synth.w2_f32(cfg, e), 128, 128)

@@ -669,3 +669,186 @@ ORACLE_EXPORT void oracle_fp8_moe_tokens(const float* x, int64_t ntok, int64_t H
     free(y);
   }
 }
+
+/* ------------------------------------------------------------------ W4A8 path (int4 weights, FP8 activations)
+ *
+ * SGLang PR #8311 (w4a8 DeepSeek-R1 in DeepEP low-latency mode; its layer enables the path with a
+ * w4afp8 flag): weights in 4-bit integers, activations in FP8.  The pages give no formats or
+ * scales; the readings taken here:
+ *  - weights: symmetric int4 in [-7, 7], one scale per (output row, 128-wide K group):
+ *    scale = max(max|w| / 7, 1e-8), q = clamp(round-half-even(w / scale), -7, 7);
+ *  - packing: two values per byte, 4 bytes per 8 consecutive K values: byte b of the group holds
+ *    value 8g+b in its low nibble and value 8g+4+b in its high nibble; a nibble is sign (bit 3)
+ *    and magnitude (bits 0-2), zero always as 0;
+ *  - activations and the intermediate: the FP8 path's E4M3 per-token-group rule (above);
+ *  - product per 128-wide K-block: the exact sum of decoded activation x integer weight products
+ *    rounded once to fp32, then acc = acc + ((part * a_s[kb]) * w_s[n][kb]) in fp32, ascending
+ *    K-blocks; after the sums the FP8 path's arithmetic (SiLU(gate) * up, FP8 requantization,
+ *    combine). */
+
+static int w4_nibble(int v) { return v < 0 ? (8 | -v) : v; }
+static int w4_value(int nib) { return (nib & 8) ? -(nib & 7) : (nib & 7); }
+
+/* Integer value of element k of a packed row. */
+static int w4_at(const uint8_t* row, int64_t k) {
+  const uint8_t byte = row[(k / 8) * 4 + (k % 4)];
+  return w4_value((k % 8) < 4 ? (byte & 15) : (byte >> 4));
+}
+
+ORACLE_EXPORT void oracle_w4_unpack(const uint8_t* packed, int64_t rows, int64_t cols, int8_t* out) {
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t c = 0; c < cols; ++c) out[r * cols + c] = (int8_t)w4_at(packed + r * (cols / 2), c);
+}
+
+/* Int4 quantization of a row-major [rows, cols] fp32 matrix, one scale per (row, 128 columns);
+ * cols a multiple of 128.  q: [rows, cols/2] packed bytes; s: [rows, cols/128]. */
+ORACLE_EXPORT void oracle_w4_quant(const float* x, int64_t rows, int64_t cols, uint8_t* q, float* s) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t g0 = 0, gi = 0; g0 < cols; g0 += 128, ++gi) {
+      float amax = 0.0f;
+      for (int64_t c = g0; c < g0 + 128; ++c) {
+        const float a = fabsf(x[r * cols + c]);
+        if (a > amax) amax = a;
+      }
+      float sc = amax / 7.0f;
+      if (sc < 1e-8f) sc = 1e-8f;
+      s[r * (cols / 128) + gi] = sc;
+      for (int64_t c = g0; c < g0 + 128; c += 8)
+        for (int b = 0; b < 4; ++b) {
+          int v[2];
+          for (int h = 0; h < 2; ++h) {
+            float t = nearbyintf(x[r * cols + c + 4 * h + b] / sc);
+            if (t > 7.0f) t = 7.0f;
+            if (t < -7.0f) t = -7.0f;
+            v[h] = (int)t;
+          }
+          q[r * (cols / 2) + c / 2 + b] = (uint8_t)(w4_nibble(v[0]) | (w4_nibble(v[1]) << 4));
+        }
+    }
+  }
+}
+
+/* One K-block of FP8 activations against int4 weights: exact, rounded once to fp32. */
+static float w4_part(const uint8_t* a, const uint8_t* wrow, int64_t k0) {
+  double sum = 0.0;
+  for (int i = 0; i < 128; ++i) sum += e4m3_table[a[i]] * (double)w4_at(wrow, k0 + i);
+  return (float)sum;
+}
+
+/* One expert row of the W4A8 first GEMM: a [H] FP8 codes, a_s [H/128], w13 [2I, H/2] packed,
+ * w_s [2I, H/128]; writes h_q [I] FP8 codes and h_s [I/128]. */
+static void w4_w13_row(const uint8_t* a, const float* a_s, const uint8_t* w13, const float* w_s, int64_t H,
+                       int64_t I, float* hf, uint8_t* h_q, float* h_s) {
+  const int64_t nkb = H / 128;
+  for (int64_t n = 0; n < I; ++n) {
+    float g = 0.0f, u = 0.0f;
+    for (int64_t kb = 0; kb < nkb; ++kb) {
+      const float pg = w4_part(a + kb * 128, w13 + n * (H / 2), kb * 128);
+      const float pu = w4_part(a + kb * 128, w13 + (n + I) * (H / 2), kb * 128);
+      g = g + ((pg * a_s[kb]) * w_s[n * nkb + kb]);
+      u = u + ((pu * a_s[kb]) * w_s[(n + I) * nkb + kb]);
+    }
+    hf[n] = silu_mul(g, u);
+  }
+  fp8_requant_row(hf, I, h_q, h_s);
+}
+
+/* One expert row of the W4A8 second GEMM: y [H]. */
+static void w4_w2_row(const uint8_t* hq, const float* h_s, const uint8_t* w2, const float* w_s, int64_t H,
+                      int64_t I, float* y) {
+  const int64_t nkb = I / 128;
+  for (int64_t n = 0; n < H; ++n) {
+    float acc = 0.0f;
+    for (int64_t kb = 0; kb < nkb; ++kb) {
+      const float part = w4_part(hq + kb * 128, w2 + n * (I / 2), kb * 128);
+      acc = acc + ((part * h_s[kb]) * w_s[n * nkb + kb]);
+    }
+    y[n] = acc;
+  }
+}
+
+/* W4A8 first GEMM over sorted rows (as oracle_fp8_w13_silu; w13[e] [2I, H/2] packed, w13_s[e]
+ * [2I, H/128]). */
+ORACLE_EXPORT void oracle_w4_w13_silu(const uint8_t* a_q, const float* a_s, const uint8_t* const* w13,
+                                      const float* const* w13_s, const int32_t* sorted_pair_ids,
+                                      const int32_t* tile_expert, int64_t block_m, int64_t T, int64_t k, int64_t H,
+                                      int64_t I, const int64_t* rows, int64_t nrows, uint8_t* h_q, float* h_s) {
+  e4m3_table_init();
+  const int64_t P = T * k;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t i = 0; i < nrows; ++i) {
+    const int64_t r = row_at(rows, i);
+    const int64_t p = sorted_pair_ids[r];
+    if (p >= P) continue;
+    const int64_t t = p / k, e = tile_expert[r / block_m];
+    float* hf = (float*)malloc(sizeof(float) * I);
+    w4_w13_row(a_q + t * H, a_s + t * (H / 128), w13[e], w13_s[e], H, I, hf, h_q + r * I, h_s + r * (I / 128));
+    free(hf);
+  }
+}
+
+/* W4A8 second GEMM + top-k weighted combine (as oracle_fp8_w2_combine; w2[e] [H, I/2] packed,
+ * w2_s[e] [H, I/128]). */
+ORACLE_EXPORT void oracle_w4_w2_combine(const uint8_t* h_q, const float* h_s, const uint8_t* const* w2,
+                                        const float* const* w2_s, const int32_t* sorted_pair_ids,
+                                        const int32_t* tile_expert, int32_t num_tiles, int64_t block_m,
+                                        const float* topk_weights, int64_t T, int64_t k, int64_t H, int64_t I,
+                                        const int64_t* tokens, int64_t ntok, float* out) {
+  e4m3_table_init();
+  const int64_t P = T * k, R = (int64_t)num_tiles * block_m;
+  int64_t* pair_row = (int64_t*)malloc(sizeof(int64_t) * (P > 0 ? P : 1));
+  for (int64_t p = 0; p < P; ++p) pair_row[p] = -1;
+  for (int64_t r = 0; r < R; ++r)
+    if (sorted_pair_ids[r] < P) pair_row[sorted_pair_ids[r]] = r;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t i = 0; i < ntok; ++i) {
+    const int64_t t = tokens ? tokens[i] : i;
+    float* y = (float*)malloc(sizeof(float) * H);
+    float* o = out + i * H;
+    for (int64_t n = 0; n < H; ++n) o[n] = 0.0f;
+    for (int64_t j = 0; j < k; ++j) {
+      const int64_t r = pair_row[t * k + j];
+      if (r < 0) continue;
+      const int64_t e = tile_expert[r / block_m];
+      w4_w2_row(h_q + r * I, h_s + r * (I / 128), w2[e], w2_s[e], H, I, y);
+      const float wj = topk_weights[t * k + j];
+      for (int64_t n = 0; n < H; ++n) o[n] = o[n] + (wj * y[n]);
+    }
+    free(y);
+  }
+  free(pair_row);
+}
+
+/* The whole W4A8 layer for a list of tokens, straight from the routing. */
+ORACLE_EXPORT void oracle_w4_moe_tokens(const float* x, int64_t ntok, int64_t H, int64_t I, int64_t k,
+                                        const int32_t* ids, const float* topk_weights, const uint8_t* const* w13,
+                                        const float* const* w13_s, const uint8_t* const* w2,
+                                        const float* const* w2_s, float* out) {
+  e4m3_table_init();
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t t = 0; t < ntok; ++t) {
+    uint8_t* aq = (uint8_t*)malloc(H);
+    float* as = (float*)malloc(sizeof(float) * (H / 128));
+    float* hf = (float*)malloc(sizeof(float) * I);
+    uint8_t* hq = (uint8_t*)malloc(I);
+    float* hs = (float*)malloc(sizeof(float) * (I / 128));
+    float* y = (float*)malloc(sizeof(float) * H);
+    fp8_requant_row(x + t * H, H, aq, as);
+    float* o = out + t * H;
+    for (int64_t n = 0; n < H; ++n) o[n] = 0.0f;
+    for (int64_t j = 0; j < k; ++j) {
+      const int64_t e = ids[t * k + j];
+      w4_w13_row(aq, as, w13[e], w13_s[e], H, I, hf, hq, hs);
+      w4_w2_row(hq, hs, w2[e], w2_s[e], H, I, y);
+      const float wj = topk_weights[t * k + j];
+      for (int64_t n = 0; n < H; ++n) o[n] = o[n] + (wj * y[n]);
+    }
+    free(aq);
+    free(as);
+    free(hf);
+    free(hq);
+    free(hs);
+    free(y);
+  }
+}
