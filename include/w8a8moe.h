@@ -68,8 +68,9 @@ enum { W8A8_DTYPE_F32 = 0, W8A8_DTYPE_BF16 = 1 };
 enum { W8A8_SCORE_SOFTMAX = 0, W8A8_SCORE_SIGMOID = 1 };
 
 /* Scale layouts.  W8A8_SCALE_FP8_BLOCK128: the block-wise layouts with FP8 (E4M3) codes in place
- * of int8 values (see "FP8 block-wise variant" below). */
-enum { W8A8_SCALE_CHANNEL = 0, W8A8_SCALE_BLOCK128 = 1, W8A8_SCALE_FP8_BLOCK128 = 2 };
+ * of int8 values (see "FP8 block-wise variant" below).  W8A8_SCALE_W4A8: packed int4 weights with
+ * one scale per (output row, 128-wide K group) and FP8 activations (see "W4A8 variant" below). */
+enum { W8A8_SCALE_CHANNEL = 0, W8A8_SCALE_BLOCK128 = 1, W8A8_SCALE_FP8_BLOCK128 = 2, W8A8_SCALE_W4A8 = 3 };
 
 /* Name of a status code ("W8A8_OK", ...); never NULL. */
 const char* w8a8_status_string(int32_t status);
@@ -257,6 +258,39 @@ int32_t w8a8_fp8_grouped_gemm_w2_combine(const uint8_t* h_q, const float* h_scal
                                          int64_t E, int64_t H, int64_t I, int64_t block_m, float* out, void* ws,
                                          size_t ws_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------ W4A8 variant
+ * SGLang PR #8311 (w4a8 DeepSeek-R1; its MoE layer enables the path with a w4afp8 flag): 4-bit
+ * integer weights, FP8 activations.  Weights: symmetric int4 in [-7, 7], one fp32 scale per (output
+ * row, 128-wide K group): scale = max(max|w| / 7, 1e-8), q = clamp(round-half-even(w / scale)).
+ * Packing: a row of K values is K/2 bytes; each run of 8 values is 4 bytes, byte b holding value b
+ * in its low nibble and value 4 + b in its high nibble; a nibble is sign (bit 3) | magnitude
+ * (bits 0-2), zero as 0.  Activations and the intermediate: FP8 codes by the FP8 variant's rule
+ * per token-group (w8a8_fp8_quant_blocks with 1 x 128 blocks).  Product: per 128-wide K-block the
+ * FP8 MFMA on the activations and the weights widened to E4M3 (exact), then
+ * acc += (part_kb * a_s[t, kb]) * w_s[e, n, kb] in fp32, ascending K-blocks; the rest as in the
+ * FP8 variant (same summation-order caveat).
+ *
+ * w8a8_w4a8_quant_weights: x device [rows, cols] fp32 or bf16, cols a multiple of 128;
+ *   q device [rows, cols/2] packed (output); scale device [rows, cols/128] fp32 (output).
+ * GEMMs: w13 device [E, 2I, H/2] packed, w13_scale [E, 2I, H/128]; w2 [E, H, I/2] packed,
+ *   w2_scale [E, H, I/128]; a_q / h_q FP8 codes with a_scale [T, H/128] / h_scale [max_rows, I/128];
+ *   other arguments, shape limits and workspaces (scale_mode = W8A8_SCALE_W4A8) as in the FP8
+ *   variant. */
+int32_t w8a8_w4a8_quant_weights(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, uint8_t* q,
+                                float* scale, hipStream_t stream);
+int32_t w8a8_w4a8_grouped_gemm_w13_silu(const uint8_t* a_q, const float* a_scale, const uint8_t* w13,
+                                        const float* w13_scale, const int32_t* sorted_pair_ids,
+                                        const int32_t* padded_offsets, const int32_t* tile_expert,
+                                        const int32_t* num_tiles, int64_t T, int64_t k, int64_t E, int64_t H,
+                                        int64_t I, int64_t block_m, uint8_t* h_q, float* h_scale, void* ws,
+                                        size_t ws_bytes, hipStream_t stream);
+int32_t w8a8_w4a8_grouped_gemm_w2_combine(const uint8_t* h_q, const float* h_scale, const uint8_t* w2,
+                                          const float* w2_scale, const int32_t* sorted_pair_ids,
+                                          const int32_t* padded_offsets, const int32_t* tile_expert,
+                                          const int32_t* num_tiles, const float* topk_weights, int64_t T, int64_t k,
+                                          int64_t E, int64_t H, int64_t I, int64_t block_m, float* out, void* ws,
+                                          size_t ws_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------------ dense linear
  * W8A8 INT8 linear for the model's non-MoE projections (PR #3888 Modifications, "Norm Linear": the
  * dense layers run as w8a8 int8 GEMMs; article, "Quantization exploration": channel-wise weights
@@ -279,15 +313,16 @@ int32_t w8a8_linear(const int8_t* a_q, const float* a_scale, const int8_t* w, co
  * Steps 2, 1, 3, 4, 5 on one stream, intermediates carved from `ws`.
  * block_m = 0 picks a tile height from the average rows per expert.  With scale_mode =
  * W8A8_SCALE_FP8_BLOCK128 the w13 / w2 buffers hold FP8 codes and the activations are quantized
- * to FP8 per token-group (the FP8 variant's rule and shape limits). */
+ * to FP8 per token-group (the FP8 variant's rule and shape limits); with W8A8_SCALE_W4A8 they hold
+ * packed int4 weights with per-(row, K-group) scales and the activations are FP8 as well. */
 struct w8a8_moe_args {
   const void* x;               /* device, [T, H] fp32 or bf16 activations */
   int32_t x_dtype;             /* W8A8_DTYPE_* */
   const float* router_logits;  /* device, [T, E] fp32 */
-  const int8_t* w13;           /* device, [E, 2I, H] int8 (or FP8 codes) */
-  const float* w13_scale;      /* device, [E, 2I] or [E, 2I/128, H/128] fp32 */
-  const int8_t* w2;            /* device, [E, H, I] int8 (or FP8 codes) */
-  const float* w2_scale;       /* device, [E, H] or [E, H/128, I/128] fp32 */
+  const int8_t* w13;           /* device, [E, 2I, H] int8 (or FP8 codes; W4A8: [E, 2I, H/2] packed int4) */
+  const float* w13_scale;      /* device, [E, 2I], [E, 2I/128, H/128] or (W4A8) [E, 2I, H/128] fp32 */
+  const int8_t* w2;            /* device, [E, H, I] int8 (or FP8 codes; W4A8: [E, H, I/2] packed int4) */
+  const float* w2_scale;       /* device, [E, H], [E, H/128, I/128] or (W4A8) [E, H, I/128] fp32 */
   const float* correction_bias;/* device, [E] fp32 or NULL */
   float* out;                  /* device, [T, H] fp32 (output) */
   int32_t* topk_ids;           /* device, [T, k] int32 (output), or NULL to keep it in ws */

@@ -62,7 +62,7 @@ class MoEConfig:
     outlier_threshold: int
     outlier_mult: float
     w_sigma: float
-    scale_mode: str  # "channel", "block" (INT8, 128x128) or "fp8" (E4M3, 128x128)
+    scale_mode: str  # "channel", "block" (INT8, 128x128), "fp8" (E4M3, 128x128) or "w4a8" (int4, FP8 acts)
     zipf_s: Optional[float] = None
     zipf_beta: Optional[float] = None
     note: str = field(default="", compare=False)

@@ -28,6 +28,7 @@ SCORE_SIGMOID = 1
 SCALE_CHANNEL = 0
 SCALE_BLOCK128 = 1
 SCALE_FP8_BLOCK128 = 2
+SCALE_W4A8 = 3
 
 # Every symbol the C header declares (checked by the CPU test suite).
 EXPORTS = (
@@ -37,6 +38,7 @@ EXPORTS = (
     "w8a8_block_grouped_gemm_w13_silu", "w8a8_block_grouped_gemm_w2_combine", "w8a8_moe_pick_block_m",
     "w8a8_moe_workspace_bytes", "w8a8_moe_forward", "w8a8_linear_workspace_bytes", "w8a8_linear",
     "w8a8_fp8_quant_blocks", "w8a8_fp8_grouped_gemm_w13_silu", "w8a8_fp8_grouped_gemm_w2_combine",
+    "w8a8_w4a8_quant_weights", "w8a8_w4a8_grouped_gemm_w13_silu", "w8a8_w4a8_grouped_gemm_w2_combine",
 )
 
 
@@ -97,6 +99,11 @@ def lib() -> ctypes.CDLL:
             "w8a8_linear_workspace_bytes": (sz, [i64, i64, i64]),
             "w8a8_linear": (i32, [vp, vp, vp, vp, i64, i64, i64, vp, vp, sz, vp]),
             "w8a8_fp8_quant_blocks": (i32, [vp, i32, i64, i64, i64, i64, vp, vp, vp]),
+            "w8a8_w4a8_quant_weights": (i32, [vp, i32, i64, i64, vp, vp, vp]),
+            "w8a8_w4a8_grouped_gemm_w13_silu": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                                                      vp, vp, vp, sz, vp]),
+            "w8a8_w4a8_grouped_gemm_w2_combine": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                                        i64, vp, vp, sz, vp]),
             "w8a8_fp8_grouped_gemm_w13_silu": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
                                                      vp, vp, vp, sz, vp]),
             "w8a8_fp8_grouped_gemm_w2_combine": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
@@ -170,6 +177,12 @@ def w8a8_fp8_quant_blocks(x, block_rows: int, block_cols: int, q, scale, stream=
     rows, cols = x.shape
     _call("w8a8_fp8_quant_blocks", _ptr(x), _dtype_code(x), rows, cols, block_rows, block_cols, _ptr(q), _ptr(scale),
           _stream(stream))
+
+
+def w8a8_w4a8_quant_weights(x, q, scale, stream=None) -> None:
+    """Packed int4 weights (uint8 q [rows, cols/2]) with one scale per (row, 128 columns)."""
+    rows, cols = x.shape
+    _call("w8a8_w4a8_quant_weights", _ptr(x), _dtype_code(x), rows, cols, _ptr(q), _ptr(scale), _stream(stream))
 
 
 def moe_topk_route(logits, k: int, score_fn: int, n_group: int, topk_group: int, renormalize: bool,
@@ -264,6 +277,30 @@ def w8a8_fp8_grouped_gemm_w2_combine(h_q, h_scale, w2, w2_scale, sorted_pair_ids
                                      num_tiles, topk_weights, T, k, block_m, out, ws, stream=None) -> None:
     _w2("w8a8_fp8_grouped_gemm_w2_combine", h_q, h_scale, w2, w2_scale, sorted_pair_ids, padded_offsets,
         tile_expert, num_tiles, topk_weights, T, k, block_m, out, ws, stream)
+
+
+def _w13_w4(a_q, a_scale, w13, w13_scale, sorted_pair_ids, padded_offsets, tile_expert, num_tiles, T, k, block_m,
+            h_q, h_scale, ws, stream):
+    E, N2, Hh = w13.shape  # packed: H/2 bytes per row
+    _call("w8a8_w4a8_grouped_gemm_w13_silu", _ptr(a_q), _ptr(a_scale), _ptr(w13), _ptr(w13_scale),
+          _ptr(sorted_pair_ids), _ptr(padded_offsets), _ptr(tile_expert), _ptr(num_tiles), T, k, E, 2 * Hh, N2 // 2,
+          block_m, _ptr(h_q), _ptr(h_scale), _ptr(ws), _nbytes(ws), _stream(stream))
+
+
+def w8a8_w4a8_grouped_gemm_w13_silu(a_q, a_scale, w13, w13_scale, sorted_pair_ids, padded_offsets, tile_expert,
+                                    num_tiles, T, k, block_m, h_q, h_scale, ws, stream=None) -> None:
+    """w13: packed int4 [E, 2I, H/2] (uint8)."""
+    _w13_w4(a_q, a_scale, w13, w13_scale, sorted_pair_ids, padded_offsets, tile_expert, num_tiles, T, k, block_m,
+            h_q, h_scale, ws, stream)
+
+
+def w8a8_w4a8_grouped_gemm_w2_combine(h_q, h_scale, w2, w2_scale, sorted_pair_ids, padded_offsets, tile_expert,
+                                      num_tiles, topk_weights, T, k, block_m, out, ws, stream=None) -> None:
+    """w2: packed int4 [E, H, I/2] (uint8)."""
+    E, H, Ih = w2.shape
+    _call("w8a8_w4a8_grouped_gemm_w2_combine", _ptr(h_q), _ptr(h_scale), _ptr(w2), _ptr(w2_scale),
+          _ptr(sorted_pair_ids), _ptr(padded_offsets), _ptr(tile_expert), _ptr(num_tiles), _ptr(topk_weights), T, k,
+          E, H, 2 * Ih, block_m, _ptr(out), _ptr(ws), _nbytes(ws), _stream(stream))
 
 
 def w8a8_linear_workspace_bytes(M: int, N: int, K: int) -> int:

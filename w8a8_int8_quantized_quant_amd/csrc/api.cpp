@@ -28,8 +28,11 @@ bool valid_block_m(int64_t bm) { return bm == 16 || bm == 32 || bm == 64 || bm =
 bool valid_dim(int64_t d) { return d >= 128 && d <= kMaxDim && d % 128 == 0; }
 
 bool valid_mode(int32_t m) {
-  return m == W8A8_SCALE_CHANNEL || m == W8A8_SCALE_BLOCK128 || m == W8A8_SCALE_FP8_BLOCK128;
+  return m == W8A8_SCALE_CHANNEL || m == W8A8_SCALE_BLOCK128 || m == W8A8_SCALE_FP8_BLOCK128 || m == W8A8_SCALE_W4A8;
 }
+
+// FP8 activations (and the ring engine's shape limits): the FP8 and W4A8 modes.
+bool fp8_mode(int32_t m) { return m == W8A8_SCALE_FP8_BLOCK128 || m == W8A8_SCALE_W4A8; }
 
 // T, k, E limits shared by every MoE entry point.
 int32_t check_tke(int64_t T, int64_t k, int64_t E) {
@@ -124,6 +127,17 @@ int32_t w8a8_fp8_quant_blocks(const void* x, int32_t x_dtype, int64_t rows, int6
                      true);
 }
 
+int32_t w8a8_w4a8_quant_weights(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, uint8_t* q,
+                                float* scale, hipStream_t stream) {
+  if (rows < 0 || cols < 0) return W8A8_INVALID_ARGUMENT;
+  if (x_dtype != W8A8_DTYPE_F32 && x_dtype != W8A8_DTYPE_BF16) return W8A8_UNSUPPORTED_DTYPE;
+  if (cols % 128 != 0) return W8A8_UNSUPPORTED_SHAPE;
+  if (rows == 0 || cols == 0) return W8A8_OK;
+  if (!aligned(x, x_dtype == W8A8_DTYPE_F32 ? 4 : 2) || q == nullptr || !ok4(scale)) return W8A8_INVALID_ARGUMENT;
+  if (rows >= (int64_t(1) << 31) || rows * cols >= (int64_t(1) << 40)) return W8A8_UNSUPPORTED_SHAPE;
+  return hip_status(w8a8::quant_w4(x, x_dtype, rows, cols, q, scale, stream));
+}
+
 int32_t w8a8_quant_per_token(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t group, int8_t* q,
                              float* scale, hipStream_t stream) {
   if (group < 0 || cols < 0) return W8A8_INVALID_ARGUMENT;
@@ -192,7 +206,7 @@ size_t w8a8_w13_workspace_bytes(int64_t T, int64_t k, int64_t E, int64_t H, int6
   if (check_tke(T, k, E) || !valid_dim(H) || !valid_dim(I) || !valid_block_m(block_m) || !valid_mode(scale_mode))
     return 0;
   const GroupedShape s = shape_of(T, k, E, H, I, block_m);
-  if (scale_mode == W8A8_SCALE_FP8_BLOCK128 && !w8a8::fp8_supported(s)) return 0;
+  if (fp8_mode(scale_mode) && !w8a8::fp8_supported(s)) return 0;
   return w8a8::w13_ws_bytes(s, scale_mode);
 }
 
@@ -201,7 +215,7 @@ size_t w8a8_w2_workspace_bytes(int64_t T, int64_t k, int64_t E, int64_t H, int64
   if (check_tke(T, k, E) || !valid_dim(H) || !valid_dim(I) || !valid_block_m(block_m) || !valid_mode(scale_mode))
     return 0;
   const GroupedShape s = shape_of(T, k, E, H, I, block_m);
-  if (scale_mode == W8A8_SCALE_FP8_BLOCK128 && !w8a8::fp8_supported(s)) return 0;
+  if (fp8_mode(scale_mode) && !w8a8::fp8_supported(s)) return 0;
   return w8a8::w2_ws_bytes(s, scale_mode);
 }
 
@@ -213,7 +227,7 @@ static int32_t w13_entry(int32_t mode, const int8_t* a_q, const float* a_scale, 
   int32_t st = check_grouped(sorted, padded_offsets, tile_expert, num_tiles, T, k, E, H, I, block_m);
   if (st) return st;
   const GroupedShape s = shape_of(T, k, E, H, I, block_m);
-  if (mode == W8A8_SCALE_FP8_BLOCK128 && !w8a8::fp8_supported(s)) return W8A8_UNSUPPORTED_SHAPE;
+  if (fp8_mode(mode) && !w8a8::fp8_supported(s)) return W8A8_UNSUPPORTED_SHAPE;
   if (T == 0) return W8A8_OK;
   if (!ok16(a_q) || !ok4(a_scale) || !ok16(w13) || !ok4(w13_scale) || !ok16(h_q) || !ok4(h_scale))
     return W8A8_INVALID_ARGUMENT;
@@ -232,7 +246,7 @@ static int32_t w2_entry(int32_t mode, const int8_t* h_q, const float* h_scale, c
   int32_t st = check_grouped(sorted, padded_offsets, tile_expert, num_tiles, T, k, E, H, I, block_m);
   if (st) return st;
   const GroupedShape s = shape_of(T, k, E, H, I, block_m);
-  if (mode == W8A8_SCALE_FP8_BLOCK128 && !w8a8::fp8_supported(s)) return W8A8_UNSUPPORTED_SHAPE;
+  if (fp8_mode(mode) && !w8a8::fp8_supported(s)) return W8A8_UNSUPPORTED_SHAPE;
   if (T == 0) return W8A8_OK;
   if (!ok16(h_q) || !ok4(h_scale) || !ok16(w2) || !ok4(w2_scale) || !ok4(topk_weights) || !ok16(out))
     return W8A8_INVALID_ARGUMENT;
@@ -301,6 +315,28 @@ int32_t w8a8_fp8_grouped_gemm_w2_combine(const uint8_t* h_q, const float* h_scal
                                          int64_t E, int64_t H, int64_t I, int64_t block_m, float* out, void* ws,
                                          size_t ws_bytes, hipStream_t stream) {
   return w2_entry(W8A8_SCALE_FP8_BLOCK128, reinterpret_cast<const int8_t*>(h_q), h_scale,
+                  reinterpret_cast<const int8_t*>(w2), w2_scale, sorted_pair_ids, padded_offsets, tile_expert,
+                  num_tiles, topk_weights, T, k, E, H, I, block_m, out, ws, ws_bytes, stream);
+}
+
+int32_t w8a8_w4a8_grouped_gemm_w13_silu(const uint8_t* a_q, const float* a_scale, const uint8_t* w13,
+                                        const float* w13_scale, const int32_t* sorted_pair_ids,
+                                        const int32_t* padded_offsets, const int32_t* tile_expert,
+                                        const int32_t* num_tiles, int64_t T, int64_t k, int64_t E, int64_t H,
+                                        int64_t I, int64_t block_m, uint8_t* h_q, float* h_scale, void* ws,
+                                        size_t ws_bytes, hipStream_t stream) {
+  return w13_entry(W8A8_SCALE_W4A8, reinterpret_cast<const int8_t*>(a_q), a_scale,
+                   reinterpret_cast<const int8_t*>(w13), w13_scale, sorted_pair_ids, padded_offsets, tile_expert,
+                   num_tiles, T, k, E, H, I, block_m, reinterpret_cast<int8_t*>(h_q), h_scale, ws, ws_bytes, stream);
+}
+
+int32_t w8a8_w4a8_grouped_gemm_w2_combine(const uint8_t* h_q, const float* h_scale, const uint8_t* w2,
+                                          const float* w2_scale, const int32_t* sorted_pair_ids,
+                                          const int32_t* padded_offsets, const int32_t* tile_expert,
+                                          const int32_t* num_tiles, const float* topk_weights, int64_t T, int64_t k,
+                                          int64_t E, int64_t H, int64_t I, int64_t block_m, float* out, void* ws,
+                                          size_t ws_bytes, hipStream_t stream) {
+  return w2_entry(W8A8_SCALE_W4A8, reinterpret_cast<const int8_t*>(h_q), h_scale,
                   reinterpret_cast<const int8_t*>(w2), w2_scale, sorted_pair_ids, padded_offsets, tile_expert,
                   num_tiles, topk_weights, T, k, E, H, I, block_m, out, ws, ws_bytes, stream);
 }
@@ -380,7 +416,7 @@ size_t w8a8_moe_workspace_bytes(int64_t T, int64_t k, int64_t E, int64_t H, int6
   if (block_m == 0) block_m = w8a8_moe_pick_block_m(T, k, E);
   if (!valid_block_m(block_m)) return 0;
   if (!valid_mode(scale_mode)) return 0;
-  if (scale_mode == W8A8_SCALE_FP8_BLOCK128 && !w8a8::fp8_supported(shape_of(T, k, E, H, I, block_m))) return 0;
+  if (fp8_mode(scale_mode) && !w8a8::fp8_supported(shape_of(T, k, E, H, I, block_m))) return 0;
   return layout_of(T, k, E, H, I, block_m, scale_mode).total;
 }
 
@@ -394,7 +430,7 @@ int32_t w8a8_moe_forward(const struct w8a8_moe_args* a, void* ws, size_t ws_byte
   if (a->x_dtype != W8A8_DTYPE_F32 && a->x_dtype != W8A8_DTYPE_BF16) return W8A8_UNSUPPORTED_DTYPE;
   const int64_t bm = a->block_m == 0 ? w8a8_moe_pick_block_m(a->T, a->k, a->E) : a->block_m;
   if (!valid_block_m(bm)) return W8A8_UNSUPPORTED_SHAPE;
-  if (a->scale_mode == W8A8_SCALE_FP8_BLOCK128 && !w8a8::fp8_supported(shape_of(a->T, a->k, a->E, a->H, a->I, bm)))
+  if (fp8_mode(a->scale_mode) && !w8a8::fp8_supported(shape_of(a->T, a->k, a->E, a->H, a->I, bm)))
     return W8A8_UNSUPPORTED_SHAPE;
   if (a->T == 0) return W8A8_OK;
   st = route_check(a->router_logits, a->T, a->E, a->k, a->score_fn, a->n_group, a->topk_group, a->correction_bias,
@@ -423,7 +459,7 @@ int32_t w8a8_moe_forward(const struct w8a8_moe_args* a, void* ws, size_t ws_byte
   float* h_s = reinterpret_cast<float*>(base + L.h_s);
   void* gws = base + L.gemm_ws;
   const bool block = a->scale_mode != W8A8_SCALE_CHANNEL;
-  const bool fp8 = a->scale_mode == W8A8_SCALE_FP8_BLOCK128;
+  const bool fp8 = fp8_mode(a->scale_mode);
   const GroupedShape s = shape_of(a->T, a->k, a->E, a->H, a->I, bm);
 
   hipError_t e = w8a8::topk_route(a->router_logits, a->T, a->E, a->k, a->score_fn, a->n_group, a->topk_group,

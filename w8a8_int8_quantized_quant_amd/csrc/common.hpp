@@ -54,6 +54,20 @@ __device__ __forceinline__ uint8_t fp8_value(float x, float s) {
   return (uint8_t)(fp8_pack2<false>(v, v, 0u) & 0xFFu);
 }
 
+// Int4 weight rule (the W4A8 path): scale = max(max|x| / 7, 1e-8); q = clamp(rne(x / scale), -7, 7),
+// IEEE division; stored as a nibble of sign (bit 3) and magnitude (bits 0-2), zero as 0.
+__device__ __forceinline__ float w4_scale(float amax) {
+  float s = amax / 7.0f;
+  return s < 1e-8f ? 1e-8f : s;
+}
+__device__ __forceinline__ uint32_t w4_nibble(float x, float s) {
+  float v = __builtin_rintf(x / s);
+  v = v > 7.0f ? 7.0f : v;
+  v = v < -7.0f ? -7.0f : v;
+  const int q = (int)v;
+  return q < 0 ? (uint32_t)(8 | -q) : (uint32_t)q;
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));

@@ -52,12 +52,18 @@ constexpr int kThreads = 256;
 
 enum class BMap { Plain, Split };
 // W13Fp8 / W2Fp8: the block-wise epilogues for FP8 (E4M3) operands, whose per-K-block partial
-// sums come from the FP8 MFMA in fp32; the first GEMM requantizes to E4M3.
-enum class Epi { I32, W13Channel, W2Channel, W13Block, W2Block, W13Fp8, W2Fp8 };
+// sums come from the FP8 MFMA in fp32; the first GEMM requantizes to E4M3.  W13W4 / W2W4: the
+// same with packed int4 weights (widened to E4M3 codes on the way to the MFMA) and one weight
+// scale per (output row, K-block).
+enum class Epi { I32, W13Channel, W2Channel, W13Block, W2Block, W13Fp8, W2Fp8, W13W4, W2W4 };
 
 template <Epi EPI>
+constexpr bool is_w4() {
+  return EPI == Epi::W13W4 || EPI == Epi::W2W4;
+}
+template <Epi EPI>
 constexpr bool is_fp8() {
-  return EPI == Epi::W13Fp8 || EPI == Epi::W2Fp8;
+  return EPI == Epi::W13Fp8 || EPI == Epi::W2Fp8 || is_w4<EPI>();
 }
 template <Epi EPI>
 constexpr bool is_block() {
@@ -156,7 +162,7 @@ __device__ __forceinline__ void epilogue(const Params& p, const AccT (&acc)[FM][
         for (int fn = 0; fn < FN; ++fn)
           p.out_i32[(row0 + trow) * p.N + nt * BN + brow_of<BN, WN, FN, MAP>(wn, fn) + (l % 16)] = acc[fm][fn][r];
       }
-  } else if constexpr (EPI == Epi::W2Channel || EPI == Epi::W2Block || EPI == Epi::W2Fp8) {
+  } else if constexpr (EPI == Epi::W2Channel || EPI == Epi::W2Block || EPI == Epi::W2Fp8 || EPI == Epi::W2W4) {
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
@@ -555,6 +561,74 @@ __device__ __forceinline__ void dma_stage_f8(const int8_t* stage, int8_t* next, 
   }
 }
 
+// Packed int4 -> E4M3 codes.  One dword holds 8 consecutive K values: byte b carries value b in
+// its low nibble and value 4 + b in its high nibble, each nibble sign (bit 3) and magnitude
+// (bits 0-2).  The magnitudes 0..7 are exact E4M3 values: a byte permute looks their codes up,
+// and the sign moves to bit 7.  Out: codes of values 0-3 (first) and 4-7 (second).
+constexpr uint32_t kW4CodesLo = 0x44403800u;  // E4M3 codes of 0, 1, 2, 3
+constexpr uint32_t kW4CodesHi = 0x4E4C4A48u;  // E4M3 codes of 4, 5, 6, 7
+__device__ __forceinline__ uint32_t w4_codes4(uint32_t nib) {  // nibble per byte -> code per byte
+  return __builtin_amdgcn_perm(kW4CodesHi, kW4CodesLo, nib & 0x07070707u) | ((nib & 0x08080808u) << 4);
+}
+__device__ __forceinline__ void w4_to_fp8(uint32_t x, int32_t& lo, int32_t& hi) {
+  lo = (int32_t)w4_codes4(x & 0x0F0F0F0Fu);
+  hi = (int32_t)w4_codes4((x >> 4) & 0x0F0F0F0Fu);
+}
+
+// The K loop step for FP8 activations against packed int4 weights: as dma_stage_f8, with B rows
+// of 64 bytes (128 int4 values) whose 16-byte chunks are swizzled by (row / 4) mod 4; lane (g, fr)
+// widens chunk g of B row fr (values 32 g .. 32 g + 31) into the 32 E4M3 codes of its operand.
+__device__ __forceinline__ int swz4(int row) { return (row >> 2) & 3; }
+template <int BM, int BN, int WM, int WN, int A_LD, int LD, BMap MAP>
+__device__ __forceinline__ void dma_stage_w4(const int8_t* stage, int8_t* next, const int8_t* a_base,
+                                             const int8_t* b_base, const uint32_t (&off)[LD], int a_dst, int b_dst,
+                                             uint32_t next_off, bool prefetch, f32x4 (&acc)[BM / WM / 16][BN / WN / 16],
+                                             int wm, int wn, int g, int fr, int rows) {
+  constexpr int FM = BM / WM / 16, FN = BN / WN / 16, FNH = FN / 2;
+  constexpr int GROUPS = 2 * FM;
+  constexpr int BROW = kDmaBK / 2;  // bytes of one B row in a stage
+  static_assert(GROUPS >= LD && FN % 2 == 0, "DMA slots");
+  constexpr int kScaleOne = 127;
+  const int c0 = fr * kDmaBK + (((2 * g) ^ swz(fr)) << 4);
+  const int c1 = fr * kDmaBK + (((2 * g + 1) ^ swz(fr)) << 4);
+  i32x8 bf[FN];
+#pragma unroll
+  for (int fn = 0; fn < FN; ++fn) {
+    const int j = brow_of<BN, WN, FN, MAP>(wn, fn) + fr;
+    const i32x4 v = *reinterpret_cast<const i32x4*>(stage + BM * kDmaBK + j * BROW + ((g ^ swz4(j)) << 4));
+    int32_t o[8];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) w4_to_fp8((uint32_t)v[d], o[2 * d], o[2 * d + 1]);
+    bf[fn] = i32x8{o[0], o[1], o[2], o[3], o[4], o[5], o[6], o[7]};
+  }
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) {
+    const int8_t* arow = stage + (wm * FM + fm) * 16 * kDmaBK;
+    const i32x4 lo = *reinterpret_cast<const i32x4*>(arow + c0);
+    const i32x4 hi = *reinterpret_cast<const i32x4*>(arow + c1);
+    const i32x8 af = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int grp = fm * 2 + h;
+#pragma unroll
+      for (int c = 0; c < LD; ++c)
+        if ((c * GROUPS) / LD == grp && prefetch) {
+          if (c < A_LD)
+            dma16(a_base + (off[c] + next_off), next + a_dst + c * 1024);
+          else
+            dma16_nt(b_base + (off[c] + next_off), next + b_dst + (c - A_LD) * 1024);
+        }
+      if (fm * 16 < rows) {
+#pragma unroll
+        for (int f = 0; f < FNH; ++f)
+          acc[fm][h * FNH + f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              af, bf[h * FNH + f], acc[fm][h * FNH + f], 0, 0, 0, kScaleOne, 0, kScaleOne);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
 // Channel-wise epilogues of the DMA engine, staged through the (then idle) stage buffers: each
 // pass turns the accumulators of a band of fragment rows into fp32 values in LDS (wavefront-half
 // wm in buffer wm), then whole rows leave as contiguous float4 stores.  Second GEMM: y rows of BN
@@ -790,22 +864,26 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_ring_kernel(c
                                                                               const int32_t* __restrict__ work) {
   constexpr bool kBlock = is_block<EPI>();
   constexpr bool kFp8 = is_fp8<EPI>();
+  constexpr bool kW4 = is_w4<EPI>();          // packed int4 weights, one scale per (row, K-block)
+  constexpr bool kBlkScales = kBlock && !kW4;  // 128 x 128 weight-scale blocks
   using AccT = typename std::conditional<kFp8, f32x4, i32x4>::type;
   constexpr int NT = WM * WN * kWave;
   constexpr int NW = WM * WN;
   constexpr int FM = BM / WM / 16;
   constexpr int FN = BN / WN / 16;
   constexpr int CPR = kDmaBK / 16;
+  constexpr int BKB = kW4 ? kDmaBK / 2 : kDmaBK;  // bytes of one B row per stage
+  constexpr int CPRB = BKB / 16;
   constexpr int A_LD = BM * CPR / NT;
-  constexpr int B_LD = BN * CPR / NT;
+  constexpr int B_LD = BN * CPRB / NT;
   constexpr int LD = A_LD + B_LD;
-  constexpr int STAGE = (BM + BN) * kDmaBK;
+  constexpr int STAGE = BM * kDmaBK + BN * BKB;
   constexpr int SG = 4;  // K-blocks per activation-scale DMA
   static_assert(EPI != Epi::I32, "scaled epilogues only");
-  static_assert(A_LD >= 1 && B_LD >= 1 && (BM * CPR) % NT == 0 && (BN * CPR) % NT == 0, "tile shape");
+  static_assert(A_LD >= 1 && B_LD >= 1 && (BM * CPR) % NT == 0 && (BN * CPRB) % NT == 0, "tile shape");
   static_assert(KT >= 1 && LD + 1 < 64, "K steps");
   static_assert(!kBlock || (NW * 16 == BM && kWave == 16 * SG), "one scale DMA per wavefront: 16 rows x SG blocks");
-  static_assert(!kBlock || BN == 256, "two 128-row weight-scale blocks per tile");
+  static_assert(!kBlkScales || BN == 256, "two 128-row weight-scale blocks per tile");
   static_assert(MAP == BMap::Plain || FN % 2 == 0, "split tiles need gate and up fragments");
 
   __shared__ __attribute__((aligned(1024))) int8_t st0[STAGE];
@@ -813,7 +891,7 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_ring_kernel(c
   __shared__ __attribute__((aligned(1024))) int8_t st2[STAGE];
   __shared__ __attribute__((aligned(16))) float sas0[kBlock ? NW * kWave : 1];  // activation scales, even groups
   __shared__ __attribute__((aligned(16))) float sas1[kBlock ? NW * kWave : 1];  // odd groups
-  __shared__ float sh_ws[kBlock ? 2 : 1][kBlock ? KT : 1];
+  __shared__ float sh_ws[kBlkScales ? 2 : 1][kBlkScales ? KT : 1];
   __shared__ int32_t sh_pid[BM];
   __shared__ float sh_red[kBlock ? WN : 1][BM];
 
@@ -833,13 +911,14 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_ring_kernel(c
   const int64_t e = work[1 + kWorkFields * ti];
   const int64_t row0 = work[2 + kWorkFields * ti];
   const int nrows = work[3 + kWorkFields * ti];
-  const int8_t* wexp = p.w + e * p.N * p.K;
+  const int64_t wrow_bytes = kW4 ? p.K / 2 : p.K;
+  const int8_t* wexp = p.w + e * p.N * wrow_bytes;
 
   const int tid = threadIdx.x, l = lane_id();
   const int wv = __builtin_amdgcn_readfirstlane(tid / kWave), wm = wv / WN, wn = wv % WN;
   const int g = l >> 4, fr = l & 15;
   for (int i = tid; i < BM; i += NT) sh_pid[i] = i < nrows ? p.sorted[row0 + i] : (int32_t)p.P;
-  if constexpr (kBlock) {
+  if constexpr (kBlkScales) {
     for (int i = tid; i < 2 * KT; i += NT) {
       const int64_t blk = wrow_of<BN, MAP>(nt, (i / KT) * 128, p.I) / 128;
       sh_ws[i / KT][i % KT] = p.w_s[(e * (p.N / 128) + blk) * KT + i % KT];
@@ -860,8 +939,17 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_ring_kernel(c
   }
 #pragma unroll
   for (int c = 0; c < B_LD; ++c) {
-    const int q = (wv * B_LD + c) * kWave + l, j = q / CPR, kc = (q % CPR) ^ swz(j);
-    off[A_LD + c] = (uint32_t)(wrow_of<BN, MAP>(nt, j, p.I) * p.K + kc * 16);
+    const int q = (wv * B_LD + c) * kWave + l, j = q / CPRB, kc = (q % CPRB) ^ (kW4 ? swz4(j) : swz(j));
+    off[A_LD + c] = (uint32_t)(wrow_of<BN, MAP>(nt, j, p.I) * wrow_bytes + kc * 16);
+  }
+  // int4 weights: this lane's weight-scale rows (fragment fn, column l % 16), one scale per K-block,
+  // loaded a step ahead (before the step's DMAs, so the step's closing wait covers them)
+  uint32_t wso[kW4 ? FN : 1];
+  float wsr[2][kW4 ? FN : 1];
+  if constexpr (kW4) {
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+      wso[fn] = (uint32_t)((e * p.N + wrow_of<BN, MAP>(nt, brow_of<BN, WN, FN, MAP>(wn, fn) + (l & 15), p.I)) * KT);
   }
   // activation-scale DMA: lane l brings row wv * 16 + (l & 15) of K-block group * SG + l / 16
   // (the last K-block again where a group runs past K)
@@ -884,6 +972,11 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_ring_kernel(c
 #define W8A8_RSTG(j) ((j) == 0 ? st0 : (j) == 1 ? st1 : st2)
 #define W8A8_RSAS(q) (((q) & 1) ? sas1 : sas0)
   __syncthreads();  // sh_pid, sh_ws
+  if constexpr (kW4) {
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) wsr[0][fn] = p.w_s[wso[fn]];
+    __builtin_amdgcn_sched_barrier(0);
+  }
 #pragma unroll
   for (int st = 0; st < (KT < 2 ? KT : 2); ++st) {
 #pragma unroll
@@ -891,7 +984,7 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_ring_kernel(c
       if (c < A_LD)
         dma16(p.a + (off[c] + (uint32_t)(st * kDmaBK)), W8A8_RSTG(st) + a_dst + c * 1024);
       else
-        dma16_nt(wexp + (off[c] + (uint32_t)(st * kDmaBK)), W8A8_RSTG(st) + b_dst + (c - A_LD) * 1024);
+        dma16_nt(wexp + (off[c] + (uint32_t)(st * BKB)), W8A8_RSTG(st) + b_dst + (c - A_LD) * 1024);
     }
     if (kBlock && st == 0) dma4(p.a_s + (s_off + s_blk(0)), sas0 + wv * kWave);
   }
@@ -904,22 +997,32 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_ring_kernel(c
   // Uniform bases of the stage two steps ahead, advanced one step at a time; the empty asm keeps
   // the compiler from precomputing every step's address up front.
   const int8_t* a_next = p.a + 2 * kDmaBK;
-  const int8_t* b_next = wexp + 2 * kDmaBK;
+  const int8_t* b_next = wexp + 2 * BKB;
 #pragma clang loop unroll(full)
   for (int kt = 0; kt < KT; ++kt) {
     __builtin_amdgcn_s_waitcnt(kLgkm0Imm);
     barrier_no_fence();
     const bool more = kt + 2 < KT;
     const bool sdma = kBlock && more && (kt + 2) % SG == 0;  // scale group of stage kt + 2 goes out now
+    if constexpr (kW4) {
+      if (kt + 1 < KT) {
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) wsr[(kt + 1) & 1][fn] = p.w_s[wso[fn] + (uint32_t)(kt + 1)];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
     if (sdma) dma4(p.a_s + (s_off + s_blk((kt + 2) / SG)), W8A8_RSAS((kt + 2) / SG) + wv * kWave);
-    if constexpr (kFp8)
+    if constexpr (kW4)
+      dma_stage_w4<BM, BN, WM, WN, A_LD, LD, MAP>(W8A8_RSTG(kt % 3), W8A8_RSTG((kt + 2) % 3), a_next, b_next, off,
+                                                  a_dst, b_dst, 0u, more, acc, wm, wn, g, fr, wrows);
+    else if constexpr (kFp8)
       dma_stage_f8<BM, BN, WM, WN, A_LD, LD, MAP>(W8A8_RSTG(kt % 3), W8A8_RSTG((kt + 2) % 3), a_next, b_next, off,
                                                   a_dst, b_dst, 0u, more, acc, wm, wn, g, fr, wrows);
     else
       dma_stage<BM, BN, WM, WN, A_LD, LD, MAP>(W8A8_RSTG(kt % 3), W8A8_RSTG((kt + 2) % 3), a_next, b_next, off, a_dst,
                                                b_dst, 0u, more, acc, wm, wn, g, fr, wrows);
     a_next += kDmaBK;
-    b_next += kDmaBK;
+    b_next += BKB;
     asm volatile("" : "+s"(a_next), "+s"(b_next));
     if constexpr (kBlock) {
       if (wrows > 0) {
@@ -931,9 +1034,14 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_ring_kernel(c
 #pragma unroll
           for (int r = 0; r < 4; ++r) as[fm][r] = s4[r];
         }
-        const float w0 = sh_ws[0][kt], w1 = sh_ws[1][kt];
+        if constexpr (kW4) {
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn) ws[fn] = brow_of<BN, WN, FN, MAP>(wn, fn) >= 128 ? w1 : w0;
+          for (int fn = 0; fn < FN; ++fn) ws[fn] = wsr[kt & 1][fn];
+        } else {
+          const float w0 = sh_ws[0][kt], w1 = sh_ws[1][kt];
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn) ws[fn] = brow_of<BN, WN, FN, MAP>(wn, fn) >= 128 ? w1 : w0;
+        }
         block_flush<FM, FN, AccT>(acc, accf, as, ws);
       }
     }
@@ -1206,12 +1314,12 @@ hipError_t launch_ring(Params prm, const GroupedShape& s, const int32_t* padded_
   return hipGetLastError();
 }
 
-// FP8 operands always take the ring engine; K sizes with an instantiated kernel (K / 128).
+// FP8 and W4A8 operands always take the ring engine; K sizes with an instantiated kernel (K / 128).
 bool fp8_kt_ok(int64_t kt) { return kt == 1 || kt == 2 || kt == 4 || kt == 8 || kt == 16 || kt == 32 || kt == 56; }
 
 template <BMap MAP, Epi EPI>
-hipError_t launch_ring_fp8(const Params& prm, const GroupedShape& s, const int32_t* padded_offsets, int32_t* work,
-                           hipStream_t stream) {
+hipError_t launch_ring_kt(const Params& prm, const GroupedShape& s, const int32_t* padded_offsets, int32_t* work,
+                          hipStream_t stream) {
   switch (prm.K / kDmaBK) {
     case 1: return launch_ring<MAP, EPI, 1>(prm, s, padded_offsets, work, stream);
     case 2: return launch_ring<MAP, EPI, 2>(prm, s, padded_offsets, work, stream);
@@ -1233,7 +1341,7 @@ bool fp8_supported(const GroupedShape& s) {
 }
 
 size_t w13_ws_bytes(const GroupedShape& s, int32_t scale_mode) {
-  if (scale_mode == 2) return work_bytes(s);
+  if (scale_mode == 2 || scale_mode == 3) return work_bytes(s);
   if (scale_mode == 1) return use_ring(s, 1) ? work_bytes(s) : 256;
   return round256(sizeof(float) * (size_t)(s.max_rows * s.I)) +
          round256(sizeof(float) * (size_t)(s.max_rows * w13_n_tiles(s, scale_mode))) + work_bytes(s);
@@ -1286,7 +1394,9 @@ hipError_t w13_silu(const GroupedShape& s, int32_t scale_mode, const int8_t* a_q
   prm.h_q = h_q;
   prm.h_s = h_s;
   if (scale_mode == 2)
-    return launch_ring_fp8<BMap::Split, Epi::W13Fp8>(prm, s, padded_offsets, static_cast<int32_t*>(ws), stream);
+    return launch_ring_kt<BMap::Split, Epi::W13Fp8>(prm, s, padded_offsets, static_cast<int32_t*>(ws), stream);
+  if (scale_mode == 3)
+    return launch_ring_kt<BMap::Split, Epi::W13W4>(prm, s, padded_offsets, static_cast<int32_t*>(ws), stream);
   if (scale_mode == 1) {
     if (use_ring(s, 1))
       return launch_ring<BMap::Split, Epi::W13Block, kRingH / kDmaBK>(prm, s, padded_offsets,
@@ -1341,7 +1451,9 @@ hipError_t w2_combine(const GroupedShape& s, int32_t scale_mode, const int8_t* h
   prm.out_f32 = y;
   hipError_t err;
   if (scale_mode == 2)
-    err = launch_ring_fp8<BMap::Plain, Epi::W2Fp8>(prm, s, padded_offsets, work, stream);
+    err = launch_ring_kt<BMap::Plain, Epi::W2Fp8>(prm, s, padded_offsets, work, stream);
+  else if (scale_mode == 3)
+    err = launch_ring_kt<BMap::Plain, Epi::W2W4>(prm, s, padded_offsets, work, stream);
   else if (scale_mode == 1)
     err = use_ring(s, 1) ? launch_ring<BMap::Plain, Epi::W2Block, kRingI / kDmaBK>(prm, s, padded_offsets, work, stream)
                          : launch_bm<BMap::Plain, Epi::W2Block, kBNStaged>(prm, s.max_rows, stream);

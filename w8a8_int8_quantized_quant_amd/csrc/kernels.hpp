@@ -11,6 +11,9 @@ namespace w8a8 {
 // fp8: E4M3 codes (as bytes in q) by the FP8 rule instead of the INT8 rule.
 hipError_t quant_blocks(const void* x, int32_t dtype, int64_t rows, int64_t cols, int64_t br, int64_t bc,
                         int8_t* q, float* scale, hipStream_t stream, bool fp8 = false);
+// Packed int4 weights, one scale per (row, 128 columns); cols a multiple of 128.
+hipError_t quant_w4(const void* x, int32_t dtype, int64_t rows, int64_t cols, uint8_t* q, float* scale,
+                    hipStream_t stream);
 
 // route.hip
 hipError_t topk_route(const float* logits, int64_t T, int64_t E, int64_t k, int32_t score_fn, int64_t n_group,
@@ -29,9 +32,10 @@ struct GroupedShape {
   int64_t T, k, E, H, I, block_m;
   int64_t max_rows;  // capacity of the sorted-row buffers
 };
-// scale_mode: 0 channel-wise INT8, 1 block-wise INT8, 2 block-wise FP8 (E4M3 codes in the int8_t buffers).
+// scale_mode: 0 channel-wise INT8, 1 block-wise INT8, 2 block-wise FP8 (E4M3 codes in the int8_t
+// buffers), 3 W4A8 (packed int4 weights with per-(row, K-block) scales, FP8 activations).
 size_t w13_ws_bytes(const GroupedShape& s, int32_t scale_mode);
-bool fp8_supported(const GroupedShape& s);  // the FP8 GEMMs' shape limits
+bool fp8_supported(const GroupedShape& s);  // the FP8 and W4A8 GEMMs' shape limits
 size_t w2_ws_bytes(const GroupedShape& s, int32_t scale_mode);
 hipError_t gemm_i32(const int8_t* a, int32_t gather, const int8_t* w, int64_t N, int64_t K, const int32_t* sorted,
                     const int32_t* tile_expert, const int32_t* num_tiles, int64_t P, int64_t k, int64_t block_m,

@@ -1,4 +1,4 @@
-// quant.hip -- symmetric INT8 and FP8 (E4M3) quantization kernels (gfx950).
+// quant.hip -- symmetric INT8, FP8 (E4M3) and packed int4 quantization kernels (gfx950).
 //
 // Online activation quantization, one scale per token or per token-group
 // (jiqizhixin article on Meituan's INT8 DeepSeek R1, "Quantization
@@ -6,9 +6,10 @@
 // output channel or per 128 x 128 block.  INT8 rule: scale = max(max|x|/127,
 // 1e-8), q = clamp(rne(x / scale)).  FP8 (SGLang PR #8273: per-block FP8
 // weights, per-token-group FP8 activations): scale = max(max|x|/448, 1e-8), q =
-// the nearest E4M3 code of x / scale.  The max is order-independent and the
-// division is IEEE, so results are bit-exact regardless of how lanes split the
-// work.
+// the nearest E4M3 code of x / scale.  Int4 weights (SGLang PR #8311, w4a8):
+// scale = max(max|x|/7, 1e-8) per (row, 128 columns), q = clamp(rne(x / scale)).
+// The max is order-independent and the division is IEEE, so results are
+// bit-exact regardless of how lanes split the work.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -136,6 +137,24 @@ __global__ __launch_bounds__(kThreads) void quant_blocks_kernel(const T* __restr
   }
 }
 
+// Packed int4 weights: one wavefront per (row, 128 columns); lane l builds byte l of the group's
+// 64, holding value 8 (l / 4) + l % 4 in its low nibble and value 8 (l / 4) + 4 + l % 4 in its
+// high nibble (the W4A8 GEMM's packing: 8 consecutive values per 4 bytes).
+template <typename T>
+__global__ __launch_bounds__(kThreads) void quant_w4_kernel(const T* __restrict__ x, int64_t rows, int64_t cols,
+                                                            uint8_t* __restrict__ q, float* __restrict__ scale) {
+  const int64_t ngroups = cols / 128;
+  const int64_t gid = (int64_t)blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave;
+  if (gid >= rows * ngroups) return;
+  const int64_t row = gid / ngroups, gi = gid % ngroups;
+  const int l = lane_id();
+  const int64_t base = row * cols + gi * 128 + (l / 4) * 8 + (l % 4);
+  const float v0 = load_as_f32(x, base), v1 = load_as_f32(x, base + 4);
+  const float s = w4_scale(wave_max(fmaxf(fabsf(v0), fabsf(v1))));
+  if (l == 0) scale[gid] = s;
+  q[row * (cols / 2) + gi * 64 + l] = (uint8_t)(w4_nibble(v0, s) | (w4_nibble(v1, s) << 4));
+}
+
 template <typename T, typename C>
 hipError_t launch_quant(const void* xv, int64_t rows, int64_t cols, int64_t br, int64_t bc, int8_t* q,
                         float* scale, hipStream_t stream) {
@@ -158,6 +177,20 @@ hipError_t launch_quant(const void* xv, int64_t rows, int64_t cols, int64_t br, 
 }
 
 }  // namespace
+
+hipError_t quant_w4(const void* x, int32_t dtype, int64_t rows, int64_t cols, uint8_t* q, float* scale,
+                    hipStream_t stream) {
+  if (rows == 0 || cols == 0) return hipSuccess;
+  const int64_t waves = rows * (cols / 128);
+  const int64_t blocks = (waves + kThreads / kWave - 1) / (kThreads / kWave);
+  if (dtype == 1)
+    hipLaunchKernelGGL(quant_w4_kernel<uint16_t>, dim3((uint32_t)blocks), dim3(kThreads), 0, stream,
+                       static_cast<const uint16_t*>(x), rows, cols, q, scale);
+  else
+    hipLaunchKernelGGL(quant_w4_kernel<float>, dim3((uint32_t)blocks), dim3(kThreads), 0, stream,
+                       static_cast<const float*>(x), rows, cols, q, scale);
+  return hipGetLastError();
+}
 
 hipError_t quant_blocks(const void* x, int32_t dtype, int64_t rows, int64_t cols, int64_t br, int64_t bc,
                         int8_t* q, float* scale, hipStream_t stream, bool fp8) {

@@ -14,8 +14,9 @@ import torch
 
 import synth
 
-from . import (SCALE_BLOCK128, SCALE_CHANNEL, SCALE_FP8_BLOCK128, SCORE_SIGMOID, SCORE_SOFTMAX, w8a8_fp8_quant_blocks,
-               w8a8_moe_forward, w8a8_moe_workspace_bytes, w8a8_quant_blocks)
+from . import (SCALE_BLOCK128, SCALE_CHANNEL, SCALE_FP8_BLOCK128, SCALE_W4A8, SCORE_SIGMOID, SCORE_SOFTMAX,
+               w8a8_fp8_quant_blocks, w8a8_moe_forward, w8a8_moe_workspace_bytes, w8a8_quant_blocks,
+               w8a8_w4a8_quant_weights)
 
 
 @dataclass
@@ -30,7 +31,8 @@ class DeviceLayer:
 
     @property
     def scale_mode(self) -> int:
-        return {"block": SCALE_BLOCK128, "fp8": SCALE_FP8_BLOCK128}.get(self.cfg.scale_mode, SCALE_CHANNEL)
+        return {"block": SCALE_BLOCK128, "fp8": SCALE_FP8_BLOCK128, "w4a8": SCALE_W4A8}.get(self.cfg.scale_mode,
+                                                                                           SCALE_CHANNEL)
 
     @property
     def score_fn(self) -> int:
@@ -38,10 +40,14 @@ class DeviceLayer:
 
 
 def _quantize_experts(cfg, stream_tag: int, E: int, N: int, K: int, block: bool, device, chunk_bytes: int,
-                      fp8: bool = False):
-    """Draw [E, N, K] fp32 weights chunk by chunk and quantize them into int8 (or FP8 codes) + scales."""
-    q = torch.empty((E, N, K), dtype=torch.uint8 if fp8 else torch.int8, device=device)
-    scale = torch.empty((E, N // 128, K // 128) if block else (E, N), dtype=torch.float32, device=device)
+                      fp8: bool = False, w4: bool = False):
+    """Draw [E, N, K] fp32 weights chunk by chunk and quantize them into int8 (FP8 codes, packed int4)
+    + scales."""
+    q = torch.empty((E, N, K // 2 if w4 else K), dtype=torch.uint8 if (fp8 or w4) else torch.int8, device=device)
+    if w4:
+        scale = torch.empty((E, N, K // 128), dtype=torch.float32, device=device)
+    else:
+        scale = torch.empty((E, N // 128, K // 128) if block else (E, N), dtype=torch.float32, device=device)
     per_expert = N * K
     chunk = max(1, min(E, chunk_bytes // (4 * per_expert)))
     scratch = torch.empty(chunk * per_expert, dtype=torch.float32, device=device)
@@ -51,7 +57,9 @@ def _quantize_experts(cfg, stream_tag: int, E: int, N: int, K: int, block: bool,
         buf = scratch[: c * per_expert]
         synth.dev_normal(buf.data_ptr(), c * per_expert, cfg.seed, stream_tag, e0 * per_expert, cfg.w_sigma, hs)
         mat = buf.view(c * N, K)
-        if fp8:
+        if w4:
+            w8a8_w4a8_quant_weights(mat, q[e0:e0 + c].view(c * N, K // 2), scale[e0:e0 + c].view(c * N, K // 128))
+        elif fp8:
             w8a8_fp8_quant_blocks(mat, 128, 128, q[e0:e0 + c].view(c * N, K),
                                   scale[e0:e0 + c].view(c * N // 128, K // 128))
         elif block:
@@ -74,10 +82,11 @@ def make_layer(cfg: synth.MoEConfig, device="cuda", T: Optional[int] = None,
     bias = synth.zipf_bias(cfg)
     bias_t = None if bias is None else torch.from_numpy(bias).to(device)
     synth.dev_logits(logits.data_ptr(), cfg, None if bias_t is None else bias_t.data_ptr(), hs, T=T)
-    fp8 = cfg.scale_mode == "fp8"
+    fp8, w4 = cfg.scale_mode == "fp8", cfg.scale_mode == "w4a8"
     block = cfg.scale_mode == "block" or fp8
-    w13, w13_s = _quantize_experts(cfg, synth.STREAM_W13, cfg.E, 2 * cfg.I, cfg.H, block, device, chunk_bytes, fp8)
-    w2, w2_s = _quantize_experts(cfg, synth.STREAM_W2, cfg.E, cfg.H, cfg.I, block, device, chunk_bytes, fp8)
+    w13, w13_s = _quantize_experts(cfg, synth.STREAM_W13, cfg.E, 2 * cfg.I, cfg.H, block, device, chunk_bytes, fp8,
+                                   w4)
+    w2, w2_s = _quantize_experts(cfg, synth.STREAM_W2, cfg.E, cfg.H, cfg.I, block, device, chunk_bytes, fp8, w4)
     torch.cuda.synchronize(device)
     return DeviceLayer(cfg, x, logits, w13, w13_s, w2, w2_s)
 
