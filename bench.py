@@ -9,7 +9,8 @@ weights and scales) are resident in HBM before timing starts.
 Prints one JSON line.  value = tokens/s of the DeepSeek-V3 decode layer
 (T=128, hidden 7168, intermediate 2048, 256 experts, top-8); the same line
 carries the T=8192 prefill layer's figures under "prefill", the tiny (T=16), skewed
-(T=4096) and block-wise (T=2048, INT8 and FP8) layers under "configs", the dense W8A8 linear
+(T=4096), block-wise (T=2048, INT8 and FP8) layers and the FP8 / W4A8 variants of the decode
+and block-wise workloads under "configs", the dense W8A8 linear
 under "linear", the roofline of the
 dominant kernel (the gate+up GEMM, weight-streaming and so HBM-bound at T=128),
 the device's measured read / copy / INT8-MFMA rates under "peaks_measured", and
@@ -36,7 +37,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="decode",
-                    help="decode (the headline), prefill, tiny, skew, block, or fp8-block")
+                    help="decode (the headline), prefill, tiny, skew, block, fp8-block, fp8-decode, w4a8-decode "
+                         "or w4a8-block")
     ap.add_argument("--no-prefill", action="store_true", help="skip the T=8192 prefill figures")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=128, help="tokens in the CPU oracle sample")
@@ -74,7 +76,8 @@ class Stages:
         c = layer.cfg
         T = layer.x.shape[0]
         self.T = T
-        self.fp8 = c.scale_mode == "fp8"
+        self.w4 = c.scale_mode == "w4a8"
+        self.fp8 = c.scale_mode == "fp8" or self.w4  # FP8 activations and intermediate
         self.block = c.scale_mode == "block" or self.fp8
         self.bm = block_m or w8.w8a8_moe_pick_block_m(T, c.k, c.E)
         dev = layer.x.device
@@ -94,7 +97,8 @@ class Stages:
         self.h_q = torch.empty((max(R, 1), c.I), dtype=code, device=dev)
         self.h_s = torch.empty((max(R, 1), c.I // 128) if self.block else (max(R, 1),), dtype=f32, device=dev)
         self.out = torch.empty((T, c.H), dtype=f32, device=dev)
-        mode = w8.SCALE_FP8_BLOCK128 if self.fp8 else w8.SCALE_BLOCK128 if self.block else w8.SCALE_CHANNEL
+        mode = (w8.SCALE_W4A8 if self.w4 else w8.SCALE_FP8_BLOCK128 if self.fp8 else w8.SCALE_BLOCK128 if self.block
+                else w8.SCALE_CHANNEL)
         self.ws_align = torch.empty(max(w8.moe_align_workspace_bytes(T, c.k, c.E), 256), dtype=torch.uint8, device=dev)
         gws = max(w8.w8a8_w13_workspace_bytes(T, c.k, c.E, c.H, c.I, self.bm, mode),
                   w8.w8a8_w2_workspace_bytes(T, c.k, c.E, c.H, c.I, self.bm, mode))
@@ -116,14 +120,16 @@ class Stages:
                                     self.sorted, self.tile_expert, self.num_tiles, self.ws_align)
 
     def w13(self):
-        fn = (self.w8.w8a8_fp8_grouped_gemm_w13_silu if self.fp8 else self.w8.w8a8_block_grouped_gemm_w13_silu
-              if self.block else self.w8.w8a8_grouped_gemm_w13_silu)
+        fn = (self.w8.w8a8_w4a8_grouped_gemm_w13_silu if self.w4 else self.w8.w8a8_fp8_grouped_gemm_w13_silu
+              if self.fp8 else self.w8.w8a8_block_grouped_gemm_w13_silu if self.block
+              else self.w8.w8a8_grouped_gemm_w13_silu)
         fn(self.a_q, self.a_s, self.L.w13, self.L.w13_scale, self.sorted, self.padded, self.tile_expert,
            self.num_tiles, self.T, self.L.cfg.k, self.bm, self.h_q, self.h_s, self.ws_gemm)
 
     def w2(self):
-        fn = (self.w8.w8a8_fp8_grouped_gemm_w2_combine if self.fp8 else self.w8.w8a8_block_grouped_gemm_w2_combine
-              if self.block else self.w8.w8a8_grouped_gemm_w2_combine)
+        fn = (self.w8.w8a8_w4a8_grouped_gemm_w2_combine if self.w4 else self.w8.w8a8_fp8_grouped_gemm_w2_combine
+              if self.fp8 else self.w8.w8a8_block_grouped_gemm_w2_combine if self.block
+              else self.w8.w8a8_grouped_gemm_w2_combine)
         fn(self.h_q, self.h_s, self.L.w2, self.L.w2_scale, self.sorted, self.padded, self.tile_expert,
            self.num_tiles, self.tw, self.T, self.L.cfg.k, self.bm, self.out, self.ws_gemm)
 
@@ -138,14 +144,26 @@ class Stages:
             events[len(self.NAMES)].record()
 
 
-def fp8_block_config():
-    """The block-wise workload (T=2048, DeepSeek-V3 shapes, same draws) with FP8 (E4M3) operands."""
+VARIANTS = {  # name: (workload it re-quantizes, scale mode, description)
+    "fp8-block": ("block", "fp8", "DeepSeek-V3 shapes, 128x128 block-wise FP8 (E4M3), T=2048"),
+    "fp8-decode": ("decode", "fp8", "DeepSeek-V3 MoE layer, decode batch T=128, 128x128 block-wise FP8 (E4M3)"),
+    "w4a8-decode": ("decode", "w4a8", "DeepSeek-V3 MoE layer, decode batch T=128, W4A8 (int4 weights, FP8 "
+                                      "activations)"),
+    "w4a8-block": ("block", "w4a8", "DeepSeek-V3 shapes, W4A8 (int4 weights, FP8 activations), T=2048"),
+}
+
+
+def config_of(name):
+    """A workload by name: the five base workloads, or a variant that re-quantizes one of them
+    (same shapes, same draws) in FP8 or W4A8."""
     import dataclasses
 
     import synth
 
-    return dataclasses.replace(synth.CONFIGS["block"], name="fp8-block", scale_mode="fp8",
-                               note="DeepSeek-V3 shapes, 128x128 block-wise FP8 (E4M3), T=2048")
+    if name in VARIANTS:
+        base, mode, note = VARIANTS[name]
+        return dataclasses.replace(synth.CONFIGS[base], name=name, scale_mode=mode, note=note)
+    return synth.CONFIGS[name]
 
 
 def measure(layer, steps, warmup):
@@ -171,12 +189,14 @@ def layer_figures(cfg, T, ms, counts):
     P = T * cfg.k
     ops = 2.0 * P * (2 * cfg.I * cfg.H + cfg.H * cfg.I)
     active = int((counts > 0).sum())
-    blk = cfg.scale_mode in ("block", "fp8")
+    w4 = cfg.scale_mode == "w4a8"
+    blk = cfg.scale_mode in ("block", "fp8", "w4a8")
     nsh = cfg.I // 128 if blk else 1
-    nsw13 = (2 * cfg.I // 128) * (cfg.H // 128) if blk else 2 * cfg.I
-    nsw2 = (cfg.H // 128) * (cfg.I // 128) if blk else cfg.H
+    nsw13 = (2 * cfg.I * (cfg.H // 128) if w4 else (2 * cfg.I // 128) * (cfg.H // 128)) if blk else 2 * cfg.I
+    nsw2 = (cfg.H * (cfg.I // 128) if w4 else (cfg.H // 128) * (cfg.I // 128)) if blk else cfg.H
     nsa = cfg.H // 128 if blk else 1
-    w_bytes = active * (2 * cfg.I * cfg.H + cfg.H * cfg.I + 4 * (nsw13 + nsw2))
+    wdiv = 2 if w4 else 1  # int4: two weights per byte
+    w_bytes = active * ((2 * cfg.I * cfg.H + cfg.H * cfg.I) // wdiv + 4 * (nsw13 + nsw2))
     x_bytes = T * cfg.H * (2 if cfg.x_dtype else 4)
     other = (T * cfg.E * 4 + x_bytes + 2 * (T * cfg.H + 4 * T * nsa) + 2 * (P * cfg.I + 4 * P * nsh)
              + T * cfg.H * 4 + P * 8)
@@ -192,11 +212,12 @@ def w13_algorithmic_bytes(cfg, T, counts):
     the int8 token rows and their scales, and the int8 intermediate with its scales."""
     P = T * cfg.k
     active = int((counts > 0).sum())
-    blk = cfg.scale_mode in ("block", "fp8")
-    nsw = (2 * cfg.I // 128) * (cfg.H // 128) if blk else 2 * cfg.I
+    w4 = cfg.scale_mode == "w4a8"
+    blk = cfg.scale_mode in ("block", "fp8", "w4a8")
+    nsw = (2 * cfg.I * (cfg.H // 128) if w4 else (2 * cfg.I // 128) * (cfg.H // 128)) if blk else 2 * cfg.I
     nsa = cfg.H // 128 if blk else 1
     nsh = cfg.I // 128 if blk else 1
-    return active * (2 * cfg.I * cfg.H + 4 * nsw) + T * (cfg.H + 4 * nsa) + P * (cfg.I + 4 * nsh)
+    return active * (2 * cfg.I * cfg.H // (2 if w4 else 1) + 4 * nsw) + T * (cfg.H + 4 * nsa) + P * (cfg.I + 4 * nsh)
 
 
 def measured_peaks():
@@ -333,9 +354,11 @@ def cpu_baseline(cfg, ntok):
     w13q, w13s, w2q, w2s = [None] * cfg.E, [None] * cfg.E, [None] * cfg.E, [None] * cfg.E
     hs = torch.cuda.current_stream().cuda_stream
     buf = torch.empty(2 * cfg.I * cfg.H, dtype=torch.float32, device="cuda")
-    fp8 = cfg.scale_mode == "fp8"
+    fp8, w4 = cfg.scale_mode == "fp8", cfg.scale_mode == "w4a8"
 
     def quant(w):
+        if w4:
+            return oracle.w4_quant(w)
         return oracle.fp8_quant_blocks(w, 128, 128) if fp8 else oracle.quant_weight(w, cfg.scale_mode)
 
     for e in experts:
@@ -348,7 +371,9 @@ def cpu_baseline(cfg, ntok):
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     t0 = time.perf_counter()
     ids, tw = oracle.route_cfg(cfg, lg)
-    if fp8:
+    if w4:
+        oracle.w4_moe_tokens(x, ids, tw, w13q, w13s, w2q, w2s, I=cfg.I)
+    elif fp8:
         oracle.fp8_moe_tokens(x, ids, tw, w13q, w13s, w2q, w2s, I=cfg.I)
     else:
         oracle.moe_tokens(x, ids, tw, w13q, w13s, w2q, w2s, I=cfg.I, block=cfg.scale_mode == "block")
@@ -376,7 +401,7 @@ def main():
     import synth
     from w8a8_int8_quantized_quant_amd import workload
 
-    cfg = fp8_block_config() if args.config == "fp8-block" else synth.CONFIGS[args.config]
+    cfg = config_of(args.config)
     print(f"[bench] drawing {cfg.note}", file=sys.stderr, flush=True)
     layer = workload.make_layer(cfg)
     ms, stage_ms, st, counts = measure(layer, args.steps, args.warmup)
@@ -409,8 +434,8 @@ def main():
     configs = None
     if not args.no_configs and args.config == "decode":
         configs = {}
-        for name in ("tiny", "skew", "block", "fp8-block"):
-            oc = fp8_block_config() if name == "fp8-block" else synth.CONFIGS[name]
+        for name in ("tiny", "skew", "block", "fp8-block", "fp8-decode", "w4a8-decode", "w4a8-block"):
+            oc = config_of(name)
             print(f"[bench] drawing {oc.note}", file=sys.stderr, flush=True)
             ol = workload.make_layer(oc)
             oms, ostage, ost, ocounts = measure(ol, max(3, args.steps // 2), args.warmup)
@@ -421,7 +446,7 @@ def main():
                      "hbm_gbs": round(of["hbm_gbs"], 1), "frac_hbm_peak": round(of["frac_hbm_peak"], 4),
                      "active_experts": of["active_experts"], "scale": oc.scale_mode,
                      "stage_ms": {k: round(v, 4) for k, v in ostage.items()}}
-            if name == "fp8-block":  # the same operation count on the FP8 MFMA
+            if oc.scale_mode in ("fp8", "w4a8"):  # the same operation count on the FP8 MFMA
                 for key in ("int8_tops", "frac_int8_peak"):
                     del entry[key]
                 entry["fp8_tflops"] = round(of["int8_tops"], 3)
@@ -466,10 +491,11 @@ def main():
         "metric": METRIC, "value": round(fig["tokens_per_s"], 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp8" if cfg.scale_mode == "fp8" else "int8", "data": "synthetic",
+        "dtype": {"fp8": "fp8", "w4a8": "int4xfp8"}.get(cfg.scale_mode, "int8"), "data": "synthetic",
         "config": {"workload": f"{cfg.note}: hidden {cfg.H}, intermediate {cfg.I}, {cfg.E} experts, top-{cfg.k}, "
-                               + ("128x128 block-wise FP8 (E4M3)" if cfg.scale_mode == "fp8" else
-                                  f"{cfg.scale_mode}-wise W8A8 INT8"), "T": cfg.T, "H": cfg.H, "I": cfg.I, "E": cfg.E,
+                               + {"fp8": "128x128 block-wise FP8 (E4M3)",
+                                  "w4a8": "W4A8 (int4 weights, FP8 activations)"}.get(
+                                      cfg.scale_mode, f"{cfg.scale_mode}-wise W8A8 INT8"), "T": cfg.T, "H": cfg.H, "I": cfg.I, "E": cfg.E,
                    "k": cfg.k, "scale": cfg.scale_mode, "active_experts": fig["active_experts"]},
         "int8_tops": round(fig["int8_tops"], 3), "frac_int8_peak": round(fig["frac_int8_peak"], 4),
         "hbm_gbs": round(fig["hbm_gbs"], 1), "frac_hbm_peak": round(fig["frac_hbm_peak"], 4),

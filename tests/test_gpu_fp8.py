@@ -77,6 +77,8 @@ CFG = {
                            topk_group=2, scaling=2.5),
     # DeepSeek-V3 expert shapes, few experts: several 128-row tiles per expert
     "fp8-dsv3-e8": small_cfg("fp8-dsv3-e8", 62, T=1000, H=7168, I=2048, E=8, k=2),
+    # fewer than 32 rows per expert on average: the 64-row tiles of the few-rows case
+    "fp8-dsv3-e64": small_cfg("fp8-dsv3-e64", 63, T=533, H=7168, I=2048, E=64, k=2),
     # the block-wise workload's shapes and draws in FP8 (T=2048, 256 experts, top-8)
     "fp8-block": dataclasses.replace(synth.CONFIGS["block"], name="fp8-block", scale_mode="fp8"),
     "fp8-decode": dataclasses.replace(synth.CONFIGS["decode"], name="fp8-decode", scale_mode="fp8"),
@@ -408,29 +410,35 @@ def test_fp8_second_gemm_combine(name):
     run_check_w2(name, ids, tw, tokens)
 
 
-EDGE_COUNTS = [0, 1, 17, 128, 129, 650, 330, 745]
+EDGE_COUNTS = {
+    "fp8-dsv3-e8": [0, 1, 17, 128, 129, 650, 330, 745],
+    "fp8-dsv3-e64": [0, 1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 100, 127, 128, 129] + [5] * 49,
+}
 
 
-def test_fp8_tile_edges():
+@pytest.mark.parametrize("name", ["fp8-dsv3-e8", "fp8-dsv3-e64"])
+def test_fp8_tile_edges(name):
     """Both FP8 GEMMs at the DeepSeek-V3 expert shapes with routing whose expert row counts
-    straddle the 128-row tile and 16-row fragment boundaries."""
-    name = "fp8-dsv3-e8"
+    straddle the 128- and 64-row tile and 16-row fragment boundaries (E = 8: 128-row tiles;
+    E = 64, under 32 rows per expert: 64-row tiles)."""
     cfg = CFG[name]
-    flat = np.repeat(np.arange(cfg.E, dtype=np.int32), EDGE_COUNTS)
+    counts = EDGE_COUNTS[name]
+    flat = np.repeat(np.arange(cfg.E, dtype=np.int32), counts)
     T = len(flat) // 2
-    assert T == cfg.T and max(EDGE_COUNTS) <= T
+    assert T == cfg.T and max(counts) <= T
     ids = np.stack([flat[:T], flat[T:]], axis=1)
     assert np.all(ids[:, 0] != ids[:, 1])
     ids = np.ascontiguousarray(ids[np.random.default_rng(41).permutation(T)])
     tw = synth.positive_scales(T * 2, cfg.seed, 0.05, 1.0).reshape(T, 2)
     al, bm, a_q, a_s, gq, gs = run_w13(name, ids)
-    assert list(al["counts"]) == EDGE_COUNTS
+    assert list(al["counts"]) == counts
     rows = set()
-    for e, n in enumerate(EDGE_COUNTS):
+    for e, n in enumerate(counts[:17]):  # every boundary case, and two of the 5-row experts
         r0 = int(al["padded_offsets"][e])
         js = {0, 1, 15, 16, 17, n - 2, n - 1}
-        for m in range(1, n // 128 + 1):
-            js |= {m * 128 - 1, m * 128}
+        for b in (32, 64, 128):
+            for m in range(1, n // b + 1):
+                js |= {m * b - 1, m * b}
         rows |= {r0 + j for j in js if 0 <= j < n}
     rows = np.array(sorted(rows), dtype=np.int64)
     check_w13(name, al, bm, a_q, a_s, gq, gs, rows)

@@ -524,8 +524,8 @@ __device__ __forceinline__ void dma_stage_f8(const int8_t* stage, int8_t* next, 
                                              int wm, int wn, int g, int fr, int rows) {
   constexpr int FM = BM / WM / 16, FN = BN / WN / 16, FNH = FN / 2;
   constexpr int GROUPS = 2 * FM;
-  static_assert(GROUPS >= LD && FN % 2 == 0, "DMA slots");  // DMA c goes out before group (c * GROUPS) / LD
-  constexpr int kScaleOne = 127;                             // E8M0 exponent of 1.0
+  static_assert(FN % 2 == 0, "gate and up fragments");  // DMA c goes out before group (c * GROUPS) / LD
+  constexpr int kScaleOne = 127;                         // E8M0 exponent of 1.0
   const int c0 = fr * kDmaBK + (((2 * g) ^ swz(fr)) << 4);
   const int c1 = fr * kDmaBK + (((2 * g + 1) ^ swz(fr)) << 4);
   auto ld32 = [&](const int8_t* rowbase) {
@@ -587,19 +587,21 @@ __device__ __forceinline__ void dma_stage_w4(const int8_t* stage, int8_t* next, 
   constexpr int FM = BM / WM / 16, FN = BN / WN / 16, FNH = FN / 2;
   constexpr int GROUPS = 2 * FM;
   constexpr int BROW = kDmaBK / 2;  // bytes of one B row in a stage
-  static_assert(GROUPS >= LD && FN % 2 == 0, "DMA slots");
+  static_assert(FN % 2 == 0, "gate and up fragments");  // DMA c goes out before group (c * GROUPS) / LD
   constexpr int kScaleOne = 127;
   const int c0 = fr * kDmaBK + (((2 * g) ^ swz(fr)) << 4);
   const int c1 = fr * kDmaBK + (((2 * g + 1) ^ swz(fr)) << 4);
   i32x8 bf[FN];
+  if (rows > 0) {  // wavefronts whose rows are all past the tile's real rows widen nothing
 #pragma unroll
-  for (int fn = 0; fn < FN; ++fn) {
-    const int j = brow_of<BN, WN, FN, MAP>(wn, fn) + fr;
-    const i32x4 v = *reinterpret_cast<const i32x4*>(stage + BM * kDmaBK + j * BROW + ((g ^ swz4(j)) << 4));
-    int32_t o[8];
+    for (int fn = 0; fn < FN; ++fn) {
+      const int j = brow_of<BN, WN, FN, MAP>(wn, fn) + fr;
+      const i32x4 v = *reinterpret_cast<const i32x4*>(stage + BM * kDmaBK + j * BROW + ((g ^ swz4(j)) << 4));
+      int32_t o[8];
 #pragma unroll
-    for (int d = 0; d < 4; ++d) w4_to_fp8((uint32_t)v[d], o[2 * d], o[2 * d + 1]);
-    bf[fn] = i32x8{o[0], o[1], o[2], o[3], o[4], o[5], o[6], o[7]};
+      for (int d = 0; d < 4; ++d) w4_to_fp8((uint32_t)v[d], o[2 * d], o[2 * d + 1]);
+      bf[fn] = i32x8{o[0], o[1], o[2], o[3], o[4], o[5], o[6], o[7]};
+    }
   }
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm) {
@@ -882,7 +884,8 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_ring_kernel(c
   static_assert(EPI != Epi::I32, "scaled epilogues only");
   static_assert(A_LD >= 1 && B_LD >= 1 && (BM * CPR) % NT == 0 && (BN * CPRB) % NT == 0, "tile shape");
   static_assert(KT >= 1 && LD + 1 < 64, "K steps");
-  static_assert(!kBlock || (NW * 16 == BM && kWave == 16 * SG), "one scale DMA per wavefront: 16 rows x SG blocks");
+  // one scale DMA per wavefront: 16 rows x SG blocks (wavefronts past BM rows bring the first row's)
+  static_assert(!kBlock || (NW * 16 >= BM && kWave == 16 * SG), "scale DMA shape");
   static_assert(!kBlkScales || BN == 256, "two 128-row weight-scale blocks per tile");
   static_assert(MAP == BMap::Plain || FN % 2 == 0, "split tiles need gate and up fragments");
 
@@ -973,8 +976,10 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_ring_kernel(c
 #define W8A8_RSAS(q) (((q) & 1) ? sas1 : sas0)
   __syncthreads();  // sh_pid, sh_ws
   if constexpr (kW4) {
+    if (wrows > 0) {
 #pragma unroll
-    for (int fn = 0; fn < FN; ++fn) wsr[0][fn] = p.w_s[wso[fn]];
+      for (int fn = 0; fn < FN; ++fn) wsr[0][fn] = p.w_s[wso[fn]];
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
@@ -1005,7 +1010,7 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_ring_kernel(c
     const bool more = kt + 2 < KT;
     const bool sdma = kBlock && more && (kt + 2) % SG == 0;  // scale group of stage kt + 2 goes out now
     if constexpr (kW4) {
-      if (kt + 1 < KT) {
+      if (kt + 1 < KT && wrows > 0) {
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) wsr[(kt + 1) & 1][fn] = p.w_s[wso[fn] + (uint32_t)(kt + 1)];
       }
@@ -1243,6 +1248,7 @@ bool use_dma(const GroupedShape& s) {
 // channel-wise the batches between that and kRingMaxAvgRows rows per expert, above which the
 // 320-row tiles of the DMA engine feed the MFMAs with fewer bytes per operation.
 constexpr int kRingBM = 128;
+constexpr int kRingSmallBM = 64;  // FP8 / W4A8 at the DeepSeek-V3 shapes with fewer than 32 rows per expert
 constexpr int kRingH = 7168, kRingI = 2048;
 constexpr int64_t kRingMinAvgRows = 16, kRingMaxAvgRows = 192;
 bool use_ring(const GroupedShape& s, int32_t scale_mode) {
@@ -1258,7 +1264,7 @@ int64_t dma_max_tiles(const GroupedShape& s, int64_t bm = kDmaBM) {
 
 // Tile lists of either DMA engine fit.
 size_t work_bytes(const GroupedShape& s) {
-  return round256(sizeof(int32_t) * (size_t)(1 + kWorkFields * dma_max_tiles(s, kRingBM)));
+  return round256(sizeof(int32_t) * (size_t)(1 + kWorkFields * dma_max_tiles(s, kRingSmallBM)));
 }
 
 // N-tiles of the first GEMM (one row maximum each per row).
@@ -1301,15 +1307,15 @@ hipError_t launch_dma(Params prm, const GroupedShape& s, const int32_t* padded_o
   return hipGetLastError();
 }
 
-template <BMap MAP, Epi EPI, int KT>
+template <BMap MAP, Epi EPI, int KT, int BM = kRingBM>
 hipError_t launch_ring(Params prm, const GroupedShape& s, const int32_t* padded_offsets, int32_t* work,
                             hipStream_t stream) {
   prm.n_tiles = MAP == BMap::Plain ? prm.N / kDmaBN : prm.I / (kDmaBN / 2);
   prm.ksplit = 1;
   hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(kListThreads), 0, stream, prm.sorted, padded_offsets,
-                     (int)s.E, (int32_t)prm.P, kRingBM, work);
-  const int64_t grid = (dma_max_tiles(s, kRingBM) * prm.n_tiles + 7) / 8 * 8;
-  hipLaunchKernelGGL((grouped_gemm_ring_kernel<kRingBM, kDmaBN, kDmaWM, kDmaWN, KT, MAP, EPI>),
+                     (int)s.E, (int32_t)prm.P, BM, work);
+  const int64_t grid = (dma_max_tiles(s, BM) * prm.n_tiles + 7) / 8 * 8;
+  hipLaunchKernelGGL((grouped_gemm_ring_kernel<BM, kDmaBN, kDmaWM, kDmaWN, KT, MAP, EPI>),
                      dim3((uint32_t)grid), dim3(kDmaWM * kDmaWN * kWave), 0, stream, prm, (const int32_t*)work);
   return hipGetLastError();
 }
@@ -1320,6 +1326,12 @@ bool fp8_kt_ok(int64_t kt) { return kt == 1 || kt == 2 || kt == 4 || kt == 8 || 
 template <BMap MAP, Epi EPI>
 hipError_t launch_ring_kt(const Params& prm, const GroupedShape& s, const int32_t* padded_offsets, int32_t* work,
                           hipStream_t stream) {
+  // few rows per expert (decode) at the DeepSeek-V3 shapes: 64-row tiles halve the redundant A stream
+  if (s.H == kRingH && s.I == kRingI && s.T * s.k < 32 * s.E) {
+    if (prm.K / kDmaBK == kRingH / kDmaBK)
+      return launch_ring<MAP, EPI, kRingH / kDmaBK, kRingSmallBM>(prm, s, padded_offsets, work, stream);
+    return launch_ring<MAP, EPI, kRingI / kDmaBK, kRingSmallBM>(prm, s, padded_offsets, work, stream);
+  }
   switch (prm.K / kDmaBK) {
     case 1: return launch_ring<MAP, EPI, 1>(prm, s, padded_offsets, work, stream);
     case 2: return launch_ring<MAP, EPI, 2>(prm, s, padded_offsets, work, stream);
