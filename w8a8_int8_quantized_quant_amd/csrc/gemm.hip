@@ -439,6 +439,20 @@ constexpr int vmcnt_imm() {
 }
 constexpr int kLgkm0Imm = 15 | (7 << 4) | (0 << 8) | (3 << 14);  // lgkmcnt(0) only
 
+// vmcnt(n) for an n that is a constant once the K loop is unrolled (the switch folds away).
+__device__ __forceinline__ void vm_wait(int n) {
+  switch (n) {
+#define W8A8_VMW(i) \
+  case i: __builtin_amdgcn_s_waitcnt(vmcnt_imm<i>()); break;
+    W8A8_VMW(0) W8A8_VMW(1) W8A8_VMW(2) W8A8_VMW(3) W8A8_VMW(4) W8A8_VMW(5) W8A8_VMW(6) W8A8_VMW(7)
+    W8A8_VMW(8) W8A8_VMW(9) W8A8_VMW(10) W8A8_VMW(11) W8A8_VMW(12) W8A8_VMW(13) W8A8_VMW(14) W8A8_VMW(15)
+    W8A8_VMW(16) W8A8_VMW(17) W8A8_VMW(18) W8A8_VMW(19) W8A8_VMW(20) W8A8_VMW(21) W8A8_VMW(22) W8A8_VMW(23)
+    W8A8_VMW(24) W8A8_VMW(25) W8A8_VMW(26) W8A8_VMW(27) W8A8_VMW(28) W8A8_VMW(29) W8A8_VMW(30) W8A8_VMW(31)
+#undef W8A8_VMW
+    default: __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>()); break;
+  }
+}
+
 // Workgroup barrier without a memory fence: LDS data written by the DMA is published by the
 // explicit vmcnt wait that precedes it, and a fence would drain every stage still in flight.
 // The "memory" clobber keeps the compiler from moving LDS accesses across it.
@@ -849,10 +863,10 @@ __device__ __forceinline__ void dma4(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds, 4, 0, 0);
 }
 
-// Ring engine: the DMA engine's tiles and work order with a 3-stage LDS ring (the tile is 128 rows
-// x 256 columns, 48 KB a stage).  Step kt reads stage kt, the DMA of stage kt + 2 goes out between
-// its MFMA groups, and at its end only stage kt + 1 must have landed, so two stages stay in flight
-// at all times.  The K loop (KT steps of 128 bytes, a compile-time count) is fully unrolled: every
+// Ring engine: the DMA engine's tiles and work order with an NS-stage LDS ring (NS = 3 for 8-bit
+// weights: 128 x 256 tiles, 48 KB a stage; deeper for the half-size int4 stages).  Step kt reads
+// stage kt, the DMA of stage kt + NS - 1 goes out between its MFMA groups, and at its end only
+// stage kt + 1 must have landed, so NS - 1 stages stay in flight at all times.  The K loop (KT steps of 128 bytes, a compile-time count) is fully unrolled: every
 // stage index and wait count is known, so the compiler tells the buffer being read from the two
 // being filled, and no loop back edge joins in-flight DMA.
 // Block-wise scales: each step is one 128-wide K-block, whose int32 partials are folded into the
@@ -861,7 +875,7 @@ __device__ __forceinline__ void dma4(const void* g, void* lds) {
 // into one of two buffers), so the data waits cover them; the weight scales of the tile's two
 // 128-row weight blocks (every K-block) are read into LDS once, before the loop.
 // Channel-wise: int32 sums over all of K, then the DMA engine's LDS-staged epilogue.
-template <int BM, int BN, int WM, int WN, int KT, BMap MAP, Epi EPI>
+template <int BM, int BN, int WM, int WN, int KT, BMap MAP, Epi EPI, int NS = 3>
 __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_ring_kernel(const Params p,
                                                                               const int32_t* __restrict__ work) {
   constexpr bool kBlock = is_block<EPI>();
@@ -883,7 +897,10 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_ring_kernel(c
   constexpr int SG = 4;  // K-blocks per activation-scale DMA
   static_assert(EPI != Epi::I32, "scaled epilogues only");
   static_assert(A_LD >= 1 && B_LD >= 1 && (BM * CPR) % NT == 0 && (BN * CPRB) % NT == 0, "tile shape");
-  static_assert(KT >= 1 && LD + 1 < 64, "K steps");
+  static_assert(KT >= 1 && (NS - 2) * (LD + 1) < 32, "K steps");
+  // NS <= 5: the scale group a DMA overwrites was last read before the step that issues it
+  static_assert(NS >= 3 && NS <= 5 && (NS == 3 || kW4), "ring depth");
+  static_assert(!kW4 || (BN * KT) % kWave == 0, "scale table in whole 64-float chunks");
   // one scale DMA per wavefront: 16 rows x SG blocks (wavefronts past BM rows bring the first row's)
   static_assert(!kBlock || (NW * 16 >= BM && kWave == 16 * SG), "scale DMA shape");
   static_assert(!kBlkScales || BN == 256, "two 128-row weight-scale blocks per tile");
@@ -892,9 +909,12 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_ring_kernel(c
   __shared__ __attribute__((aligned(1024))) int8_t st0[STAGE];
   __shared__ __attribute__((aligned(1024))) int8_t st1[STAGE];
   __shared__ __attribute__((aligned(1024))) int8_t st2[STAGE];
+  __shared__ __attribute__((aligned(1024))) int8_t st3[NS > 3 ? STAGE : 1];
+  __shared__ __attribute__((aligned(1024))) int8_t st4[NS > 4 ? STAGE : 1];
   __shared__ __attribute__((aligned(16))) float sas0[kBlock ? NW * kWave : 1];  // activation scales, even groups
   __shared__ __attribute__((aligned(16))) float sas1[kBlock ? NW * kWave : 1];  // odd groups
   __shared__ float sh_ws[kBlkScales ? 2 : 1][kBlkScales ? KT : 1];
+  __shared__ __attribute__((aligned(16))) float sh_wst[kW4 ? BN * KT : 1];  // int4: the tile rows' scales
   __shared__ int32_t sh_pid[BM];
   __shared__ float sh_red[kBlock ? WN : 1][BM];
 
@@ -945,15 +965,7 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_ring_kernel(c
     const int q = (wv * B_LD + c) * kWave + l, j = q / CPRB, kc = (q % CPRB) ^ (kW4 ? swz4(j) : swz(j));
     off[A_LD + c] = (uint32_t)(wrow_of<BN, MAP>(nt, j, p.I) * wrow_bytes + kc * 16);
   }
-  // int4 weights: this lane's weight-scale rows (fragment fn, column l % 16), one scale per K-block,
-  // loaded a step ahead (before the step's DMAs, so the step's closing wait covers them)
-  uint32_t wso[kW4 ? FN : 1];
-  float wsr[2][kW4 ? FN : 1];
-  if constexpr (kW4) {
-#pragma unroll
-    for (int fn = 0; fn < FN; ++fn)
-      wso[fn] = (uint32_t)((e * p.N + wrow_of<BN, MAP>(nt, brow_of<BN, WN, FN, MAP>(wn, fn) + (l & 15), p.I)) * KT);
-  }
+
   // activation-scale DMA: lane l brings row wv * 16 + (l & 15) of K-block group * SG + l / 16
   // (the last K-block again where a group runs past K)
   const uint32_t s_off = kBlock ? (uint32_t)(src_row(wv * 16 + (l & 15)) * KT) : 0u;
@@ -972,18 +984,23 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_ring_kernel(c
     }
   const int wrows = nrows - wm * (BM / WM);
 
-#define W8A8_RSTG(j) ((j) == 0 ? st0 : (j) == 1 ? st1 : st2)
+#define W8A8_RSTG(j) ((j) % NS == 0 ? st0 : (j) % NS == 1 ? st1 : (j) % NS == 2 ? st2 : (j) % NS == 3 ? st3 : st4)
+  // VMEM operations that stage st brings: its DMAs, and with every SG-th stage its scale group
+  auto stage_ops = [&](int st) { return st < KT ? LD + ((kBlock && st % SG == 0) ? 1 : 0) : 0; };
 #define W8A8_RSAS(q) (((q) & 1) ? sas1 : sas0)
   __syncthreads();  // sh_pid, sh_ws
   if constexpr (kW4) {
-    if (wrows > 0) {
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn) wsr[0][fn] = p.w_s[wso[fn]];
+    // int4 weights: the scales of the tile's BN weight rows for every K-block ([BN][KT], one per
+    // (row, K-block)) go to LDS by DMA ahead of the first stage, so the prologue wait covers them;
+    // chunk c of 64 floats is table entries 64 c .. 64 c + 63
+    for (int c = wv; c < (BN * KT) / kWave; c += NW) {
+      const int f = c * kWave + l, j = f / KT;
+      dma4(p.w_s + ((e * p.N + wrow_of<BN, MAP>(nt, j, p.I)) * KT + (f - j * KT)), sh_wst + c * kWave);
     }
-    __builtin_amdgcn_sched_barrier(0);
   }
+  constexpr int PRE = KT < NS - 1 ? KT : NS - 1;  // stages loaded before the loop
 #pragma unroll
-  for (int st = 0; st < (KT < 2 ? KT : 2); ++st) {
+  for (int st = 0; st < PRE; ++st) {
 #pragma unroll
     for (int c = 0; c < LD; ++c) {
       if (c < A_LD)
@@ -991,41 +1008,36 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_ring_kernel(c
       else
         dma16_nt(wexp + (off[c] + (uint32_t)(st * BKB)), W8A8_RSTG(st) + b_dst + (c - A_LD) * 1024);
     }
-    if (kBlock && st == 0) dma4(p.a_s + (s_off + s_blk(0)), sas0 + wv * kWave);
+    if (kBlock && st % SG == 0) dma4(p.a_s + (s_off + s_blk(st / SG)), W8A8_RSAS(st / SG) + wv * kWave);
   }
-  // stage 0 (and the first scale group) landed
-  if constexpr (KT >= 2)
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm<LD>());
-  else
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
+  {  // stage 0 (and the first scale group) landed: only stages 1 .. PRE - 1 may be outstanding
+    int later = 0;
+#pragma unroll
+    for (int st = 1; st < PRE; ++st) later += stage_ops(st);
+    vm_wait(later);
+  }
 
   // Uniform bases of the stage two steps ahead, advanced one step at a time; the empty asm keeps
   // the compiler from precomputing every step's address up front.
-  const int8_t* a_next = p.a + 2 * kDmaBK;
-  const int8_t* b_next = wexp + 2 * BKB;
+  const int8_t* a_next = p.a + (NS - 1) * kDmaBK;
+  const int8_t* b_next = wexp + (NS - 1) * BKB;
 #pragma clang loop unroll(full)
   for (int kt = 0; kt < KT; ++kt) {
     __builtin_amdgcn_s_waitcnt(kLgkm0Imm);
     barrier_no_fence();
-    const bool more = kt + 2 < KT;
-    const bool sdma = kBlock && more && (kt + 2) % SG == 0;  // scale group of stage kt + 2 goes out now
-    if constexpr (kW4) {
-      if (kt + 1 < KT && wrows > 0) {
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn) wsr[(kt + 1) & 1][fn] = p.w_s[wso[fn] + (uint32_t)(kt + 1)];
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if (sdma) dma4(p.a_s + (s_off + s_blk((kt + 2) / SG)), W8A8_RSAS((kt + 2) / SG) + wv * kWave);
+    const int nxt = kt + NS - 1;  // the stage whose DMA goes out in this step
+    const bool more = nxt < KT;
+    const bool sdma = kBlock && more && nxt % SG == 0;  // with its scale group
+    if (sdma) dma4(p.a_s + (s_off + s_blk(nxt / SG)), W8A8_RSAS(nxt / SG) + wv * kWave);
     if constexpr (kW4)
-      dma_stage_w4<BM, BN, WM, WN, A_LD, LD, MAP>(W8A8_RSTG(kt % 3), W8A8_RSTG((kt + 2) % 3), a_next, b_next, off,
-                                                  a_dst, b_dst, 0u, more, acc, wm, wn, g, fr, wrows);
+      dma_stage_w4<BM, BN, WM, WN, A_LD, LD, MAP>(W8A8_RSTG(kt), W8A8_RSTG(nxt), a_next, b_next, off, a_dst, b_dst,
+                                                  0u, more, acc, wm, wn, g, fr, wrows);
     else if constexpr (kFp8)
-      dma_stage_f8<BM, BN, WM, WN, A_LD, LD, MAP>(W8A8_RSTG(kt % 3), W8A8_RSTG((kt + 2) % 3), a_next, b_next, off,
-                                                  a_dst, b_dst, 0u, more, acc, wm, wn, g, fr, wrows);
+      dma_stage_f8<BM, BN, WM, WN, A_LD, LD, MAP>(W8A8_RSTG(kt), W8A8_RSTG(nxt), a_next, b_next, off, a_dst, b_dst,
+                                                  0u, more, acc, wm, wn, g, fr, wrows);
     else
-      dma_stage<BM, BN, WM, WN, A_LD, LD, MAP>(W8A8_RSTG(kt % 3), W8A8_RSTG((kt + 2) % 3), a_next, b_next, off, a_dst,
-                                               b_dst, 0u, more, acc, wm, wn, g, fr, wrows);
+      dma_stage<BM, BN, WM, WN, A_LD, LD, MAP>(W8A8_RSTG(kt), W8A8_RSTG(nxt), a_next, b_next, off, a_dst, b_dst, 0u,
+                                               more, acc, wm, wn, g, fr, wrows);
     a_next += kDmaBK;
     b_next += BKB;
     asm volatile("" : "+s"(a_next), "+s"(b_next));
@@ -1041,7 +1053,7 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_ring_kernel(c
         }
         if constexpr (kW4) {
 #pragma unroll
-          for (int fn = 0; fn < FN; ++fn) ws[fn] = wsr[kt & 1][fn];
+          for (int fn = 0; fn < FN; ++fn) ws[fn] = sh_wst[(brow_of<BN, WN, FN, MAP>(wn, fn) + (l & 15)) * KT + kt];
         } else {
           const float w0 = sh_ws[0][kt], w1 = sh_ws[1][kt];
 #pragma unroll
@@ -1050,12 +1062,12 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_ring_kernel(c
         block_flush<FM, FN, AccT>(acc, accf, as, ws);
       }
     }
-    if (sdma)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm<LD + 1>());
-    else if (more)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm<LD>());
-    else
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
+    {  // stage kt + 1 landed: only the stages after it may be outstanding
+      int later = 0;
+#pragma unroll
+      for (int st = kt + 2; st < kt + NS; ++st) later += stage_ops(st);
+      vm_wait(later);
+    }
   }
 #undef W8A8_RSAS
 #undef W8A8_RSTG
@@ -1310,12 +1322,13 @@ hipError_t launch_dma(Params prm, const GroupedShape& s, const int32_t* padded_o
 template <BMap MAP, Epi EPI, int KT, int BM = kRingBM>
 hipError_t launch_ring(Params prm, const GroupedShape& s, const int32_t* padded_offsets, int32_t* work,
                             hipStream_t stream) {
+  constexpr int NS = 3;
   prm.n_tiles = MAP == BMap::Plain ? prm.N / kDmaBN : prm.I / (kDmaBN / 2);
   prm.ksplit = 1;
   hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(kListThreads), 0, stream, prm.sorted, padded_offsets,
                      (int)s.E, (int32_t)prm.P, BM, work);
   const int64_t grid = (dma_max_tiles(s, BM) * prm.n_tiles + 7) / 8 * 8;
-  hipLaunchKernelGGL((grouped_gemm_ring_kernel<BM, kDmaBN, kDmaWM, kDmaWN, KT, MAP, EPI>),
+  hipLaunchKernelGGL((grouped_gemm_ring_kernel<BM, kDmaBN, kDmaWM, kDmaWN, KT, MAP, EPI, NS>),
                      dim3((uint32_t)grid), dim3(kDmaWM * kDmaWN * kWave), 0, stream, prm, (const int32_t*)work);
   return hipGetLastError();
 }
