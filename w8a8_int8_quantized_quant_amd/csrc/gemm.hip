@@ -129,15 +129,18 @@ __device__ __forceinline__ void block_scales(const Params& p, const int32_t* sh_
 
 // Block-wise: fold the int32 partials of one K-block into the fp32 sums, in the written order
 // acc_f = acc_f + (((float)part * a_s) * w_s), and clear them.
+// Fragment rows at or past `rows` (the wavefront's real rows) hold zero partials and are skipped.
 template <int FM, int FN, typename AccT>
 __device__ __forceinline__ void block_flush(AccT (&acc)[FM][FN], float (&accf)[FM][FN][4], const float (&as)[FM][4],
-                                            const float (&ws)[FN]) {
+                                            const float (&ws)[FN], int rows = 1 << 30) {
 #pragma unroll
-  for (int fm = 0; fm < FM; ++fm)
+  for (int fm = 0; fm < FM; ++fm) {
+    if (fm * 16 >= rows) continue;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) accf[fm][fn][r] = accf[fm][fn][r] + (((float)acc[fm][fn][r] * as[fm][r]) * ws[fn]);
+  }
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
@@ -552,7 +555,8 @@ __device__ __forceinline__ void dma_stage_f8(const int8_t* stage, int8_t* next, 
   for (int fn = 0; fn < FN; ++fn) bf[fn] = ld32(stage + BM * kDmaBK + brow_of<BN, WN, FN, MAP>(wn, fn) * kDmaBK);
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm) {
-    const i32x8 af = ld32(stage + (wm * FM + fm) * 16 * kDmaBK);
+    i32x8 af;
+    if (fm * 16 < rows) af = ld32(stage + (wm * FM + fm) * 16 * kDmaBK);  // rows past the real ones: no read
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int grp = fm * 2 + h;
@@ -619,10 +623,13 @@ __device__ __forceinline__ void dma_stage_w4(const int8_t* stage, int8_t* next, 
   }
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm) {
-    const int8_t* arow = stage + (wm * FM + fm) * 16 * kDmaBK;
-    const i32x4 lo = *reinterpret_cast<const i32x4*>(arow + c0);
-    const i32x4 hi = *reinterpret_cast<const i32x4*>(arow + c1);
-    const i32x8 af = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    i32x8 af;
+    if (fm * 16 < rows) {  // rows past the real ones: no read
+      const int8_t* arow = stage + (wm * FM + fm) * 16 * kDmaBK;
+      const i32x4 lo = *reinterpret_cast<const i32x4*>(arow + c0);
+      const i32x4 hi = *reinterpret_cast<const i32x4*>(arow + c1);
+      af = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int grp = fm * 2 + h;
@@ -1059,7 +1066,7 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_ring_kernel(c
 #pragma unroll
           for (int fn = 0; fn < FN; ++fn) ws[fn] = brow_of<BN, WN, FN, MAP>(wn, fn) >= 128 ? w1 : w0;
         }
-        block_flush<FM, FN, AccT>(acc, accf, as, ws);
+        block_flush<FM, FN, AccT>(acc, accf, as, ws, wrows);
       }
     }
     {  // stage kt + 1 landed: only the stages after it may be outstanding
@@ -1328,8 +1335,11 @@ hipError_t launch_ring(Params prm, const GroupedShape& s, const int32_t* padded_
   hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(kListThreads), 0, stream, prm.sorted, padded_offsets,
                      (int)s.E, (int32_t)prm.P, BM, work);
   const int64_t grid = (dma_max_tiles(s, BM) * prm.n_tiles + 7) / 8 * 8;
-  hipLaunchKernelGGL((grouped_gemm_ring_kernel<BM, kDmaBN, kDmaWM, kDmaWN, KT, MAP, EPI, NS>),
-                     dim3((uint32_t)grid), dim3(kDmaWM * kDmaWN * kWave), 0, stream, prm, (const int32_t*)work);
+  // 64-row tiles: all 8 wavefronts side by side along N (64 x 32 each), so at a handful of rows
+  // per expert every wavefront has rows and the per-step widening and folding is split 8 ways
+  constexpr int WM = BM == kRingSmallBM ? 1 : kDmaWM, WN = BM == kRingSmallBM ? 8 : kDmaWN;
+  hipLaunchKernelGGL((grouped_gemm_ring_kernel<BM, kDmaBN, WM, WN, KT, MAP, EPI, NS>), dim3((uint32_t)grid),
+                     dim3(WM * WN * kWave), 0, stream, prm, (const int32_t*)work);
   return hipGetLastError();
 }
 
