@@ -64,6 +64,8 @@ CFG = {
     "w4-dsv3-e8": small_cfg("w4-dsv3-e8", 82, T=1000, H=7168, I=2048, E=8, k=2),
     # fewer than 32 rows per expert on average: the 64-row tiles of the few-rows case
     "w4-dsv3-e64": small_cfg("w4-dsv3-e64", 83, T=533, H=7168, I=2048, E=64, k=2),
+    # fewer than 16 rows per expert on average: the 16-row tiles of the streaming engine
+    "w4-dsv3-e64s": small_cfg("w4-dsv3-e64s", 84, T=251, H=7168, I=2048, E=64, k=2),
     "w4-decode": dataclasses.replace(synth.CONFIGS["decode"], name="w4-decode", scale_mode="w4a8"),
     "w4-block": dataclasses.replace(synth.CONFIGS["block"], name="w4-block", scale_mode="w4a8"),
 }
@@ -291,14 +293,16 @@ def test_w4_second_gemm_combine(name):
 EDGE_COUNTS = {
     "w4-dsv3-e8": [0, 1, 17, 128, 129, 650, 330, 745],
     "w4-dsv3-e64": [0, 1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 100, 127, 128, 129] + [5] * 49,
+    "w4-dsv3-e64s": [0, 1, 15, 16, 17, 31, 32, 33, 47, 48, 49] + [4] * 52 + [5],
 }
 
 
-@pytest.mark.parametrize("name", ["w4-dsv3-e8", "w4-dsv3-e64"])
+@pytest.mark.parametrize("name", ["w4-dsv3-e8", "w4-dsv3-e64", "w4-dsv3-e64s"])
 def test_w4_tile_edges(name):
     """Both W4A8 GEMMs at the DeepSeek-V3 expert shapes with expert row counts straddling the
     128- and 64-row tile and 16-row fragment boundaries (E = 8: 128-row tiles; E = 64, under 32
-    rows per expert: 64-row tiles)."""
+    rows per expert: 64-row tiles; E = 64, under 16 rows per expert: the streaming engine's
+    16-row tiles)."""
     cfg = CFG[name]
     counts = EDGE_COUNTS[name]
     flat = np.repeat(np.arange(cfg.E, dtype=np.int32), counts)
@@ -314,7 +318,7 @@ def test_w4_tile_edges(name):
     for e, n in enumerate(counts[:17]):  # every boundary case, and two of the 5-row experts
         r0 = int(al["padded_offsets"][e])
         js = {0, 1, 15, 16, 17, n - 2, n - 1}
-        for b in (32, 64, 128):
+        for b in (16, 32, 64, 128):
             for m in range(1, n // b + 1):
                 js |= {m * b - 1, m * b}
         rows |= {r0 + j for j in js if 0 <= j < n}

@@ -1085,6 +1085,134 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_ring_kernel(c
     dma_epilogue<BM, BN, WM, WN, STAGE, MAP, EPI>(p, acc, sh_pid, st0, st1, row0, nt, e, wm, wn, wv, l, 0);
 }
 
+// Streaming engine for packed int4 weights when experts hold few rows (decode): tiles of 16 rows
+// x 256 weight rows on four wavefronts that share nothing until the epilogue.  Wavefront wn owns
+// 64 weight rows (FN = 4 fragments); for each 128-wide K-block lane (g, fr) loads the 16 bytes
+// (32 int4 values, K values 32 g .. 32 g + 31 of the block) of weight row fr of each fragment
+// straight into registers with the non-temporal policy, widens them to E4M3 codes, and takes the
+// matching 32 activation codes of tile row fr from the (L1/L2-resident) activation rows.  PD
+// K-blocks are in flight ahead of the one being multiplied, so a wavefront always has 8 KB of
+// weights on the way and no barrier or LDS round trip sits between a load and its MFMA.
+// Scales: lane (g, fr) holds four consecutive K-blocks (4 g .. 4 g + 3 of a 16-block window) of
+// the weight scale of row fr of each fragment and of the activation scale of tile row fr; each
+// K-block's values are fetched from the owning lane by a cross-lane read (ds_bpermute).  Each
+// K-block's FP8 MFMA sum starts from zero and is folded into the fp32 sums as
+// acc + ((part * a_s) * w_s), in ascending K-block order.
+constexpr int kStreamBM = 16, kStreamBN = 256, kStreamWN = 4;
+template <int KT, BMap MAP, Epi EPI>
+__global__ __launch_bounds__(kStreamWN * kWave) void grouped_gemm_w4_stream_kernel(const Params p,
+                                                                                  const int32_t* __restrict__ work) {
+  static_assert(is_w4<EPI>(), "packed int4 weights");
+  constexpr int BM = kStreamBM, BN = kStreamBN, WN = kStreamWN;
+  constexpr int FN = BN / WN / 16, FNH = FN / 2;
+  constexpr int PD = 2, NB = PD + 1;  // K-blocks in flight ahead of the current one; register slots
+  constexpr int WIN = 16;             // K-blocks per scale window (four per lane group)
+  constexpr int NWIN = (KT + WIN - 1) / WIN;
+  constexpr int kScaleOne = 127;
+  static_assert(KT >= 1 && (MAP == BMap::Plain || FN % 2 == 0), "shape");
+  __shared__ int32_t sh_pid[BM];
+  __shared__ float sh_red[WN][BM];
+
+  const int64_t total = (int64_t)work[0] * p.n_tiles;
+  const int64_t per = (total + 7) / 8;
+  const int64_t v = blockIdx.x;
+  if (v >= 8 * per) return;
+  // consecutive items on one XCD (workgroups are dealt round-robin over the 8 XCDs), so the row
+  // tiles of one expert that read the same weight rows meet in that XCD's L2
+  const int64_t logical = (v % 8) * per + v / 8;
+  if (logical >= total) return;
+  const int64_t ti = logical / p.n_tiles, nt = logical % p.n_tiles;
+  const int64_t e = work[1 + kWorkFields * ti];
+  const int64_t row0 = work[2 + kWorkFields * ti];
+  const int nrows = work[3 + kWorkFields * ti];
+  const int64_t KB = p.K / 2;  // bytes of one packed weight row
+  const int8_t* wexp = p.w + e * p.N * KB;
+
+  const int tid = threadIdx.x, l = lane_id();
+  const int wn = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int g = l >> 4, fr = l & 15;
+  for (int i = tid; i < BM; i += WN * kWave) sh_pid[i] = i < nrows ? p.sorted[row0 + i] : (int32_t)p.P;
+
+  // tile row fr (rows past the real ones read the first row: finite values, never stored)
+  const int64_t rr = fr < nrows ? fr : 0;
+  const int64_t arow = p.gather ? (int64_t)(p.sorted[row0 + rr] / p.k) : row0 + rr;
+  const int8_t* a_src = p.a + arow * p.K + g * 32;
+  const float* as_src = p.a_s + arow * KT;
+  const int8_t* b_src[FN];
+  const float* ws_src[FN];
+#pragma unroll
+  for (int fn = 0; fn < FN; ++fn) {
+    const int64_t wrow = wrow_of<BN, MAP>(nt, brow_of<BN, WN, FN, MAP>(wn, fn) + fr, p.I);
+    b_src[fn] = wexp + wrow * KB + g * 16;
+    ws_src[fn] = p.w_s + (e * p.N + wrow) * KT;
+  }
+
+  i32x4 bq[NB][FN], aq[NB][2];
+  auto load = [&](int kb, int slot) {
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+      bq[slot][fn] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(b_src[fn] + kb * (kDmaBK / 2)));
+    aq[slot][0] = *reinterpret_cast<const i32x4*>(a_src + kb * kDmaBK);
+    aq[slot][1] = *reinterpret_cast<const i32x4*>(a_src + kb * kDmaBK + 16);
+  };
+  float wsw[2][FN][4], asw[2][4];
+  auto load_scales = [&](int w, int set) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int kb = min(w * WIN + 4 * g + i, KT - 1);
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) wsw[set][fn][i] = ws_src[fn][kb];
+      asw[set][i] = as_src[kb];
+    }
+  };
+
+  float accf[1][FN][4];
+#pragma unroll
+  for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) accf[0][fn][r] = 0.0f;
+
+#pragma unroll
+  for (int s = 0; s < PD; ++s)
+    if (s < KT) load(s, s);
+  load_scales(0, 0);
+#pragma clang loop unroll(full)
+  for (int kb = 0; kb < KT; ++kb) {
+    if (kb + PD < KT) load(kb + PD, (kb + PD) % NB);
+    if (kb % WIN == 0 && kb / WIN + 1 < NWIN) load_scales(kb / WIN + 1, (kb / WIN + 1) & 1);
+    const int slot = kb % NB, set = (kb / WIN) & 1;
+    const int src = ((kb % WIN) / 4) * 16;  // lane group holding this K-block's scales
+    i32x8 bf[FN];
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+      int32_t o[8];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) w4_to_fp8((uint32_t)bq[slot][fn][d], o[2 * d], o[2 * d + 1]);
+      bf[fn] = i32x8{o[0], o[1], o[2], o[3], o[4], o[5], o[6], o[7]};
+    }
+    const i32x8 af = i32x8{aq[slot][0][0], aq[slot][0][1], aq[slot][0][2], aq[slot][0][3],
+                           aq[slot][1][0], aq[slot][1][1], aq[slot][1][2], aq[slot][1][3]};
+    f32x4 part[FN];
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+      part[fn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[fn], f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0,
+                                                                  0, kScaleOne, 0, kScaleOne);
+    float as[4], ws[FN];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) as[r] = __shfl(asw[set][kb % 4], src + g * 4 + r, kWave);
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) ws[fn] = __shfl(wsw[set][fn][kb % 4], src + fr, kWave);
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) accf[0][fn][r] = accf[0][fn][r] + ((part[fn][r] * as[r]) * ws[fn]);
+  }
+  (void)FNH;
+  i32x4 unused[1][FN] = {};  // the block-wise epilogues read only the fp32 sums
+  __syncthreads();  // sh_pid
+  epilogue<BM, BN, 1, WN, 1, FN, MAP, EPI>(p, unused, accf, sh_pid, sh_red, row0, nt, e, 0, wn, l, tid);
+}
+
 // Work list of the DMA engine: per expert, tiles of up to bmk real rows of its sorted segment.
 // work[0] = number of tiles; tile i = (expert, first sorted row, rows, index of the expert's
 // first tile, number of the expert's tiles) at work[1 + kWorkFields * i].
@@ -1281,9 +1409,9 @@ int64_t dma_max_tiles(const GroupedShape& s, int64_t bm = kDmaBM) {
   return (P + bm - 1) / bm + std::min<int64_t>(s.E, P);
 }
 
-// Tile lists of either DMA engine fit.
+// Tile lists of every work-list engine fit (the streaming engine's 16-row tiles are the most).
 size_t work_bytes(const GroupedShape& s) {
-  return round256(sizeof(int32_t) * (size_t)(1 + kWorkFields * dma_max_tiles(s, kRingSmallBM)));
+  return round256(sizeof(int32_t) * (size_t)(1 + kWorkFields * dma_max_tiles(s, kStreamBM)));
 }
 
 // N-tiles of the first GEMM (one row maximum each per row).
@@ -1343,12 +1471,41 @@ hipError_t launch_ring(Params prm, const GroupedShape& s, const int32_t* padded_
   return hipGetLastError();
 }
 
-// FP8 and W4A8 operands always take the ring engine; K sizes with an instantiated kernel (K / 128).
+// FP8 and W4A8 operands take the ring engine, W4A8 with fewer than kStreamMaxAvgRows rows per
+// expert on average the streaming engine; K sizes with an instantiated kernel (K / 128).
 bool fp8_kt_ok(int64_t kt) { return kt == 1 || kt == 2 || kt == 4 || kt == 8 || kt == 16 || kt == 32 || kt == 56; }
+constexpr int64_t kStreamMaxAvgRows = 16;
+
+template <BMap MAP, Epi EPI, int KT>
+hipError_t launch_w4_stream(Params prm, const GroupedShape& s, const int32_t* padded_offsets, int32_t* work,
+                            hipStream_t stream) {
+  prm.n_tiles = MAP == BMap::Plain ? prm.N / kStreamBN : prm.I / (kStreamBN / 2);
+  prm.ksplit = 1;
+  hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(kListThreads), 0, stream, prm.sorted, padded_offsets,
+                     (int)s.E, (int32_t)prm.P, kStreamBM, work);
+  const int64_t grid = (dma_max_tiles(s, kStreamBM) * prm.n_tiles + 7) / 8 * 8;
+  hipLaunchKernelGGL((grouped_gemm_w4_stream_kernel<KT, MAP, EPI>), dim3((uint32_t)grid), dim3(kStreamWN * kWave), 0,
+                     stream, prm, (const int32_t*)work);
+  return hipGetLastError();
+}
 
 template <BMap MAP, Epi EPI>
 hipError_t launch_ring_kt(const Params& prm, const GroupedShape& s, const int32_t* padded_offsets, int32_t* work,
                           hipStream_t stream) {
+  if constexpr (is_w4<EPI>()) {
+    if (s.T * s.k < kStreamMaxAvgRows * s.E) {
+      switch (prm.K / kDmaBK) {
+        case 1: return launch_w4_stream<MAP, EPI, 1>(prm, s, padded_offsets, work, stream);
+        case 2: return launch_w4_stream<MAP, EPI, 2>(prm, s, padded_offsets, work, stream);
+        case 4: return launch_w4_stream<MAP, EPI, 4>(prm, s, padded_offsets, work, stream);
+        case 8: return launch_w4_stream<MAP, EPI, 8>(prm, s, padded_offsets, work, stream);
+        case 16: return launch_w4_stream<MAP, EPI, 16>(prm, s, padded_offsets, work, stream);
+        case 32: return launch_w4_stream<MAP, EPI, 32>(prm, s, padded_offsets, work, stream);
+        case 56: return launch_w4_stream<MAP, EPI, 56>(prm, s, padded_offsets, work, stream);
+        default: return hipErrorInvalidValue;
+      }
+    }
+  }
   // few rows per expert (decode) at the DeepSeek-V3 shapes: 64-row tiles halve the redundant A stream
   if (s.H == kRingH && s.I == kRingI && s.T * s.k < 32 * s.E) {
     if (prm.K / kDmaBK == kRingH / kDmaBK)
