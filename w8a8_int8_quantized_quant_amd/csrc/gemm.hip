@@ -1207,6 +1207,13 @@ __global__ __launch_bounds__(kStreamWN * kWave) void grouped_gemm_w4_stream_kern
 #pragma unroll
       for (int r = 0; r < 4; ++r) accf[0][fn][r] = accf[0][fn][r] + ((part[fn][r] * as[r]) * ws[fn]);
   }
+  // The down GEMM's epilogue reads the sums only inside per-row conditional stores; this empty
+  // asm takes them as operands after the loop, so the compiler cannot sink every fold into those
+  // stores (keeping all K-blocks' partial sums live to the end), while the loop itself stays one
+  // scheduling region.
+#pragma unroll
+  for (int fn = 0; fn < FN; ++fn)
+    asm volatile("" : "+v"(accf[0][fn][0]), "+v"(accf[0][fn][1]), "+v"(accf[0][fn][2]), "+v"(accf[0][fn][3]));
   (void)FNH;
   i32x4 unused[1][FN] = {};  // the block-wise epilogues read only the fp32 sums
   __syncthreads();  // sh_pid
