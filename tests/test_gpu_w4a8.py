@@ -66,10 +66,14 @@ CFG = {
     "w4-dsv3-e64": small_cfg("w4-dsv3-e64", 83, T=533, H=7168, I=2048, E=64, k=2),
     # fewer than 16 rows per expert on average: the 16-row tiles of the streaming engine
     "w4-dsv3-e64s": small_cfg("w4-dsv3-e64s", 84, T=251, H=7168, I=2048, E=64, k=2),
+    # the streaming engine's K loops at K / 128 = 4, 8, 16 and 32 (16-row tiles, few rows per expert)
+    "w4-s4": small_cfg("w4-s4", 85, T=100, H=512, I=2048, E=16, k=2),
+    "w4-s32": small_cfg("w4-s32", 86, T=100, H=4096, I=1024, E=16, k=2, route="sigmoid", n_group=4,
+                        topk_group=2, scaling=2.5),
     "w4-decode": dataclasses.replace(synth.CONFIGS["decode"], name="w4-decode", scale_mode="w4a8"),
     "w4-block": dataclasses.replace(synth.CONFIGS["block"], name="w4-block", scale_mode="w4a8"),
 }
-SMALL = ("w4-tiny", "w4-small")
+SMALL = ("w4-tiny", "w4-small", "w4-s4", "w4-s32")
 
 
 def dt(a):
@@ -244,7 +248,7 @@ def w13_rows(al, bm, P, name):
     return rows
 
 
-@pytest.mark.parametrize("name", ["w4-tiny", "w4-small", "w4-block"])
+@pytest.mark.parametrize("name", ["w4-tiny", "w4-small", "w4-s4", "w4-s32", "w4-block"])
 def test_w4_first_gemm_silu_requant(name):
     cfg = CFG[name]
     ids, _ = oracle.route_cfg(cfg, synth.logits(cfg))
@@ -282,7 +286,7 @@ def run_check_w2(name, ids, tw, tokens):
     assert np.all(err <= tol * B)
 
 
-@pytest.mark.parametrize("name", ["w4-tiny", "w4-small", "w4-block"])
+@pytest.mark.parametrize("name", ["w4-tiny", "w4-small", "w4-s4", "w4-s32", "w4-block"])
 def test_w4_second_gemm_combine(name):
     cfg = CFG[name]
     ids, tw = oracle.route_cfg(cfg, synth.logits(cfg))
@@ -330,7 +334,7 @@ def test_w4_tile_edges(name):
 
 # ------------------------------------------------------------------ the whole layer
 
-@pytest.mark.parametrize("name", ["w4-tiny", "w4-small", "w4-decode", "w4-block"])
+@pytest.mark.parametrize("name", ["w4-tiny", "w4-small", "w4-s4", "w4-s32", "w4-decode", "w4-block"])
 def test_w4_forward_matches_oracle(name):
     cfg = CFG[name]
     say(f"[w4 forward] {name}")
