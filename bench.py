@@ -378,7 +378,13 @@ def cpu_baseline(cfg, ntok):
     else:
         oracle.moe_tokens(x, ids, tw, w13q, w13s, w2q, w2s, I=cfg.I, block=cfg.scale_mode == "block")
     dt = time.perf_counter() - t0
-    return {"value": ntok / dt, "unit": "tokens/s", "cores": min(threads, ntok), "kind": "oracle",
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), model)
+    except OSError:
+        pass
+    return {"value": ntok / dt, "unit": "tokens/s", "cores": min(threads, ntok), "kind": "oracle", "cpu_model": model,
             "sample": f"first {ntok} of the {cfg.T} tokens of the same layer (routing + dense per-token "
                       f"quantized MoE over {len(experts)} experts, OpenMP over tokens), {dt:.2f} s wall, "
                       f"host has {os.cpu_count()} logical CPUs"}
