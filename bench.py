@@ -166,6 +166,31 @@ def config_of(name):
     return synth.CONFIGS[name]
 
 
+def measure_graph(st, steps, warmup):
+    """The same step captured once into a HIP graph (the five stages' kernels, no host work) and
+    replayed: wall time per replay, synchronised on both sides."""
+    import torch
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        st.step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        st.step()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    del g
+    return (t1 - t0) * 1000.0 / steps
+
+
 def measure(layer, steps, warmup):
     """Whole-step wall time (synchronised on both sides) and per-stage event times."""
     import torch
@@ -413,6 +438,8 @@ def main():
     ms, stage_ms, st, counts = measure(layer, args.steps, args.warmup)
     fig = layer_figures(cfg, cfg.T, ms, counts)
     print(f"[bench] {cfg.name}: {ms:.3f} ms/step, stages {stage_ms}", file=sys.stderr, flush=True)
+    graph_ms = measure_graph(st, args.steps, args.warmup)
+    print(f"[bench] {cfg.name}: {graph_ms:.3f} ms/step replayed from a HIP graph", file=sys.stderr, flush=True)
     w13_bytes = w13_algorithmic_bytes(cfg, cfg.T, counts)
     achieved = w13_bytes / (stage_ms["w13"] / 1000.0) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -506,6 +533,8 @@ def main():
         "int8_tops": round(fig["int8_tops"], 3), "frac_int8_peak": round(fig["frac_int8_peak"], 4),
         "hbm_gbs": round(fig["hbm_gbs"], 1), "frac_hbm_peak": round(fig["frac_hbm_peak"], 4),
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "graph": {"ms_per_step": round(graph_ms, 4), "tokens_per_s": round(cfg.T / (graph_ms / 1000.0), 1),
+                  "note": "the same step captured once into a HIP graph and replayed (value: eager launches)"},
         "roofline": roofline, "prefill": prefill, "configs": configs, "linear": linear, "peaks_measured": peaks,
         "cpu_baseline": cpu,
     }
