@@ -106,6 +106,24 @@ __device__ __forceinline__ int64_t wrow_of(int64_t nt, int br, int64_t I) {
   return br < BN / 2 ? nt * (BN / 2) + br : I + nt * (BN / 2) + (br - BN / 2);
 }
 
+// Tile row block (16 rows) of fragment row fm of wavefront row wm: the FM fragment rows of a
+// wavefront row one after another (contiguous bands), or interleaved, fragment fm of wavefront row
+// wm at block fm * WM + wm, so that a tile holding fewer real rows than BM still gives every
+// wavefront row a share of them.
+template <int WM, int FM, bool ILV>
+__device__ __forceinline__ int rblk(int wm, int fm) {
+  return ILV ? fm * WM + wm : wm * FM + fm;
+}
+// Fragment rows (bit fm) of wavefront row wm that hold real rows of a tile with nrows of them.
+template <int WM, int FM, bool ILV>
+__device__ __forceinline__ uint32_t real_frags(int wm, int nrows) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm)
+    if (rblk<WM, FM, ILV>(wm, fm) * 16 < nrows) m |= 1u << fm;
+  return m;
+}
+
 // Block-wise scales of K-block kb for this lane's accumulators: the activation (or intermediate)
 // scale of each of its rows (sh_arow: the row's index into the scale matrix, -1 past the real
 // rows) and the weight scale of each of its fragments' 128-row weight block.
@@ -129,13 +147,13 @@ __device__ __forceinline__ void block_scales(const Params& p, const int32_t* sh_
 
 // Block-wise: fold the int32 partials of one K-block into the fp32 sums, in the written order
 // acc_f = acc_f + (((float)part * a_s) * w_s), and clear them.
-// Fragment rows at or past `rows` (the wavefront's real rows) hold zero partials and are skipped.
+// Fragment rows outside `fmask` (no real rows) hold zero partials and are skipped.
 template <int FM, int FN, typename AccT>
 __device__ __forceinline__ void block_flush(AccT (&acc)[FM][FN], float (&accf)[FM][FN][4], const float (&as)[FM][4],
-                                            const float (&ws)[FN], int rows = 1 << 30) {
+                                            const float (&ws)[FN], uint32_t fmask = ~0u) {
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm) {
-    if (fm * 16 >= rows) continue;
+    if (!((fmask >> fm) & 1u)) continue;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
@@ -148,7 +166,7 @@ __device__ __forceinline__ void block_flush(AccT (&acc)[FM][FN], float (&accf)[F
 }
 
 // Epilogues.  Rows whose sh_pid is the sentinel (>= P) are skipped.
-template <int BM, int BN, int WM, int WN, int FM, int FN, BMap MAP, Epi EPI, typename AccT>
+template <int BM, int BN, int WM, int WN, int FM, int FN, BMap MAP, Epi EPI, bool ILV = false, typename AccT>
 __device__ __forceinline__ void epilogue(const Params& p, const AccT (&acc)[FM][FN], const float (&accf)[FM][FN][4],
                                          const int32_t* sh_pid, float (*sh_red)[BM], int64_t row0, int64_t nt,
                                          int64_t e, int wm, int wn, int l, int tid) {
@@ -159,7 +177,7 @@ __device__ __forceinline__ void epilogue(const Params& p, const AccT (&acc)[FM][
     for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int trow = wm * (BM / WM) + fm * 16 + (l / 16) * 4 + r;
+        const int trow = rblk<WM, FM, ILV>(wm, fm) * 16 + (l / 16) * 4 + r;
         if (sh_pid[trow] >= p.P) continue;
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn)
@@ -170,7 +188,7 @@ __device__ __forceinline__ void epilogue(const Params& p, const AccT (&acc)[FM][
     for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int trow = wm * (BM / WM) + fm * 16 + (l / 16) * 4 + r;
+        const int trow = rblk<WM, FM, ILV>(wm, fm) * 16 + (l / 16) * 4 + r;
         if (sh_pid[trow] >= p.P) continue;
         const int64_t grow = row0 + trow;
         const float hs = kBlock ? 0.0f : p.a_s[grow];
@@ -195,7 +213,7 @@ __device__ __forceinline__ void epilogue(const Params& p, const AccT (&acc)[FM][
       float rmax[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int trow = wm * (BM / WM) + fm * 16 + (l / 16) * 4 + r;
+        const int trow = rblk<WM, FM, ILV>(wm, fm) * 16 + (l / 16) * 4 + r;
         const int32_t pid = sh_pid[trow];
         const bool valid = pid < p.P;
         const float as = valid ? p.a_s[pid / p.k] : 0.0f;
@@ -218,7 +236,7 @@ __device__ __forceinline__ void epilogue(const Params& p, const AccT (&acc)[FM][
         float m = rmax[r];
 #pragma unroll
         for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
-        if ((l % 16) == 0) sh_red[wn][wm * (BM / WM) + fm * 16 + (l / 16) * 4 + r] = m;
+        if ((l % 16) == 0) sh_red[wn][rblk<WM, FM, ILV>(wm, fm) * 16 + (l / 16) * 4 + r] = m;
       }
     }
     __syncthreads();
@@ -239,7 +257,7 @@ __device__ __forceinline__ void epilogue(const Params& p, const AccT (&acc)[FM][
     for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int trow = wm * (BM / WM) + fm * 16 + (l / 16) * 4 + r;
+        const int trow = rblk<WM, FM, ILV>(wm, fm) * 16 + (l / 16) * 4 + r;
         const bool valid = sh_pid[trow] < p.P;
         rmax[fm][r] = 0.0f;
 #pragma unroll
@@ -256,14 +274,14 @@ __device__ __forceinline__ void epilogue(const Params& p, const AccT (&acc)[FM][
         float m = rmax[fm][r];
 #pragma unroll
         for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
-        if ((l % 16) == 0) sh_red[wn][wm * (BM / WM) + fm * 16 + (l / 16) * 4 + r] = m;
+        if ((l % 16) == 0) sh_red[wn][rblk<WM, FM, ILV>(wm, fm) * 16 + (l / 16) * 4 + r] = m;
       }
     __syncthreads();
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int trow = wm * (BM / WM) + fm * 16 + (l / 16) * 4 + r;
+        const int trow = rblk<WM, FM, ILV>(wm, fm) * 16 + (l / 16) * 4 + r;
         if (sh_pid[trow] >= p.P) continue;
         float m = sh_red[0][trow];
 #pragma unroll
@@ -489,11 +507,11 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // MFMAs and issues the next stage's DMA instructions between the groups, spread evenly, so
 // the memory pipe is fed for the whole stage instead of in a burst that stalls the MFMAs behind
 // it.  Scheduling barriers keep the compiler from regrouping them.
-template <int BM, int BN, int WM, int WN, int A_LD, int LD, BMap MAP>
+template <int BM, int BN, int WM, int WN, int A_LD, int LD, BMap MAP, bool ILV = false>
 __device__ __forceinline__ void dma_stage(const int8_t* stage, int8_t* next, const int8_t* a_base,
                                           const int8_t* b_base, const uint32_t (&off)[LD], int a_dst, int b_dst,
                                           uint32_t next_off, bool prefetch, i32x4 (&acc)[BM / WM / 16][BN / WN / 16],
-                                          int wm, int wn, int g, int fr, int rows) {
+                                          int wm, int wn, int g, int fr, uint32_t fmask) {
   constexpr int FM = BM / WM / 16, FN = BN / WN / 16;
   constexpr int GROUPS = (kDmaBK / 64) * FM;
   static_assert(GROUPS >= LD, "DMA slots");  // DMA c goes out before group (c * GROUPS) / LD
@@ -503,7 +521,7 @@ __device__ __forceinline__ void dma_stage(const int8_t* stage, int8_t* next, con
     i32x4 af[FM], bf[FN];
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm)
-      af[fm] = *reinterpret_cast<const i32x4*>(stage + lane + (wm * FM + fm) * 16 * kDmaBK);
+      af[fm] = *reinterpret_cast<const i32x4*>(stage + lane + rblk<WM, FM, ILV>(wm, fm) * 16 * kDmaBK);
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn)
       bf[fn] = *reinterpret_cast<const i32x4*>(stage + BM * kDmaBK + lane + brow_of<BN, WN, FN, MAP>(wn, fn) * kDmaBK);
@@ -518,7 +536,7 @@ __device__ __forceinline__ void dma_stage(const int8_t* stage, int8_t* next, con
           else
             dma16_nt(b_base + (off[c] + next_off), next + b_dst + (c - A_LD) * 1024);
         }
-      if (fm * 16 < rows) {  // fragment rows past the tile's real rows are never stored
+      if ((fmask >> fm) & 1u) {  // fragment rows past the tile's real rows are never stored
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn)
           acc[fm][fn] = __builtin_amdgcn_mfma_i32_16x16x64_i8(af[fm], bf[fn], acc[fm][fn], 0, 0, 0);
@@ -534,11 +552,11 @@ __device__ __forceinline__ void dma_stage(const int8_t* stage, int8_t* next, con
 // A and B hold the same K-elements at the same register positions.  Groups are (fragment row,
 // half of the fragment columns), two MFMAs each, with the next stage's DMA spread between them as
 // in dma_stage.
-template <int BM, int BN, int WM, int WN, int A_LD, int LD, BMap MAP>
+template <int BM, int BN, int WM, int WN, int A_LD, int LD, BMap MAP, bool ILV = false>
 __device__ __forceinline__ void dma_stage_f8(const int8_t* stage, int8_t* next, const int8_t* a_base,
                                              const int8_t* b_base, const uint32_t (&off)[LD], int a_dst, int b_dst,
                                              uint32_t next_off, bool prefetch, f32x4 (&acc)[BM / WM / 16][BN / WN / 16],
-                                             int wm, int wn, int g, int fr, int rows) {
+                                             int wm, int wn, int g, int fr, uint32_t fmask) {
   constexpr int FM = BM / WM / 16, FN = BN / WN / 16, FNH = FN / 2;
   constexpr int GROUPS = 2 * FM;
   static_assert(FN % 2 == 0, "gate and up fragments");  // DMA c goes out before group (c * GROUPS) / LD
@@ -556,7 +574,7 @@ __device__ __forceinline__ void dma_stage_f8(const int8_t* stage, int8_t* next, 
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm) {
     i32x8 af;
-    if (fm * 16 < rows) af = ld32(stage + (wm * FM + fm) * 16 * kDmaBK);  // rows past the real ones: no read
+    if ((fmask >> fm) & 1u) af = ld32(stage + rblk<WM, FM, ILV>(wm, fm) * 16 * kDmaBK);  // rows past the real ones: no read
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int grp = fm * 2 + h;
@@ -568,7 +586,7 @@ __device__ __forceinline__ void dma_stage_f8(const int8_t* stage, int8_t* next, 
           else
             dma16_nt(b_base + (off[c] + next_off), next + b_dst + (c - A_LD) * 1024);
         }
-      if (fm * 16 < rows) {
+      if ((fmask >> fm) & 1u) {
 #pragma unroll
         for (int f = 0; f < FNH; ++f)
           acc[fm][h * FNH + f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
@@ -597,11 +615,11 @@ __device__ __forceinline__ void w4_to_fp8(uint32_t x, int32_t& lo, int32_t& hi) 
 // of 64 bytes (128 int4 values) whose 16-byte chunks are swizzled by (row / 4) mod 4; lane (g, fr)
 // widens chunk g of B row fr (values 32 g .. 32 g + 31) into the 32 E4M3 codes of its operand.
 __device__ __forceinline__ int swz4(int row) { return (row >> 2) & 3; }
-template <int BM, int BN, int WM, int WN, int A_LD, int LD, BMap MAP>
+template <int BM, int BN, int WM, int WN, int A_LD, int LD, BMap MAP, bool ILV = false>
 __device__ __forceinline__ void dma_stage_w4(const int8_t* stage, int8_t* next, const int8_t* a_base,
                                              const int8_t* b_base, const uint32_t (&off)[LD], int a_dst, int b_dst,
                                              uint32_t next_off, bool prefetch, f32x4 (&acc)[BM / WM / 16][BN / WN / 16],
-                                             int wm, int wn, int g, int fr, int rows) {
+                                             int wm, int wn, int g, int fr, uint32_t fmask) {
   constexpr int FM = BM / WM / 16, FN = BN / WN / 16, FNH = FN / 2;
   constexpr int GROUPS = 2 * FM;
   constexpr int BROW = kDmaBK / 2;  // bytes of one B row in a stage
@@ -610,7 +628,7 @@ __device__ __forceinline__ void dma_stage_w4(const int8_t* stage, int8_t* next, 
   const int c0 = fr * kDmaBK + (((2 * g) ^ swz(fr)) << 4);
   const int c1 = fr * kDmaBK + (((2 * g + 1) ^ swz(fr)) << 4);
   i32x8 bf[FN];
-  if (rows > 0) {  // wavefronts whose rows are all past the tile's real rows widen nothing
+  if (fmask != 0u) {  // wavefronts whose rows are all past the tile's real rows widen nothing
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) {
       const int j = brow_of<BN, WN, FN, MAP>(wn, fn) + fr;
@@ -624,8 +642,8 @@ __device__ __forceinline__ void dma_stage_w4(const int8_t* stage, int8_t* next, 
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm) {
     i32x8 af;
-    if (fm * 16 < rows) {  // rows past the real ones: no read
-      const int8_t* arow = stage + (wm * FM + fm) * 16 * kDmaBK;
+    if ((fmask >> fm) & 1u) {  // rows past the real ones: no read
+      const int8_t* arow = stage + rblk<WM, FM, ILV>(wm, fm) * 16 * kDmaBK;
       const i32x4 lo = *reinterpret_cast<const i32x4*>(arow + c0);
       const i32x4 hi = *reinterpret_cast<const i32x4*>(arow + c1);
       af = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -641,7 +659,7 @@ __device__ __forceinline__ void dma_stage_w4(const int8_t* stage, int8_t* next, 
           else
             dma16_nt(b_base + (off[c] + next_off), next + b_dst + (c - A_LD) * 1024);
         }
-      if (fm * 16 < rows) {
+      if ((fmask >> fm) & 1u) {
 #pragma unroll
         for (int f = 0; f < FNH; ++f)
           acc[fm][h * FNH + f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
@@ -657,7 +675,7 @@ __device__ __forceinline__ void dma_stage_w4(const int8_t* stage, int8_t* next, 
 // wm in buffer wm), then whole rows leave as contiguous float4 stores.  Second GEMM: y rows of BN
 // columns.  First GEMM: SiLU(gate) * up rows of BN / 2 columns, plus the row maximum of |h| over
 // them, which a half wavefront reduces while it stores the row.
-template <int BM, int BN, int WM, int WN, int STAGE_BYTES, BMap MAP, Epi EPI>
+template <int BM, int BN, int WM, int WN, int STAGE_BYTES, BMap MAP, Epi EPI, bool ILV = false>
 __device__ __forceinline__ void dma_epilogue(const Params& p, const i32x4 (&acc)[BM / WM / 16][BN / WN / 16],
                                              const int32_t* sh_pid, int8_t* buf0, int8_t* buf1, int64_t row0,
                                              int64_t nt, int64_t e, int wm, int wn, int wv, int l,
@@ -681,7 +699,7 @@ __device__ __forceinline__ void dma_epilogue(const Params& p, const i32x4 (&acc)
       if (fm < f0 || fm >= f0 + F) continue;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int trow = wm * (BM / WM) + fm * 16 + (l / 16) * 4 + r;
+        const int trow = rblk<WM, FM, ILV>(wm, fm) * 16 + (l / 16) * 4 + r;
         const int32_t pid = sh_pid[trow];
         float* dst = reinterpret_cast<float*>(half + ((fm - f0) * 16 + (l / 16) * 4 + r) * STRIDE);
         if constexpr (kW13) {
@@ -719,7 +737,7 @@ __device__ __forceinline__ void dma_epilogue(const Params& p, const i32x4 (&acc)
       for (int idx = wv * 2 + l / 32; idx < rows; idx += NW * 2) {
         const int hf = idx / (F * 16), lr = idx % (F * 16);
         const bool in = f0 * 16 + lr < FM * 16;  // the last pass may hold fewer fragment rows
-        const int trow = hf * (BM / WM) + f0 * 16 + (in ? lr : 0);
+        const int trow = rblk<WM, FM, ILV>(hf, f0 + (in ? lr : 0) / 16) * 16 + (in ? lr : 0) % 16;
         const int32_t pid = in ? sh_pid[trow] : (int32_t)p.P;
         float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         if (in) v = *reinterpret_cast<const float4*>((hf == 0 ? buf0 : buf1) + lr * STRIDE + hl * 16);
@@ -735,8 +753,8 @@ __device__ __forceinline__ void dma_epilogue(const Params& p, const i32x4 (&acc)
       // a wavefront per row: 64 lanes x float4 = 256 columns
       for (int idx = wv; idx < rows; idx += NW) {
         const int hf = idx / (F * 16), lr = idx % (F * 16);
-        const int trow = hf * (BM / WM) + f0 * 16 + lr;
         if (f0 * 16 + lr >= FM * 16) continue;
+        const int trow = rblk<WM, FM, ILV>(hf, f0 + lr / 16) * 16 + lr % 16;
         if (sh_pid[trow] >= p.P) continue;
 #pragma unroll
         for (int c = l; c < COLS / 4; c += kWave) {
@@ -832,7 +850,7 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_dma_kernel(co
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
   const int g = l >> 4, fr = l & 15;
-  const int wrows = nrows - wm * (BM / WM);  // real rows in this wavefront's fragment rows
+  const uint32_t fmask = real_frags<WM, BM / WM / 16, false>(wm, nrows);  // fragment rows with real rows
 
   // Prologue: stage 0 lands before the loop.
 #pragma unroll
@@ -852,12 +870,12 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_dma_kernel(co
     __builtin_amdgcn_s_waitcnt(kLgkm0Imm);
     barrier_no_fence();
     dma_stage<BM, BN, WM, WN, A_LD, LD, MAP>(st0, st1, p.a, wexp, off, a_dst, b_dst, (uint32_t)(kt + 1) * kDmaBK, true,
-                                             acc, wm, wn, g, fr, wrows);
+                                             acc, wm, wn, g, fr, fmask);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
     __builtin_amdgcn_s_waitcnt(kLgkm0Imm);
     barrier_no_fence();
     dma_stage<BM, BN, WM, WN, A_LD, LD, MAP>(st1, st0, p.a, wexp, off, a_dst, b_dst, (uint32_t)(kt + 2) * kDmaBK,
-                                             kt + 2 < KT, acc, wm, wn, g, fr, wrows);
+                                             kt + 2 < KT, acc, wm, wn, g, fr, fmask);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
   }
   __syncthreads();
@@ -989,7 +1007,12 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_ring_kernel(c
 #pragma unroll
       for (int r = 0; r < (kBlock ? 4 : 1); ++r) accf[i][j][r] = 0.0f;
     }
-  const int wrows = nrows - wm * (BM / WM);
+  // fragment rows interleaved over the two wavefront rows, so a tile with fewer real rows than BM (an
+  // expert's last tile, or experts with about BM / 2 rows) keeps both wavefront rows busy (block-wise
+  // T = 2048: 2.46 -> 2.41 ms INT8, 2.44 -> 2.40 ms FP8); not for int4 weights, whose widening both
+  // wavefront rows would then repeat (2.57 -> 2.69 ms)
+  constexpr bool ILV = WM > 1 && !kW4;
+  const uint32_t fmask = real_frags<WM, FM, ILV>(wm, nrows);  // fragment rows with real rows
 
 #define W8A8_RSTG(j) ((j) % NS == 0 ? st0 : (j) % NS == 1 ? st1 : (j) % NS == 2 ? st2 : (j) % NS == 3 ? st3 : st4)
   // VMEM operations that stage st brings: its DMAs, and with every SG-th stage its scale group
@@ -1037,24 +1060,24 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_ring_kernel(c
     const bool sdma = kBlock && more && nxt % SG == 0;  // with its scale group
     if (sdma) dma4(p.a_s + (s_off + s_blk(nxt / SG)), W8A8_RSAS(nxt / SG) + wv * kWave);
     if constexpr (kW4)
-      dma_stage_w4<BM, BN, WM, WN, A_LD, LD, MAP>(W8A8_RSTG(kt), W8A8_RSTG(nxt), a_next, b_next, off, a_dst, b_dst,
-                                                  0u, more, acc, wm, wn, g, fr, wrows);
+      dma_stage_w4<BM, BN, WM, WN, A_LD, LD, MAP, ILV>(W8A8_RSTG(kt), W8A8_RSTG(nxt), a_next, b_next, off, a_dst,
+                                                       b_dst, 0u, more, acc, wm, wn, g, fr, fmask);
     else if constexpr (kFp8)
-      dma_stage_f8<BM, BN, WM, WN, A_LD, LD, MAP>(W8A8_RSTG(kt), W8A8_RSTG(nxt), a_next, b_next, off, a_dst, b_dst,
-                                                  0u, more, acc, wm, wn, g, fr, wrows);
+      dma_stage_f8<BM, BN, WM, WN, A_LD, LD, MAP, ILV>(W8A8_RSTG(kt), W8A8_RSTG(nxt), a_next, b_next, off, a_dst,
+                                                       b_dst, 0u, more, acc, wm, wn, g, fr, fmask);
     else
-      dma_stage<BM, BN, WM, WN, A_LD, LD, MAP>(W8A8_RSTG(kt), W8A8_RSTG(nxt), a_next, b_next, off, a_dst, b_dst, 0u,
-                                               more, acc, wm, wn, g, fr, wrows);
+      dma_stage<BM, BN, WM, WN, A_LD, LD, MAP, ILV>(W8A8_RSTG(kt), W8A8_RSTG(nxt), a_next, b_next, off, a_dst, b_dst,
+                                                    0u, more, acc, wm, wn, g, fr, fmask);
     a_next += kDmaBK;
     b_next += BKB;
     asm volatile("" : "+s"(a_next), "+s"(b_next));
     if constexpr (kBlock) {
-      if (wrows > 0) {
+      if (fmask != 0u) {
         float as[FM][4], ws[FN];
         const float* sa = W8A8_RSAS(kt / SG) + (kt % SG) * 16 + (l >> 4) * 4;
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) {
-          const f32x4 s4 = *reinterpret_cast<const f32x4*>(sa + (wm * FM + fm) * kWave);
+          const f32x4 s4 = *reinterpret_cast<const f32x4*>(sa + rblk<WM, FM, ILV>(wm, fm) * kWave);
 #pragma unroll
           for (int r = 0; r < 4; ++r) as[fm][r] = s4[r];
         }
@@ -1066,7 +1089,7 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_ring_kernel(c
 #pragma unroll
           for (int fn = 0; fn < FN; ++fn) ws[fn] = brow_of<BN, WN, FN, MAP>(wn, fn) >= 128 ? w1 : w0;
         }
-        block_flush<FM, FN, AccT>(acc, accf, as, ws, wrows);
+        block_flush<FM, FN, AccT>(acc, accf, as, ws, fmask);
       }
     }
     {  // stage kt + 1 landed: only the stages after it may be outstanding
@@ -1080,9 +1103,9 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_ring_kernel(c
 #undef W8A8_RSTG
   __syncthreads();
   if constexpr (kBlock)
-    epilogue<BM, BN, WM, WN, FM, FN, MAP, EPI>(p, acc, accf, sh_pid, sh_red, row0, nt, e, wm, wn, l, tid);
+    epilogue<BM, BN, WM, WN, FM, FN, MAP, EPI, ILV>(p, acc, accf, sh_pid, sh_red, row0, nt, e, wm, wn, l, tid);
   else
-    dma_epilogue<BM, BN, WM, WN, STAGE, MAP, EPI>(p, acc, sh_pid, st0, st1, row0, nt, e, wm, wn, wv, l, 0);
+    dma_epilogue<BM, BN, WM, WN, STAGE, MAP, EPI, ILV>(p, acc, sh_pid, st0, st1, row0, nt, e, wm, wn, wv, l, 0);
 }
 
 // Streaming engine for packed int4 weights when experts hold few rows (decode): tiles of 16 rows
