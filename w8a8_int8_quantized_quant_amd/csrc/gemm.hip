@@ -1110,12 +1110,15 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_ring_kernel(c
 
 // Streaming engine for packed int4 weights when experts hold few rows (decode): tiles of 16 rows
 // x 256 weight rows on four wavefronts that share nothing until the epilogue.  Wavefront wn owns
-// 64 weight rows (FN = 4 fragments); for each 128-wide K-block lane (g, fr) loads the 16 bytes
-// (32 int4 values, K values 32 g .. 32 g + 31 of the block) of weight row fr of each fragment
-// straight into registers with the non-temporal policy, widens them to E4M3 codes, and takes the
-// matching 32 activation codes of tile row fr from the (L1/L2-resident) activation rows.  PD
-// K-blocks are in flight ahead of the one being multiplied, so a wavefront always has 8 KB of
-// weights on the way and no barrier or LDS round trip sits between a load and its MFMA.
+// 64 weight rows (FN = 4 fragments); for each 128-wide K-block lane (g, fr) needs the 16 bytes
+// (32 int4 values, K values 32 g .. 32 g + 31 of the block) of weight row fr of each fragment, widens
+// them to E4M3 codes, and takes the matching 32 activation codes of tile row fr from the (L1/L2-
+// resident) activation rows.  The weights are loaded straight into registers with the non-temporal
+// policy, two K-blocks (one 128-byte line of each row) per pair of load instructions that each cover
+// whole lines, and put in place by one DPP row shift per dword (see the loads); loading each lane's
+// own 16 bytes instead covered half of each line per instruction and ran the weight stream at 4.9
+// instead of 5.7 TB/s.  PD pairs of K-blocks are in flight ahead of the pair being multiplied, and no
+// barrier or LDS round trip sits between a load and its MFMA.
 // Scales: lane (g, fr) holds four consecutive K-blocks (4 g .. 4 g + 3 of a 16-block window) of
 // the weight scale of row fr of each fragment and of the activation scale of tile row fr; each
 // K-block's values are fetched from the owning lane by a cross-lane read (ds_bpermute).  Each
@@ -1128,7 +1131,7 @@ __global__ __launch_bounds__(kStreamWN * kWave) void grouped_gemm_w4_stream_kern
   static_assert(is_w4<EPI>(), "packed int4 weights");
   constexpr int BM = kStreamBM, BN = kStreamBN, WN = kStreamWN;
   constexpr int FN = BN / WN / 16, FNH = FN / 2;
-  constexpr int PD = 2, NB = PD + 1;  // K-blocks in flight ahead of the current one; register slots
+  constexpr int PD = 1, NB = PD + 1;  // K-block pairs in flight ahead of the current one; register slots
   constexpr int WIN = 16;             // K-blocks per scale window (four per lane group)
   constexpr int NWIN = (KT + WIN - 1) / WIN;
   constexpr int kScaleOne = 127;
@@ -1161,22 +1164,39 @@ __global__ __launch_bounds__(kStreamWN * kWave) void grouped_gemm_w4_stream_kern
   const int64_t arow = p.gather ? (int64_t)(p.sorted[row0 + rr] / p.k) : row0 + rr;
   const int8_t* a_src = p.a + arow * p.K + g * 32;
   const float* as_src = p.a_s + arow * KT;
+  // Weights go in whole 128-byte lines: a K-block pair (2q, 2q + 1) is one line of each row.  Load X
+  // covers the fragment's rows 0-7, load Y rows 8-15; lane (g, fr) takes row fr % 8 (resp. 8 + fr % 8)
+  // and 16-byte chunk g + 4 (fr / 8) of the line.  X then holds in lanes fr < 8 exactly the MFMA
+  // operand of K-block 2q (row fr, chunk g) and Y in lanes fr >= 8 that of K-block 2q + 1; the other
+  // halves come one DPP row shift by 8 lanes away (see below).
   const int8_t* b_src[FN];
   const float* ws_src[FN];
+  const int bchunk = g + 4 * (fr >> 3);
 #pragma unroll
   for (int fn = 0; fn < FN; ++fn) {
-    const int64_t wrow = wrow_of<BN, MAP>(nt, brow_of<BN, WN, FN, MAP>(wn, fn) + fr, p.I);
-    b_src[fn] = wexp + wrow * KB + g * 16;
-    ws_src[fn] = p.w_s + (e * p.N + wrow) * KT;
+    const int brow = brow_of<BN, WN, FN, MAP>(wn, fn);
+    b_src[fn] = wexp + wrow_of<BN, MAP>(nt, brow + (fr & 7), p.I) * KB;
+    ws_src[fn] = p.w_s + (e * p.N + wrow_of<BN, MAP>(nt, brow + fr, p.I)) * KT;
   }
+  const int64_t y_off = 8 * KB;  // rows 8-15 of a fragment (the fragment's 16 rows are consecutive)
 
-  i32x4 bq[NB][FN], aq[NB][2];
-  auto load = [&](int kb, int slot) {
+  i32x4 bx[NB][FN], by[NB][FN], aq[NB][2][2];
+  // pair q into register slot `slot`; with an odd KT the last pair has one K-block, whose line half
+  // is read twice (the second copy is never used)
+  auto load = [&](int q, int slot) {
+    const int chunk = 2 * q + 1 < KT ? bchunk : (bchunk & 3);
 #pragma unroll
-    for (int fn = 0; fn < FN; ++fn)
-      bq[slot][fn] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(b_src[fn] + kb * (kDmaBK / 2)));
-    aq[slot][0] = *reinterpret_cast<const i32x4*>(a_src + kb * kDmaBK);
-    aq[slot][1] = *reinterpret_cast<const i32x4*>(a_src + kb * kDmaBK + 16);
+    for (int fn = 0; fn < FN; ++fn) {
+      const int8_t* src = b_src[fn] + q * kDmaBK + chunk * 16;
+      bx[slot][fn] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(src));
+      by[slot][fn] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(src + y_off));
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (2 * q + h >= KT) break;
+      aq[slot][h][0] = *reinterpret_cast<const i32x4*>(a_src + (2 * q + h) * kDmaBK);
+      aq[slot][h][1] = *reinterpret_cast<const i32x4*>(a_src + (2 * q + h) * kDmaBK + 16);
+    }
   };
   float wsw[2][FN][4], asw[2][4];
   auto load_scales = [&](int w, int set) {
@@ -1195,26 +1215,34 @@ __global__ __launch_bounds__(kStreamWN * kWave) void grouped_gemm_w4_stream_kern
 #pragma unroll
     for (int r = 0; r < 4; ++r) accf[0][fn][r] = 0.0f;
 
+  constexpr int NP = (KT + 1) / 2;  // K-block pairs
 #pragma unroll
   for (int s = 0; s < PD; ++s)
-    if (s < KT) load(s, s);
+    if (s < NP) load(s, s);
   load_scales(0, 0);
 #pragma clang loop unroll(full)
   for (int kb = 0; kb < KT; ++kb) {
-    if (kb + PD < KT) load(kb + PD, (kb + PD) % NB);
+    const int q = kb / 2, h = kb % 2;
+    if (h == 0 && q + PD < NP) load(q + PD, (q + PD) % NB);
     if (kb % WIN == 0 && kb / WIN + 1 < NWIN) load_scales(kb / WIN + 1, (kb / WIN + 1) & 1);
-    const int slot = kb % NB, set = (kb / WIN) & 1;
+    const int slot = q % NB, set = (kb / WIN) & 1;
     const int src = ((kb % WIN) / 4) * 16;  // lane group holding this K-block's scales
     i32x8 bf[FN];
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) {
       int32_t o[8];
 #pragma unroll
-      for (int d = 0; d < 4; ++d) w4_to_fp8((uint32_t)bq[slot][fn][d], o[2 * d], o[2 * d + 1]);
+      for (int d = 0; d < 4; ++d) {
+        // K-block 2q: X, lanes 8-15 of each 16-lane row from Y 8 lanes down (row_shr:8, banks 2-3);
+        // K-block 2q + 1: Y, lanes 0-7 from X 8 lanes up (row_shl:8, banks 0-1)
+        const int32_t w = h == 0 ? __builtin_amdgcn_update_dpp(bx[slot][fn][d], by[slot][fn][d], 0x118, 0xF, 0xC, false)
+                                 : __builtin_amdgcn_update_dpp(by[slot][fn][d], bx[slot][fn][d], 0x108, 0xF, 0x3, false);
+        w4_to_fp8((uint32_t)w, o[2 * d], o[2 * d + 1]);
+      }
       bf[fn] = i32x8{o[0], o[1], o[2], o[3], o[4], o[5], o[6], o[7]};
     }
-    const i32x8 af = i32x8{aq[slot][0][0], aq[slot][0][1], aq[slot][0][2], aq[slot][0][3],
-                           aq[slot][1][0], aq[slot][1][1], aq[slot][1][2], aq[slot][1][3]};
+    const i32x8 af = i32x8{aq[slot][h][0][0], aq[slot][h][0][1], aq[slot][h][0][2], aq[slot][h][0][3],
+                           aq[slot][h][1][0], aq[slot][h][1][1], aq[slot][h][1][2], aq[slot][h][1][3]};
     f32x4 part[FN];
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn)
