@@ -657,7 +657,9 @@ __device__ __forceinline__ void dma_stage_w4(const int8_t* stage, int8_t* next, 
           if (c < A_LD)
             dma16(a_base + (off[c] + next_off), next + a_dst + c * 1024);
           else
-            dma16_nt(b_base + (off[c] + next_off), next + b_dst + (c - A_LD) * 1024);
+            // int4 stages are half a 128-byte line of each weight row; the normal cache policy keeps
+            // the line in L2 for the next step's half (2.59 -> 2.52 ms at T = 2048)
+            dma16(b_base + (off[c] + next_off), next + b_dst + (c - A_LD) * 1024);
         }
       if ((fmask >> fm) & 1u) {
 #pragma unroll
@@ -1036,7 +1038,7 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_ring_kernel(c
       if (c < A_LD)
         dma16(p.a + (off[c] + (uint32_t)(st * kDmaBK)), W8A8_RSTG(st) + a_dst + c * 1024);
       else
-        dma16_nt(wexp + (off[c] + (uint32_t)(st * BKB)), W8A8_RSTG(st) + b_dst + (c - A_LD) * 1024);
+        (kW4 ? dma16 : dma16_nt)(wexp + (off[c] + (uint32_t)(st * BKB)), W8A8_RSTG(st) + b_dst + (c - A_LD) * 1024);
     }
     if (kBlock && st % SG == 0) dma4(p.a_s + (s_off + s_blk(st / SG)), W8A8_RSAS(st / SG) + wv * kWave);
   }
