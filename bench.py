@@ -37,8 +37,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="decode",
-                    help="decode (the headline), prefill, tiny, skew, block, fp8-block, fp8-decode, w4a8-decode "
-                         "or w4a8-block")
+                    help="decode (the headline), prefill, tiny, skew, skew-empty, block, fp8-block, fp8-decode, "
+                         "w4a8-decode or w4a8-block")
     ap.add_argument("--no-prefill", action="store_true", help="skip the T=8192 prefill figures")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=128, help="tokens in the CPU oracle sample")
@@ -243,6 +243,22 @@ def w13_algorithmic_bytes(cfg, T, counts):
     nsa = cfg.H // 128 if blk else 1
     nsh = cfg.I // 128 if blk else 1
     return active * (2 * cfg.I * cfg.H // (2 if w4 else 1) + 4 * nsw) + T * (cfg.H + 4 * nsa) + P * (cfg.I + 4 * nsh)
+
+
+def w13_algorithmic_ops(cfg, T):
+    """INT8 multiply-add operations of the gate+up GEMM on the real (token, expert) pairs."""
+    return 2 * T * cfg.k * 2 * cfg.I * cfg.H
+
+
+def engine_name(cfg, T):
+    """The GEMM engine the library picks for this workload (include/w8a8moe.h, w8a8_moe_engine)."""
+    import w8a8_int8_quantized_quant_amd as w8
+
+    mode = {"block": w8.SCALE_BLOCK128, "fp8": w8.SCALE_FP8_BLOCK128, "w4a8": w8.SCALE_W4A8}.get(cfg.scale_mode,
+                                                                                               w8.SCALE_CHANNEL)
+    e = w8.w8a8_moe_engine(T, cfg.k, cfg.E, cfg.H, cfg.I, w8.w8a8_moe_pick_block_m(T, cfg.k, cfg.E), mode)
+    return {w8.ENGINE_STAGED: "staged", w8.ENGINE_DMA: "dma", w8.ENGINE_RING: "ring",
+            w8.ENGINE_STREAM: "stream"}.get(e, "none")
 
 
 def measured_peaks():
@@ -458,16 +474,25 @@ def main():
         pms, pstage, pst, pcounts = measure(pl, max(3, args.steps // 4), args.warmup)
         pf = layer_figures(pc, pc.T, pms, pcounts)
         print(f"[bench] prefill: {pms:.3f} ms/step, stages {pstage}", file=sys.stderr, flush=True)
+        w13_ops = w13_algorithmic_ops(pc, pc.T)
+        w13_tops = w13_ops / (pstage["w13"] / 1000.0) / 1e12
         prefill = {"T": pc.T, "ms_per_step": round(pms, 4), "tokens_per_s": round(pf["tokens_per_s"], 1),
                    "int8_tops": round(pf["int8_tops"], 2), "frac_int8_peak": round(pf["frac_int8_peak"], 4),
-                   "hbm_gbs": round(pf["hbm_gbs"], 1), "stage_ms": {k: round(v, 4) for k, v in pstage.items()}}
+                   "hbm_gbs": round(pf["hbm_gbs"], 1), "stage_ms": {k: round(v, 4) for k, v in pstage.items()},
+                   "engine": engine_name(pc, pc.T),
+                   "roofline": {"bound": "mfma", "achieved": round(w13_tops, 1), "peak": INT8_PEAK_TOPS,
+                                "unit": "TOPS", "frac": round(w13_tops / INT8_PEAK_TOPS, 4),
+                                "traffic": measured_traffic("prefill-w13-stage"),
+                                "kernel": "gate+up grouped GEMM stage (w8a8_grouped_gemm_w13_silu)",
+                                "kernel_ms": round(pstage["w13"], 4), "algorithmic_ops": w13_ops,
+                                "algorithmic_bytes": w13_algorithmic_bytes(pc, pc.T, pcounts)}}
         del pst, pl
         torch.cuda.empty_cache()
 
     configs = None
     if not args.no_configs and args.config == "decode":
         configs = {}
-        for name in ("tiny", "skew", "block", "fp8-block", "fp8-decode", "w4a8-decode", "w4a8-block"):
+        for name in ("tiny", "skew", "skew-empty", "block", "fp8-block", "fp8-decode", "w4a8-decode", "w4a8-block"):
             oc = config_of(name)
             print(f"[bench] drawing {oc.note}", file=sys.stderr, flush=True)
             ol = workload.make_layer(oc)
@@ -477,14 +502,14 @@ def main():
             entry = {"T": oc.T, "ms_per_step": round(oms, 4), "tokens_per_s": round(of["tokens_per_s"], 1),
                      "int8_tops": round(of["int8_tops"], 3), "frac_int8_peak": round(of["frac_int8_peak"], 4),
                      "hbm_gbs": round(of["hbm_gbs"], 1), "frac_hbm_peak": round(of["frac_hbm_peak"], 4),
-                     "active_experts": of["active_experts"], "scale": oc.scale_mode,
+                     "active_experts": of["active_experts"], "scale": oc.scale_mode, "engine": engine_name(oc, oc.T),
                      "stage_ms": {k: round(v, 4) for k, v in ostage.items()}}
             if oc.scale_mode in ("fp8", "w4a8"):  # the same operation count on the FP8 MFMA
                 for key in ("int8_tops", "frac_int8_peak"):
                     del entry[key]
                 entry["fp8_tflops"] = round(of["int8_tops"], 3)
                 entry["frac_fp8_peak"] = round(of["int8_tops"] / FP8_PEAK_TFLOPS, 4)
-            if name == "skew":
+            if name in ("skew", "skew-empty"):
                 import numpy as np
 
                 c = np.sort(ocounts)[::-1]
@@ -507,6 +532,8 @@ def main():
         roofline["frac_of_measured_read"] = round(achieved / peaks["hbm_read_gbs"], 4)
         if prefill is not None:
             prefill["frac_of_measured_mfma"] = round(prefill["int8_tops"] / peaks["int8_mfma_tops"], 4)
+            prefill["roofline"]["frac_of_measured_mfma"] = round(prefill["roofline"]["achieved"]
+                                                                 / peaks["int8_mfma_tops"], 4)
         for entry in (linear or {}).values():
             entry["frac_of_measured_mfma"] = round(entry["int8_tops"] / peaks["int8_mfma_tops"], 4)
             entry["frac_of_measured_read"] = round(entry["hbm_gbs"] / peaks["hbm_read_gbs"], 4)

@@ -147,21 +147,41 @@ int32_t moe_align_by_expert(const int32_t* topk_ids, int64_t T, int64_t k, int64
 
 /* ------------------------------------------------------------------ steps 4-5: grouped INT8 GEMMs
  * Common arguments (outputs of moe_align_by_expert with the same block_m):
- *   sorted_pair_ids, tile_expert, num_tiles (device; num_tiles is read on the
+ *   sorted_pair_ids, padded_offsets, tile_expert, num_tiles (device; num_tiles is read on the
  *   device only).  Rows of the intermediate are the padded expert-sorted rows;
  *   rows holding the sentinel are skipped and their outputs are unspecified.
  *
- * Raw int32 accumulators (the exact integer products before any scaling).
- *   gather = 1: A row of sorted row r is a[sorted_pair_ids[r] / k] ([T, K],
- *               the first GEMM); gather = 0: A row is a[r] ([max_rows, K],
- *               the second GEMM on the sorted intermediate).
+ * Raw int32 accumulators (the exact integer products before any scaling), for checking the
+ * integer core of the channel-wise GEMMs bit for bit (PR #3888, Performance: the fused MoE with an
+ * int32 accumulator; article, "Quantization exploration": the int8 matmul before its single
+ * dequantization).  The call runs the engine, tile shape, gate/up tile pairing and work order that
+ * the channel-wise GEMM of the same layer shape runs (w8a8_moe_engine with W8A8_SCALE_CHANNEL);
+ * only its epilogue differs, storing the int32 sums instead of scaling them.
+ *   gather = 1: the first GEMM of a layer with H = K, I = N / 2: the A row of sorted row r is
+ *               a[sorted_pair_ids[r] / k] ([T, K]) and w is w13 [E, N, K];
+ *   gather = 0: the second GEMM of a layer with H = N, I = K: the A row of sorted row r is a[r]
+ *               ([max_rows, K], the sorted intermediate) and w is w2 [E, N, K].
  *   w    device, [E, N, K] int8
- *   out  device, [max_rows, N] int32 (output)
+ *   out  device, [max_rows, N] int32 (output; pad rows untouched)
+ *   ws   device workspace of w8a8_grouped_gemm_i32_workspace_bytes() bytes (the engine's tile list)
+ * Shapes: H and I as for the layer (multiples of 128, at most 65536); N even when gather = 1.
  */
+size_t w8a8_grouped_gemm_i32_workspace_bytes(int32_t gather, int64_t N, int64_t K, int64_t T, int64_t k, int64_t E,
+                                             int64_t block_m); /* 0 for invalid arguments */
 int32_t w8a8_grouped_gemm_i32(const int8_t* a, int32_t gather, const int8_t* w, int64_t N, int64_t K,
-                              const int32_t* sorted_pair_ids, const int32_t* tile_expert,
-                              const int32_t* num_tiles, int64_t T, int64_t k, int64_t E, int64_t block_m,
-                              int32_t* out, hipStream_t stream);
+                              const int32_t* sorted_pair_ids, const int32_t* padded_offsets,
+                              const int32_t* tile_expert, const int32_t* num_tiles, int64_t T, int64_t k, int64_t E,
+                              int64_t block_m, int32_t* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Which GEMM engine the grouped GEMMs of a layer of this shape and scale mode run (both GEMMs of
+ * a layer run the same one), decided on the host from the shapes alone: W8A8_ENGINE_STAGED (few
+ * rows per expert: register-staged LDS tiles of block_m rows), W8A8_ENGINE_DMA (hundreds of rows
+ * per expert: 320 x 256 tiles filled by direct-to-LDS loads), W8A8_ENGINE_RING (tens to ~200 rows
+ * per expert at the DeepSeek-V3 shapes, the block-wise and FP8 paths: a 3-stage LDS ring) or
+ * W8A8_ENGINE_STREAM (W4A8 with few rows per expert: int4 weights straight to registers).
+ * Returns -1 for arguments the GEMM entry points would reject. */
+enum { W8A8_ENGINE_STAGED = 0, W8A8_ENGINE_DMA = 1, W8A8_ENGINE_RING = 2, W8A8_ENGINE_STREAM = 3 };
+int32_t w8a8_moe_engine(int64_t T, int64_t k, int64_t E, int64_t H, int64_t I, int64_t block_m, int32_t scale_mode);
 
 /* Channel-wise first GEMM (PR #3888: fused MoE with channel-wise int8 and an
  * int32 accumulator; article: one dequantization after the INT8 matmul):

@@ -95,11 +95,17 @@ CONFIGS = {
     "skew": MoEConfig(name="skew", index=3, T=4096, scale_mode="channel", zipf_s=1.2,
                       zipf_beta=0.580934, note="DeepSeek-V3 shapes, Zipf(1.2)-skewed expert load, T=4096",
                       **_DSV3),
+    # The same seeded logits with a stronger bias, calibrated (oracle/calibrate_zipf.py) so that at
+    # least 30 of the 256 experts receive no assignment: empty experts, their zero tiles and
+    # offsets at the DeepSeek-V3 shapes.
+    "skew-empty": MoEConfig(name="skew-empty", index=3, T=4096, scale_mode="channel", zipf_s=1.2,
+                            zipf_beta=0.774107, note="DeepSeek-V3 shapes, Zipf(1.2)-skewed expert load with ~30 "
+                                                 "empty experts, T=4096", **_DSV3),
     "block": MoEConfig(name="block", index=4, T=2048, scale_mode="block",
                        note="DeepSeek-V3 shapes, 128x128 block-wise INT8, T=2048", **_DSV3),
 }
 
-CONFIG_ORDER = ["tiny", "decode", "prefill", "skew", "block"]
+CONFIG_ORDER = ["tiny", "decode", "prefill", "skew", "skew-empty", "block"]
 
 
 # --------------------------------------------------------------------------- libraries

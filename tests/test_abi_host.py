@@ -131,12 +131,18 @@ def test_align_validation():
 
 def test_gemm_validation():
     L = w8.lib()
-    g = lambda gather, N, K, bm, out=P16: (P16, gather, P16, N, K, P16, P16, P16, 16, 2, 8, bm, out, None)
+    ineed = w8.w8a8_grouped_gemm_i32_workspace_bytes(True, 256, 256, 16, 2, 8, 16)
+    assert ineed > 0
+    g = lambda gather, N, K, bm, out=P16, ws_bytes=ineed: (P16, gather, P16, N, K, P16, P16, P16, P16, 16, 2, 8, bm,
+                                                          out, P16, ws_bytes, None)
     assert L.w8a8_grouped_gemm_i32(*g(1, 100, 256, 16)) == SHAPE
     assert L.w8a8_grouped_gemm_i32(*g(1, 256, 200, 16)) == SHAPE
+    assert L.w8a8_grouped_gemm_i32(*g(1, 258, 256, 16)) == SHAPE  # odd I = N / 2
     assert L.w8a8_grouped_gemm_i32(*g(2, 256, 256, 16)) == INV
     assert L.w8a8_grouped_gemm_i32(*g(1, 256, 256, 24)) == SHAPE
     assert L.w8a8_grouped_gemm_i32(*g(1, 256, 256, 16, out=P16 + 4)) == INV
+    assert L.w8a8_grouped_gemm_i32(*g(1, 256, 256, 16, ws_bytes=ineed - 1)) == WS
+    assert w8.w8a8_grouped_gemm_i32_workspace_bytes(True, 100, 256, 16, 2, 8, 16) == 0
     T, k, E, H, I, bm = 16, 2, 8, 256, 128, 16
     need = w8.w8a8_w13_workspace_bytes(T, k, E, H, I, bm)
     w13 = lambda H_, a_q=P16, ws_bytes=need, T_=T: (a_q, P16, P16, P16, P16, P16, P16, P16, T_, k, E, H_, I, bm,
@@ -175,6 +181,22 @@ def test_forward_validation():
     assert L.w8a8_moe_forward(args(block_m=8), P16, need, None) == SHAPE
     assert L.w8a8_moe_forward(args(n_group=3), P16, need, None) == SHAPE
     assert L.w8a8_moe_forward(args(T=0), P16, need, None) == OK
+
+
+def test_engine_choice():
+    """The GEMM engine follows the average rows per expert (decode: staged; skewed and block-wise
+    mid-size batches: ring; prefill: DMA; W4A8 decode: streaming); invalid shapes give -1."""
+    H, I, E, k = 7168, 2048, 256, 8
+    assert w8.w8a8_moe_engine(128, k, E, H, I, 16, w8.SCALE_CHANNEL) == w8.ENGINE_STAGED
+    assert w8.w8a8_moe_engine(8192, k, E, H, I, 128, w8.SCALE_CHANNEL) == w8.ENGINE_DMA
+    assert w8.w8a8_moe_engine(4096, k, E, H, I, 128, w8.SCALE_CHANNEL) == w8.ENGINE_RING
+    assert w8.w8a8_moe_engine(2048, k, E, H, I, 64, w8.SCALE_BLOCK128) == w8.ENGINE_RING
+    assert w8.w8a8_moe_engine(2048, k, E, H, I, 64, w8.SCALE_FP8_BLOCK128) == w8.ENGINE_RING
+    assert w8.w8a8_moe_engine(128, k, E, H, I, 16, w8.SCALE_W4A8) == w8.ENGINE_STREAM
+    assert w8.w8a8_moe_engine(16, 2, 8, 256, 128, 16, w8.SCALE_CHANNEL) == w8.ENGINE_STAGED
+    assert w8.w8a8_moe_engine(128, k, E, 7000, I, 16, w8.SCALE_CHANNEL) == -1
+    assert w8.w8a8_moe_engine(128, k, E, H, I, 24, w8.SCALE_CHANNEL) == -1
+    assert w8.w8a8_moe_engine(128, k, E, H, I, 16, 7) == -1
 
 
 def test_size_queries():

@@ -19,8 +19,10 @@ import sys
 import numpy as np
 import pytest
 
+import gpu_checks
 import oracle
 import synth
+from gpu_checks import check_align_equal, check_routing
 
 torch = pytest.importorskip("torch")
 
@@ -33,7 +35,6 @@ import w8a8_int8_quantized_quant_amd as w8  # noqa: E402
 from w8a8_int8_quantized_quant_amd import workload  # noqa: E402
 
 DEV = "cuda"
-FULL = ["decode", "prefill", "skew", "block"]
 ULP = 2.0 ** -23
 
 
@@ -120,18 +121,7 @@ def block_m_of(cfg):
 
 
 def dev_align(ids_np, E, bm):
-    T, k = ids_np.shape
-    R = max(w8.w8a8_moe_max_rows(T, k, E, bm), 1)
-    o = dict(counts=torch.empty(E, dtype=torch.int32, device=DEV),
-             offsets=torch.empty(E + 1, dtype=torch.int32, device=DEV),
-             padded_offsets=torch.empty(E + 1, dtype=torch.int32, device=DEV),
-             sorted_pair_ids=torch.full((R,), -7, dtype=torch.int32, device=DEV),
-             tile_expert=torch.full((max(R // bm, 1),), -7, dtype=torch.int32, device=DEV),
-             num_tiles=torch.empty(1, dtype=torch.int32, device=DEV))
-    ws = torch.empty(max(w8.moe_align_workspace_bytes(T, k, E), 256), dtype=torch.uint8, device=DEV)
-    w8.moe_align_by_expert(dt(ids_np), E, bm, o["counts"], o["offsets"], o["padded_offsets"], o["sorted_pair_ids"],
-                           o["tile_expert"], o["num_tiles"], ws)
-    return o
+    return gpu_checks.dev_align(w8, torch, DEV, ids_np, E, bm)
 
 
 def oracle_align_dev(ids_np, E, bm):
@@ -166,7 +156,7 @@ def test_device_generator_matches_host(name):
 
 # ------------------------------------------------------------------ step 1: quantization
 
-@pytest.mark.parametrize("name", ["tiny", "ds-small", "decode", "prefill", "skew", "block"])
+@pytest.mark.parametrize("name", ["tiny", "ds-small"])
 def test_activation_quant_bit_exact(name):
     cfg = cfg_of(name)
     group = 128 if cfg.scale_mode == "block" else 0
@@ -219,44 +209,9 @@ def test_weight_quant_blocks_bit_exact(shape, block):
     assert np.array_equal(host(s), rs)
 
 
-@pytest.mark.parametrize("name", ["decode", "block"])
-def test_layer_weights_bit_exact(name):
-    """Expert weights drawn and quantized on the device equal the oracle's own draw + quantization."""
-    cfg = cfg_of(name)
-    L = layer_of(name)
-    experts = [0, 97, cfg.E - 1]
-    w = oracle_weights(name, experts)
-    for e in experts:
-        assert np.array_equal(host(L.w13[e]), w[0][e])
-        assert np.array_equal(host(L.w13_scale[e]), w[1][e])
-        assert np.array_equal(host(L.w2[e]), w[2][e])
-        assert np.array_equal(host(L.w2_scale[e]), w[3][e])
-
-
 # ------------------------------------------------------------------ step 2: routing
 
-def check_routing(cfg, logits, ids_g, w_g, ids_o, w_o):
-    fn = oracle.SOFTMAX if cfg.route == "softmax" else oracle.SIGMOID
-    score = logits.astype(np.float64) if fn == oracle.SOFTMAX else 1.0 / (1.0 + np.exp(-logits.astype(np.float64)))
-    bad = 0
-    same = np.all(ids_g == ids_o, axis=1)
-    for t in np.nonzero(~same)[0]:
-        A, B = set(ids_o[t]), set(ids_g[t])
-        if A == B:
-            # same set, slots swapped: only a near-tie can do that
-            j = np.nonzero(ids_g[t] != ids_o[t])[0]
-            gap = np.abs(score[t, ids_o[t, j]] - score[t, ids_g[t, j]]).max()
-        else:
-            gap = abs(score[t, list(A)].sum() - score[t, list(B)].sum())
-        if gap > 5e-7 * np.abs(score[t]).max():
-            bad += 1
-    assert bad == 0, f"{bad} tokens differ beyond a near-tie"
-    assert (~same).sum() <= max(1, cfg.T // 100)
-    rel = np.abs(w_g[same] - w_o[same]) / np.abs(w_o[same])
-    assert rel.max() <= 8 * ULP, rel.max()
-
-
-@pytest.mark.parametrize("name", ["tiny", "ds-small", "decode", "prefill", "skew", "block"])
+@pytest.mark.parametrize("name", ["tiny", "ds-small"])
 def test_routing(name):
     cfg = cfg_of(name)
     say(f"[route] {name}")
@@ -292,17 +247,7 @@ def test_routing_variants(E, k, ng, tg, fn, renorm, bias):
 
 # ------------------------------------------------------------------ step 3: align
 
-def check_align_equal(d, al):
-    nt = int(al["num_tiles"][0])
-    assert int(host(d["num_tiles"])[0]) == nt
-    for key in ("counts", "offsets", "padded_offsets"):
-        assert np.array_equal(host(d[key]), al[key]), key
-    R = int(al["padded_offsets"][-1])
-    assert np.array_equal(host(d["sorted_pair_ids"])[:R], al["sorted_pair_ids"][:R])
-    assert np.array_equal(host(d["tile_expert"])[:nt], al["tile_expert"][:nt])
-
-
-@pytest.mark.parametrize("name", ["tiny", "ds-small", "decode", "prefill", "skew", "block"])
+@pytest.mark.parametrize("name", ["tiny", "ds-small"])
 @pytest.mark.parametrize("bm", [16, 32, 64, 128])
 def test_align_bit_exact(name, bm):
     cfg = cfg_of(name)
@@ -347,62 +292,64 @@ def test_align_is_deterministic():
 
 # ------------------------------------------------------------------ steps 4-5: grouped GEMMs
 
-def stage_rows(al, bm, P, name, nsample, seed):
-    """Non-pad sorted rows to check: all of them for small workloads; else, for three
-    experts (most loaded, least loaded non-empty, median), the first and last rows of
-    their segments (tile edges and the ragged tail) plus a random sample."""
+def stage_rows(al, bm, P):
+    """Every non-pad sorted row (the small workloads' oracle runs them all in well under a second)."""
     R = int(al["num_tiles"][0]) * bm
-    real = np.nonzero(al["sorted_pair_ids"][:R] < P)[0]
-    if name in SMALL:
-        return real
-    counts = al["counts"]
-    order = np.argsort(counts, kind="stable")
-    nonempty = order[counts[order] > 0]
-    picks = [nonempty[-1], nonempty[0], nonempty[len(nonempty) // 2]]
-    rows = []
-    rng = np.random.default_rng(seed)
-    for e in picks:
-        r0, n = int(al["padded_offsets"][e]), int(counts[e])
-        seg = np.arange(r0, r0 + n)
-        rows += list(seg[:6]) + list(seg[-6:]) + list(rng.choice(seg, size=min(n, nsample // 3), replace=False))
-    return np.unique(np.array(rows, dtype=np.int64))
+    return np.nonzero(al["sorted_pair_ids"][:R] < P)[0]
 
 
-def experts_of_rows(al, bm, rows):
-    return sorted({int(al["tile_expert"][r // bm]) for r in rows})
+def run_i32(L, cfg, a, gather, d, bm):
+    """Raw int32 accumulators of the first (gather) or second GEMM through the C ABI."""
+    R = w8.w8a8_moe_max_rows(cfg.T, cfg.k, cfg.E, bm)
+    N, K = (2 * cfg.I, cfg.H) if gather else (cfg.H, cfg.I)
+    out = torch.empty((R, N), dtype=torch.int32, device=DEV)
+    ws = torch.empty(max(w8.w8a8_grouped_gemm_i32_workspace_bytes(gather, N, K, cfg.T, cfg.k, cfg.E, bm), 256),
+                     dtype=torch.uint8, device=DEV)
+    w8.w8a8_grouped_gemm_i32(dt(a), gather, L.w13 if gather else L.w2, d["sorted_pair_ids"], d["padded_offsets"],
+                             d["tile_expert"], d["num_tiles"], cfg.T, cfg.k, bm, out, ws)
+    return host(out)
 
 
-@pytest.mark.parametrize("name", ["tiny", "ds-small", "decode", "prefill", "skew", "block"])
-def test_gemm_i32_bit_exact(name):
+@pytest.mark.parametrize("bm", [16, 32, 64, 128])
+@pytest.mark.parametrize("name", ["tiny", "ds-small"])
+def test_gemm_i32_bit_exact(name, bm):
     cfg = cfg_of(name)
-    bm = block_m_of(cfg)
     say(f"[gemm_i32] {name} block_m={bm}")
     L = layer_of(name)
     ids, _ = route_host(cfg)
     P = cfg.T * cfg.k
     al, d = oracle_align_dev(ids, cfg.E, bm)
-    group = 128 if cfg.scale_mode == "block" else 0
-    a_q, _ = oracle.quant_per_token(oracle.activations_f32(cfg), group)
+    a_q, _ = oracle.quant_per_token(oracle.activations_f32(cfg), 0)
     R = w8.w8a8_moe_max_rows(cfg.T, cfg.k, cfg.E, bm)
-    rows = stage_rows(al, bm, P, name, 48, 1)
-    w = oracle_weights(name, experts_of_rows(al, bm, rows))
+    rows = stage_rows(al, bm, P)
+    w = oracle_weights(name, range(cfg.E))
     # first GEMM: gathered token rows x w13
-    out = torch.empty((R, 2 * cfg.I), dtype=torch.int32, device=DEV)
-    w8.w8a8_grouped_gemm_i32(dt(a_q), True, L.w13, d["sorted_pair_ids"], d["tile_expert"], d["num_tiles"], cfg.T,
-                             cfg.k, bm, out)
-    ref = oracle.grouped_gemm_i32(a_q, True, w[0], al, bm, P, cfg.k, rows)
-    got = host(out)
-    assert np.array_equal(got[rows], ref[rows])
+    got = run_i32(L, cfg, a_q, True, d, bm)
+    assert np.array_equal(got[rows], oracle.grouped_gemm_i32(a_q, True, w[0], al, bm, P, cfg.k, rows)[rows])
     # second GEMM form: sorted rows of an int8 intermediate x w2
     h = synth.int8_matrix(R, cfg.I, cfg.seed)
-    out2 = torch.empty((R, cfg.H), dtype=torch.int32, device=DEV)
-    w8.w8a8_grouped_gemm_i32(dt(h), False, L.w2, d["sorted_pair_ids"], d["tile_expert"], d["num_tiles"], cfg.T,
-                             cfg.k, bm, out2)
-    ref2 = oracle.grouped_gemm_i32(h, False, w[2], al, bm, P, cfg.k, rows)
-    assert np.array_equal(host(out2)[rows], ref2[rows])
+    got2 = run_i32(L, cfg, h, False, d, bm)
+    assert np.array_equal(got2[rows], oracle.grouped_gemm_i32(h, False, w[2], al, bm, P, cfg.k, rows)[rows])
 
 
-@pytest.mark.parametrize("name", ["tiny", "ds-small", "ds-small-block", "decode", "prefill", "skew", "block"])
+def test_i32_rejects_bad_calls():
+    cfg = cfg_of("ds-small")
+    L = layer_of("ds-small")
+    bm = 16
+    ids, _ = route_host(cfg)
+    _, d = oracle_align_dev(ids, cfg.E, bm)
+    a = torch.zeros((cfg.T, cfg.H), dtype=torch.int8, device=DEV)
+    R = w8.w8a8_moe_max_rows(cfg.T, cfg.k, cfg.E, bm)
+    out = torch.empty((R, 2 * cfg.I), dtype=torch.int32, device=DEV)
+    need = w8.w8a8_grouped_gemm_i32_workspace_bytes(True, 2 * cfg.I, cfg.H, cfg.T, cfg.k, cfg.E, bm)
+    short = torch.empty(max(need - 256, 0), dtype=torch.uint8, device=DEV)
+    with pytest.raises(w8.W8A8Error) as ex:
+        w8.w8a8_grouped_gemm_i32(a, True, L.w13, d["sorted_pair_ids"], d["padded_offsets"], d["tile_expert"],
+                                 d["num_tiles"], cfg.T, cfg.k, bm, out, short)
+    assert ex.value.status == w8.W8A8_WORKSPACE_TOO_SMALL
+
+
+@pytest.mark.parametrize("name", ["tiny", "ds-small", "ds-small-block"])
 def test_first_gemm_silu_requant(name):
     cfg = cfg_of(name)
     block = cfg.scale_mode == "block"
@@ -422,8 +369,8 @@ def test_first_gemm_silu_requant(name):
     fn = w8.w8a8_block_grouped_gemm_w13_silu if block else w8.w8a8_grouped_gemm_w13_silu
     fn(dt(a_q), dt(a_s), L.w13, L.w13_scale, d["sorted_pair_ids"], d["padded_offsets"], d["tile_expert"],
        d["num_tiles"], cfg.T, cfg.k, bm, h_q, h_s, ws)
-    rows = stage_rows(al, bm, P, name, 48, 2)
-    w = oracle_weights(name, experts_of_rows(al, bm, rows))
+    rows = stage_rows(al, bm, P)
+    w = oracle_weights(name, range(cfg.E))
     rq, rs = oracle.w13_silu(a_q, a_s, w[0], w[1], al, bm, cfg.T, cfg.k, cfg.H, cfg.I, block, rows)
     gq, gs = host(h_q)[rows], host(h_s)[rows]
     rq, rs = rq[rows], rs[rows]
@@ -433,7 +380,7 @@ def test_first_gemm_silu_requant(name):
     assert np.mean(diff > 0) <= 1e-3, np.mean(diff > 0)
 
 
-@pytest.mark.parametrize("name", ["tiny", "ds-small", "ds-small-block", "decode", "prefill", "skew", "block"])
+@pytest.mark.parametrize("name", ["tiny", "ds-small", "ds-small-block"])
 def test_second_gemm_combine_bit_exact(name):
     """Fed the same intermediate, the second GEMM + combine performs the oracle's fp32
     operations in the oracle's order, so the output matches bit for bit."""
@@ -456,8 +403,8 @@ def test_second_gemm_combine_bit_exact(name):
     fn = w8.w8a8_block_grouped_gemm_w2_combine if block else w8.w8a8_grouped_gemm_w2_combine
     fn(dt(h_q), dt(h_s), L.w2, L.w2_scale, d["sorted_pair_ids"], d["padded_offsets"], d["tile_expert"],
        d["num_tiles"], dt(tw), cfg.T, cfg.k, bm, out, ws)
-    tokens = np.arange(cfg.T) if name in SMALL else sample(cfg.T, 3, 3)
-    w = oracle_weights(name, np.unique(ids[tokens]))
+    tokens = np.arange(cfg.T)
+    w = oracle_weights(name, range(cfg.E))
     ref = oracle.w2_combine(h_q, h_s, w[2], w[3], al, bm, tw, cfg.T, cfg.k, cfg.H, cfg.I, block, tokens)
     got = host(out)
     assert np.array_equal(got[tokens], ref)
@@ -521,6 +468,15 @@ def test_large_batch_engine_tile_edges(name):
     rows = edge_rows(al, counts)
     R = w8.w8a8_moe_max_rows(cfg.T, cfg.k, cfg.E, bm)
     w = oracle_weights(name, [e for e, n in enumerate(counts) if n])
+    engine = w8.w8a8_moe_engine(cfg.T, cfg.k, cfg.E, cfg.H, cfg.I, bm, mode)
+    assert engine == {"dsv3-e8": w8.ENGINE_DMA, "dsv3-e16": w8.ENGINE_RING, "dsv3-e8-block": w8.ENGINE_RING}[name]
+    if not block:  # raw int32 accumulators of both GEMMs through the same engine, bit for bit
+        a8, _ = oracle.quant_per_token(oracle.activations_f32(cfg), 0)
+        got = run_i32(L, cfg, a8, True, d, bm)
+        assert np.array_equal(got[rows], oracle.grouped_gemm_i32(a8, True, w[0], al, bm, P, cfg.k, rows)[rows])
+        h8 = synth.int8_matrix(R, cfg.I, cfg.seed + 7)
+        got2 = run_i32(L, cfg, h8, False, d, bm)
+        assert np.array_equal(got2[rows], oracle.grouped_gemm_i32(h8, False, w[2], al, bm, P, cfg.k, rows)[rows])
 
     a_q, a_s = oracle.quant_per_token(oracle.activations_f32(cfg), 128 if block else 0)
     h_q = torch.empty((R, cfg.I), dtype=torch.int8, device=DEV)
@@ -556,7 +512,7 @@ def test_large_batch_engine_tile_edges(name):
 
 # ------------------------------------------------------------------ the whole layer
 
-@pytest.mark.parametrize("name", ["tiny", "ds-small", "ds-small-block", "decode", "prefill", "skew", "block"])
+@pytest.mark.parametrize("name", ["tiny", "ds-small", "ds-small-block"])
 def test_forward_matches_oracle(name):
     cfg = cfg_of(name)
     say(f"[forward] {name}")
@@ -567,7 +523,7 @@ def test_forward_matches_oracle(name):
     ws = workload.forward_workspace(L)
     workload.forward(L, out, ws, topk_ids=ids, topk_weights=tw)
     got, gids = host(out), host(ids)
-    tokens = np.arange(cfg.T) if name in SMALL else sample(cfg.T, 3, 4)
+    tokens = np.arange(cfg.T)
     lg = synth.logits(cfg, slice(0, cfg.T))[tokens]
     ids_o, tw_o = oracle.route_cfg(cfg, lg)
     keep = np.all(gids[tokens] == ids_o, axis=1)

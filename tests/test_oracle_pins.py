@@ -413,6 +413,57 @@ def test_grouped_sigmoid_routing_brute_force():
         assert np.all(np.abs(w[t] - ref) <= 1e-6 * ref)
 
 
+def test_softmax_routing_without_renormalize_brute_force():
+    """renormalize = 0: the weight of a selected expert is its softmax probability over all E
+    logits (not over the selected ones), times the routed scaling; the selection is the best
+    k-subset by logit sum.  A sum over the selected logits only (the renormalized rule) fails."""
+    E = 8
+    lg = synth.normal(150 * E, 12, synth.STREAM_MISC).reshape(150, E)
+    for k in (1, 2, 3, 8):
+        ids, w = oracle.route(lg, k, oracle.SOFTMAX, 1, 1, False, 1.5)
+        for t in range(lg.shape[0]):
+            best = max(itertools.combinations(range(E), k), key=lambda c: sum(float(lg[t, i]) for i in c))
+            assert set(ids[t]) == set(best)
+            full = np.exp(lg[t].astype(np.float64) - lg[t].max())
+            ref = full[ids[t]] / full.sum() * 1.5
+            assert np.all(np.abs(w[t] - ref) <= 16 * U * ref), (k, t)
+            if k < E:
+                assert w[t].astype(np.float64).sum() < 1.5 * (1 - 1e-4)
+        if k == E:  # every expert selected: the probabilities sum to one before the scaling
+            assert np.all(np.abs(w.astype(np.float64).sum(1) - 1.5) <= 1.5 * 16 * U)
+
+
+@pytest.mark.parametrize("renorm", [True, False])
+def test_sigmoid_routing_with_correction_bias_brute_force(renorm):
+    """A correction bias moves the selection, not the weights: groups and experts are chosen by
+    c = sigmoid(l) + bias (group score = sum of its two largest c), the weights are the selected
+    sigmoid(l) (normalized if renorm) times the scaling.  Brute force over every group subset and
+    expert subset on E = 8; a dropped bias, or weights taken from c, fails."""
+    E, ng, tg, k = 8, 4, 2, 3
+    T = 300
+    lg = synth.normal(T * E, 13, synth.STREAM_MISC).reshape(T, E)
+    bias = synth.normal(E, 14, synth.STREAM_MISC, 0, 0.4)
+    ids, w = oracle.route(lg, k, oracle.SIGMOID, ng, tg, renorm, 2.5, bias)
+    ids0, _ = oracle.route(lg, k, oracle.SIGMOID, ng, tg, renorm, 2.5, None)
+    moved = 0
+    for t in range(T):
+        s = _sig64(lg[t])
+        c = s + bias.astype(np.float64)
+        gscore = [sum(sorted(c[g * 2:(g + 1) * 2])[-2:]) for g in range(ng)]
+        groups = max(itertools.combinations(range(ng), tg), key=lambda gs: sum(gscore[g] for g in gs))
+        allowed = [e for g in groups for e in range(g * 2, g * 2 + 2)]
+        best = max(itertools.combinations(allowed, k), key=lambda sel: sum(c[e] for e in sel))
+        margin = sum(c[e] for e in best) - max(sum(c[e] for e in sel)
+                                               for sel in itertools.combinations(allowed, k) if set(sel) != set(best))
+        if margin > 1e-5:  # no near-tie between fp32 and fp64 scores
+            assert set(ids[t]) == set(best), t
+        assert np.all(np.diff(c[ids[t]]) <= 1e-6)  # slots in descending c
+        ref = s[ids[t]] / s[ids[t]].sum() * 2.5 if renorm else s[ids[t]] * 2.5
+        assert np.all(np.abs(w[t] - ref) <= 1e-6 * ref), t
+        moved += set(ids[t]) != set(ids0[t])
+    assert moved >= T // 10  # the bias changed many selections
+
+
 def test_deepseek_routing_invariants():
     cfg = synth.CONFIGS["decode"]
     lg = synth.logits(cfg)

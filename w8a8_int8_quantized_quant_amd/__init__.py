@@ -33,7 +33,8 @@ SCALE_W4A8 = 3
 # Every symbol the C header declares (checked by the CPU test suite).
 EXPORTS = (
     "w8a8_status_string", "w8a8_quant_per_token", "w8a8_quant_blocks", "moe_topk_route", "w8a8_moe_max_rows",
-    "moe_align_workspace_bytes", "moe_align_by_expert", "w8a8_grouped_gemm_i32", "w8a8_w13_workspace_bytes",
+    "moe_align_workspace_bytes", "moe_align_by_expert", "w8a8_grouped_gemm_i32",
+    "w8a8_grouped_gemm_i32_workspace_bytes", "w8a8_moe_engine", "w8a8_w13_workspace_bytes",
     "w8a8_grouped_gemm_w13_silu", "w8a8_w2_workspace_bytes", "w8a8_grouped_gemm_w2_combine",
     "w8a8_block_grouped_gemm_w13_silu", "w8a8_block_grouped_gemm_w2_combine", "w8a8_moe_pick_block_m",
     "w8a8_moe_workspace_bytes", "w8a8_moe_forward", "w8a8_linear_workspace_bytes", "w8a8_linear",
@@ -82,7 +83,10 @@ def lib() -> ctypes.CDLL:
             "w8a8_moe_max_rows": (i64, [i64, i64, i64, i64]),
             "moe_align_workspace_bytes": (sz, [i64, i64, i64]),
             "moe_align_by_expert": (i32, [vp, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
-            "w8a8_grouped_gemm_i32": (i32, [vp, i32, vp, i64, i64, vp, vp, vp, i64, i64, i64, i64, vp, vp]),
+            "w8a8_grouped_gemm_i32": (i32, [vp, i32, vp, i64, i64, vp, vp, vp, vp, i64, i64, i64, i64, vp, vp, sz,
+                                            vp]),
+            "w8a8_grouped_gemm_i32_workspace_bytes": (sz, [i32, i64, i64, i64, i64, i64, i64]),
+            "w8a8_moe_engine": (i32, [i64, i64, i64, i64, i64, i64, i32]),
             "w8a8_w13_workspace_bytes": (sz, [i64, i64, i64, i64, i64, i64, i32]),
             "w8a8_w2_workspace_bytes": (sz, [i64, i64, i64, i64, i64, i64, i32]),
             "w8a8_grouped_gemm_w13_silu": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, vp, vp,
@@ -208,11 +212,26 @@ def moe_align_by_expert(topk_ids, E: int, block_m: int, expert_counts, expert_of
           0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
 
 
-def w8a8_grouped_gemm_i32(a, gather: bool, w, sorted_pair_ids, tile_expert, num_tiles, T: int, k: int,
-                          block_m: int, out, stream=None) -> None:
+def w8a8_grouped_gemm_i32_workspace_bytes(gather: bool, N: int, K: int, T: int, k: int, E: int, block_m: int) -> int:
+    return lib().w8a8_grouped_gemm_i32_workspace_bytes(int(gather), N, K, T, k, E, block_m)
+
+
+def w8a8_grouped_gemm_i32(a, gather: bool, w, sorted_pair_ids, padded_offsets, tile_expert, num_tiles, T: int, k: int,
+                          block_m: int, out, ws, stream=None) -> None:
     E, N, K = w.shape
-    _call("w8a8_grouped_gemm_i32", _ptr(a), int(gather), _ptr(w), N, K, _ptr(sorted_pair_ids), _ptr(tile_expert),
-          _ptr(num_tiles), T, k, E, block_m, _ptr(out), _stream(stream))
+    _call("w8a8_grouped_gemm_i32", _ptr(a), int(gather), _ptr(w), N, K, _ptr(sorted_pair_ids), _ptr(padded_offsets),
+          _ptr(tile_expert), _ptr(num_tiles), T, k, E, block_m, _ptr(out), _ptr(ws), _nbytes(ws), _stream(stream))
+
+
+ENGINE_STAGED = 0
+ENGINE_DMA = 1
+ENGINE_RING = 2
+ENGINE_STREAM = 3
+
+
+def w8a8_moe_engine(T: int, k: int, E: int, H: int, I: int, block_m: int, scale_mode: int = SCALE_CHANNEL) -> int:
+    """GEMM engine of a layer of this shape (ENGINE_*), -1 for an invalid shape."""
+    return lib().w8a8_moe_engine(T, k, E, H, I, block_m, scale_mode)
 
 
 def w8a8_w13_workspace_bytes(T, k, E, H, I, block_m, scale_mode=SCALE_CHANNEL) -> int:

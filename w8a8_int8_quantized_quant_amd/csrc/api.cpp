@@ -186,19 +186,49 @@ int32_t moe_align_by_expert(const int32_t* topk_ids, int64_t T, int64_t k, int64
                                           sorted_pair_ids, tile_expert, num_tiles, mr / block_m, ws, stream));
 }
 
-int32_t w8a8_grouped_gemm_i32(const int8_t* a, int32_t gather, const int8_t* w, int64_t N, int64_t K,
-                              const int32_t* sorted_pair_ids, const int32_t* tile_expert, const int32_t* num_tiles,
-                              int64_t T, int64_t k, int64_t E, int64_t block_m, int32_t* out, hipStream_t stream) {
+// Shape of the layer whose first (gather = 1: N = 2I, K = H) or second (gather = 0: N = H, K = I) GEMM
+// the raw int32 entry runs.
+static int32_t i32_shape(int32_t gather, int64_t N, int64_t K, int64_t T, int64_t k, int64_t E, int64_t block_m,
+                         GroupedShape* s) {
   int32_t st = check_tke(T, k, E);
   if (st) return st;
   if (N < 0 || K < 0 || block_m < 0 || (gather != 0 && gather != 1)) return W8A8_INVALID_ARGUMENT;
-  if (!valid_dim(N) || !valid_dim(K) || !valid_block_m(block_m)) return W8A8_UNSUPPORTED_SHAPE;
+  const int64_t H = gather ? K : N, I = gather ? N / 2 : K;
+  if ((gather && N % 2) || !valid_dim(H) || !valid_dim(I) || !valid_block_m(block_m)) return W8A8_UNSUPPORTED_SHAPE;
+  *s = shape_of(T, k, E, H, I, block_m);
+  return W8A8_OK;
+}
+
+size_t w8a8_grouped_gemm_i32_workspace_bytes(int32_t gather, int64_t N, int64_t K, int64_t T, int64_t k, int64_t E,
+                                             int64_t block_m) {
+  GroupedShape s;
+  if (i32_shape(gather, N, K, T, k, E, block_m, &s)) return 0;
+  return w8a8::i32_ws_bytes(s);
+}
+
+int32_t w8a8_grouped_gemm_i32(const int8_t* a, int32_t gather, const int8_t* w, int64_t N, int64_t K,
+                              const int32_t* sorted_pair_ids, const int32_t* padded_offsets,
+                              const int32_t* tile_expert, const int32_t* num_tiles, int64_t T, int64_t k, int64_t E,
+                              int64_t block_m, int32_t* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  GroupedShape s;
+  int32_t st = i32_shape(gather, N, K, T, k, E, block_m, &s);
+  if (st) return st;
   if (T == 0) return W8A8_OK;
-  if (!ok16(a) || !ok16(w) || !ok16(out) || !ok4(sorted_pair_ids) || !ok4(tile_expert) || !ok4(num_tiles))
+  if (!ok16(a) || !ok16(w) || !ok16(out) || !ok4(sorted_pair_ids) || !ok4(padded_offsets) || !ok4(tile_expert) ||
+      !ok4(num_tiles))
     return W8A8_INVALID_ARGUMENT;
-  const int64_t mr = max_rows_of(T, k, E, block_m);
-  return hip_status(w8a8::gemm_i32(a, gather, w, N, K, sorted_pair_ids, tile_expert, num_tiles, T * k, k, block_m,
-                                   mr, out, stream));
+  if (ws_bytes < w8a8::i32_ws_bytes(s)) return W8A8_WORKSPACE_TOO_SMALL;
+  if (!aligned(ws, 256)) return W8A8_INVALID_ARGUMENT;
+  return hip_status(w8a8::gemm_i32(s, gather, a, w, sorted_pair_ids, padded_offsets, tile_expert, num_tiles, out,
+                                   ws, stream));
+}
+
+int32_t w8a8_moe_engine(int64_t T, int64_t k, int64_t E, int64_t H, int64_t I, int64_t block_m, int32_t scale_mode) {
+  if (check_tke(T, k, E) || !valid_dim(H) || !valid_dim(I) || !valid_block_m(block_m) || !valid_mode(scale_mode))
+    return -1;
+  const GroupedShape s = shape_of(T, k, E, H, I, block_m);
+  if (fp8_mode(scale_mode) && !w8a8::fp8_supported(s)) return -1;
+  return w8a8::engine_of(s, scale_mode);
 }
 
 size_t w8a8_w13_workspace_bytes(int64_t T, int64_t k, int64_t E, int64_t H, int64_t I, int64_t block_m,

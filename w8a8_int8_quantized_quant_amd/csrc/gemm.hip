@@ -173,6 +173,7 @@ __device__ __forceinline__ void epilogue(const Params& p, const AccT (&acc)[FM][
   constexpr int FNH = FN / 2;
   constexpr bool kBlock = is_block<EPI>();
   if constexpr (EPI == Epi::I32) {
+    // raw accumulators at their weight rows (gate and up halves of a split tile go to their own columns)
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
@@ -181,7 +182,8 @@ __device__ __forceinline__ void epilogue(const Params& p, const AccT (&acc)[FM][
         if (sh_pid[trow] >= p.P) continue;
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn)
-          p.out_i32[(row0 + trow) * p.N + nt * BN + brow_of<BN, WN, FN, MAP>(wn, fn) + (l % 16)] = acc[fm][fn][r];
+          p.out_i32[(row0 + trow) * p.N + wrow_of<BN, MAP>(nt, brow_of<BN, WN, FN, MAP>(wn, fn) + (l % 16), p.I)] =
+              acc[fm][fn][r];
       }
   } else if constexpr (EPI == Epi::W2Channel || EPI == Epi::W2Block || EPI == Epi::W2Fp8 || EPI == Epi::W2W4) {
 #pragma unroll
@@ -761,8 +763,8 @@ __device__ __forceinline__ void dma_epilogue(const Params& p, const i32x4 (&acc)
 #pragma unroll
         for (int c = l; c < COLS / 4; c += kWave) {
           const float4 v = *reinterpret_cast<const float4*>((hf == 0 ? buf0 : buf1) + lr * STRIDE + c * 16);
-          if constexpr (EPI == Epi::I32)
-            reinterpret_cast<float4*>(p.out_i32 + i32_off + (row0 + trow) * p.N + nt * BN)[c] = v;  // int32 bits
+          if constexpr (EPI == Epi::I32)  // int32 bits; a split tile's 4 columns lie in one half (BN / 2 % 4 == 0)
+            *reinterpret_cast<float4*>(p.out_i32 + i32_off + (row0 + trow) * p.N + wrow_of<BN, MAP>(nt, 4 * c, I)) = v;
           else
             reinterpret_cast<float4*>(p.out_f32 + (row0 + trow) * p.N + nt * BN)[c] = v;
         }
@@ -922,7 +924,7 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_ring_kernel(c
   constexpr int LD = A_LD + B_LD;
   constexpr int STAGE = BM * kDmaBK + BN * BKB;
   constexpr int SG = 4;  // K-blocks per activation-scale DMA
-  static_assert(EPI != Epi::I32, "scaled epilogues only");
+  static_assert(EPI != Epi::I32 || !kW4, "raw int32 sums of 8-bit operands");
   static_assert(A_LD >= 1 && B_LD >= 1 && (BM * CPR) % NT == 0 && (BN * CPRB) % NT == 0, "tile shape");
   static_assert(KT >= 1 && (NS - 2) * (LD + 1) < 32, "K steps");
   // NS <= 5: the scale group a DMA overwrites was last read before the step that issues it
@@ -1605,23 +1607,50 @@ size_t w2_ws_bytes(const GroupedShape& s, int32_t scale_mode) {
          work_bytes(s);
 }
 
-hipError_t gemm_i32(const int8_t* a, int32_t gather, const int8_t* w, int64_t N, int64_t K, const int32_t* sorted,
-                    const int32_t* tile_expert, const int32_t* num_tiles, int64_t P, int64_t k, int64_t block_m,
-                    int64_t max_rows, int32_t* out, hipStream_t stream) {
+int32_t engine_of(const GroupedShape& s, int32_t scale_mode) {
+  if (scale_mode == 2 || scale_mode == 3) {
+    if (scale_mode == 3 && s.T * s.k < kStreamMaxAvgRows * s.E) return kEngineStream;
+    return kEngineRing;
+  }
+  if (scale_mode == 1) return use_ring(s, 1) ? kEngineRing : kEngineStaged;
+  return use_ring(s, 0) ? kEngineRing : use_dma(s) ? kEngineDma : kEngineStaged;
+}
+
+size_t i32_ws_bytes(const GroupedShape& s) { return work_bytes(s); }
+
+// The raw accumulators through the engine, tile shape, gate/up pairing and work order of the
+// channel-wise GEMM of the same shape (gather = 1: the first GEMM, gather = 0: the second), with
+// an epilogue that stores the int32 sums instead of scaling them.
+hipError_t gemm_i32(const GroupedShape& s, int32_t gather, const int8_t* a, const int8_t* w, const int32_t* sorted,
+                    const int32_t* padded_offsets, const int32_t* tile_expert, const int32_t* num_tiles, int32_t* out,
+                    void* ws, hipStream_t stream) {
+  if (s.T == 0) return hipSuccess;
   Params prm{};
   prm.a = a;
   prm.gather = gather;
   prm.w = w;
-  prm.N = N;
-  prm.K = K;
+  prm.N = gather ? 2 * s.I : s.H;
+  prm.K = gather ? s.H : s.I;
   prm.sorted = sorted;
   prm.tile_expert = tile_expert;
   prm.num_tiles = num_tiles;
-  prm.P = P;
-  prm.k = k;
-  prm.block_m = block_m;
+  prm.P = s.T * s.k;
+  prm.k = s.k;
+  prm.block_m = s.block_m;
+  prm.I = s.I;
   prm.out_i32 = out;
-  return launch_bm<BMap::Plain, Epi::I32, kBNStaged>(prm, max_rows, stream);
+  int32_t* work = static_cast<int32_t*>(ws);
+  const int32_t engine = engine_of(s, 0);
+  if (gather) {
+    if (engine == kEngineRing)
+      return launch_ring<BMap::Split, Epi::I32, kRingH / kDmaBK>(prm, s, padded_offsets, work, stream);
+    if (engine == kEngineDma) return launch_dma<BMap::Split, Epi::I32>(prm, s, padded_offsets, work, stream);
+    return launch_bm<BMap::Split, Epi::I32, kBNStaged>(prm, s.max_rows, stream);
+  }
+  if (engine == kEngineRing)
+    return launch_ring<BMap::Plain, Epi::I32, kRingI / kDmaBK>(prm, s, padded_offsets, work, stream);
+  if (engine == kEngineDma) return launch_dma<BMap::Plain, Epi::I32>(prm, s, padded_offsets, work, stream);
+  return launch_bm<BMap::Plain, Epi::I32, kBNStaged>(prm, s.max_rows, stream);
 }
 
 hipError_t w13_silu(const GroupedShape& s, int32_t scale_mode, const int8_t* a_q, const float* a_s,

@@ -37,9 +37,13 @@ struct GroupedShape {
 size_t w13_ws_bytes(const GroupedShape& s, int32_t scale_mode);
 bool fp8_supported(const GroupedShape& s);  // the FP8 and W4A8 GEMMs' shape limits
 size_t w2_ws_bytes(const GroupedShape& s, int32_t scale_mode);
-hipError_t gemm_i32(const int8_t* a, int32_t gather, const int8_t* w, int64_t N, int64_t K, const int32_t* sorted,
-                    const int32_t* tile_expert, const int32_t* num_tiles, int64_t P, int64_t k, int64_t block_m,
-                    int64_t max_rows, int32_t* out, hipStream_t stream);
+// GEMM engines (the values of w8a8_moe_engine in the C ABI).
+constexpr int32_t kEngineStaged = 0, kEngineDma = 1, kEngineRing = 2, kEngineStream = 3;
+int32_t engine_of(const GroupedShape& s, int32_t scale_mode);  // the same engine for both GEMMs of a layer
+size_t i32_ws_bytes(const GroupedShape& s);
+hipError_t gemm_i32(const GroupedShape& s, int32_t gather, const int8_t* a, const int8_t* w, const int32_t* sorted,
+                    const int32_t* padded_offsets, const int32_t* tile_expert, const int32_t* num_tiles, int32_t* out,
+                    void* ws, hipStream_t stream);
 hipError_t w13_silu(const GroupedShape& s, int32_t scale_mode, const int8_t* a_q, const float* a_s,
                     const int8_t* w13, const float* w13_s, const int32_t* sorted, const int32_t* padded_offsets,
                     const int32_t* tile_expert, const int32_t* num_tiles, int8_t* h_q, float* h_s, void* ws,
