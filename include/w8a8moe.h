@@ -145,6 +145,24 @@ int32_t moe_align_by_expert(const int32_t* topk_ids, int64_t T, int64_t k, int64
                             int32_t* sorted_pair_ids, int32_t* tile_expert, int32_t* num_tiles, void* ws,
                             size_t ws_bytes, hipStream_t stream);
 
+/* The same align for callers that cannot allocate or pass a workspace (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  Arguments and outputs as
+ * moe_align_by_expert, bit-identical to it; no ws.  Its scratch (the per-chunk histograms and the
+ * pairs' ranks, align's workspace) is a device array of moe_align_noalloc_scratch_bytes() = 4 MiB
+ * inside the library, one per GPU, held until the process ends; the call allocates nothing and
+ * needs nothing cleared (every scratch word it reads, it wrote earlier in the same call).
+ * Returns W8A8_UNSUPPORTED_SHAPE when moe_align_workspace_bytes(T, k, E) exceeds that size (for
+ * E = 256 up to about 838k pairs; 4*T*k + 4*E*ceil(T*k/1024) bytes, each term rounded up to 256).
+ * Calls on one GPU share its array: two calls whose kernels overlap on that GPU (other streams,
+ * other host threads) race and give wrong results; calls in one stream order are safe.  The first
+ * call on each device resolves the array's device address (hipGetSymbolAddress, no allocation);
+ * make that first call outside stream capture. */
+int32_t moe_align_by_expert_noalloc(const int32_t* topk_ids, int64_t T, int64_t k, int64_t E, int64_t block_m,
+                                    int32_t* expert_counts, int32_t* expert_offsets, int32_t* padded_offsets,
+                                    int32_t* sorted_pair_ids, int32_t* tile_expert, int32_t* num_tiles,
+                                    hipStream_t stream);
+size_t moe_align_noalloc_scratch_bytes(void);
+
 /* ------------------------------------------------------------------ steps 4-5: grouped INT8 GEMMs
  * Common arguments (outputs of moe_align_by_expert with the same block_m):
  *   sorted_pair_ids, padded_offsets, tile_expert, num_tiles (device; num_tiles is read on the

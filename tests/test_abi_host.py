@@ -129,6 +129,23 @@ def test_align_validation():
                                  None) == SHAPE  # too many pairs
 
 
+def test_noalloc_align_validation():
+    """The allocation-free align rejects, before any HIP call, pair counts whose align scratch
+    exceeds its fixed 4 MiB, and the same invalid arguments as the workspace align."""
+    L = w8.lib()
+    assert w8.moe_align_noalloc_scratch_bytes() == 4 << 20
+    na = lambda T, k, E, bm: (P16, T, k, E, bm, P16, P16, P16, P16, P16, P16, None)
+    assert w8.moe_align_workspace_bytes(131072, 8, 256) > 4 << 20
+    assert L.moe_align_by_expert_noalloc(*na(131072, 8, 256, 16)) == SHAPE   # 1M pairs
+    assert L.moe_align_by_expert_noalloc(*na(60000, 16, 1024, 16)) == SHAPE  # E = 1024: 8 bytes a pair
+    assert L.moe_align_by_expert_noalloc(*na(128, 8, 256, 24)) == SHAPE
+    assert L.moe_align_by_expert_noalloc(*na(128, 300, 256, 16)) == SHAPE
+    assert L.moe_align_by_expert_noalloc(*na(-1, 8, 256, 16)) == INV
+    bad = list(na(128, 8, 256, 16))
+    bad[5] = P16 + 2  # counts not 4-byte aligned
+    assert L.moe_align_by_expert_noalloc(*bad) == INV
+
+
 def test_gemm_validation():
     L = w8.lib()
     ineed = w8.w8a8_grouped_gemm_i32_workspace_bytes(True, 256, 256, 16, 2, 8, 16)

@@ -33,7 +33,8 @@ SCALE_W4A8 = 3
 # Every symbol the C header declares (checked by the CPU test suite).
 EXPORTS = (
     "w8a8_status_string", "w8a8_quant_per_token", "w8a8_quant_blocks", "moe_topk_route", "w8a8_moe_max_rows",
-    "moe_align_workspace_bytes", "moe_align_by_expert", "w8a8_grouped_gemm_i32",
+    "moe_align_workspace_bytes", "moe_align_by_expert", "moe_align_by_expert_noalloc",
+    "moe_align_noalloc_scratch_bytes", "w8a8_grouped_gemm_i32",
     "w8a8_grouped_gemm_i32_workspace_bytes", "w8a8_moe_engine", "w8a8_w13_workspace_bytes",
     "w8a8_grouped_gemm_w13_silu", "w8a8_w2_workspace_bytes", "w8a8_grouped_gemm_w2_combine",
     "w8a8_block_grouped_gemm_w13_silu", "w8a8_block_grouped_gemm_w2_combine", "w8a8_moe_pick_block_m",
@@ -83,6 +84,8 @@ def lib() -> ctypes.CDLL:
             "w8a8_moe_max_rows": (i64, [i64, i64, i64, i64]),
             "moe_align_workspace_bytes": (sz, [i64, i64, i64]),
             "moe_align_by_expert": (i32, [vp, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+            "moe_align_by_expert_noalloc": (i32, [vp, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp]),
+            "moe_align_noalloc_scratch_bytes": (sz, []),
             "w8a8_grouped_gemm_i32": (i32, [vp, i32, vp, i64, i64, vp, vp, vp, vp, i64, i64, i64, i64, vp, vp, sz,
                                             vp]),
             "w8a8_grouped_gemm_i32_workspace_bytes": (sz, [i32, i64, i64, i64, i64, i64, i64]),
@@ -210,6 +213,18 @@ def moe_align_by_expert(topk_ids, E: int, block_m: int, expert_counts, expert_of
     _call("moe_align_by_expert", _ptr(topk_ids), T, k, E, block_m, _ptr(expert_counts), _ptr(expert_offsets),
           _ptr(padded_offsets), _ptr(sorted_pair_ids), _ptr(tile_expert), _ptr(num_tiles), _ptr(ws),
           0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+
+
+def moe_align_by_expert_noalloc(topk_ids, E: int, block_m: int, expert_counts, expert_offsets, padded_offsets,
+                                sorted_pair_ids, tile_expert, num_tiles, stream=None) -> None:
+    """moe_align_by_expert without a workspace (the library's own 4 MiB device scratch)."""
+    T, k = topk_ids.shape
+    _call("moe_align_by_expert_noalloc", _ptr(topk_ids), T, k, E, block_m, _ptr(expert_counts), _ptr(expert_offsets),
+          _ptr(padded_offsets), _ptr(sorted_pair_ids), _ptr(tile_expert), _ptr(num_tiles), _stream(stream))
+
+
+def moe_align_noalloc_scratch_bytes() -> int:
+    return lib().moe_align_noalloc_scratch_bytes()
 
 
 def w8a8_grouped_gemm_i32_workspace_bytes(gather: bool, N: int, K: int, T: int, k: int, E: int, block_m: int) -> int:

@@ -11,6 +11,8 @@
 // holding the same expert form a mask; the rank is the popcount below the
 // lane), wave histograms give the rank inside the chunk, one scan over chunks
 // gives each chunk's base per expert, and a scatter writes every pair once.
+#include <mutex>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -178,6 +180,34 @@ __global__ __launch_bounds__(kThreads) void align_scatter_kernel(const int32_t* 
 size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 
 }  // namespace
+
+// Scratch of the allocation-free align entry point: the histogram and rank buffers live in this
+// array instead of a caller's workspace.  Each device holds its own copy (at its own address) for
+// the life of the process.  In host code `scratch` names a host-side stand-in, never the device
+// memory: kernels and copies get the address resolved per device below.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+// Device address of this device's `scratch`, resolved once per device (with that device current)
+// and kept; later calls reuse it.
+hipError_t noalloc_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return err;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 size_t align_ws_bytes(int64_t P, int64_t E) {
   const int64_t nchunks = (P + kAlignChunk - 1) / kAlignChunk;

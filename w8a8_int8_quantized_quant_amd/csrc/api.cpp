@@ -186,6 +186,29 @@ int32_t moe_align_by_expert(const int32_t* topk_ids, int64_t T, int64_t k, int64
                                           sorted_pair_ids, tile_expert, num_tiles, mr / block_m, ws, stream));
 }
 
+int32_t moe_align_by_expert_noalloc(const int32_t* topk_ids, int64_t T, int64_t k, int64_t E, int64_t block_m,
+                                    int32_t* expert_counts, int32_t* expert_offsets, int32_t* padded_offsets,
+                                    int32_t* sorted_pair_ids, int32_t* tile_expert, int32_t* num_tiles,
+                                    hipStream_t stream) {
+  int32_t st = check_tke(T, k, E);
+  if (st) return st;
+  if (block_m < 0) return W8A8_INVALID_ARGUMENT;
+  if (!valid_block_m(block_m)) return W8A8_UNSUPPORTED_SHAPE;
+  if (!ok4(expert_counts) || !ok4(expert_offsets) || !ok4(padded_offsets) || !ok4(num_tiles))
+    return W8A8_INVALID_ARGUMENT;
+  const int64_t P = T * k;
+  if (P > 0 && (!ok4(topk_ids) || !ok4(sorted_pair_ids) || !ok4(tile_expert))) return W8A8_INVALID_ARGUMENT;
+  if (w8a8::align_ws_bytes(P, E) > w8a8::kNoAllocScratchBytes) return W8A8_UNSUPPORTED_SHAPE;
+  void* scratch = nullptr;
+  hipError_t e = w8a8::noalloc_scratch(&scratch);
+  if (e != hipSuccess) return W8A8_HIP_ERROR;
+  const int64_t mr = max_rows_of(T, k, E, block_m);
+  return hip_status(w8a8::align_by_expert(topk_ids, P, E, block_m, expert_counts, expert_offsets, padded_offsets,
+                                          sorted_pair_ids, tile_expert, num_tiles, mr / block_m, scratch, stream));
+}
+
+size_t moe_align_noalloc_scratch_bytes(void) { return w8a8::kNoAllocScratchBytes; }
+
 // Shape of the layer whose first (gather = 1: N = 2I, K = H) or second (gather = 0: N = H, K = I) GEMM
 // the raw int32 entry runs.
 static int32_t i32_shape(int32_t gather, int64_t N, int64_t K, int64_t T, int64_t k, int64_t E, int64_t block_m,

@@ -23,6 +23,10 @@ hipError_t topk_route(const float* logits, int64_t T, int64_t E, int64_t k, int3
 // align.hip
 constexpr int64_t kAlignChunk = 1024;  // pairs per histogram chunk
 size_t align_ws_bytes(int64_t P, int64_t E);
+// The allocation-free align entry point's scratch: a file-scope device array of this many bytes in
+// align.hip; noalloc_scratch gives its address on the current device.
+constexpr size_t kNoAllocScratchBytes = size_t(4) << 20;
+hipError_t noalloc_scratch(void** ptr);
 hipError_t align_by_expert(const int32_t* ids, int64_t P, int64_t E, int64_t block_m, int32_t* counts,
                            int32_t* offsets, int32_t* padded_offsets, int32_t* sorted, int32_t* tile_expert,
                            int32_t* num_tiles, int64_t max_tiles, void* ws, hipStream_t stream);
