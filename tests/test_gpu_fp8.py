@@ -19,8 +19,13 @@ Bars:
     the requantized value is within half an E4M3 step of the value it rounds; so every
     dequantized code is checked against the exact fp64 h, and against the oracle's code, with
     those terms, and every h_scale against max|h| / 448;
-  - whole layer: max|err| <= 2e-2 * max|ref| over the checked tokens (an intermediate code one E4M3
-    step off moves a row's contribution by up to 1/16 of that value).
+  - whole layer: max|err| <= LAYER_BAR * max|ref| over the checked tokens, LAYER_BAR = 1e-2.  A
+    fraction f of the intermediate codes sits one E4M3 step (up to 1/8 of the value) off the
+    oracle's (f ~ 0.3%); an output sums N terms with random signs, of which f N are off by up to
+    1/8, so the error's spread is delta sqrt(f N) rms(term) against the output's sqrt(N) rms(term),
+    and the largest error over a token's outputs is about delta sqrt(f) = 0.125 sqrt(0.003) = 6.8e-3
+    of the largest output, whatever the sizes (measured: 6.6e-3 at H = 512, I = 256; 2.3e-3 at the
+    DeepSeek-V3 shapes); LAYER_BAR allows 1.5 times that.
 """
 import dataclasses
 import sys
@@ -39,6 +44,8 @@ if not torch.cuda.is_available():  # pragma: no cover - CPU container
     pytest.skip("needs a GPU", allow_module_level=True)
 
 import w8a8_int8_quantized_quant_amd as w8  # noqa: E402
+
+LAYER_BAR = 1e-2  # whole-layer error over max|ref| (derivation in the module docstring)
 from w8a8_int8_quantized_quant_amd import workload  # noqa: E402
 
 DEV = "cuda"
@@ -468,7 +475,7 @@ def test_fp8_forward_matches_oracle(name):
     say(f"[fp8 forward] {name}: max err {err:.3e}, max |ref| {np.abs(ref).max():.3e}, "
         f"bit-equal {np.mean(got[tokens] == ref):.4f}")
     assert np.isfinite(got).all()
-    assert err <= 2e-2 * np.abs(ref).max()
+    assert err <= LAYER_BAR * np.abs(ref).max()
 
 
 def test_fp8_unsupported_shapes_are_rejected():

@@ -66,10 +66,12 @@ def test_linear_decode_shape_full():
     assert np.array_equal(got, oracle.linear(a_q, a_s, w, w_s))
 
 
-def test_linear_prefill_shape_sampled():
-    """8192 tokens x (N = 7168, K = 2048): the rows around every 320-row tile edge, the first and
-    last rows, and a random sample, computed one by one by the oracle."""
-    M, N, K = 8192, 7168, 2048
+@pytest.mark.parametrize("K", [2048, 16384])
+def test_linear_prefill_shape_sampled(K):
+    """8192 tokens x N = 7168 (K = 16384: the attention output projection the benchmark times,
+    unsplit): the rows around every 320-row tile edge, the first and last rows, and a random
+    sample, computed one by one by the oracle."""
+    M, N = 8192, 7168
     say(f"[linear] M={M} N={N} K={K}")
     a_q, a_s, w, w_s = inputs(M, N, K, 11)
     got = run(a_q, a_s, w, w_s).reshape(M, N)

@@ -9,7 +9,8 @@ TAU * sum|products| of the exact sum, TAU = 7 * 2^-13 + gamma_17).  Bars, derive
     + 2 gamma_(k+1)) * 1.01 * B elementwise, B the same computation on magnitudes;
   - first GEMM: every dequantized code and h_scale against the exact fp64 SiLU(g) * u, with g and
     u carrying the bound above, and against the oracle's code with both sides' terms;
-  - whole layer: max|err| <= 2e-2 * max|ref| over the checked tokens.
+  - whole layer: max|err| <= 1e-2 * max|ref| over the checked tokens, the FP8 path's bar (its
+    derivation: intermediate FP8 codes one E4M3 step off, test_gpu_fp8.py).
 """
 import dataclasses
 import sys
@@ -28,6 +29,8 @@ if not torch.cuda.is_available():  # pragma: no cover - CPU container
     pytest.skip("needs a GPU", allow_module_level=True)
 
 import w8a8_int8_quantized_quant_amd as w8  # noqa: E402
+
+LAYER_BAR = 1e-2  # whole-layer error over max|ref|, as for the FP8 path
 from w8a8_int8_quantized_quant_amd import workload  # noqa: E402
 
 DEV = "cuda"
@@ -353,4 +356,4 @@ def test_w4_forward_matches_oracle(name):
     say(f"[w4 forward] {name}: max err {err:.3e}, max |ref| {np.abs(ref).max():.3e}, "
         f"bit-equal {np.mean(got[tokens] == ref):.4f}")
     assert np.isfinite(got).all()
-    assert err <= 2e-2 * np.abs(ref).max()
+    assert err <= LAYER_BAR * np.abs(ref).max()
