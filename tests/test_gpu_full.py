@@ -45,7 +45,8 @@ ULP = 2.0 ** -23
 FULL = ["decode", "prefill", "skew", "skew-empty", "block"]
 ENGINE = {"decode": w8.ENGINE_STAGED, "prefill": w8.ENGINE_DMA, "skew": w8.ENGINE_RING,
           "skew-empty": w8.ENGINE_RING, "block": w8.ENGINE_RING}
-TILE_ROWS = {w8.ENGINE_DMA: 320, w8.ENGINE_RING: 128}  # real rows per tile (staged: block_m of the padded rows)
+# real rows per tile (staged: block_m of the padded rows)
+TILE_ROWS = {w8.ENGINE_DMA: (320,), w8.ENGINE_RING: (128,)}
 
 
 def say(msg):
@@ -95,10 +96,10 @@ class Full:
     tokens: np.ndarray
 
 
-def check_rows(al, counts, bm, tile, P, seed, all_rows=False):
+def check_rows(al, counts, bm, tiles, P, seed, all_rows=False):
     """Sorted rows to compare whole: per non-empty expert its first and last rows, the rows around
-    every `tile` boundary of its segment and the 16-row fragment boundaries of its first and last
-    tiles, and three random rows."""
+    every boundary of its segment's tiles (each size in `tiles`) and the 16-row fragment boundaries
+    of its first and last tiles, and three random rows."""
     R = int(al["num_tiles"][0]) * bm
     if all_rows:
         return np.nonzero(al["sorted_pair_ids"][:R] < P)[0].astype(np.int64)
@@ -110,8 +111,9 @@ def check_rows(al, counts, bm, tile, P, seed, all_rows=False):
             continue
         r0 = int(al["padded_offsets"][e])
         js = {0, 1, 15, 16, n - 2, n - 1, (n // 16) * 16 - 1, (n // 16) * 16}
-        for m in range(1, n // tile + 1):
-            js |= {m * tile - 1, m * tile, m * tile + 15, m * tile + 16}
+        for tile in tiles:
+            for m in range(1, n // tile + 1):
+                js |= {m * tile - 1, m * tile, m * tile + 15, m * tile + 16}
         js |= set(rng.integers(0, n, size=3).tolist())
         rows |= {r0 + j for j in js if 0 <= j < n}
     return np.array(sorted(rows), dtype=np.int64)
@@ -150,8 +152,8 @@ def full(request):
     say(f"[full] {name}: oracle weights of {len(active)} active experts, block_m={bm}")
     w = oracle_weights_all(cfg, active)
     engine = w8.w8a8_moe_engine(cfg.T, cfg.k, cfg.E, cfg.H, cfg.I, bm, L.scale_mode)
-    tile = TILE_ROWS.get(engine, bm)
-    rows = check_rows(al, al["counts"], bm, tile, cfg.T * cfg.k, 1, all_rows=(name == "decode"))
+    tiles = TILE_ROWS.get(engine, (bm,))
+    rows = check_rows(al, al["counts"], bm, tiles, cfg.T * cfg.k, 1, all_rows=(name == "decode"))
     tokens = cover_tokens(ids, cfg.E, 2)
     say(f"[full] {name}: {len(rows)} check rows, {len(tokens)} check tokens")
     f = Full(name, cfg, L, ids, tw, bm, al, d, w, active, rows, tokens)

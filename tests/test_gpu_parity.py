@@ -412,12 +412,15 @@ def test_second_gemm_combine_bit_exact(name):
 
 
 # Rows per expert for the tile-edge cases: empty, one row, a ragged fragment, exactly one 320-row
-# tile, one row past it, several tiles, and ragged multi-tile counts.
+# tile, one row past it, several tiles, and ragged multi-tile counts (with 16 experts, the ring engine's
+# 128-row tiles: 255 / 256 rows, two rows either side of a tile pair).
 EDGE_COUNTS = [0, 1, 17, 320, 321, 650, 330, 361]
+EDGE_COUNTS_E16 = [0, 1, 17, 255, 256, 650, 330, 361, 130]
 
 
 def edge_counts(cfg):
-    return EDGE_COUNTS + [0] * (cfg.E - len(EDGE_COUNTS))
+    base = EDGE_COUNTS_E16 if cfg.E == 16 else EDGE_COUNTS
+    return base + [0] * (cfg.E - len(base))
 
 
 def edge_routing(cfg):
@@ -426,7 +429,7 @@ def edge_routing(cfg):
     rows gather scattered token rows."""
     flat = np.repeat(np.arange(cfg.E, dtype=np.int32), edge_counts(cfg))
     T = len(flat) // 2
-    assert T == cfg.T and cfg.k == 2 and max(EDGE_COUNTS) <= T
+    assert T == cfg.T and cfg.k == 2 and max(edge_counts(cfg)) <= T
     ids = np.stack([flat[:T], flat[T:]], axis=1)
     assert np.all(ids[:, 0] != ids[:, 1])
     ids = ids[np.random.default_rng(40).permutation(T)]
