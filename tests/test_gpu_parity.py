@@ -227,8 +227,12 @@ def test_routing(name):
 
 @pytest.mark.parametrize("E,k,ng,tg,fn,renorm,bias", [(8, 8, 1, 1, 0, True, False), (64, 6, 1, 1, 0, False, False),
                                                       (1, 1, 1, 1, 0, True, False), (1024, 8, 16, 4, 1, True, True),
-                                                      (72, 5, 1, 1, 1, False, False), (256, 8, 8, 4, 1, True, True)])
+                                                      (72, 5, 1, 1, 1, False, False), (256, 8, 8, 4, 1, True, True),
+                                                      (384, 8, 8, 4, 1, True, True), (256, 6, 2, 1, 1, False, True),
+                                                      (256, 8, 64, 8, 1, True, False), (64, 4, 64, 8, 1, True, True),
+                                                      (512, 8, 32, 4, 1, True, True), (160, 6, 5, 3, 1, True, False)])
 def test_routing_variants(E, k, ng, tg, fn, renorm, bias):
+    """Group sizes 1, 4, 16, 32, 64 take the in-register group scores; 48 and 128 the per-lane scan."""
     T = 77
     lg = synth.normal(T * E, 5, synth.STREAM_MISC, 0).reshape(T, E)
     b = synth.normal(E, 6, synth.STREAM_MISC, 0, 0.1) if bias else None

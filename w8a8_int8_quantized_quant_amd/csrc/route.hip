@@ -20,17 +20,40 @@ __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
 }
 
-// Wave-wide best (value, index) pair; every lane returns the winner.
+// One step of a 16-lane reduction: the better of this lane's pair and the pair DPP control CTRL
+// brings from another lane of the same 16-lane row.
+template <int CTRL>
+__device__ __forceinline__ void row_step(float& v, int& i) {
+  const float ov = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+  const int oi = __builtin_amdgcn_update_dpp(0, i, CTRL, 0xF, 0xF, false);
+  if (better(ov, oi, v, i)) {
+    v = ov;
+    i = oi;
+  }
+}
+
+// Wave-wide best (value, index) pair; every lane returns the winner (the whole wavefront must be
+// active).  Within each 16-lane row: partner lanes l^1, l^2 (quad permutes), then the mirrored lane
+// in the 8-lane half and in the row, so every lane of a row holds the row's best; the four rows'
+// bests are then read as scalars and compared in row order.
 __device__ __forceinline__ void wave_argmax(float& v, int& i) {
+  row_step<0xB1>(v, i);   // quad_perm [1, 0, 3, 2]
+  row_step<0x4E>(v, i);   // quad_perm [2, 3, 0, 1]
+  row_step<0x141>(v, i);  // row_half_mirror
+  row_step<0x140>(v, i);  // row_mirror
+  float bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  int bi = __builtin_amdgcn_readlane(i, 0);
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    float ov = __shfl_xor(v, o, kWave);
-    int oi = __shfl_xor(i, o, kWave);
-    if (better(ov, oi, v, i)) {
-      v = ov;
-      i = oi;
+  for (int r = 1; r < 4; ++r) {
+    const float rv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16 * r));
+    const int ri = __builtin_amdgcn_readlane(i, 16 * r);
+    if (better(rv, ri, bv, bi)) {
+      bv = rv;
+      bi = ri;
     }
   }
+  v = bv;
+  i = bi;
 }
 
 template <int NPL>
@@ -73,7 +96,34 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const float* __restrict
     const int gs = E / n_group;
     float gscore = -INFINITY;
     int gidx = 0x7fffffff;
-    if (active && l < n_group) {
+    if (gs <= kWave && (kWave % gs) == 0) {
+      // A group is gs consecutive lanes of one 64-expert slot: a butterfly over the group's lanes
+      // leaves the group's largest and second-largest selection score in each of them (only the
+      // sum of the two counts, so ties need no index), then lane g fetches group g's sum.
+      float part[NPL];
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) {
+        float m1 = ((ok >> i) & 1u) ? key[i] : -INFINITY, m2 = -INFINITY;
+        for (int o = 1; o < gs; o <<= 1) {
+          const float p1 = __shfl_xor(m1, o, kWave), p2 = __shfl_xor(m2, o, kWave);
+          const float n2 = fmaxf(fminf(m1, p1), fmaxf(m2, p2));
+          m1 = fmaxf(m1, p1);
+          m2 = n2;
+        }
+        part[i] = gs >= 2 ? m1 + m2 : m1;
+      }
+      const int first = (l < n_group ? l : 0) * gs;  // group l's first expert
+      float got = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) {
+        const float v = __shfl(part[i], first % kWave, kWave);
+        if (i == first / kWave) got = v;
+      }
+      if (active && l < n_group) {
+        gscore = got;
+        gidx = l;
+      }
+    } else if (active && l < n_group) {
       const float* c = sh_c[w] + l * gs;
       int b1 = 0;
       for (int i = 1; i < gs; ++i)
