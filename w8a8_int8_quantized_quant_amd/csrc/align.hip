@@ -11,6 +11,8 @@
 // holding the same expert form a mask; the rank is the popcount below the
 // lane), wave histograms give the rank inside the chunk, one scan over chunks
 // gives each chunk's base per expert, and a scatter writes every pair once.
+// Up to kAlignSmallMax pairs (decode batches) one 1024-thread workgroup does all
+// of it in a single launch, with the same ranks.
 #include <mutex>
 
 #include "common.hpp"
@@ -98,35 +100,14 @@ __device__ int block_exclusive_scan(int v, int* wsum, int& total) {
   return before + x - v;
 }
 
-__global__ __launch_bounds__(kScanThreads) void align_scan_kernel(int32_t* __restrict__ hist, int64_t nchunks, int E,
-                                                                  int block_m, int32_t P, int32_t* __restrict__ counts,
-                                                                  int32_t* __restrict__ offsets,
-                                                                  int32_t* __restrict__ padded_offsets,
-                                                                  int32_t* __restrict__ sorted,
-                                                                  int32_t* __restrict__ tile_expert,
-                                                                  int32_t* __restrict__ num_tiles) {
-  __shared__ int wsum[kScanThreads / kWave];
-  __shared__ int po[kMaxE + 1];
+// Offsets from the per-expert counts (thread e of 1024 holds expert e's count): counts, offsets,
+// padded offsets (also into po, E + 1 entries of LDS), the sentinel P in each segment's padding,
+// num_tiles and the expert of every block_m-row tile.  Ends with po complete for every thread.
+__device__ void write_offsets(int cnt, int E, int block_m, int32_t P, int* wsum, int* po, int32_t* __restrict__ counts,
+                              int32_t* __restrict__ offsets, int32_t* __restrict__ padded_offsets,
+                              int32_t* __restrict__ sorted, int32_t* __restrict__ tile_expert,
+                              int32_t* __restrict__ num_tiles) {
   const int e = threadIdx.x;
-  int cnt = 0;
-  if (e < E) {
-    int64_t c = 0;
-    for (; c + 8 <= nchunks; c += 8) {
-      int h[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) h[i] = hist[(c + i) * E + e];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        hist[(c + i) * E + e] = cnt;
-        cnt += h[i];
-      }
-    }
-    for (; c < nchunks; ++c) {
-      const int h = hist[c * E + e];
-      hist[c * E + e] = cnt;
-      cnt += h;
-    }
-  }
   const int pc = (cnt + block_m - 1) / block_m * block_m;
   int total_cnt, total_pc;
   const int off = block_exclusive_scan(cnt, wsum, total_cnt);
@@ -158,6 +139,103 @@ __global__ __launch_bounds__(kScanThreads) void align_scan_kernel(int32_t* __res
     }
     tile_expert[i] = lo;
   }
+}
+
+__global__ __launch_bounds__(kScanThreads) void align_scan_kernel(int32_t* __restrict__ hist, int64_t nchunks, int E,
+                                                                  int block_m, int32_t P, int32_t* __restrict__ counts,
+                                                                  int32_t* __restrict__ offsets,
+                                                                  int32_t* __restrict__ padded_offsets,
+                                                                  int32_t* __restrict__ sorted,
+                                                                  int32_t* __restrict__ tile_expert,
+                                                                  int32_t* __restrict__ num_tiles) {
+  __shared__ int wsum[kScanThreads / kWave];
+  __shared__ int po[kMaxE + 1];
+  const int e = threadIdx.x;
+  int cnt = 0;
+  if (e < E) {
+    int64_t c = 0;
+    for (; c + 8 <= nchunks; c += 8) {
+      int h[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) h[i] = hist[(c + i) * E + e];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        hist[(c + i) * E + e] = cnt;
+        cnt += h[i];
+      }
+    }
+    for (; c < nchunks; ++c) {
+      const int h = hist[c * E + e];
+      hist[c * E + e] = cnt;
+      cnt += h;
+    }
+  }
+  write_offsets(cnt, E, block_m, P, wsum, po, counts, offsets, padded_offsets, sorted, tile_expert, num_tiles);
+}
+
+// The whole align in one workgroup of kScanThreads threads, for P <= kAlignSmallMax: pair
+// p = round * kScanThreads + thread.  A pair's rank in its expert's segment counts that expert's
+// pairs in earlier rounds, in earlier wavefronts of its round, and on lower lanes of its wavefront
+// (the ballot ranking of the chunked kernels), i.e. the pairs before it.
+constexpr int kSmallWaves = kScanThreads / kWave;
+constexpr int kSmallRounds = (int)(kAlignSmallMax / kScanThreads);
+__global__ __launch_bounds__(kScanThreads) void align_small_kernel(const int32_t* __restrict__ ids, int64_t P, int E,
+                                                                   int nbits, int block_m,
+                                                                   int32_t* __restrict__ counts,
+                                                                   int32_t* __restrict__ offsets,
+                                                                   int32_t* __restrict__ padded_offsets,
+                                                                   int32_t* __restrict__ sorted,
+                                                                   int32_t* __restrict__ tile_expert,
+                                                                   int32_t* __restrict__ num_tiles) {
+  __shared__ int wh[kSmallWaves][kMaxE];  // per-wavefront counts of the round, then their bases
+  __shared__ int seen[kMaxE];             // pairs of each expert in the rounds before
+  __shared__ int wsum[kSmallWaves];
+  __shared__ int po[kMaxE + 1];
+  const int w = threadIdx.x / kWave;
+  for (int e = threadIdx.x; e < E; e += kScanThreads) seen[e] = 0;
+  int my_rank[kSmallRounds], my_e[kSmallRounds];
+#pragma unroll
+  for (int round = 0; round < kSmallRounds; ++round) {
+    my_e[round] = -1;
+    my_rank[round] = 0;
+    if ((int64_t)round * kScanThreads >= P) continue;  // uniform
+    for (int i = threadIdx.x; i < kSmallWaves * E; i += kScanThreads) wh[i / E][i % E] = 0;
+    __syncthreads();
+    const int64_t p = (int64_t)round * kScanThreads + threadIdx.x;
+    const int e = p < P ? ids[p] : -1;
+    const bool valid = e >= 0 && e < E;
+    uint64_t peers = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = valid && ((e >> b) & 1);
+      const uint64_t m = __ballot(bit);
+      peers &= bit ? m : ~m;
+    }
+    const uint64_t below = peers & lanemask_lt();
+    if (valid && below == 0) wh[w][e] = __popcll(peers);  // one writer per (wavefront, expert)
+    __syncthreads();
+    for (int x = threadIdx.x; x < E; x += kScanThreads) {
+      int run = seen[x];
+#pragma unroll
+      for (int ww = 0; ww < kSmallWaves; ++ww) {
+        const int c = wh[ww][x];
+        wh[ww][x] = run;
+        run += c;
+      }
+      seen[x] = run;
+    }
+    __syncthreads();
+    if (valid) {
+      my_e[round] = e;
+      my_rank[round] = wh[w][e] + __popcll(below);
+    }
+    __syncthreads();  // the next round clears wh
+  }
+  const int cnt = (int)threadIdx.x < E ? seen[threadIdx.x] : 0;
+  write_offsets(cnt, E, block_m, (int32_t)P, wsum, po, counts, offsets, padded_offsets, sorted, tile_expert,
+                num_tiles);
+#pragma unroll
+  for (int round = 0; round < kSmallRounds; ++round)
+    if (my_e[round] >= 0) sorted[po[my_e[round]] + my_rank[round]] = (int32_t)((int64_t)round * kScanThreads + threadIdx.x);
 }
 
 __global__ __launch_bounds__(kThreads) void align_scatter_kernel(const int32_t* __restrict__ ids, int64_t P, int E,
@@ -223,6 +301,11 @@ hipError_t align_by_expert(const int32_t* ids, int64_t P, int64_t E, int64_t blo
   int32_t* rank = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + round256(sizeof(int32_t) * nchunks * E));
   int nbits = 0;
   while ((1ll << nbits) < E) ++nbits;
+  if (P <= kAlignSmallMax) {
+    hipLaunchKernelGGL(align_small_kernel, dim3(1), dim3(kScanThreads), 0, stream, ids, P, (int)E, nbits, (int)block_m,
+                       counts, offsets, padded_offsets, sorted, tile_expert, num_tiles);
+    return hipGetLastError();
+  }
   if (nchunks > 0) {
     hipLaunchKernelGGL(align_hist_kernel, dim3((uint32_t)nchunks), dim3(kThreads), 0, stream, ids, P, (int)E,
                        nbits, hist, rank);

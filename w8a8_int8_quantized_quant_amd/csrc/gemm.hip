@@ -87,7 +87,14 @@ struct Params {
   int8_t* h_q;
   float* h_s;
   int64_t ksplit;  // DMA engine, Epi::I32: K slices per tile (1 = none); slice s writes out_i32 + s*P*N
+  int32_t* pair_row;  // second GEMM: the workgroups of N-tile 0 store pair_row[pair] = sorted row
 };
+
+// pair_row[pid] = row for a real row of the tile (only the N-tile 0 workgroups call it, so each
+// real row is written once).
+__device__ __forceinline__ void note_pair_row(const Params& p, int32_t pid, int64_t row) {
+  if (pid >= 0 && pid < p.P) p.pair_row[pid] = (int32_t)row;
+}
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return (g / (1.0f + expf(-g))) * u; }
 
@@ -334,6 +341,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const Params p) 
   for (int i = tid; i < BM; i += kThreads) {
     const int32_t pid = p.sorted[row0 + i];
     sh_pid[i] = pid;
+    if (p.pair_row && nt == 0) note_pair_row(p, pid, row0 + i);
     if constexpr (kBlock) sh_arow[i] = pid < p.P ? (p.gather ? (int32_t)(pid / p.k) : (int32_t)(row0 + i)) : -1;
   }
 
@@ -826,8 +834,10 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_dma_kernel(co
 
   const int tid = threadIdx.x, l = lane_id();
   const int wv = __builtin_amdgcn_readfirstlane(tid / kWave), wm = wv / WN, wn = wv % WN;
-  for (int i = tid; i < BM; i += NT)
+  for (int i = tid; i < BM; i += NT) {
     sh_pid[i] = i < nrows ? (p.sorted ? p.sorted[row0 + i] : (int32_t)(row0 + i)) : (int32_t)p.P;
+    if (p.pair_row && nt == 0 && ks == 0 && i < nrows) note_pair_row(p, sh_pid[i], row0 + i);
+  }
 
   // This thread's DMA chunks: stage chunk q holds row q / CPR, K-chunk (q % CPR) ^ swz(row); lane i
   // of an instruction lands 16 i bytes after the instruction's 1 KB slot.  Sources are 32-bit
@@ -975,7 +985,10 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_ring_kernel(c
   const int tid = threadIdx.x, l = lane_id();
   const int wv = __builtin_amdgcn_readfirstlane(tid / kWave), wm = wv / WN, wn = wv % WN;
   const int g = l >> 4, fr = l & 15;
-  for (int i = tid; i < BM; i += NT) sh_pid[i] = i < nrows ? p.sorted[row0 + i] : (int32_t)p.P;
+  for (int i = tid; i < BM; i += NT) {
+    sh_pid[i] = i < nrows ? p.sorted[row0 + i] : (int32_t)p.P;
+    if (p.pair_row && nt == 0 && i < nrows) note_pair_row(p, sh_pid[i], row0 + i);
+  }
   if constexpr (kBlkScales) {
     for (int i = tid; i < 2 * KT; i += NT) {
       const int64_t blk = wrow_of<BN, MAP>(nt, (i / KT) * 128, p.I) / 128;
@@ -1167,7 +1180,10 @@ __global__ __launch_bounds__(kStreamWN * kWave) void grouped_gemm_w4_stream_kern
   const int tid = threadIdx.x, l = lane_id();
   const int wn = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int g = l >> 4, fr = l & 15;
-  for (int i = tid; i < BM; i += WN * kWave) sh_pid[i] = i < nrows ? p.sorted[row0 + i] : (int32_t)p.P;
+  for (int i = tid; i < BM; i += WN * kWave) {
+    sh_pid[i] = i < nrows ? p.sorted[row0 + i] : (int32_t)p.P;
+    if (p.pair_row && nt == 0 && i < nrows) note_pair_row(p, sh_pid[i], row0 + i);
+  }
 
   // tile row fr (rows past the real ones read the first row: finite values, never stored)
   const int64_t rr = fr < nrows ? fr : 0;
@@ -1364,37 +1380,28 @@ __global__ __launch_bounds__(kThreads) void requant_rows_kernel(const float* __r
   }
 }
 
-__global__ void fill_i32_kernel(int32_t* __restrict__ p, int64_t n, int32_t v) {
-  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (i < n) p[i] = v;
-}
-
-// pair_row[sorted[r]] = r for the real rows.
-__global__ void pair_row_kernel(const int32_t* __restrict__ sorted, const int32_t* __restrict__ num_tiles,
-                                int64_t block_m, int64_t P, int32_t* __restrict__ pair_row, int64_t max_rows) {
-  const int64_t r = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (r >= max_rows || r >= (int64_t)num_tiles[0] * block_m) return;
-  const int32_t pid = sorted[r];
-  if (pid >= 0 && pid < P) pair_row[pid] = (int32_t)r;
-}
-
 // out[t, n] = 0 + w[t,0] * y0 + w[t,1] * y1 + ... in slot order.  One token per workgroup row
 // (its slot rows and weights are uniform, so they come through scalar loads); each thread sums
-// kCombineVec float4 columns, all of a slot's loads in flight together.
+// kCombineVec float4 columns, all of a slot's loads in flight together.  pair_row is written by
+// the second GEMM for this call's pairs only (a pair the align dropped keeps whatever an earlier
+// call left): a slot counts when its row lies in this call's rows and holds that very pair.
 constexpr int kCombineVec = 4;
 __global__ __launch_bounds__(kThreads) void combine_kernel(const float* __restrict__ y,
                                                            const int32_t* __restrict__ pair_row,
+                                                           const int32_t* __restrict__ sorted,
+                                                           const int32_t* __restrict__ num_tiles, int64_t block_m,
                                                            const float* __restrict__ topk_w, int64_t k, int64_t H,
                                                            float* __restrict__ out) {
   const int64_t t = blockIdx.x;
   const int64_t H4 = H / 4;
   const int64_t c0 = (int64_t)blockIdx.y * kThreads * kCombineVec + threadIdx.x;
+  const int64_t used = (int64_t)num_tiles[0] * block_m;
   float4 o[kCombineVec];
 #pragma unroll
   for (int i = 0; i < kCombineVec; ++i) o[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   for (int64_t j = 0; j < k; ++j) {
     const int32_t r = pair_row[t * k + j];
-    if (r < 0) continue;
+    if (r < 0 || r >= used || sorted[r] != t * k + j) continue;
     const float wj = topk_w[t * k + j];
     const float4* src = reinterpret_cast<const float4*>(y + (int64_t)r * H);
     float4 v[kCombineVec];
@@ -1736,6 +1743,7 @@ hipError_t w2_combine(const GroupedShape& s, int32_t scale_mode, const int8_t* h
   prm.a_s = h_s;
   prm.w_s = w2_s;
   prm.out_f32 = y;
+  prm.pair_row = pair_row;
   hipError_t err;
   if (scale_mode == 2)
     err = launch_ring_kt<BMap::Plain, Epi::W2Fp8>(prm, s, padded_offsets, work, stream);
@@ -1751,14 +1759,9 @@ hipError_t w2_combine(const GroupedShape& s, int32_t scale_mode, const int8_t* h
   else
     err = launch_bm<BMap::Plain, Epi::W2Channel, kBNStaged>(prm, s.max_rows, stream);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(fill_i32_kernel, dim3((uint32_t)((P + kThreads - 1) / kThreads)), dim3(kThreads), 0, stream,
-                     pair_row, P, -1);
-  if (s.max_rows > 0)
-    hipLaunchKernelGGL(pair_row_kernel, dim3((uint32_t)((s.max_rows + kThreads - 1) / kThreads)), dim3(kThreads), 0,
-                       stream, sorted, num_tiles, s.block_m, P, pair_row, s.max_rows);
   const int64_t col_blocks = (s.H / 4 + kThreads * kCombineVec - 1) / (kThreads * kCombineVec);
   hipLaunchKernelGGL(combine_kernel, dim3((uint32_t)s.T, (uint32_t)col_blocks), dim3(kThreads), 0, stream, y, pair_row,
-                     topk_w, s.k, s.H, out);
+                     sorted, num_tiles, s.block_m, topk_w, s.k, s.H, out);
   return hipGetLastError();
 }
 

@@ -21,7 +21,8 @@ hipError_t topk_route(const float* logits, int64_t T, int64_t E, int64_t k, int3
                       int32_t* ids, float* weights, hipStream_t stream);
 
 // align.hip
-constexpr int64_t kAlignChunk = 1024;  // pairs per histogram chunk
+constexpr int64_t kAlignChunk = 1024;     // pairs per histogram chunk
+constexpr int64_t kAlignSmallMax = 4096;  // at most this many pairs: one single-workgroup launch
 size_t align_ws_bytes(int64_t P, int64_t E);
 // The allocation-free align entry point's scratch: a file-scope device array of this many bytes in
 // align.hip; noalloc_scratch gives its address on the current device.
