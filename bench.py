@@ -263,7 +263,8 @@ def engine_name(cfg, T):
 
 def measured_peaks():
     """Rates of the probe kernels (include/w8a8probe.h) on this device: a 4 GiB non-temporal read
-    stream, a 2 GiB non-temporal copy, and an INT8 MFMA loop on pseudo-random operands."""
+    stream, a 2 GiB non-temporal copy, and INT8 MFMA loops on pseudo-random operands with each of
+    the two instruction shapes (the larger rate is the measured INT8 ceiling)."""
     import ctypes
 
     import torch
@@ -272,7 +273,7 @@ def measured_peaks():
     vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
     lib.w8a8_probe_read.argtypes = [vp, i64, vp, vp]
     lib.w8a8_probe_copy.argtypes = [vp, vp, i64, vp]
-    lib.w8a8_probe_mfma_i8.argtypes = [i64, i32, vp, vp]
+    lib.w8a8_probe_mfma_i8.argtypes = [i64, i32, i32, vp, vp]
     lib.w8a8_probe_mfma_i8_ops.argtypes = [i64, i32]
     for f in (lib.w8a8_probe_read, lib.w8a8_probe_copy, lib.w8a8_probe_mfma_i8):
         f.restype = i32
@@ -300,15 +301,20 @@ def measured_peaks():
     t_copy = timed(lambda: lib.w8a8_probe_copy(buf.data_ptr(), buf.data_ptr() + half, half, hs))
     del buf
     torch.cuda.empty_cache()
-    iters, wgs = 4096, 2048
-    t_mfma = timed(lambda: lib.w8a8_probe_mfma_i8(iters, wgs, sink.data_ptr(), hs))
+    iters, wgs = 4096, 1024
     ops = lib.w8a8_probe_mfma_i8_ops(iters, wgs)
+    tops = {}
+    for shape in (16, 32):
+        t = timed(lambda: lib.w8a8_probe_mfma_i8(iters, wgs, shape, sink.data_ptr(), hs))
+        tops[shape] = round(ops / t / 1e12, 1)
     return {"hbm_read_gbs": round(nbytes / t_read / 1e9, 1), "hbm_copy_gbs": round(2 * half / t_copy / 1e9, 1),
-            "int8_mfma_tops": round(ops / t_mfma / 1e12, 1),
+            "int8_mfma_tops": max(tops.values()), "int8_mfma_16x16x64_tops": tops[16],
+            "int8_mfma_32x32x32_tops": tops[32],
             "note": "probe kernels of libw8a8probe.so: non-temporal 16-byte read stream over 4 GiB; "
-                    "non-temporal copy of 2 GiB (read + written bytes); 8 independent "
-                    "v_mfma_i32_16x16x64_i8 chains per wavefront on pseudo-random operands, 8 workgroups "
-                    "of 4 wavefronts per CU"}
+                    "non-temporal copy of 2 GiB (read + written bytes); independent INT8 MFMA chains "
+                    "on pseudo-random operands, 4 workgroups of 4 wavefronts per CU, either 8 chains of "
+                    "v_mfma_i32_16x16x64_i8 (the layer's GEMMs) or 4 of v_mfma_i32_32x32x32_i8 per "
+                    "wavefront; int8_mfma_tops is the larger"}
 
 
 def linear_figures(steps, warmup):

@@ -24,9 +24,11 @@ int32_t w8a8_probe_read(const void* buf, int64_t bytes, int32_t* sink, hipStream
  * loads and stores. */
 int32_t w8a8_probe_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream);
 
-/* `workgroups` workgroups of 4 wavefronts, each wavefront issuing `iters` rounds of 8
- * independent v_mfma_i32_16x16x64_i8 on pseudo-random operands; `sink` as above. */
-int32_t w8a8_probe_mfma_i8(int64_t iters, int32_t workgroups, int32_t* sink, hipStream_t stream);
+/* `workgroups` workgroups of 4 wavefronts, each wavefront issuing `iters` rounds of independent
+ * INT8 MFMAs on pseudo-random operands: shape 16 = 8 v_mfma_i32_16x16x64_i8, shape 32 = 4
+ * v_mfma_i32_32x32x32_i8 (the same multiply-adds); `sink` as above.  Returns 1 for a null sink,
+ * iters or workgroups below 1 or another shape. */
+int32_t w8a8_probe_mfma_i8(int64_t iters, int32_t workgroups, int32_t shape, int32_t* sink, hipStream_t stream);
 
 /* `blocks` independent products, one wavefront and one FP8 MFMA
  * (v_mfma_scale_f32_16x16x128_f8f6f4, E4M3 operands, scales 1.0, zero accumulator) each:
@@ -36,7 +38,7 @@ int32_t w8a8_probe_mfma_i8(int64_t iters, int32_t workgroups, int32_t* sink, hip
  * measure the accumulation that GEMM gets. */
 int32_t w8a8_probe_mfma_f8_block(const uint8_t* a, const uint8_t* b, float* c, int32_t blocks, hipStream_t stream);
 
-/* Integer operations (2 per multiply-add) of one w8a8_probe_mfma_i8 launch. */
+/* Integer operations (2 per multiply-add) of one w8a8_probe_mfma_i8 launch (either shape). */
 int64_t w8a8_probe_mfma_i8_ops(int64_t iters, int32_t workgroups);
 
 #ifdef __cplusplus

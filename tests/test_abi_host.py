@@ -46,14 +46,15 @@ def test_probe_library_exports_its_header_and_validates():
     vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
     L.w8a8_probe_read.argtypes = [vp, i64, vp, vp]
     L.w8a8_probe_copy.argtypes = [vp, vp, i64, vp]
-    L.w8a8_probe_mfma_i8.argtypes = [i64, i32, vp, vp]
+    L.w8a8_probe_mfma_i8.argtypes = [i64, i32, i32, vp, vp]
     L.w8a8_probe_mfma_i8_ops.argtypes = [i64, i32]
     L.w8a8_probe_mfma_i8_ops.restype = i64
     assert L.w8a8_probe_read(None, 1024, P16, None) == 1
     assert L.w8a8_probe_read(P16, 1000, P16, None) == 1
     assert L.w8a8_probe_copy(P16, P16, 0, None) == 1
-    assert L.w8a8_probe_mfma_i8(0, 8, P16, None) == 1
-    assert L.w8a8_probe_mfma_i8(1, 8, None, None) == 1
+    assert L.w8a8_probe_mfma_i8(0, 8, 16, P16, None) == 1
+    assert L.w8a8_probe_mfma_i8(1, 8, 16, None, None) == 1
+    assert L.w8a8_probe_mfma_i8(1, 8, 24, P16, None) == 1
     L.w8a8_probe_mfma_f8_block.argtypes = [vp, vp, vp, i32, vp]
     assert L.w8a8_probe_mfma_f8_block(P16, P16, None, 1, None) == 1
     assert L.w8a8_probe_mfma_f8_block(P16, P16, P16, 0, None) == 1

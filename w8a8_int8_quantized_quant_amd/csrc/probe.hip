@@ -51,10 +51,13 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(const i32x4* __restrict_
   }
 }
 
-// Each wavefront keeps kChains independent accumulators busy with v_mfma_i32_16x16x64_i8 on
-// operands of pseudo-random bytes (a multiply-xorshift of the lane id: all-equal operands would
-// draw less power and clock higher than real data).
-constexpr int kChains = 8;
+// Each wavefront keeps independent accumulators busy with one INT8 MFMA form on operands of
+// pseudo-random bytes (a multiply-xorshift of the lane id: all-equal operands would draw less power
+// and clock higher than real data): 8 chains of v_mfma_i32_16x16x64_i8 (FR = 16) or 4 of
+// v_mfma_i32_32x32x32_i8 (FR = 32), the same multiply-adds per round.
+constexpr int kChains = 8;  // 16 x 16 x 64 chains per round (4 of 32 x 32 x 32)
+typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
+template <int FR>
 __global__ __launch_bounds__(kThreads) void mfma_kernel(int64_t iters, int32_t* __restrict__ sink) {
   const uint32_t l = threadIdx.x + blockIdx.x * kThreads;
   auto mix = [](uint32_t x) {
@@ -66,16 +69,30 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(int64_t iters, int32_t* 
   };
   i32x4 a = {(int32_t)mix(l), (int32_t)mix(l + 1u), (int32_t)mix(l + 2u), (int32_t)mix(l + 3u)};
   i32x4 b = {(int32_t)mix(~l), (int32_t)mix(~l + 7u), (int32_t)mix(~l + 9u), (int32_t)mix(~l + 11u)};
-  i32x4 acc[kChains];
-#pragma unroll
-  for (int c = 0; c < kChains; ++c) acc[c] = i32x4{0, 0, 0, 0};
-  for (int64_t it = 0; it < iters; ++it) {
-#pragma unroll
-    for (int c = 0; c < kChains; ++c) acc[c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[c], 0, 0, 0);
-  }
   int32_t s = 0;
+  if constexpr (FR == 16) {
+    i32x4 acc[kChains];
 #pragma unroll
-  for (int c = 0; c < kChains; ++c) s ^= acc[c][0] ^ acc[c][1] ^ acc[c][2] ^ acc[c][3];
+    for (int c = 0; c < kChains; ++c) acc[c] = i32x4{0, 0, 0, 0};
+    for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int c = 0; c < kChains; ++c) acc[c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[c], 0, 0, 0);
+    }
+#pragma unroll
+    for (int c = 0; c < kChains; ++c) s ^= acc[c][0] ^ acc[c][1] ^ acc[c][2] ^ acc[c][3];
+  } else {
+    i32x16 acc[kChains / 2];
+#pragma unroll
+    for (int c = 0; c < kChains / 2; ++c) acc[c] = i32x16{};
+    for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int c = 0; c < kChains / 2; ++c) acc[c] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, acc[c], 0, 0, 0);
+    }
+#pragma unroll
+    for (int c = 0; c < kChains / 2; ++c)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s ^= acc[c][r];
+  }
   if (s == 0x13572468) sink[0] = s;
 }
 
@@ -116,9 +133,12 @@ int32_t w8a8_probe_copy(const void* src, void* dst, int64_t bytes, hipStream_t s
   return hipGetLastError() == hipSuccess ? 0 : 5;
 }
 
-int32_t w8a8_probe_mfma_i8(int64_t iters, int32_t workgroups, int32_t* sink, hipStream_t stream) {
-  if (!sink || iters < 1 || workgroups < 1) return 1;
-  hipLaunchKernelGGL(mfma_kernel, dim3((uint32_t)workgroups), dim3(kThreads), 0, stream, iters, sink);
+int32_t w8a8_probe_mfma_i8(int64_t iters, int32_t workgroups, int32_t shape, int32_t* sink, hipStream_t stream) {
+  if (!sink || iters < 1 || workgroups < 1 || (shape != 16 && shape != 32)) return 1;
+  if (shape == 16)
+    hipLaunchKernelGGL(mfma_kernel<16>, dim3((uint32_t)workgroups), dim3(kThreads), 0, stream, iters, sink);
+  else
+    hipLaunchKernelGGL(mfma_kernel<32>, dim3((uint32_t)workgroups), dim3(kThreads), 0, stream, iters, sink);
   return hipGetLastError() == hipSuccess ? 0 : 5;
 }
 
@@ -129,7 +149,7 @@ int32_t w8a8_probe_mfma_f8_block(const uint8_t* a, const uint8_t* b, float* c, i
 }
 
 int64_t w8a8_probe_mfma_i8_ops(int64_t iters, int32_t workgroups) {
-  // per wavefront and iteration: kChains MFMAs of 16 x 16 x 64 multiply-adds
+  // per wavefront and iteration: kChains MFMAs of 16 x 16 x 64 multiply-adds (either shape)
   return (int64_t)workgroups * (kThreads / 64) * iters * kChains * 2 * 16 * 16 * 64;
 }
 
