@@ -1793,14 +1793,19 @@ __global__ __launch_bounds__(kThreads) void linear_reduce_kernel(const int32_t* 
 // rounds = ceil(items * s / 256) and every slice keeps an even number of at least 8 K-steps; ties go
 // to the smaller s (less int32 partial traffic).
 constexpr int64_t kLinearCUs = 256;
+// Few rows (at most 128): 128 x 128 tiles on 4 wavefronts, two 32 KB stages, two workgroups per CU.
+constexpr int kLinSmallBM = 128, kLinSmallBN = 128, kLinSmallWM = 2, kLinSmallWN = 2;
+bool linear_small(int64_t M, int64_t N) { return M <= kLinSmallBM && N % kLinSmallBN == 0; }
 int64_t linear_ksplit(int64_t M, int64_t N, int64_t K) {
-  const int64_t items = (M + kDmaBM - 1) / kDmaBM * (N / kDmaBN);
+  const bool small = linear_small(M, N);
+  const int64_t slots = small ? 2 * kLinearCUs : kLinearCUs;
+  const int64_t items = small ? N / kLinSmallBN : (M + kDmaBM - 1) / kDmaBM * (N / kDmaBN);
   const int64_t steps = K / kDmaBK;
-  if (items >= kLinearCUs) return 1;
+  if (items >= slots) return 1;
   int64_t best = 1;
-  double best_cost = (double)((items + kLinearCUs - 1) / kLinearCUs);
+  double best_cost = (double)((items + slots - 1) / slots);
   for (int64_t s = 2; steps % (2 * s) == 0 && steps / s >= 8; s *= 2) {
-    const double cost = (double)((items * s + kLinearCUs - 1) / kLinearCUs) / (double)s;
+    const double cost = (double)((items * s + slots - 1) / slots) / (double)s;
     if (cost < best_cost) {
       best = s;
       best_cost = cost;
@@ -1810,7 +1815,7 @@ int64_t linear_ksplit(int64_t M, int64_t N, int64_t K) {
 }
 
 size_t linear_ws_bytes(int64_t M, int64_t N, int64_t K) {
-  const size_t list = round256(sizeof(int32_t) * (size_t)(1 + kWorkFields * ((M + kDmaBM - 1) / kDmaBM)));
+  const size_t list = round256(sizeof(int32_t) * (size_t)(1 + kWorkFields * ((M + kLinSmallBM - 1) / kLinSmallBM)));
   const int64_t s = linear_ksplit(M, N, K);
   return list + (s > 1 ? round256(sizeof(int32_t) * (size_t)(s * M * N)) : 0);
 }
@@ -1835,14 +1840,34 @@ hipError_t linear(const int8_t* a_q, const float* a_s, const int8_t* w, const fl
   prm.a_s = a_s;
   prm.w_s = w_s;
   prm.out_f32 = out;
-  prm.n_tiles = N / kDmaBN;
+  const bool small = linear_small(M, N);
+  const int64_t bm = small ? kLinSmallBM : kDmaBM;
+  prm.n_tiles = N / (small ? kLinSmallBN : kDmaBN);
   prm.ksplit = ksplit;
   char* base = static_cast<char*>(ws);
   int32_t* work = reinterpret_cast<int32_t*>(base);
-  const int64_t tiles = (M + kDmaBM - 1) / kDmaBM;
+  const int64_t tiles = (M + bm - 1) / bm;
   hipLaunchKernelGGL(linear_tiles_kernel, dim3((uint32_t)((tiles + kThreads - 1) / kThreads)), dim3(kThreads), 0,
-                     stream, M, kDmaBM, work);
+                     stream, M, (int)bm, work);
   const int64_t grid = (tiles * prm.n_tiles * ksplit + 7) / 8 * 8;
+  if (small) {
+    constexpr int NT = kLinSmallWM * kLinSmallWN * kWave;
+    int32_t* part = reinterpret_cast<int32_t*>(base + round256(sizeof(int32_t) * (size_t)(1 + kWorkFields * tiles)));
+    if (ksplit == 1) {
+      hipLaunchKernelGGL((grouped_gemm_dma_kernel<kLinSmallBM, kLinSmallBN, kLinSmallWM, kLinSmallWN, BMap::Plain,
+                                                  Epi::W2Channel>),
+                         dim3((uint32_t)grid), dim3(NT), 0, stream, prm, (const int32_t*)work);
+      return hipGetLastError();
+    }
+    prm.out_i32 = part;
+    hipLaunchKernelGGL((grouped_gemm_dma_kernel<kLinSmallBM, kLinSmallBN, kLinSmallWM, kLinSmallWN, BMap::Plain,
+                                                Epi::I32>),
+                       dim3((uint32_t)grid), dim3(NT), 0, stream, prm, (const int32_t*)work);
+    const int64_t q = M * N / 4;
+    hipLaunchKernelGGL(linear_reduce_kernel, dim3((uint32_t)((q + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                       stream, part, ksplit, M, N, a_s, w_s, out);
+    return hipGetLastError();
+  }
   if (ksplit == 1) {
     hipLaunchKernelGGL((grouped_gemm_dma_kernel<kDmaBM, kDmaBN, kDmaWM, kDmaWN, BMap::Plain, Epi::W2Channel>),
                        dim3((uint32_t)grid), dim3(kDmaWM * kDmaWN * kWave), 0, stream, prm, (const int32_t*)work);
