@@ -963,12 +963,16 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_ring_kernel(c
   __shared__ int32_t sh_pid[BM];
   __shared__ float sh_red[kBlock ? WN : 1][BM];
 
-  const int64_t total = (int64_t)work[0] * p.n_tiles;
+  // Raw int32 sums may split K into p.ksplit slices of KT steps (slice ks writes out_i32 + ks P N);
+  // the other epilogues run over all of K (p.ksplit = 1, K = KT steps).
+  const int64_t ksplit = EPI == Epi::I32 ? p.ksplit : 1;
+  const int64_t total = (int64_t)work[0] * p.n_tiles * ksplit;
   const int64_t per = (total + 7) / 8;
   const int64_t v = blockIdx.x;
   if (v >= 8 * per) return;
-  const int64_t logical = (v % 8) * per + v / 8;
-  if (logical >= total) return;
+  const int64_t item = (v % 8) * per + v / 8;
+  if (item >= total) return;
+  const int64_t ks = item % ksplit, logical = item / ksplit;
   const int32_t* any = work + 1 + kWorkFields * (logical / p.n_tiles);
   const int64_t first = any[3], count = any[4];
   const int64_t local = logical - p.n_tiles * first;
@@ -980,14 +984,16 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_ring_kernel(c
   const int64_t row0 = work[2 + kWorkFields * ti];
   const int nrows = work[3 + kWorkFields * ti];
   const int64_t wrow_bytes = kW4 ? p.K / 2 : p.K;
-  const int8_t* wexp = p.w + e * p.N * wrow_bytes;
+  const int64_t k0 = ks * KT * kDmaBK;  // first K byte of this slice (8-bit operands)
+  const int8_t* wexp = p.w + e * p.N * wrow_bytes + k0;
+  const int8_t* abase = p.a + k0;
 
   const int tid = threadIdx.x, l = lane_id();
   const int wv = __builtin_amdgcn_readfirstlane(tid / kWave), wm = wv / WN, wn = wv % WN;
   const int g = l >> 4, fr = l & 15;
   for (int i = tid; i < BM; i += NT) {
-    sh_pid[i] = i < nrows ? p.sorted[row0 + i] : (int32_t)p.P;
-    if (p.pair_row && nt == 0 && i < nrows) note_pair_row(p, sh_pid[i], row0 + i);
+    sh_pid[i] = i < nrows ? (p.sorted ? p.sorted[row0 + i] : (int32_t)(row0 + i)) : (int32_t)p.P;
+    if (p.pair_row && nt == 0 && ks == 0 && i < nrows) note_pair_row(p, sh_pid[i], row0 + i);
   }
   if constexpr (kBlkScales) {
     for (int i = tid; i < 2 * KT; i += NT) {
@@ -1057,7 +1063,7 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_ring_kernel(c
 #pragma unroll
     for (int c = 0; c < LD; ++c) {
       if (c < A_LD)
-        dma16(p.a + (off[c] + (uint32_t)(st * kDmaBK)), W8A8_RSTG(st) + a_dst + c * 1024);
+        dma16(abase + (off[c] + (uint32_t)(st * kDmaBK)), W8A8_RSTG(st) + a_dst + c * 1024);
       else
         (kW4 ? dma16 : dma16_nt)(wexp + (off[c] + (uint32_t)(st * BKB)), W8A8_RSTG(st) + b_dst + (c - A_LD) * 1024);
     }
@@ -1072,7 +1078,7 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_ring_kernel(c
 
   // Uniform bases of the stage two steps ahead, advanced one step at a time; the empty asm keeps
   // the compiler from precomputing every step's address up front.
-  const int8_t* a_next = p.a + (NS - 1) * kDmaBK;
+  const int8_t* a_next = abase + (NS - 1) * kDmaBK;
   const int8_t* b_next = wexp + (NS - 1) * BKB;
 #pragma clang loop unroll(full)
   for (int kt = 0; kt < KT; ++kt) {
@@ -1128,7 +1134,8 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_ring_kernel(c
   if constexpr (kBlock)
     epilogue<BM, BN, WM, WN, FM, FN, MAP, EPI, ILV>(p, acc, accf, sh_pid, sh_red, row0, nt, e, wm, wn, l, tid);
   else
-    dma_epilogue<BM, BN, WM, WN, STAGE, MAP, EPI, ILV>(p, acc, sh_pid, st0, st1, row0, nt, e, wm, wn, wv, l, 0);
+    dma_epilogue<BM, BN, WM, WN, STAGE, MAP, EPI, ILV>(p, acc, sh_pid, st0, st1, row0, nt, e, wm, wn, wv, l,
+                                                       ks * p.P * p.N);
 }
 
 // Streaming engine for packed int4 weights when experts hold few rows (decode): tiles of 16 rows
@@ -1787,37 +1794,47 @@ __global__ __launch_bounds__(kThreads) void linear_reduce_kernel(const int32_t* 
   reinterpret_cast<float4*>(out)[q] = o;
 }
 
-// K slices for a linear of this shape, planned for the MI355X's 256 CUs (a fixed count, so the
-// workspace size is a function of the shape alone; the result does not depend on it).  Only when
-// the unsplit items leave CUs idle (few rows): then the power of two s minimising rounds / s, where
-// rounds = ceil(items * s / 256) and every slice keeps an even number of at least 8 K-steps; ties go
-// to the smaller s (less int32 partial traffic).
+// Plan of a linear of this shape, for the MI355X's 256 CUs (a fixed count, so the workspace size is
+// a function of the shape alone; the result does not depend on it).
+//  - At most 128 rows and K a multiple of 2048: the ring engine's 128 x 256 tiles (three LDS stages,
+//    two of them in flight, so a CU keeps twice the weight bytes of a two-stage tile in flight),
+//    K split into 2048-byte slices (the 16-step K loop it is unrolled for).
+//  - Else the DMA engine's tiles (320 x 256; 128 x 128 on 4 wavefronts, two per CU, for at most
+//    128 rows) with K split only when the unsplit items leave CUs idle: the power of two s
+//    minimising rounds / s, rounds = ceil(items * s / slots), every slice an even number of at least
+//    8 K-steps; ties go to the smaller s (less int32 partial traffic).
 constexpr int64_t kLinearCUs = 256;
-// Few rows (at most 128): 128 x 128 tiles on 4 wavefronts, two 32 KB stages, two workgroups per CU.
 constexpr int kLinSmallBM = 128, kLinSmallBN = 128, kLinSmallWM = 2, kLinSmallWN = 2;
-bool linear_small(int64_t M, int64_t N) { return M <= kLinSmallBM && N % kLinSmallBN == 0; }
-int64_t linear_ksplit(int64_t M, int64_t N, int64_t K) {
-  const bool small = linear_small(M, N);
+constexpr int64_t kLinRingKT = kRingI / kDmaBK;  // 16 steps: 2048 K-bytes per slice
+enum class LinEngine { Dma, DmaSmall, Ring };
+struct LinearPlan {
+  LinEngine engine;
+  int64_t bm, ksplit;
+};
+LinearPlan linear_plan(int64_t M, int64_t N, int64_t K) {
+  if (M <= kRingBM && N % kDmaBN == 0 && K % (kLinRingKT * kDmaBK) == 0)
+    return {LinEngine::Ring, kRingBM, K / (kLinRingKT * kDmaBK)};
+  const bool small = M <= kLinSmallBM && N % kLinSmallBN == 0;
   const int64_t slots = small ? 2 * kLinearCUs : kLinearCUs;
   const int64_t items = small ? N / kLinSmallBN : (M + kDmaBM - 1) / kDmaBM * (N / kDmaBN);
   const int64_t steps = K / kDmaBK;
-  if (items >= slots) return 1;
-  int64_t best = 1;
+  LinearPlan plan{small ? LinEngine::DmaSmall : LinEngine::Dma, small ? kLinSmallBM : kDmaBM, 1};
+  if (items >= slots) return plan;
   double best_cost = (double)((items + slots - 1) / slots);
   for (int64_t s = 2; steps % (2 * s) == 0 && steps / s >= 8; s *= 2) {
     const double cost = (double)((items * s + slots - 1) / slots) / (double)s;
     if (cost < best_cost) {
-      best = s;
+      plan.ksplit = s;
       best_cost = cost;
     }
   }
-  return best;
+  return plan;
 }
 
 size_t linear_ws_bytes(int64_t M, int64_t N, int64_t K) {
-  const size_t list = round256(sizeof(int32_t) * (size_t)(1 + kWorkFields * ((M + kLinSmallBM - 1) / kLinSmallBM)));
-  const int64_t s = linear_ksplit(M, N, K);
-  return list + (s > 1 ? round256(sizeof(int32_t) * (size_t)(s * M * N)) : 0);
+  const LinearPlan plan = linear_plan(M, N, K);
+  const size_t list = round256(sizeof(int32_t) * (size_t)(1 + kWorkFields * ((M + plan.bm - 1) / plan.bm)));
+  return list + (plan.ksplit > 1 ? round256(sizeof(int32_t) * (size_t)(plan.ksplit * M * N)) : 0);
 }
 
 bool linear_supported(int64_t M, int64_t N, int64_t K) {
@@ -1827,7 +1844,8 @@ bool linear_supported(int64_t M, int64_t N, int64_t K) {
 hipError_t linear(const int8_t* a_q, const float* a_s, const int8_t* w, const float* w_s, int64_t M, int64_t N,
                   int64_t K, float* out, void* ws, hipStream_t stream) {
   if (M == 0) return hipSuccess;
-  const int64_t ksplit = linear_ksplit(M, N, K);
+  const LinearPlan plan = linear_plan(M, N, K);
+  const int64_t ksplit = plan.ksplit;
   Params prm{};
   prm.a = a_q;
   prm.gather = 0;
@@ -1840,8 +1858,8 @@ hipError_t linear(const int8_t* a_q, const float* a_s, const int8_t* w, const fl
   prm.a_s = a_s;
   prm.w_s = w_s;
   prm.out_f32 = out;
-  const bool small = linear_small(M, N);
-  const int64_t bm = small ? kLinSmallBM : kDmaBM;
+  const bool small = plan.engine == LinEngine::DmaSmall;
+  const int64_t bm = plan.bm;
   prm.n_tiles = N / (small ? kLinSmallBN : kDmaBN);
   prm.ksplit = ksplit;
   char* base = static_cast<char*>(ws);
@@ -1850,9 +1868,24 @@ hipError_t linear(const int8_t* a_q, const float* a_s, const int8_t* w, const fl
   hipLaunchKernelGGL(linear_tiles_kernel, dim3((uint32_t)((tiles + kThreads - 1) / kThreads)), dim3(kThreads), 0,
                      stream, M, (int)bm, work);
   const int64_t grid = (tiles * prm.n_tiles * ksplit + 7) / 8 * 8;
+  int32_t* part = reinterpret_cast<int32_t*>(base + round256(sizeof(int32_t) * (size_t)(1 + kWorkFields * tiles)));
+  if (plan.engine == LinEngine::Ring) {
+    constexpr int WM = 2, WN = 4;
+    if (ksplit == 1) {
+      hipLaunchKernelGGL((grouped_gemm_ring_kernel<kRingBM, kDmaBN, WM, WN, kLinRingKT, BMap::Plain, Epi::W2Channel>),
+                         dim3((uint32_t)grid), dim3(WM * WN * kWave), 0, stream, prm, (const int32_t*)work);
+      return hipGetLastError();
+    }
+    prm.out_i32 = part;
+    hipLaunchKernelGGL((grouped_gemm_ring_kernel<kRingBM, kDmaBN, WM, WN, kLinRingKT, BMap::Plain, Epi::I32>),
+                       dim3((uint32_t)grid), dim3(WM * WN * kWave), 0, stream, prm, (const int32_t*)work);
+    const int64_t q = M * N / 4;
+    hipLaunchKernelGGL(linear_reduce_kernel, dim3((uint32_t)((q + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                       stream, part, ksplit, M, N, a_s, w_s, out);
+    return hipGetLastError();
+  }
   if (small) {
     constexpr int NT = kLinSmallWM * kLinSmallWN * kWave;
-    int32_t* part = reinterpret_cast<int32_t*>(base + round256(sizeof(int32_t) * (size_t)(1 + kWorkFields * tiles)));
     if (ksplit == 1) {
       hipLaunchKernelGGL((grouped_gemm_dma_kernel<kLinSmallBM, kLinSmallBN, kLinSmallWM, kLinSmallWN, BMap::Plain,
                                                   Epi::W2Channel>),
@@ -1873,7 +1906,6 @@ hipError_t linear(const int8_t* a_q, const float* a_s, const int8_t* w, const fl
                        dim3((uint32_t)grid), dim3(kDmaWM * kDmaWN * kWave), 0, stream, prm, (const int32_t*)work);
     return hipGetLastError();
   }
-  int32_t* part = reinterpret_cast<int32_t*>(base + round256(sizeof(int32_t) * (size_t)(1 + kWorkFields * tiles)));
   prm.out_i32 = part;
   hipLaunchKernelGGL((grouped_gemm_dma_kernel<kDmaBM, kDmaBN, kDmaWM, kDmaWN, BMap::Plain, Epi::I32>),
                      dim3((uint32_t)grid), dim3(kDmaWM * kDmaWN * kWave), 0, stream, prm, (const int32_t*)work);
