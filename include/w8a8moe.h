@@ -338,8 +338,8 @@ int32_t w8a8_w4a8_grouped_gemm_w2_combine(const uint8_t* h_q, const float* h_sca
  *   a_scale  device, [M] fp32
  *   w        device, [N, K] int8, K-contiguous;  w_scale device, [N] fp32
  *   out      device, [M, N] fp32 (output, fully overwritten)
- *   ws       device workspace of w8a8_linear_workspace_bytes(M, N, K) bytes: a tile list and, when
- *            few rows leave CUs idle, int32 partial sums of K slices (added exactly, in slice order)
+ *   ws       device workspace of w8a8_linear_workspace_bytes(M, N, K) bytes (at least 256): when few
+ *            rows leave CUs idle, the int32 partial sums of K slices (added exactly, in slice order)
  * Shapes: K and N multiples of 256, M*K and N*K below 2^32; M = 0 is a no-op.  a_q and w 16-byte
  * aligned.  Returns W8A8_UNSUPPORTED_SHAPE for other shapes, W8A8_WORKSPACE_TOO_SMALL for a short
  * workspace.  Deterministic: every output is one fixed sequence of operations. */

@@ -67,7 +67,7 @@ def test_linear_validation():
     workspace, missing pointers."""
     L = w8.lib()
     ws = w8.w8a8_linear_workspace_bytes(1000, 256, 256)
-    assert ws >= 4 * (1 + 5 * 4) and w8.w8a8_linear_workspace_bytes(0, 256, 256) >= 4
+    assert ws >= 256 and w8.w8a8_linear_workspace_bytes(0, 256, 256) >= 256
     assert w8.w8a8_linear_workspace_bytes(4, 576, 256) == 0  # unsupported shape
     # few rows: K slices, their int32 partials in the workspace (128 x 7168 outputs, K = 16384)
     assert w8.w8a8_linear_workspace_bytes(128, 7168, 16384) >= 2 * 4 * 128 * 7168

@@ -48,11 +48,11 @@ def run(a_q, a_s, w, w_s, guard=0):
 
 @pytest.mark.parametrize("M,N,K", [(1, 256, 256), (5, 256, 4096), (37, 512, 768), (333, 768, 1024), (640, 256, 512),
                                    (1000, 1536, 7168), (100, 512, 2048), (16, 768, 6144), (64, 1024, 3072),
-                                   (128, 384, 6144)])
+                                   (128, 512, 5120)])
 def test_linear_bit_exact(M, N, K):
     """Every plan: at most 128 rows on the ring engine (K = 2048 unsplit, 4096 in two slices, 6144 in
-    three) or on 128 x 128 DMA tiles (K not a multiple of 2048, or N not of 256; 3072 and 6144 split
-    two and four ways), more rows on 320 x 256 DMA tiles."""
+    three) or, with K not a multiple of 2048, on 128 x 128 DMA tiles (3072 and 5120 split two and four
+    ways); more rows on 320 x 256 DMA tiles (7168 split four ways at 1000 rows)."""
     say(f"[linear] M={M} N={N} K={K}")
     a_q, a_s, w, w_s = inputs(M, N, K, 100 + M)
     got = run(a_q, a_s, w, w_s, guard=64)

@@ -809,7 +809,8 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_dma_kernel(co
   // Work order: expert-major, then (super-row, N-tile, row tile), so the row tiles that share a
   // weight tile run side by side and the weights come from HBM once.  XCD-aware: workgroups are
   // dispatched round-robin over the 8 XCDs; each XCD gets a contiguous stretch of that order.
-  const int64_t total = (int64_t)work[0] * p.n_tiles * p.ksplit;
+  const int64_t ntl = work ? (int64_t)work[0] : (p.P + BM - 1) / BM;  // row tiles
+  const int64_t total = ntl * p.n_tiles * p.ksplit;
   const int64_t per = (total + 7) / 8;
   const int64_t v = blockIdx.x;
   if (v >= 8 * per) return;
@@ -817,8 +818,12 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_dma_kernel(co
   if (item >= total) return;
   const int64_t ks = item % p.ksplit, logical = item / p.ksplit;  // K slice, then the (tile, N-tile) item
   const int64_t kslice = p.K / p.ksplit;                           // bytes of K per slice
-  const int32_t* any = work + 1 + kWorkFields * (logical / p.n_tiles);  // a tile of the same expert
-  const int64_t first = any[3], count = any[4];
+  int64_t first = 0, count = ntl;  // the expert's first tile and its tile count
+  if (work) {
+    const int32_t* any = work + 1 + kWorkFields * (logical / p.n_tiles);  // a tile of the same expert
+    first = any[3];
+    count = any[4];
+  }
   // Within the expert: super-rows of up to kSuperRows row tiles, N-tile-major inside each, so the
   // workgroups running together share a few row tiles and a few weight tiles (an expert with at
   // most kSuperRows row tiles is one super-row: all its row tiles of an N-tile side by side).
@@ -827,9 +832,13 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_dma_kernel(co
   const int64_t in_sr = count - sr * kSuperRows < kSuperRows ? count - sr * kSuperRows : kSuperRows;
   const int64_t rem = local - sr * kSuperRows * p.n_tiles;
   const int64_t nt = rem / in_sr, ti = first + sr * kSuperRows + rem % in_sr;
-  const int64_t e = work[1 + kWorkFields * ti];
-  const int64_t row0 = work[2 + kWorkFields * ti];
-  const int nrows = work[3 + kWorkFields * ti];
+  int64_t e = 0, row0 = ti * BM;
+  int nrows = (int)(p.P - row0 < BM ? p.P - row0 : BM);
+  if (work) {
+    e = work[1 + kWorkFields * ti];
+    row0 = work[2 + kWorkFields * ti];
+    nrows = work[3 + kWorkFields * ti];
+  }
   const int8_t* wexp = p.w + e * p.N * p.K;
 
   const int tid = threadIdx.x, l = lane_id();
@@ -966,23 +975,32 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_ring_kernel(c
   // Raw int32 sums may split K into p.ksplit slices of KT steps (slice ks writes out_i32 + ks P N);
   // the other epilogues run over all of K (p.ksplit = 1, K = KT steps).
   const int64_t ksplit = EPI == Epi::I32 ? p.ksplit : 1;
-  const int64_t total = (int64_t)work[0] * p.n_tiles * ksplit;
+  const int64_t ntl = work ? (int64_t)work[0] : (p.P + BM - 1) / BM;  // row tiles
+  const int64_t total = ntl * p.n_tiles * ksplit;
   const int64_t per = (total + 7) / 8;
   const int64_t v = blockIdx.x;
   if (v >= 8 * per) return;
   const int64_t item = (v % 8) * per + v / 8;
   if (item >= total) return;
   const int64_t ks = item % ksplit, logical = item / ksplit;
-  const int32_t* any = work + 1 + kWorkFields * (logical / p.n_tiles);
-  const int64_t first = any[3], count = any[4];
+  int64_t first = 0, count = ntl;
+  if (work) {
+    const int32_t* any = work + 1 + kWorkFields * (logical / p.n_tiles);
+    first = any[3];
+    count = any[4];
+  }
   const int64_t local = logical - p.n_tiles * first;
   const int64_t sr = local / (kSuperRows * p.n_tiles);
   const int64_t in_sr = count - sr * kSuperRows < kSuperRows ? count - sr * kSuperRows : kSuperRows;
   const int64_t rem = local - sr * kSuperRows * p.n_tiles;
   const int64_t nt = rem / in_sr, ti = first + sr * kSuperRows + rem % in_sr;
-  const int64_t e = work[1 + kWorkFields * ti];
-  const int64_t row0 = work[2 + kWorkFields * ti];
-  const int nrows = work[3 + kWorkFields * ti];
+  int64_t e = 0, row0 = ti * BM;
+  int nrows = (int)(p.P - row0 < BM ? p.P - row0 : BM);
+  if (work) {
+    e = work[1 + kWorkFields * ti];
+    row0 = work[2 + kWorkFields * ti];
+    nrows = work[3 + kWorkFields * ti];
+  }
   const int64_t wrow_bytes = kW4 ? p.K / 2 : p.K;
   const int64_t k0 = ks * KT * kDmaBK;  // first K byte of this slice (8-bit operands)
   const int8_t* wexp = p.w + e * p.N * wrow_bytes + k0;
@@ -1441,19 +1459,6 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float* __restri
 size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 
 // Work list of the dense linear: one "expert", rows in their own order, tiles of bmk rows.
-__global__ void linear_tiles_kernel(int64_t M, int bmk, int32_t* __restrict__ work) {
-  const int64_t tiles = (M + bmk - 1) / bmk;
-  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (i == 0) work[0] = (int32_t)tiles;
-  if (i >= tiles) return;
-  int32_t* t = work + 1 + kWorkFields * i;
-  t[0] = 0;
-  t[1] = (int32_t)(i * bmk);
-  t[2] = (int32_t)(M - i * bmk < bmk ? M - i * bmk : bmk);
-  t[3] = 0;
-  t[4] = (int32_t)tiles;
-}
-
 // ---------------------------------------------------------------------------------------------
 // Engine choice and launches.
 
@@ -1831,10 +1836,11 @@ LinearPlan linear_plan(int64_t M, int64_t N, int64_t K) {
   return plan;
 }
 
+// The int32 partial sums of a split K (at least 256 bytes, so that 0 stays the answer for an
+// unsupported shape); the row tiles need no list (the kernels derive them from M).
 size_t linear_ws_bytes(int64_t M, int64_t N, int64_t K) {
   const LinearPlan plan = linear_plan(M, N, K);
-  const size_t list = round256(sizeof(int32_t) * (size_t)(1 + kWorkFields * ((M + plan.bm - 1) / plan.bm)));
-  return list + (plan.ksplit > 1 ? round256(sizeof(int32_t) * (size_t)(plan.ksplit * M * N)) : 0);
+  return plan.ksplit > 1 ? round256(sizeof(int32_t) * (size_t)(plan.ksplit * M * N)) : 256;
 }
 
 bool linear_supported(int64_t M, int64_t N, int64_t K) {
@@ -1862,13 +1868,10 @@ hipError_t linear(const int8_t* a_q, const float* a_s, const int8_t* w, const fl
   const int64_t bm = plan.bm;
   prm.n_tiles = N / (small ? kLinSmallBN : kDmaBN);
   prm.ksplit = ksplit;
-  char* base = static_cast<char*>(ws);
-  int32_t* work = reinterpret_cast<int32_t*>(base);
+  const int32_t* work = nullptr;  // row tiles of bm rows, derived in the kernels
   const int64_t tiles = (M + bm - 1) / bm;
-  hipLaunchKernelGGL(linear_tiles_kernel, dim3((uint32_t)((tiles + kThreads - 1) / kThreads)), dim3(kThreads), 0,
-                     stream, M, (int)bm, work);
   const int64_t grid = (tiles * prm.n_tiles * ksplit + 7) / 8 * 8;
-  int32_t* part = reinterpret_cast<int32_t*>(base + round256(sizeof(int32_t) * (size_t)(1 + kWorkFields * tiles)));
+  int32_t* part = static_cast<int32_t*>(ws);
   if (plan.engine == LinEngine::Ring) {
     constexpr int WM = 2, WN = 4;
     if (ksplit == 1) {
