@@ -1,7 +1,10 @@
 """The allocation-free align entry point (moe_align_by_expert_noalloc, for callers that cannot
 allocate) against moe_align_by_expert with a caller workspace, through the C ABI: bit-identical
-outputs on two calls in a row, the second with a smaller input, and at a size that uses most of the
-library's 4 MiB scratch.  Both are also compared with the oracle's align."""
+outputs on calls in a row, each smaller than the one before -- the first using most of the library's
+4 MiB scratch, the second a smaller batch that also goes through the scratch (more than the 4096
+pairs the single-workgroup align takes without one) and finds the first call's contents there, then
+a decode batch and a small E on the single-workgroup path.  All are also compared with the oracle's
+align."""
 import numpy as np
 import pytest
 
@@ -59,8 +62,9 @@ def equal(a, b):
 @pytest.mark.parametrize("bm", [16, 128])
 def test_noalloc_align_matches_workspace_align(bm):
     assert w8.moe_align_noalloc_scratch_bytes() == 4 << 20
-    # 100000 tokens x top-8 (800k pairs: 3.9 of the 4 MiB), then a decode batch, then a small E
-    for T, k, E, seed in ((100000, 8, 256, 1), (128, 8, 256, 2), (300, 2, 8, 3)):
+    # 100000 tokens x top-8 (800k pairs: 3.9 of the 4 MiB), then 2000 x top-8 (16k pairs, the scratch
+    # again), then a decode batch and a small E (one workgroup, no scratch)
+    for T, k, E, seed in ((100000, 8, 256, 1), (2000, 8, 256, 4), (128, 8, 256, 2), (300, 2, 8, 3)):
         ids = skewed_ids(T, k, E, seed + bm)
         need = w8.moe_align_workspace_bytes(T, k, E)
         assert need <= w8.moe_align_noalloc_scratch_bytes()
