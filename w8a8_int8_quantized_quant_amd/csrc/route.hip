@@ -61,9 +61,13 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const float* __restrict
                                                          int score_fn, int n_group, int topk_group, int renorm,
                                                          float scaling, const float* __restrict__ bias,
                                                          int32_t* __restrict__ ids, float* __restrict__ weights) {
-  __shared__ float sh_x[kWavesPerBlock][kMaxE];  // logits (softmax) or sigmoid scores
-  __shared__ float sh_c[kWavesPerBlock][kMaxE];  // selection scores (sigmoid + bias)
-  __shared__ int sh_sel[kWavesPerBlock][kMaxE];
+  // Sized for this instantiation's E <= 64 NPL (12 KB a block at E = 256, not 48 KB for the 1024-expert
+  // maximum), so that large batches keep many blocks per CU.
+  constexpr int EP = NPL * kWave;
+  static_assert(EP <= kMaxE, "experts per wavefront");
+  __shared__ float sh_x[kWavesPerBlock][EP];  // logits (softmax) or sigmoid scores
+  __shared__ float sh_c[kWavesPerBlock][EP];  // selection scores (sigmoid + bias)
+  __shared__ int sh_sel[kWavesPerBlock][EP];
   const int w = threadIdx.x / kWave, l = lane_id();
   const int64_t t = (int64_t)blockIdx.x * kWavesPerBlock + w;
   const bool active = t < T;
