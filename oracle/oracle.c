@@ -187,7 +187,9 @@ ORACLE_EXPORT void oracle_align(const int32_t* ids, int64_t T, int64_t k, int64_
                                 int32_t* sorted_pair_ids, int32_t* tile_expert, int32_t* num_tiles) {
   const int64_t P = T * k;
   for (int64_t e = 0; e < E; ++e) counts[e] = 0;
-  for (int64_t p = 0; p < P; ++p) counts[ids[p]] += 1;
+  /* An expert id outside [0, E) names no expert: the pair is dropped (it takes no row). */
+  for (int64_t p = 0; p < P; ++p)
+    if (ids[p] >= 0 && ids[p] < E) counts[ids[p]] += 1;
   offsets[0] = 0;
   padded_offsets[0] = 0;
   for (int64_t e = 0; e < E; ++e) {
@@ -197,7 +199,8 @@ ORACLE_EXPORT void oracle_align(const int32_t* ids, int64_t T, int64_t k, int64_
   }
   int64_t* fill = (int64_t*)malloc(sizeof(int64_t) * (E > 0 ? E : 1));
   for (int64_t e = 0; e < E; ++e) fill[e] = padded_offsets[e];
-  for (int64_t p = 0; p < P; ++p) sorted_pair_ids[fill[ids[p]]++] = (int32_t)p;
+  for (int64_t p = 0; p < P; ++p)
+    if (ids[p] >= 0 && ids[p] < E) sorted_pair_ids[fill[ids[p]]++] = (int32_t)p;
   for (int64_t e = 0; e < E; ++e)
     for (int64_t r = fill[e]; r < padded_offsets[e + 1]; ++r) sorted_pair_ids[r] = (int32_t)P;
   free(fill);

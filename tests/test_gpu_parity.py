@@ -415,6 +415,39 @@ def test_second_gemm_combine_bit_exact(name):
     assert np.isfinite(got).all()
 
 
+@pytest.mark.parametrize("name", ["tiny", "dsv3-e8", "dsv3-e16", "dsv3-e8-block"])
+def test_second_gemm_combine_after_pairs_are_dropped(name):
+    """The pair -> row index the combine reads is written by the second GEMM for this call's pairs
+    only.  Two calls with one workspace: the full routing, then the same routing with every 7th pair's
+    expert id out of range (the align drops those pairs); the second call still matches the oracle,
+    which skips them, bit for bit (staged, DMA, ring and block-wise engines)."""
+    cfg = cfg_of(name)
+    block = cfg.scale_mode == "block"
+    bm = block_m_of(cfg)
+    say(f"[w2-drop] {name} block_m={bm}")
+    L = layer_of(name)
+    ids, tw = route_host(cfg)
+    R = w8.w8a8_moe_max_rows(cfg.T, cfg.k, cfg.E, bm)
+    h_q = synth.int8_matrix(R, cfg.I, cfg.seed + 200)
+    h_s = synth.positive_scales(R * (cfg.I // 128 if block else 1), cfg.seed + 1, 1e-3, 3e-2)
+    h_s = h_s.reshape(R, cfg.I // 128) if block else h_s
+    mode = w8.SCALE_BLOCK128 if block else w8.SCALE_CHANNEL
+    ws = torch.empty(max(w8.w8a8_w2_workspace_bytes(cfg.T, cfg.k, cfg.E, cfg.H, cfg.I, bm, mode), 256),
+                     dtype=torch.uint8, device=DEV)
+    fn = w8.w8a8_block_grouped_gemm_w2_combine if block else w8.w8a8_grouped_gemm_w2_combine
+    w = oracle_weights(name, range(cfg.E))
+    dropped = ids.copy()
+    flat = dropped.reshape(-1)
+    flat[::7] = np.where(np.arange(flat[::7].size) % 2 == 0, -1, cfg.E + 3)
+    for routing in (ids, dropped):
+        al, d = oracle_align_dev(routing, cfg.E, bm)
+        out = torch.full((cfg.T, cfg.H), float("nan"), dtype=torch.float32, device=DEV)
+        fn(dt(h_q), dt(h_s), L.w2, L.w2_scale, d["sorted_pair_ids"], d["padded_offsets"], d["tile_expert"],
+           d["num_tiles"], dt(tw), cfg.T, cfg.k, bm, out, ws)
+        ref = oracle.w2_combine(h_q, h_s, w[2], w[3], al, bm, tw, cfg.T, cfg.k, cfg.H, cfg.I, block)
+        assert np.array_equal(host(out), ref)
+
+
 # Rows per expert for the tile-edge cases: empty, one row, a ragged fragment, exactly one 320-row
 # tile, one row past it, several tiles, and ragged multi-tile counts (with 16 experts, the ring engine's
 # 128-row tiles: 255 / 256 rows, two rows either side of a tile pair).

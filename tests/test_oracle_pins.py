@@ -332,7 +332,8 @@ def test_block_reduces_to_channel():
 def _check_align(ids, E, bm, al):
     P = ids.size
     flat = ids.reshape(-1)
-    counts = np.bincount(flat, minlength=E)
+    valid = (flat >= 0) & (flat < E)
+    counts = np.bincount(flat[valid], minlength=E)
     assert np.array_equal(al["counts"], counts)
     # expert offsets are the zero-padded cumulative sum of the counts
     assert np.array_equal(al["offsets"], np.concatenate([[0], np.cumsum(counts)]))
@@ -342,7 +343,7 @@ def _check_align(ids, E, bm, al):
     assert nt * bm == al["padded_offsets"][-1]
     srt = al["sorted_pair_ids"][: nt * bm]
     real = srt[srt < P]
-    assert np.array_equal(np.sort(real), np.arange(P))
+    assert np.array_equal(np.sort(real), np.flatnonzero(valid))
     assert np.sum(srt == P) == np.sum(pcount - counts)
     for e in range(E):
         seg = srt[al["padded_offsets"][e]: al["padded_offsets"][e + 1]]
@@ -367,6 +368,57 @@ def test_align_invariants(bm):
     for ids, E in cases:
         ids = np.ascontiguousarray(ids, dtype=np.int32)
         _check_align(ids, E, bm, oracle.align(ids, E, bm))
+
+
+@pytest.mark.parametrize("bm", [1, 16, 64])
+def test_align_drops_out_of_range_ids(bm):
+    """An id outside [0, E) names no expert: its pair takes no row, the others group as before."""
+    rng = np.random.default_rng(100 + bm)
+    ids = rng.integers(0, 32, size=(90, 4)).astype(np.int32)
+    flat = ids.reshape(-1)
+    flat[::5] = -1
+    flat[2::9] = 32
+    flat[3::11] = -2 ** 31
+    flat[1::13] = 2 ** 31 - 1
+    al = oracle.align(ids, 32, bm)
+    _check_align(ids, 32, bm, al)
+    assert int(al["counts"].sum()) == int(((flat >= 0) & (flat < 32)).sum())
+
+
+def test_combine_skips_dropped_pairs():
+    """The combine over a routing with dropped pairs equals the combine over the same routing with
+    each dropped pair sent to a real expert at weight 0 (acc + 0 * y == acc for finite y): the
+    second path runs the oracle's align and GEMM on other rows, with no pair dropped."""
+    T, k, E, H, I = 40, 3, 4, 256, 128
+    rng = np.random.default_rng(7)
+    ids = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    tw = rng.uniform(0.1, 1.0, size=(T, k)).astype(np.float32)
+    drop = np.zeros((T, k), bool)
+    drop.reshape(-1)[::4] = True
+    bad = ids.copy()
+    bad[drop] = np.where(np.arange(drop.sum()) % 2 == 0, -1, E)
+    zeroed = tw.copy()
+    zeroed[drop] = 0.0
+    w2 = [synth.int8_matrix(H, I, 30 + e) for e in range(E)]
+    w2_s = [synth.positive_scales(H, 40 + e, 1e-3, 3e-2) for e in range(E)]
+    pair_q = synth.int8_matrix(T * k, I, 50)
+    pair_s = synth.positive_scales(T * k, 51, 1e-3, 3e-2)
+
+    def run(routing, weights, bm):
+        al = oracle.align(routing, E, bm)
+        R = int(al["num_tiles"][0]) * bm
+        srt = al["sorted_pair_ids"][:R]
+        real = srt < T * k
+        h_q = np.zeros((max(R, 1), I), np.int8)
+        h_s = np.ones(max(R, 1), np.float32)
+        h_q[:R][real] = pair_q[srt[real]]
+        h_s[:R][real] = pair_s[srt[real]]
+        return oracle.w2_combine(h_q, h_s, w2, w2_s, al, bm, weights, T, k, H, I, False)
+
+    for bm in (1, 16):
+        got = run(bad, tw, bm)
+        assert np.array_equal(got, run(ids, zeroed, bm))
+        assert not np.array_equal(got, run(ids, tw, bm))
 
 
 # ---------------------------------------------------------------- P9 routing
