@@ -172,11 +172,29 @@ __device__ __forceinline__ void block_flush(AccT (&acc)[FM][FN], float (&accf)[F
     for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = AccT{0, 0, 0, 0};
 }
 
-// Epilogues.  Rows whose sh_pid is the sentinel (>= P) are skipped.
+// The channel-wise epilogues scale each tile row by one activation scale: the token's (first GEMM,
+// rows gathered from tokens) or the sorted row's own (second GEMM); 0 for rows that hold no pair.
+// The kernels gather it into LDS (sh_as) while their first stage loads, so the epilogue reads it
+// there: a global load per row inside the epilogue left the wavefronts waiting on one round trip
+// after another (with the prologue's pair ids also read from LDS, the gate+up stage at 8192 tokens
+// went from 2.39 to 2.24 ms and the down stage from 1.73 to 1.69 ms).
+template <Epi EPI>
+constexpr bool has_row_scale() {
+  return EPI == Epi::W13Channel || EPI == Epi::W2Channel;
+}
+template <Epi EPI>
+__device__ __forceinline__ float row_scale(const Params& p, int32_t pid, int64_t row) {
+  if constexpr (EPI == Epi::W13Channel) return pid < p.P ? p.a_s[pid / p.k] : 0.0f;
+  else if constexpr (EPI == Epi::W2Channel) return pid < p.P ? p.a_s[row] : 0.0f;
+  else return 0.0f;
+}
+
+// Epilogues.  Rows whose sh_pid is the sentinel (>= P) are skipped; sh_as holds the channel-wise
+// row scales (row_scale).
 template <int BM, int BN, int WM, int WN, int FM, int FN, BMap MAP, Epi EPI, bool ILV = false, typename AccT>
 __device__ __forceinline__ void epilogue(const Params& p, const AccT (&acc)[FM][FN], const float (&accf)[FM][FN][4],
-                                         const int32_t* sh_pid, float (*sh_red)[BM], int64_t row0, int64_t nt,
-                                         int64_t e, int wm, int wn, int l, int tid) {
+                                         const int32_t* sh_pid, const float* sh_as, float (*sh_red)[BM], int64_t row0,
+                                         int64_t nt, int64_t e, int wm, int wn, int l, int tid) {
   constexpr int FNH = FN / 2;
   constexpr bool kBlock = is_block<EPI>();
   if constexpr (EPI == Epi::I32) {
@@ -200,7 +218,7 @@ __device__ __forceinline__ void epilogue(const Params& p, const AccT (&acc)[FM][
         const int trow = rblk<WM, FM, ILV>(wm, fm) * 16 + (l / 16) * 4 + r;
         if (sh_pid[trow] >= p.P) continue;
         const int64_t grow = row0 + trow;
-        const float hs = kBlock ? 0.0f : p.a_s[grow];
+        const float hs = kBlock ? 0.0f : sh_as[trow];
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
           const int64_t n = nt * BN + brow_of<BN, WN, FN, MAP>(wn, fn) + (l % 16);
@@ -223,9 +241,8 @@ __device__ __forceinline__ void epilogue(const Params& p, const AccT (&acc)[FM][
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int trow = rblk<WM, FM, ILV>(wm, fm) * 16 + (l / 16) * 4 + r;
-        const int32_t pid = sh_pid[trow];
-        const bool valid = pid < p.P;
-        const float as = valid ? p.a_s[pid / p.k] : 0.0f;
+        const bool valid = sh_pid[trow] < p.P;
+        const float as = sh_as[trow];
         rmax[r] = 0.0f;
 #pragma unroll
         for (int f = 0; f < FNH; ++f) {
@@ -327,6 +344,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const Params p) 
   __shared__ __attribute__((aligned(16))) int8_t lds[2][(BM + BN) * kLdsStride];
   __shared__ int32_t sh_pid[BM];
   __shared__ int32_t sh_arow[kBlock ? BM : 1];  // block-wise: row index into the activation scales
+  __shared__ float sh_as[has_row_scale<EPI>() ? BM : 1];
   __shared__ float sh_red[WN][BM];
 
   const int64_t mt = blockIdx.x / p.n_tiles, nt = blockIdx.x % p.n_tiles;
@@ -343,6 +361,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const Params p) 
     sh_pid[i] = pid;
     if (p.pair_row && nt == 0) note_pair_row(p, pid, row0 + i);
     if constexpr (kBlock) sh_arow[i] = pid < p.P ? (p.gather ? (int32_t)(pid / p.k) : (int32_t)(row0 + i)) : -1;
+    if constexpr (has_row_scale<EPI>()) sh_as[i] = row_scale<EPI>(p, pid, row0 + i);
   }
 
   // Global sources of this thread's 16-byte chunks (row-major chunks of 8 per 128-byte row).
@@ -449,7 +468,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const Params p) 
   }
 #undef W8A8_GLOAD
 #undef W8A8_SSTORE
-  epilogue<BM, BN, WM, WN, FM, FN, MAP, EPI>(p, acc, accf, sh_pid, sh_red, row0, nt, e, wm, wn, l, tid);
+  epilogue<BM, BN, WM, WN, FM, FN, MAP, EPI>(p, acc, accf, sh_pid, sh_as, sh_red, row0, nt, e, wm, wn, l, tid);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -689,8 +708,8 @@ __device__ __forceinline__ void dma_stage_w4(const int8_t* stage, int8_t* next, 
 // them, which a half wavefront reduces while it stores the row.
 template <int BM, int BN, int WM, int WN, int STAGE_BYTES, BMap MAP, Epi EPI, bool ILV = false>
 __device__ __forceinline__ void dma_epilogue(const Params& p, const i32x4 (&acc)[BM / WM / 16][BN / WN / 16],
-                                             const int32_t* sh_pid, int8_t* buf0, int8_t* buf1, int64_t row0,
-                                             int64_t nt, int64_t e, int wm, int wn, int wv, int l,
+                                             const int32_t* sh_pid, const float* sh_as, int8_t* buf0, int8_t* buf1,
+                                             int64_t row0, int64_t nt, int64_t e, int wm, int wn, int wv, int l,
                                              int64_t i32_off) {
   constexpr int FM = BM / WM / 16, FN = BN / WN / 16, FNH = FN / 2;
   constexpr int NW = WM * WN;
@@ -712,10 +731,9 @@ __device__ __forceinline__ void dma_epilogue(const Params& p, const i32x4 (&acc)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int trow = rblk<WM, FM, ILV>(wm, fm) * 16 + (l / 16) * 4 + r;
-        const int32_t pid = sh_pid[trow];
         float* dst = reinterpret_cast<float*>(half + ((fm - f0) * 16 + (l / 16) * 4 + r) * STRIDE);
         if constexpr (kW13) {
-          const float as = pid < p.P ? p.a_s[pid / p.k] : 0.0f;
+          const float as = sh_as[trow];
 #pragma unroll
           for (int f = 0; f < FNH; ++f) {
             const int col = brow_of<BN, WN, FN, MAP>(wn, f) + (l % 16);
@@ -731,7 +749,7 @@ __device__ __forceinline__ void dma_epilogue(const Params& p, const i32x4 (&acc)
             reinterpret_cast<int32_t*>(dst)[col] = acc[fm][fn][r];
           }
         } else {
-          const float hs = pid < p.P ? p.a_s[row0 + trow] : 0.0f;
+          const float hs = sh_as[trow];
 #pragma unroll
           for (int fn = 0; fn < FN; ++fn) {
             const int col = brow_of<BN, WN, FN, MAP>(wn, fn) + (l % 16);
@@ -805,6 +823,7 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_dma_kernel(co
   __shared__ __attribute__((aligned(1024))) int8_t st0[STAGE];
   __shared__ __attribute__((aligned(1024))) int8_t st1[STAGE];
   __shared__ int32_t sh_pid[BM];
+  __shared__ float sh_as[has_row_scale<EPI>() ? BM : 1];
 
   // Work order: expert-major, then (super-row, N-tile, row tile), so the row tiles that share a
   // weight tile run side by side and the weights come from HBM once.  XCD-aware: workgroups are
@@ -843,21 +862,28 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_dma_kernel(co
 
   const int tid = threadIdx.x, l = lane_id();
   const int wv = __builtin_amdgcn_readfirstlane(tid / kWave), wm = wv / WN, wn = wv % WN;
-  for (int i = tid; i < BM; i += NT) {
-    sh_pid[i] = i < nrows ? (p.sorted ? p.sorted[row0 + i] : (int32_t)(row0 + i)) : (int32_t)p.P;
-    if (p.pair_row && nt == 0 && ks == 0 && i < nrows) note_pair_row(p, sh_pid[i], row0 + i);
+  static_assert(BM <= NT, "one tile row per thread");
+  float my_as = 0.0f;  // row tid's scale, into LDS once the first stage has landed
+  if (tid < BM) {
+    const int32_t pid = tid < nrows ? (p.sorted ? p.sorted[row0 + tid] : (int32_t)(row0 + tid)) : (int32_t)p.P;
+    sh_pid[tid] = pid;
+    if (p.pair_row && nt == 0 && ks == 0 && tid < nrows) note_pair_row(p, pid, row0 + tid);
+    if constexpr (has_row_scale<EPI>()) my_as = row_scale<EPI>(p, pid, row0 + tid);
   }
 
   // This thread's DMA chunks: stage chunk q holds row q / CPR, K-chunk (q % CPR) ^ swz(row); lane i
   // of an instruction lands 16 i bytes after the instruction's 1 KB slot.  Sources are 32-bit
   // offsets from the A matrix and from the expert's weights (the host checks they fit).  Rows past
-  // the tile read row 0 (their results are never stored).
+  // the tile read row 0 (their results are never stored).  Gathered rows come from sh_pid: reading
+  // the ids from global memory cost a round trip per chunk before the first DMA could go out.
+  __builtin_amdgcn_s_waitcnt(kLgkm0Imm);
+  barrier_no_fence();  // sh_pid complete (the scale loads stay in flight)
   uint32_t off[LD];
 #pragma unroll
   for (int c = 0; c < A_LD; ++c) {
     const int q = (wv * A_LD + c) * kWave + l, r = q / CPR, kc = (q % CPR) ^ swz(r);
     int64_t row = 0;
-    if (r < nrows) row = p.gather ? (int64_t)(p.sorted[row0 + r] / p.k) : row0 + r;
+    if (r < nrows) row = p.gather ? (int64_t)(sh_pid[r] / p.k) : row0 + r;
     off[c] = (uint32_t)(row * p.K + ks * kslice + kc * 16);
   }
 #pragma unroll
@@ -884,6 +910,7 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_dma_kernel(co
       dma16_nt(wexp + off[c], st0 + b_dst + (c - A_LD) * 1024);
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
+  if (has_row_scale<EPI>() && tid < BM) sh_as[tid] = my_as;  // read after the K loop's barriers
 
   // Step kt: every wavefront is done with step kt - 1 (barrier), so the other buffer is free; the
   // MFMAs read stage kt while the DMA of step kt + 1 goes out between them; then wait until it
@@ -908,7 +935,7 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_dma_kernel(co
     __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
   }
   __syncthreads();
-  dma_epilogue<BM, BN, WM, WN, STAGE, MAP, EPI>(p, acc, sh_pid, st0, st1, row0, nt, e, wm, wn, wv, l,
+  dma_epilogue<BM, BN, WM, WN, STAGE, MAP, EPI>(p, acc, sh_pid, sh_as, st0, st1, row0, nt, e, wm, wn, wv, l,
                                                 ks * p.P * p.N);
 }
 
@@ -970,6 +997,7 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_ring_kernel(c
   __shared__ float sh_ws[kBlkScales ? 2 : 1][kBlkScales ? KT : 1];
   __shared__ __attribute__((aligned(16))) float sh_wst[kW4 ? BN * KT : 1];  // int4: the tile rows' scales
   __shared__ int32_t sh_pid[BM];
+  __shared__ float sh_as[has_row_scale<EPI>() ? BM : 1];
   __shared__ float sh_red[kBlock ? WN : 1][BM];
 
   // Raw int32 sums may split K into p.ksplit slices of KT steps (slice ks writes out_i32 + ks P N);
@@ -1009,9 +1037,13 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_ring_kernel(c
   const int tid = threadIdx.x, l = lane_id();
   const int wv = __builtin_amdgcn_readfirstlane(tid / kWave), wm = wv / WN, wn = wv % WN;
   const int g = l >> 4, fr = l & 15;
-  for (int i = tid; i < BM; i += NT) {
-    sh_pid[i] = i < nrows ? (p.sorted ? p.sorted[row0 + i] : (int32_t)(row0 + i)) : (int32_t)p.P;
-    if (p.pair_row && nt == 0 && ks == 0 && i < nrows) note_pair_row(p, sh_pid[i], row0 + i);
+  static_assert(BM <= NT, "one tile row per thread");
+  float my_as = 0.0f;  // row tid's scale, into LDS once the first stage has landed
+  if (tid < BM) {
+    const int32_t pid = tid < nrows ? (p.sorted ? p.sorted[row0 + tid] : (int32_t)(row0 + tid)) : (int32_t)p.P;
+    sh_pid[tid] = pid;
+    if (p.pair_row && nt == 0 && ks == 0 && tid < nrows) note_pair_row(p, pid, row0 + tid);
+    if constexpr (has_row_scale<EPI>()) my_as = row_scale<EPI>(p, pid, row0 + tid);
   }
   if constexpr (kBlkScales) {
     for (int i = tid; i < 2 * KT; i += NT) {
@@ -1019,11 +1051,14 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_ring_kernel(c
       sh_ws[i / KT][i % KT] = p.w_s[(e * (p.N / 128) + blk) * KT + i % KT];
     }
   }
+  __builtin_amdgcn_s_waitcnt(kLgkm0Imm);
+  barrier_no_fence();  // sh_pid, sh_ws complete (the row-scale loads stay in flight)
   // Source row of a tile row; rows past the real ones read the first row (finite values whose
-  // results are never stored).
+  // results are never stored).  Gathered rows come from sh_pid, not from global memory (a round
+  // trip per DMA chunk before the first stage could go out).
   auto src_row = [&](int r) -> int64_t {
     const int64_t rr = r < nrows ? r : 0;
-    return p.gather ? (int64_t)(p.sorted[row0 + rr] / p.k) : row0 + rr;
+    return p.gather ? (int64_t)(sh_pid[rr] / p.k) : row0 + rr;
   };
 
   uint32_t off[LD];
@@ -1065,7 +1100,6 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_ring_kernel(c
   // VMEM operations that stage st brings: its DMAs, and with every SG-th stage its scale group
   auto stage_ops = [&](int st) { return st < KT ? LD + ((kBlock && st % SG == 0) ? 1 : 0) : 0; };
 #define W8A8_RSAS(q) (((q) & 1) ? sas1 : sas0)
-  __syncthreads();  // sh_pid, sh_ws
   if constexpr (kW4) {
     // int4 weights: the scales of the tile's BN weight rows for every K-block ([BN][KT], one per
     // (row, K-block)) go to LDS by DMA ahead of the first stage, so the prologue wait covers them;
@@ -1093,6 +1127,7 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_ring_kernel(c
     for (int st = 1; st < PRE; ++st) later += stage_ops(st);
     vm_wait(later);
   }
+  if (has_row_scale<EPI>() && tid < BM) sh_as[tid] = my_as;  // read after the K loop's barriers
 
   // Uniform bases of the stage two steps ahead, advanced one step at a time; the empty asm keeps
   // the compiler from precomputing every step's address up front.
@@ -1150,9 +1185,9 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_ring_kernel(c
 #undef W8A8_RSTG
   __syncthreads();
   if constexpr (kBlock)
-    epilogue<BM, BN, WM, WN, FM, FN, MAP, EPI, ILV>(p, acc, accf, sh_pid, sh_red, row0, nt, e, wm, wn, l, tid);
+    epilogue<BM, BN, WM, WN, FM, FN, MAP, EPI, ILV>(p, acc, accf, sh_pid, sh_as, sh_red, row0, nt, e, wm, wn, l, tid);
   else
-    dma_epilogue<BM, BN, WM, WN, STAGE, MAP, EPI, ILV>(p, acc, sh_pid, st0, st1, row0, nt, e, wm, wn, wv, l,
+    dma_epilogue<BM, BN, WM, WN, STAGE, MAP, EPI, ILV>(p, acc, sh_pid, sh_as, st0, st1, row0, nt, e, wm, wn, wv, l,
                                                        ks * p.P * p.N);
 }
 
@@ -1319,7 +1354,8 @@ __global__ __launch_bounds__(kStreamWN * kWave) void grouped_gemm_w4_stream_kern
   (void)FNH;
   i32x4 unused[1][FN] = {};  // the block-wise epilogues read only the fp32 sums
   __syncthreads();  // sh_pid
-  epilogue<BM, BN, 1, WN, 1, FN, MAP, EPI>(p, unused, accf, sh_pid, sh_red, row0, nt, e, 0, wn, l, tid);
+  static_assert(!has_row_scale<EPI>(), "block-wise epilogues take no row scales");
+  epilogue<BM, BN, 1, WN, 1, FN, MAP, EPI>(p, unused, accf, sh_pid, nullptr, sh_red, row0, nt, e, 0, wn, l, tid);
 }
 
 // Work list of the DMA engine: per expert, tiles of up to bmk real rows of its sorted segment.
