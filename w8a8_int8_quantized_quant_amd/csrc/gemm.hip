@@ -701,6 +701,24 @@ __device__ __forceinline__ void dma_stage_w4(const int8_t* stage, int8_t* next, 
   }
 }
 
+// Maximum over each half wavefront (32 lanes), held by the half's upper 16 lanes: within each 16-lane
+// DPP row, partner lanes l^1 and l^2 (quad permutes), then the mirrored lane in the 8-lane half and in
+// the row leave the row's maximum in every lane; row_bcast:15 then brings lane 15 of rows 0 and 2 to
+// rows 1 and 3.  VALU only: the xor shuffles it replaces went through the LDS crossbar, five dependent
+// round trips per row.  The whole wavefront must be active.
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ float dpp_max_step(float v) {
+  return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, ROWS, 0xF,
+                                                             false)));
+}
+__device__ __forceinline__ float half_wave_max(float v) {
+  v = dpp_max_step<0xB1>(v);        // quad_perm [1, 0, 3, 2]
+  v = dpp_max_step<0x4E>(v);        // quad_perm [2, 3, 0, 1]
+  v = dpp_max_step<0x141>(v);       // row_half_mirror
+  v = dpp_max_step<0x140>(v);       // row_mirror
+  return dpp_max_step<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+}
+
 // Channel-wise epilogues of the DMA engine, staged through the (then idle) stage buffers: each
 // pass turns the accumulators of a band of fragment rows into fp32 values in LDS (wavefront-half
 // wm in buffer wm), then whole rows leave as contiguous float4 stores.  Second GEMM: y rows of BN
@@ -771,12 +789,10 @@ __device__ __forceinline__ void dma_epilogue(const Params& p, const i32x4 (&acc)
         const int32_t pid = in ? sh_pid[trow] : (int32_t)p.P;
         float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         if (in) v = *reinterpret_cast<const float4*>((hf == 0 ? buf0 : buf1) + lr * STRIDE + hl * 16);
-        float m = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-#pragma unroll
-        for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));  // within the half wavefront
+        const float m = half_wave_max(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
         if (pid < p.P) {
           reinterpret_cast<float4*>(p.out_f32 + (row0 + trow) * I + nt * (BN / 2))[hl] = v;
-          if (hl == 0) p.part_amax[(row0 + trow) * p.n_tiles + nt] = m;
+          if (hl == 16) p.part_amax[(row0 + trow) * p.n_tiles + nt] = m;  // lanes 16..31 of a half hold its max
         }
       }
     } else {
