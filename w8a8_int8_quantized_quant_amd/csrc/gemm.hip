@@ -172,6 +172,21 @@ __device__ __forceinline__ void block_flush(AccT (&acc)[FM][FN], float (&accf)[F
     for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = AccT{0, 0, 0, 0};
 }
 
+// Maximum over each 16-lane DPP row, left in every lane of the row: partner lanes l^1 and l^2 (quad
+// permutes), then the mirrored lane in the 8-lane half and in the row.  Max is order-free, so this
+// equals any other reduction order.  The whole wavefront must be active.
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ float dpp_max_step(float v) {
+  return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, ROWS, 0xF,
+                                                             false)));
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = dpp_max_step<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  v = dpp_max_step<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  v = dpp_max_step<0x141>(v);  // row_half_mirror
+  return dpp_max_step<0x140>(v);  // row_mirror
+}
+
 // The channel-wise epilogues scale each tile row by one activation scale: the token's (first GEMM,
 // rows gathered from tokens) or the sorted row's own (second GEMM); 0 for rows that hold no pair.
 // The kernels gather it into LDS (sh_as) while their first stage loads, so the epilogue reads it
@@ -259,9 +274,7 @@ __device__ __forceinline__ void epilogue(const Params& p, const AccT (&acc)[FM][
       // reduce over the 16 lanes that share a row
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        float m = rmax[r];
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+        const float m = row16_max(rmax[r]);  // over the 16 lanes that share a row
         if ((l % 16) == 0) sh_red[wn][rblk<WM, FM, ILV>(wm, fm) * 16 + (l / 16) * 4 + r] = m;
       }
     }
@@ -297,9 +310,7 @@ __device__ __forceinline__ void epilogue(const Params& p, const AccT (&acc)[FM][
     for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        float m = rmax[fm][r];
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+        const float m = row16_max(rmax[fm][r]);  // over the 16 lanes that share a row
         if ((l % 16) == 0) sh_red[wn][rblk<WM, FM, ILV>(wm, fm) * 16 + (l / 16) * 4 + r] = m;
       }
     __syncthreads();
@@ -701,22 +712,12 @@ __device__ __forceinline__ void dma_stage_w4(const int8_t* stage, int8_t* next, 
   }
 }
 
-// Maximum over each half wavefront (32 lanes), held by the half's upper 16 lanes: within each 16-lane
-// DPP row, partner lanes l^1 and l^2 (quad permutes), then the mirrored lane in the 8-lane half and in
-// the row leave the row's maximum in every lane; row_bcast:15 then brings lane 15 of rows 0 and 2 to
-// rows 1 and 3.  VALU only: the xor shuffles it replaces went through the LDS crossbar, five dependent
-// round trips per row.  The whole wavefront must be active.
-template <int CTRL, int ROWS = 0xF>
-__device__ __forceinline__ float dpp_max_step(float v) {
-  return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, ROWS, 0xF,
-                                                             false)));
-}
+// Maximum over each half wavefront (32 lanes), held by the half's upper 16 lanes: the 16-lane row
+// maximum, then row_bcast:15 brings lane 15 of rows 0 and 2 to rows 1 and 3.  VALU only: the xor
+// shuffles it replaces went through the LDS crossbar, five dependent round trips per row.  The whole
+// wavefront must be active.
 __device__ __forceinline__ float half_wave_max(float v) {
-  v = dpp_max_step<0xB1>(v);        // quad_perm [1, 0, 3, 2]
-  v = dpp_max_step<0x4E>(v);        // quad_perm [2, 3, 0, 1]
-  v = dpp_max_step<0x141>(v);       // row_half_mirror
-  v = dpp_max_step<0x140>(v);       // row_mirror
-  return dpp_max_step<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  return dpp_max_step<0x142, 0xA>(row16_max(v));  // row_bcast:15 into rows 1 and 3
 }
 
 // Channel-wise epilogues of the DMA engine, staged through the (then idle) stage buffers: each
