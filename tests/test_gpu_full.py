@@ -337,3 +337,50 @@ def test_forward_matches_oracle(full):
     err = np.abs(got[tokens] - ref).max()
     assert err <= 5e-3 * np.abs(ref).max(), (err, np.abs(ref).max())
     assert np.isfinite(got).all()
+
+
+def test_forward_past_4gib_of_pair_outputs():
+    """DeepSeek-V3 shapes at T = 32768, four times the prefill batch, on the engine the library picks
+    for it (the DMA engine): the second GEMM's per-pair fp32 outputs span 7.5 GB, so the rows of the
+    later experts sit past byte offset 2^32, where the GEMM's epilogue writes them and the combine reads
+    them back.  Tokens with a pair past that mark, the last tokens and a seeded spread match the oracle
+    (whole-layer bar); the oracle draws only the experts those tokens use."""
+    import dataclasses
+    cfg = dataclasses.replace(synth.CONFIGS["prefill"], name="prefill-x4", T=4 * synth.CONFIGS["prefill"].T)
+    bm = w8.w8a8_moe_pick_block_m(cfg.T, cfg.k, cfg.E)
+    say(f"[4gib] T={cfg.T}: drawing the device layer, block_m={bm}")
+    L = workload.make_layer(cfg, device=DEV)
+    assert w8.w8a8_moe_engine(cfg.T, cfg.k, cfg.E, cfg.H, cfg.I, bm, L.scale_mode) == w8.ENGINE_DMA
+    ids, tw = oracle.route_cfg(cfg, synth.logits(cfg))
+    al = oracle.align(ids, cfg.E, bm)
+    P = cfg.T * cfg.k
+    R = int(al["num_tiles"][0]) * bm
+    srt = al["sorted_pair_ids"][:R]
+    first_far = (1 << 32) // (cfg.H * 4) + 1  # first sorted row whose fp32 output starts past 2^32 bytes
+    assert R > first_far + 1000
+    far_pairs = srt[first_far:][srt[first_far:] < P]
+    rng = np.random.default_rng(5)
+    tokens = np.unique(np.concatenate([
+        rng.choice(far_pairs // cfg.k, size=6, replace=False),  # a pair past the 4 GiB mark
+        np.array([cfg.T - 1, cfg.T - 2]),                        # the last tokens
+        rng.choice(cfg.T, size=4, replace=False),                # a spread
+    ]).astype(np.int64))
+    assert np.any(np.isin(tokens, far_pairs // cfg.k))
+    out = torch.empty((cfg.T, cfg.H), dtype=torch.float32, device=DEV)
+    gids = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=DEV)
+    gtw = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=DEV)
+    ws = workload.forward_workspace(L)
+    say(f"[4gib] workspace {ws.numel() / 2**30:.1f} GiB; forward")
+    workload.forward(L, out, ws, topk_ids=gids, topk_weights=gtw)
+    got = host(out[torch.from_numpy(tokens).to(DEV)])
+    keep = np.all(host(gids)[tokens] == ids[tokens], axis=1)
+    assert keep.sum() >= len(tokens) - 1
+    tokens, got = tokens[keep], got[keep]
+    experts = np.unique(ids[tokens])
+    say(f"[4gib] oracle over {len(tokens)} tokens, {len(experts)} experts")
+    w = oracle_weights_all(cfg, experts)
+    x = np.concatenate([oracle.activations_f32(cfg, rows=slice(int(t), int(t) + 1)) for t in tokens])
+    ref = oracle.moe_tokens(x, ids[tokens], tw[tokens], *w, I=cfg.I, block=False)
+    err = np.abs(got - ref).max()
+    assert err <= 5e-3 * np.abs(ref).max(), (err, np.abs(ref).max())
+    assert np.isfinite(got).all()
