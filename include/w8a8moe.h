@@ -36,7 +36,7 @@
  *    scale = max(max|x| / 127, 1e-8), q = round-half-even(x / scale), clamped.
  *
  * Shape limits (W8A8_UNSUPPORTED_SHAPE otherwise): 1 <= E <= 1024;
- * 1 <= k <= E; T * k < 2^31; H and I multiples of 128, at most 65536;
+ * 1 <= k <= E; T * k <= 2^30; H and I multiples of 128, at most 65536;
  * block_m one of 16, 32, 64, 128.
  */
 #ifndef W8A8MOE_H
@@ -95,6 +95,9 @@ int32_t w8a8_quant_per_token(const void* x, int32_t x_dtype, int64_t rows, int64
  *   x      device, [rows, cols] fp32 or bf16
  *   q      device, [rows, cols] int8 (output)
  *   scale  device, [ceil(rows/block_rows), ceil(cols/block_cols)] fp32 (output)
+ * Shapes (W8A8_UNSUPPORTED_SHAPE otherwise): rows and the block count below 2^31, rows * cols
+ * below 2^40, at most 2^20 blocks across a row (w8a8_quant_per_token: the same, with blocks of
+ * 1 x group, or 1 x cols for group 0).
  */
 int32_t w8a8_quant_blocks(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t block_rows,
                           int64_t block_cols, int8_t* q, float* scale, hipStream_t stream);
@@ -280,7 +283,8 @@ int32_t w8a8_block_grouped_gemm_w2_combine(const int8_t* h_q, const float* h_sca
  * GEMM requantizes SiLU(gate) * up to FP8 per (row, 128-group).  Workspaces from the size queries
  * with scale_mode = W8A8_SCALE_FP8_BLOCK128.
  * Shapes (W8A8_UNSUPPORTED_SHAPE otherwise): H a multiple of 256; H/128 and I/128 each one of
- * 1, 2, 4, 8, 16, 32, 56; T*H, max_rows*I and 2*I*H below 2^32.  Operand pointers 16-byte aligned. */
+ * 1, 2, 4, 8, 16, 32, 56; T*H, max_rows*I and 2*I*H below 2^32; at most 2^20 work items of 128-row
+ * tiles, (ceil(T*k/128) + min(E, T*k)) * max(I/128, H/256).  Operand pointers 16-byte aligned. */
 int32_t w8a8_fp8_quant_blocks(const void* x, int32_t x_dtype, int64_t rows, int64_t cols, int64_t block_rows,
                               int64_t block_cols, uint8_t* q, float* scale, hipStream_t stream);
 int32_t w8a8_fp8_grouped_gemm_w13_silu(const uint8_t* a_q, const float* a_scale, const uint8_t* w13,
@@ -308,7 +312,8 @@ int32_t w8a8_fp8_grouped_gemm_w2_combine(const uint8_t* h_q, const float* h_scal
  * acc += (part_kb * a_s[t, kb]) * w_s[e, n, kb] in fp32, ascending K-blocks; the rest as in the
  * FP8 variant (same summation-order caveat).
  *
- * w8a8_w4a8_quant_weights: x device [rows, cols] fp32 or bf16, cols a multiple of 128;
+ * w8a8_w4a8_quant_weights: x device [rows, cols] fp32 or bf16, cols a multiple of 128 and at most
+ *   2^27; rows below 2^31, rows * cols below 2^40;
  *   q device [rows, cols/2] packed (output); scale device [rows, cols/128] fp32 (output).
  * GEMMs: w13 device [E, 2I, H/2] packed, w13_scale [E, 2I, H/128]; w2 [E, H, I/2] packed,
  *   w2_scale [E, H, I/128]; a_q / h_q FP8 codes with a_scale [T, H/128] / h_scale [max_rows, I/128];
@@ -340,7 +345,8 @@ int32_t w8a8_w4a8_grouped_gemm_w2_combine(const uint8_t* h_q, const float* h_sca
  *   out      device, [M, N] fp32 (output, fully overwritten)
  *   ws       device workspace of w8a8_linear_workspace_bytes(M, N, K) bytes (at least 256): when few
  *            rows leave CUs idle, the int32 partial sums of K slices (added exactly, in slice order)
- * Shapes: K and N multiples of 256, M*K and N*K below 2^32; M = 0 is a no-op.  a_q and w 16-byte
+ * Shapes: K and N multiples of 256, M*K and N*K below 2^32, at most 2^20 output tiles (of 320 x 256,
+ * or 128-row tiles times K slices for few rows); M = 0 is a no-op.  a_q and w 16-byte
  * aligned.  Returns W8A8_UNSUPPORTED_SHAPE for other shapes, W8A8_WORKSPACE_TOO_SMALL for a short
  * workspace.  Deterministic: every output is one fixed sequence of operations. */
 size_t w8a8_linear_workspace_bytes(int64_t M, int64_t N, int64_t K);  /* 0 for an unsupported shape */

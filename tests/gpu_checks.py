@@ -58,3 +58,27 @@ def check_align_equal(d, al):
     R = int(al["padded_offsets"][-1])
     assert np.array_equal(h(d["sorted_pair_ids"])[:R], al["sorted_pair_ids"][:R])
     assert np.array_equal(h(d["tile_expert"])[:nt], al["tile_expert"][:nt])
+
+
+def oracle_weights(torch, dev, cfg, experts):
+    """The oracle's quantized copy of the listed experts (None for the others): fp32 weights drawn
+    by the shared generator's device fill (bit-identical to its host fill), quantized by the oracle."""
+    import synth
+
+    E = cfg.E
+    w13q, w13s, w2q, w2s = [None] * E, [None] * E, [None] * E, [None] * E
+    n13, n2 = 2 * cfg.I * cfg.H, cfg.H * cfg.I
+    buf = torch.empty(n13, dtype=torch.float32, device=dev)
+    hs = torch.cuda.current_stream().cuda_stream
+
+    def host(t):
+        torch.cuda.synchronize()
+        return t.cpu().numpy()
+
+    for e in experts:
+        synth.dev_normal(buf.data_ptr(), n13, cfg.seed, synth.STREAM_W13, int(e) * n13, cfg.w_sigma, hs)
+        w13q[e], w13s[e] = oracle.quant_weight(host(buf).reshape(2 * cfg.I, cfg.H), cfg.scale_mode)
+        synth.dev_normal(buf.data_ptr(), n2, cfg.seed, synth.STREAM_W2, int(e) * n2, cfg.w_sigma, hs)
+        w2q[e], w2s[e] = oracle.quant_weight(host(buf[:n2]).reshape(cfg.H, cfg.I), cfg.scale_mode)
+    del buf
+    return w13q, w13s, w2q, w2s

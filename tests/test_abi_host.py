@@ -217,6 +217,33 @@ def test_engine_choice():
     assert w8.w8a8_moe_engine(128, k, E, H, I, 16, 7) == -1
 
 
+def test_engine_choice_keeps_grids_launchable():
+    """A dispatch counts its work-items in 32 bits, so a work-list engine takes a shape only while
+    its (row tile, N-tile) items stay within 2^20 workgroups; past that the staged engine, which
+    launches in pieces, runs the layer.  Here H = 65536, I = 256, E = 64, k = 32: 65535 tokens make
+    (ceil(P / 320) + E) * (H / 256) = 6618 * 256 items (over 2^20), half of them 3341 * 256 (under)."""
+    H, I, E, k = 65536, 256, 64, 32
+    assert (-(-32768 * k // 320) + E) * (H // 256) <= 1 << 20 < (-(-65535 * k // 320) + E) * (H // 256)
+    assert w8.w8a8_moe_engine(32768, k, E, H, I, 128, w8.SCALE_CHANNEL) == w8.ENGINE_DMA
+    assert w8.w8a8_moe_engine(65535, k, E, H, I, 128, w8.SCALE_CHANNEL) == w8.ENGINE_STAGED
+    # 2^24 + 4096 tokens of a 256-wide layer (more than 2^32 activation elements): staged
+    assert w8.w8a8_moe_engine((1 << 24) + 4096, 2, 8, 256, 256, 128, w8.SCALE_CHANNEL) == w8.ENGINE_STAGED
+
+
+def test_launch_size_limits():
+    """Shapes whose one grid would pass 2^20 workgroups are rejected before any HIP call: the dense
+    linear's output tiles, and a quantization block row that would not fit one launch."""
+    L = w8.lib()
+    assert w8.w8a8_linear_workspace_bytes(1 << 20, 1 << 16, 256) >= 256  # 3277 * 256 tiles
+    assert w8.w8a8_linear_workspace_bytes(1 << 20, 1 << 19, 256) == 0    # 3277 * 2048 tiles
+    assert L.w8a8_linear(P16, P16, P16, P16, 1 << 20, 1 << 19, 256, P16, P16, 1 << 30, None) == SHAPE
+    # 2^21 + 1 column blocks of 1 x 1 in a row; then 2^20 of them (accepted, but rows = 0 is a no-op)
+    assert L.w8a8_quant_blocks(P16, 0, 2, (1 << 21) + 1, 2, 1, P16, P16, None) == SHAPE
+    assert L.w8a8_quant_per_token(P16, 0, 2, (1 << 21) + 2, 2, P16, P16, None) == SHAPE
+    assert L.w8a8_quant_blocks(P16, 0, 0, 1 << 20, 2, 1, P16, P16, None) == OK
+    assert L.w8a8_w4a8_quant_weights(P16, 0, 2, 128 * ((1 << 20) + 1), P16, P16, None) == SHAPE
+
+
 def test_size_queries():
     assert w8.w8a8_moe_max_rows(128, 8, 256, 16) == (1024 + 256 * 15) // 16 * 16
     assert w8.w8a8_moe_max_rows(1, 8, 256, 128) == (8 + 8 * 127) // 128 * 128

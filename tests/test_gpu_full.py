@@ -63,20 +63,7 @@ def host(t):
 
 
 def oracle_weights_all(cfg, experts):
-    """The oracle's quantized copy of the listed experts: fp32 weights drawn by the shared
-    generator's device fill (bit-identical to its host fill) and quantized by the oracle."""
-    E = cfg.E
-    w13q, w13s, w2q, w2s = [None] * E, [None] * E, [None] * E, [None] * E
-    n13, n2 = 2 * cfg.I * cfg.H, cfg.H * cfg.I
-    buf = torch.empty(n13, dtype=torch.float32, device=DEV)
-    hs = torch.cuda.current_stream().cuda_stream
-    for e in experts:
-        synth.dev_normal(buf.data_ptr(), n13, cfg.seed, synth.STREAM_W13, int(e) * n13, cfg.w_sigma, hs)
-        w13q[e], w13s[e] = oracle.quant_weight(host(buf).reshape(2 * cfg.I, cfg.H), cfg.scale_mode)
-        synth.dev_normal(buf.data_ptr(), n2, cfg.seed, synth.STREAM_W2, int(e) * n2, cfg.w_sigma, hs)
-        w2q[e], w2s[e] = oracle.quant_weight(host(buf[:n2]).reshape(cfg.H, cfg.I), cfg.scale_mode)
-    del buf
-    return w13q, w13s, w2q, w2s
+    return gpu_checks.oracle_weights(torch, DEV, cfg, experts)
 
 
 @dataclass
@@ -384,3 +371,4 @@ def test_forward_past_4gib_of_pair_outputs():
     err = np.abs(got - ref).max()
     assert err <= 5e-3 * np.abs(ref).max(), (err, np.abs(ref).max())
     assert np.isfinite(got).all()
+

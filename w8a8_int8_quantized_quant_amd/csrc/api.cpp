@@ -111,7 +111,8 @@ static int32_t quant_entry(const void* x, int32_t x_dtype, int64_t rows, int64_t
   if (rows == 0 || cols == 0) return W8A8_OK;
   if (!aligned(x, x_dtype == W8A8_DTYPE_F32 ? 4 : 2) || q == nullptr || !ok4(scale)) return W8A8_INVALID_ARGUMENT;
   const int64_t nb = ((rows + block_rows - 1) / block_rows) * ((cols + block_cols - 1) / block_cols);
-  if (rows >= (int64_t(1) << 31) || nb >= (int64_t(1) << 31) || rows * cols >= (int64_t(1) << 40))
+  if (rows >= (int64_t(1) << 31) || nb >= (int64_t(1) << 31) || rows * cols >= (int64_t(1) << 40) ||
+      (cols + block_cols - 1) / block_cols > w8a8::kMaxGridBlocks)  // one block row fits one launch
     return W8A8_UNSUPPORTED_SHAPE;
   return hip_status(w8a8::quant_blocks(x, x_dtype, rows, cols, block_rows, block_cols, q, scale, stream, fp8));
 }
@@ -134,7 +135,8 @@ int32_t w8a8_w4a8_quant_weights(const void* x, int32_t x_dtype, int64_t rows, in
   if (cols % 128 != 0) return W8A8_UNSUPPORTED_SHAPE;
   if (rows == 0 || cols == 0) return W8A8_OK;
   if (!aligned(x, x_dtype == W8A8_DTYPE_F32 ? 4 : 2) || q == nullptr || !ok4(scale)) return W8A8_INVALID_ARGUMENT;
-  if (rows >= (int64_t(1) << 31) || rows * cols >= (int64_t(1) << 40)) return W8A8_UNSUPPORTED_SHAPE;
+  if (rows >= (int64_t(1) << 31) || rows * cols >= (int64_t(1) << 40) || cols / 128 > w8a8::kMaxGridBlocks)
+    return W8A8_UNSUPPORTED_SHAPE;
   return hip_status(w8a8::quant_w4(x, x_dtype, rows, cols, q, scale, stream));
 }
 

@@ -88,6 +88,7 @@ struct Params {
   float* h_s;
   int64_t ksplit;  // DMA engine, Epi::I32: K slices per tile (1 = none); slice s writes out_i32 + s*P*N
   int32_t* pair_row;  // second GEMM: the workgroups of N-tile 0 store pair_row[pair] = sorted row
+  int64_t block0;     // staged engine: the (row tile, N-tile) item of this launch's workgroup 0
 };
 
 // pair_row[pid] = row for a real row of the tile (only the N-tile 0 workgroups call it, so each
@@ -358,7 +359,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const Params p) 
   __shared__ float sh_as[has_row_scale<EPI>() ? BM : 1];
   __shared__ float sh_red[WN][BM];
 
-  const int64_t mt = blockIdx.x / p.n_tiles, nt = blockIdx.x % p.n_tiles;
+  const int64_t v = p.block0 + blockIdx.x;
+  const int64_t mt = v / p.n_tiles, nt = v % p.n_tiles;
   const int64_t row0 = mt * BM;
   if (row0 >= (int64_t)p.num_tiles[0] * p.block_m) return;
   const int64_t e = p.tile_expert[row0 / p.block_m];
@@ -1434,27 +1436,29 @@ __global__ __launch_bounds__(kListThreads) void build_tiles_kernel(const int32_t
 }
 
 // ---------------------------------------------------------------------------------------------
-// Channel-wise requantization of the first GEMM's rows: one wavefront per row.
+// Channel-wise requantization of the first GEMM's rows: one wavefront per row (grid stride).
 __global__ __launch_bounds__(kThreads) void requant_rows_kernel(const float* __restrict__ hf,
                                                                 const float* __restrict__ part_amax,
                                                                 const int32_t* __restrict__ sorted,
                                                                 const int32_t* __restrict__ num_tiles, int64_t block_m,
                                                                 int64_t P, int64_t I, int64_t n_tiles,
                                                                 int8_t* __restrict__ h_q, float* __restrict__ h_s) {
-  const int64_t r = (int64_t)blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave;
-  if (r >= (int64_t)num_tiles[0] * block_m) return;
-  if (sorted[r] >= P) return;
-  const int l = lane_id();
-  float m = 0.0f;
-  for (int64_t i = l; i < n_tiles; i += kWave) m = fmaxf(m, part_amax[r * n_tiles + i]);
-  const float s = quant_scale(wave_max(m));
-  if (l == 0) h_s[r] = s;
-  const float4* src = reinterpret_cast<const float4*>(hf + r * I);
-  uint32_t* dst = reinterpret_cast<uint32_t*>(h_q + r * I);
-  for (int64_t c = l; c < I / 4; c += kWave) {
-    const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src) + c);
-    dst[c] = (uint32_t)(uint8_t)quant_value(v.x, s) | ((uint32_t)(uint8_t)quant_value(v.y, s) << 8) |
-             ((uint32_t)(uint8_t)quant_value(v.z, s) << 16) | ((uint32_t)(uint8_t)quant_value(v.w, s) << 24);
+  const int64_t used = (int64_t)num_tiles[0] * block_m;
+  const int64_t stride = (int64_t)gridDim.x * (kThreads / kWave);
+  for (int64_t r = (int64_t)blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave; r < used; r += stride) {
+    if (sorted[r] >= P) continue;
+    const int l = lane_id();
+    float m = 0.0f;
+    for (int64_t i = l; i < n_tiles; i += kWave) m = fmaxf(m, part_amax[r * n_tiles + i]);
+    const float s = quant_scale(wave_max(m));
+    if (l == 0) h_s[r] = s;
+    const float4* src = reinterpret_cast<const float4*>(hf + r * I);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(h_q + r * I);
+    for (int64_t c = l; c < I / 4; c += kWave) {
+      const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src) + c);
+      dst[c] = (uint32_t)(uint8_t)quant_value(v.x, s) | ((uint32_t)(uint8_t)quant_value(v.y, s) << 8) |
+               ((uint32_t)(uint8_t)quant_value(v.z, s) << 16) | ((uint32_t)(uint8_t)quant_value(v.w, s) << 24);
+    }
   }
 }
 
@@ -1463,49 +1467,51 @@ __global__ __launch_bounds__(kThreads) void requant_rows_kernel(const float* __r
 // kCombineVec float4 columns, all of a slot's loads in flight together.  pair_row is written by
 // the second GEMM for this call's pairs only (a pair the align dropped keeps whatever an earlier
 // call left): a slot counts when its row lies in this call's rows and holds that very pair.
+// Tokens beyond the grid's kMaxGridBlocks rows of workgroups are taken with a grid stride.
 constexpr int kCombineVec = 4;
 __global__ __launch_bounds__(kThreads) void combine_kernel(const float* __restrict__ y,
                                                            const int32_t* __restrict__ pair_row,
                                                            const int32_t* __restrict__ sorted,
                                                            const int32_t* __restrict__ num_tiles, int64_t block_m,
-                                                           const float* __restrict__ topk_w, int64_t k, int64_t H,
-                                                           float* __restrict__ out) {
-  const int64_t t = blockIdx.x;
+                                                           const float* __restrict__ topk_w, int64_t T, int64_t k,
+                                                           int64_t H, float* __restrict__ out) {
   const int64_t H4 = H / 4;
   const int64_t c0 = (int64_t)blockIdx.y * kThreads * kCombineVec + threadIdx.x;
   const int64_t used = (int64_t)num_tiles[0] * block_m;
-  float4 o[kCombineVec];
+  for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
+    float4 o[kCombineVec];
 #pragma unroll
-  for (int i = 0; i < kCombineVec; ++i) o[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  for (int64_t j = 0; j < k; ++j) {
-    const int32_t r = pair_row[t * k + j];
-    if (r < 0 || r >= used || sorted[r] != t * k + j) continue;
-    const float wj = topk_w[t * k + j];
-    const float4* src = reinterpret_cast<const float4*>(y + (int64_t)r * H);
-    float4 v[kCombineVec];
+    for (int i = 0; i < kCombineVec; ++i) o[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int64_t j = 0; j < k; ++j) {
+      const int32_t r = pair_row[t * k + j];
+      if (r < 0 || r >= used || sorted[r] != t * k + j) continue;
+      const float wj = topk_w[t * k + j];
+      const float4* src = reinterpret_cast<const float4*>(y + (int64_t)r * H);
+      float4 v[kCombineVec];
+#pragma unroll
+      for (int i = 0; i < kCombineVec; ++i) {
+        const int64_t c = c0 + i * kThreads;
+        if (c < H4) {
+          const f32x4 q = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src) + c);
+          v[i] = make_float4(q.x, q.y, q.z, q.w);
+        } else {
+          v[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kCombineVec; ++i) {
+        o[i].x = o[i].x + wj * v[i].x;
+        o[i].y = o[i].y + wj * v[i].y;
+        o[i].z = o[i].z + wj * v[i].z;
+        o[i].w = o[i].w + wj * v[i].w;
+      }
+    }
+    float4* dst = reinterpret_cast<float4*>(out + t * H);
 #pragma unroll
     for (int i = 0; i < kCombineVec; ++i) {
       const int64_t c = c0 + i * kThreads;
-      if (c < H4) {
-        const f32x4 q = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src) + c);
-        v[i] = make_float4(q.x, q.y, q.z, q.w);
-      } else {
-        v[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-      }
+      if (c < H4) dst[c] = o[i];
     }
-#pragma unroll
-    for (int i = 0; i < kCombineVec; ++i) {
-      o[i].x = o[i].x + wj * v[i].x;
-      o[i].y = o[i].y + wj * v[i].y;
-      o[i].z = o[i].z + wj * v[i].z;
-      o[i].w = o[i].w + wj * v[i].w;
-    }
-  }
-  float4* dst = reinterpret_cast<float4*>(out + t * H);
-#pragma unroll
-  for (int i = 0; i < kCombineVec; ++i) {
-    const int64_t c = c0 + i * kThreads;
-    if (c < H4) dst[c] = o[i];
   }
 }
 
@@ -1521,13 +1527,25 @@ constexpr int kDmaBM = 320;      // DMA engine: 320 x 256 tiles on 2 x 4 wavefro
 constexpr int kDmaBN = 256;      // 128 gate + 128 up rows, or 256 output columns
 constexpr int kDmaWM = 2, kDmaWN = 4;
 
+int64_t dma_max_tiles(const GroupedShape& s, int64_t bm = kDmaBM) {
+  const int64_t P = s.T * s.k;
+  return (P + bm - 1) / bm + std::min<int64_t>(s.E, P);
+}
+
+// The work-list engines launch all (row tile, N-tile) items of a GEMM in one grid: they take only
+// shapes whose items, for the wider N-tiling of the two GEMMs, stay within kMaxGridBlocks.
+bool list_grid_fits(const GroupedShape& s, int64_t bm, int64_t bn) {
+  return dma_max_tiles(s, bm) * std::max(s.I / (bn / 2), s.H / bn) <= kMaxGridBlocks;
+}
+
 // The DMA engine pays off once experts hold tens of rows (on average 64 or more here); its K steps
 // go in pairs and its down GEMM's N-tiles are 256 wide, so hidden and intermediate sizes must be
 // multiples of 256; other shapes run on the staged engine.
 // Its DMA sources are 32-bit offsets into the activation or intermediate matrix and into one expert.
 bool use_dma(const GroupedShape& s) {
   return s.T * s.k >= 64 * s.E && s.H % 256 == 0 && s.I % 256 == 0 && (uint64_t)s.T * s.H < (1ull << 32) &&
-         (uint64_t)s.max_rows * s.I < (1ull << 32) && (uint64_t)2 * s.I * s.H < (1ull << 32);
+         (uint64_t)s.max_rows * s.I < (1ull << 32) && (uint64_t)2 * s.I * s.H < (1ull << 32) &&
+         list_grid_fits(s, kDmaBM, kDmaBN);
 }
 
 // Ring engine: 128-row tiles, its K loops unrolled for the DeepSeek-V3 layer (hidden 7168,
@@ -1541,12 +1559,8 @@ constexpr int64_t kRingMinAvgRows = 16, kRingMaxAvgRows = 192;
 bool use_ring(const GroupedShape& s, int32_t scale_mode) {
   const int64_t P = s.T * s.k;
   return P >= kRingMinAvgRows * s.E && (scale_mode == 1 || P < kRingMaxAvgRows * s.E) && s.H == kRingH &&
-         s.I == kRingI && (uint64_t)s.T * s.H < (1ull << 32) && (uint64_t)s.max_rows * s.I < (1ull << 32);
-}
-
-int64_t dma_max_tiles(const GroupedShape& s, int64_t bm = kDmaBM) {
-  const int64_t P = s.T * s.k;
-  return (P + bm - 1) / bm + std::min<int64_t>(s.E, P);
+         s.I == kRingI && (uint64_t)s.T * s.H < (1ull << 32) && (uint64_t)s.max_rows * s.I < (1ull << 32) &&
+         list_grid_fits(s, kRingBM, kDmaBN);
 }
 
 // Tile lists of every work-list engine fit (the streaming engine's 16-row tiles are the most).
@@ -1560,13 +1574,17 @@ int64_t w13_n_tiles(const GroupedShape& s, int32_t scale_mode) {
   return use_ring(s, scale_mode) || use_dma(s) ? s.I / (kDmaBN / 2) : s.I / (kBNStaged / 2);
 }
 
+// One workgroup per (row tile, N-tile) item, in launches of at most kMaxGridBlocks items.
 template <int BM, int BN, int WM, int WN, BMap MAP, Epi EPI>
-hipError_t launch_staged(const Params& prm, int64_t max_rows, hipStream_t stream) {
-  const int64_t grid = (max_rows / BM) * prm.n_tiles;
-  if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((grouped_gemm_kernel<BM, BN, WM, WN, MAP, EPI>), dim3((uint32_t)grid), dim3(kThreads), 0,
-                     stream, prm);
-  return hipGetLastError();
+hipError_t launch_staged(Params prm, int64_t max_rows, hipStream_t stream) {
+  const int64_t items = (max_rows / BM) * prm.n_tiles;
+  for (int64_t b0 = 0; b0 < items; b0 += kMaxGridBlocks) {
+    prm.block0 = b0;
+    hipLaunchKernelGGL((grouped_gemm_kernel<BM, BN, WM, WN, MAP, EPI>),
+                       dim3((uint32_t)std::min(items - b0, kMaxGridBlocks)), dim3(kThreads), 0, stream, prm);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 // Staged engine, tile height = block_m (64 for the block-wise first GEMM's 128-row tiles).
@@ -1586,9 +1604,10 @@ hipError_t launch_dma(Params prm, const GroupedShape& s, const int32_t* padded_o
                       hipStream_t stream) {
   prm.n_tiles = MAP == BMap::Plain ? prm.N / kDmaBN : prm.I / (kDmaBN / 2);
   prm.ksplit = 1;
+  const int64_t grid = (dma_max_tiles(s) * prm.n_tiles + 7) / 8 * 8;
+  if (grid > kMaxGridBlocks) return hipErrorInvalidConfiguration;  // shape gates keep it below
   hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(kListThreads), 0, stream, prm.sorted, padded_offsets,
                      (int)s.E, (int32_t)prm.P, kDmaBM, work);
-  const int64_t grid = (dma_max_tiles(s) * prm.n_tiles + 7) / 8 * 8;
   hipLaunchKernelGGL((grouped_gemm_dma_kernel<kDmaBM, kDmaBN, kDmaWM, kDmaWN, MAP, EPI>),
                      dim3((uint32_t)grid), dim3(kDmaWM * kDmaWN * kWave), 0, stream, prm, (const int32_t*)work);
   return hipGetLastError();
@@ -1600,9 +1619,10 @@ hipError_t launch_ring(Params prm, const GroupedShape& s, const int32_t* padded_
   constexpr int NS = 3;
   prm.n_tiles = MAP == BMap::Plain ? prm.N / kDmaBN : prm.I / (kDmaBN / 2);
   prm.ksplit = 1;
+  const int64_t grid = (dma_max_tiles(s, BM) * prm.n_tiles + 7) / 8 * 8;
+  if (grid > kMaxGridBlocks) return hipErrorInvalidConfiguration;  // shape gates keep it below
   hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(kListThreads), 0, stream, prm.sorted, padded_offsets,
                      (int)s.E, (int32_t)prm.P, BM, work);
-  const int64_t grid = (dma_max_tiles(s, BM) * prm.n_tiles + 7) / 8 * 8;
   // 64-row tiles: all 8 wavefronts side by side along N (64 x 32 each), so at a handful of rows
   // per expert every wavefront has rows and the per-step widening and folding is split 8 ways
   constexpr int WM = BM == kRingSmallBM ? 1 : kDmaWM, WN = BM == kRingSmallBM ? 8 : kDmaWN;
@@ -1621,9 +1641,10 @@ hipError_t launch_w4_stream(Params prm, const GroupedShape& s, const int32_t* pa
                             hipStream_t stream) {
   prm.n_tiles = MAP == BMap::Plain ? prm.N / kStreamBN : prm.I / (kStreamBN / 2);
   prm.ksplit = 1;
+  const int64_t grid = (dma_max_tiles(s, kStreamBM) * prm.n_tiles + 7) / 8 * 8;
+  if (grid > kMaxGridBlocks) return hipErrorInvalidConfiguration;  // shape gates keep it below
   hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(kListThreads), 0, stream, prm.sorted, padded_offsets,
                      (int)s.E, (int32_t)prm.P, kStreamBM, work);
-  const int64_t grid = (dma_max_tiles(s, kStreamBM) * prm.n_tiles + 7) / 8 * 8;
   hipLaunchKernelGGL((grouped_gemm_w4_stream_kernel<KT, MAP, EPI>), dim3((uint32_t)grid), dim3(kStreamWN * kWave), 0,
                      stream, prm, (const int32_t*)work);
   return hipGetLastError();
@@ -1669,7 +1690,7 @@ hipError_t launch_ring_kt(const Params& prm, const GroupedShape& s, const int32_
 bool fp8_supported(const GroupedShape& s) {
   return s.H % kDmaBN == 0 && s.I % (kDmaBN / 2) == 0 && fp8_kt_ok(s.H / kDmaBK) && fp8_kt_ok(s.I / kDmaBK) &&
          (uint64_t)s.T * s.H < (1ull << 32) && (uint64_t)s.max_rows * s.I < (1ull << 32) &&
-         (uint64_t)2 * s.I * s.H < (1ull << 32);
+         (uint64_t)2 * s.I * s.H < (1ull << 32) && list_grid_fits(s, kRingBM, kDmaBN);
 }
 
 size_t w13_ws_bytes(const GroupedShape& s, int32_t scale_mode) {
@@ -1775,7 +1796,7 @@ hipError_t w13_silu(const GroupedShape& s, int32_t scale_mode, const int8_t* a_q
                    : use_dma(s) ? launch_dma<BMap::Split, Epi::W13Channel>(prm, s, padded_offsets, work, stream)
                                 : launch_bm<BMap::Split, Epi::W13Channel, kBNStaged>(prm, s.max_rows, stream);
   if (err != hipSuccess) return err;
-  const int64_t blocks = (s.max_rows + kThreads / kWave - 1) / (kThreads / kWave);
+  const int64_t blocks = std::min((s.max_rows + kThreads / kWave - 1) / (kThreads / kWave), kMaxGridBlocks);
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL(requant_rows_kernel, dim3((uint32_t)blocks), dim3(kThreads), 0, stream, hf, part, sorted,
                      num_tiles, s.block_m, s.T * s.k, s.I, n_tiles, h_q, h_s);
@@ -1825,8 +1846,8 @@ hipError_t w2_combine(const GroupedShape& s, int32_t scale_mode, const int8_t* h
     err = launch_bm<BMap::Plain, Epi::W2Channel, kBNStaged>(prm, s.max_rows, stream);
   if (err != hipSuccess) return err;
   const int64_t col_blocks = (s.H / 4 + kThreads * kCombineVec - 1) / (kThreads * kCombineVec);
-  hipLaunchKernelGGL(combine_kernel, dim3((uint32_t)s.T, (uint32_t)col_blocks), dim3(kThreads), 0, stream, y, pair_row,
-                     sorted, num_tiles, s.block_m, topk_w, s.k, s.H, out);
+  hipLaunchKernelGGL(combine_kernel, dim3((uint32_t)std::min(s.T, kMaxGridBlocks), (uint32_t)col_blocks), dim3(kThreads),
+                     0, stream, y, pair_row, sorted, num_tiles, s.block_m, topk_w, s.T, s.k, s.H, out);
   return hipGetLastError();
 }
 
@@ -1838,18 +1859,27 @@ __global__ __launch_bounds__(kThreads) void linear_reduce_kernel(const int32_t* 
                                                                  int64_t M, int64_t N, const float* __restrict__ a_s,
                                                                  const float* __restrict__ w_s,
                                                                  float* __restrict__ out) {
-  const int64_t q = (int64_t)blockIdx.x * kThreads + threadIdx.x;  // 4 outputs per thread
-  if (q >= M * N / 4) return;
-  const int64_t m = (4 * q) / N, n = (4 * q) % N;
-  i32x4 acc = reinterpret_cast<const i32x4*>(part)[q];
-  for (int64_t s = 1; s < ksplit; ++s) acc += reinterpret_cast<const i32x4*>(part + s * M * N)[q];
-  const float as = a_s[m];
-  float4 o;
-  o.x = ((float)acc[0] * as) * w_s[n];
-  o.y = ((float)acc[1] * as) * w_s[n + 1];
-  o.z = ((float)acc[2] * as) * w_s[n + 2];
-  o.w = ((float)acc[3] * as) * w_s[n + 3];
-  reinterpret_cast<float4*>(out)[q] = o;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t q = (int64_t)blockIdx.x * kThreads + threadIdx.x; q < M * N / 4; q += stride) {  // 4 outputs each
+    const int64_t m = (4 * q) / N, n = (4 * q) % N;
+    i32x4 acc = reinterpret_cast<const i32x4*>(part)[q];
+    for (int64_t s = 1; s < ksplit; ++s) acc += reinterpret_cast<const i32x4*>(part + s * M * N)[q];
+    const float as = a_s[m];
+    float4 o;
+    o.x = ((float)acc[0] * as) * w_s[n];
+    o.y = ((float)acc[1] * as) * w_s[n + 1];
+    o.z = ((float)acc[2] * as) * w_s[n + 2];
+    o.w = ((float)acc[3] * as) * w_s[n + 3];
+    reinterpret_cast<float4*>(out)[q] = o;
+  }
+}
+
+static hipError_t linear_reduce(const int32_t* part, int64_t ksplit, int64_t M, int64_t N, const float* a_s,
+                         const float* w_s, float* out, hipStream_t stream) {
+  const int64_t blocks = std::min((M * N / 4 + kThreads - 1) / kThreads, kMaxGridBlocks);
+  hipLaunchKernelGGL(linear_reduce_kernel, dim3((uint32_t)blocks), dim3(kThreads), 0, stream, part, ksplit, M, N, a_s,
+                     w_s, out);
+  return hipGetLastError();
 }
 
 // Plan of a linear of this shape, for the MI355X's 256 CUs (a fixed count, so the workspace size is
@@ -1897,7 +1927,11 @@ size_t linear_ws_bytes(int64_t M, int64_t N, int64_t K) {
 }
 
 bool linear_supported(int64_t M, int64_t N, int64_t K) {
-  return K % 256 == 0 && N % kDmaBN == 0 && (uint64_t)M * K < (1ull << 32) && (uint64_t)N * K < (1ull << 32);
+  if (K % 256 != 0 || N % kDmaBN != 0 || (uint64_t)M * K >= (1ull << 32) || (uint64_t)N * K >= (1ull << 32))
+    return false;
+  const LinearPlan plan = linear_plan(M, N, K);
+  const int64_t bn = plan.engine == LinEngine::DmaSmall ? kLinSmallBN : kDmaBN;
+  return (M + plan.bm - 1) / plan.bm * (N / bn) * plan.ksplit <= kMaxGridBlocks;  // one grid of items
 }
 
 hipError_t linear(const int8_t* a_q, const float* a_s, const int8_t* w, const float* w_s, int64_t M, int64_t N,
@@ -1924,6 +1958,7 @@ hipError_t linear(const int8_t* a_q, const float* a_s, const int8_t* w, const fl
   const int32_t* work = nullptr;  // row tiles of bm rows, derived in the kernels
   const int64_t tiles = (M + bm - 1) / bm;
   const int64_t grid = (tiles * prm.n_tiles * ksplit + 7) / 8 * 8;
+  if (grid > kMaxGridBlocks) return hipErrorInvalidConfiguration;  // linear_supported keeps it below
   int32_t* part = static_cast<int32_t*>(ws);
   if (plan.engine == LinEngine::Ring) {
     constexpr int WM = 2, WN = 4;
@@ -1935,10 +1970,7 @@ hipError_t linear(const int8_t* a_q, const float* a_s, const int8_t* w, const fl
     prm.out_i32 = part;
     hipLaunchKernelGGL((grouped_gemm_ring_kernel<kRingBM, kDmaBN, WM, WN, kLinRingKT, BMap::Plain, Epi::I32>),
                        dim3((uint32_t)grid), dim3(WM * WN * kWave), 0, stream, prm, (const int32_t*)work);
-    const int64_t q = M * N / 4;
-    hipLaunchKernelGGL(linear_reduce_kernel, dim3((uint32_t)((q + kThreads - 1) / kThreads)), dim3(kThreads), 0,
-                       stream, part, ksplit, M, N, a_s, w_s, out);
-    return hipGetLastError();
+    return linear_reduce(part, ksplit, M, N, a_s, w_s, out, stream);
   }
   if (small) {
     constexpr int NT = kLinSmallWM * kLinSmallWN * kWave;
@@ -1952,10 +1984,7 @@ hipError_t linear(const int8_t* a_q, const float* a_s, const int8_t* w, const fl
     hipLaunchKernelGGL((grouped_gemm_dma_kernel<kLinSmallBM, kLinSmallBN, kLinSmallWM, kLinSmallWN, BMap::Plain,
                                                 Epi::I32>),
                        dim3((uint32_t)grid), dim3(NT), 0, stream, prm, (const int32_t*)work);
-    const int64_t q = M * N / 4;
-    hipLaunchKernelGGL(linear_reduce_kernel, dim3((uint32_t)((q + kThreads - 1) / kThreads)), dim3(kThreads), 0,
-                       stream, part, ksplit, M, N, a_s, w_s, out);
-    return hipGetLastError();
+    return linear_reduce(part, ksplit, M, N, a_s, w_s, out, stream);
   }
   if (ksplit == 1) {
     hipLaunchKernelGGL((grouped_gemm_dma_kernel<kDmaBM, kDmaBN, kDmaWM, kDmaWN, BMap::Plain, Epi::W2Channel>),
@@ -1965,10 +1994,7 @@ hipError_t linear(const int8_t* a_q, const float* a_s, const int8_t* w, const fl
   prm.out_i32 = part;
   hipLaunchKernelGGL((grouped_gemm_dma_kernel<kDmaBM, kDmaBN, kDmaWM, kDmaWN, BMap::Plain, Epi::I32>),
                      dim3((uint32_t)grid), dim3(kDmaWM * kDmaWN * kWave), 0, stream, prm, (const int32_t*)work);
-  const int64_t q = M * N / 4;
-  hipLaunchKernelGGL(linear_reduce_kernel, dim3((uint32_t)((q + kThreads - 1) / kThreads)), dim3(kThreads), 0, stream,
-                     part, ksplit, M, N, a_s, w_s, out);
-  return hipGetLastError();
+  return linear_reduce(part, ksplit, M, N, a_s, w_s, out, stream);
 }
 
 }  // namespace w8a8

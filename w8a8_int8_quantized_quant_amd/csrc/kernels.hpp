@@ -7,6 +7,13 @@
 
 namespace w8a8 {
 
+// A dispatch counts the work-items of its x extent in 32 bits, so blocks times threads must stay
+// below 2^32 or the grid silently wraps.  Every launch keeps to kMaxGridBlocks workgroups (2^30
+// work-items at 1024 threads): the per-row and per-token kernels go in pieces or walk their rows
+// with a grid stride, the staged GEMM goes in pieces, and the work-list GEMM engines are chosen
+// only for shapes whose grid fits.
+constexpr int64_t kMaxGridBlocks = int64_t(1) << 20;
+
 // quant.hip
 // fp8: E4M3 codes (as bytes in q) by the FP8 rule instead of the INT8 rule.
 hipError_t quant_blocks(const void* x, int32_t dtype, int64_t rows, int64_t cols, int64_t br, int64_t bc,

@@ -10,6 +10,8 @@
 // scale = max(max|x|/7, 1e-8) per (row, 128 columns), q = clamp(rne(x / scale)).
 // The max is order-independent and the division is IEEE, so results are
 // bit-exact regardless of how lanes split the work.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -155,25 +157,41 @@ __global__ __launch_bounds__(kThreads) void quant_w4_kernel(const T* __restrict_
   q[row * (cols / 2) + gi * 64 + l] = (uint8_t)(w4_nibble(v0, s) | (w4_nibble(v1, s) << 4));
 }
 
+// Rows go in pieces of at most kMaxGridBlocks workgroups; each piece starts on a row (and on a
+// row block), so it is the same quantization of its rows with offset pointers.
 template <typename T, typename C>
 hipError_t launch_quant(const void* xv, int64_t rows, int64_t cols, int64_t br, int64_t bc, int8_t* q,
                         float* scale, hipStream_t stream) {
   const T* x = static_cast<const T*>(xv);
   const bool aligned = (reinterpret_cast<uintptr_t>(x) % 16 == 0) && (reinterpret_cast<uintptr_t>(q) % 8 == 0);
   if (br == 1 && bc == cols && cols % 8 == 0 && aligned) {
-    hipLaunchKernelGGL((quant_rows_vec_kernel<T, C>), dim3((uint32_t)rows), dim3(kThreads), 0, stream, x, cols, q,
-                       scale);
+    for (int64_t r0 = 0; r0 < rows; r0 += kMaxGridBlocks) {
+      const int64_t n = std::min(rows - r0, kMaxGridBlocks);
+      hipLaunchKernelGGL((quant_rows_vec_kernel<T, C>), dim3((uint32_t)n), dim3(kThreads), 0, stream, x + r0 * cols,
+                         cols, q + r0 * cols, scale + r0);
+      if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    }
   } else if (br == 1 && bc <= 512 && cols % bc == 0) {
-    const int64_t waves = rows * (cols / bc);
-    const int64_t blocks = (waves + kThreads / kWave - 1) / (kThreads / kWave);
-    hipLaunchKernelGGL((quant_groups_kernel<T, C>), dim3((uint32_t)blocks), dim3(kThreads), 0, stream, x, rows,
-                       cols, bc, q, scale);
+    const int64_t per_row = cols / bc;  // wavefronts (groups) per row
+    const int64_t step = std::max<int64_t>(1, kMaxGridBlocks * (kThreads / kWave) / per_row);
+    for (int64_t r0 = 0; r0 < rows; r0 += step) {
+      const int64_t n = std::min(rows - r0, step);
+      const int64_t blocks = (n * per_row + kThreads / kWave - 1) / (kThreads / kWave);
+      hipLaunchKernelGGL((quant_groups_kernel<T, C>), dim3((uint32_t)blocks), dim3(kThreads), 0, stream,
+                         x + r0 * cols, n, cols, bc, q + r0 * cols, scale + r0 * per_row);
+      if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    }
   } else {
-    const int64_t nb = ((rows + br - 1) / br) * ((cols + bc - 1) / bc);
-    hipLaunchKernelGGL((quant_blocks_kernel<T, C>), dim3((uint32_t)nb), dim3(kThreads), 0, stream, x, rows, cols,
-                       br, bc, q, scale);
+    const int64_t nbr = (rows + br - 1) / br, nbc = (cols + bc - 1) / bc;
+    const int64_t step = std::max<int64_t>(1, kMaxGridBlocks / nbc);  // row blocks per piece
+    for (int64_t b0 = 0; b0 < nbr; b0 += step) {
+      const int64_t nb = std::min(nbr - b0, step), r0 = b0 * br;
+      hipLaunchKernelGGL((quant_blocks_kernel<T, C>), dim3((uint32_t)(nb * nbc)), dim3(kThreads), 0, stream,
+                         x + r0 * cols, std::min(rows - r0, nb * br), cols, br, bc, q + r0 * cols, scale + b0 * nbc);
+      if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    }
   }
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 }  // namespace
@@ -181,15 +199,22 @@ hipError_t launch_quant(const void* xv, int64_t rows, int64_t cols, int64_t br, 
 hipError_t quant_w4(const void* x, int32_t dtype, int64_t rows, int64_t cols, uint8_t* q, float* scale,
                     hipStream_t stream) {
   if (rows == 0 || cols == 0) return hipSuccess;
-  const int64_t waves = rows * (cols / 128);
-  const int64_t blocks = (waves + kThreads / kWave - 1) / (kThreads / kWave);
-  if (dtype == 1)
-    hipLaunchKernelGGL(quant_w4_kernel<uint16_t>, dim3((uint32_t)blocks), dim3(kThreads), 0, stream,
-                       static_cast<const uint16_t*>(x), rows, cols, q, scale);
-  else
-    hipLaunchKernelGGL(quant_w4_kernel<float>, dim3((uint32_t)blocks), dim3(kThreads), 0, stream,
-                       static_cast<const float*>(x), rows, cols, q, scale);
-  return hipGetLastError();
+  const int64_t per_row = cols / 128;  // wavefronts (groups) per row
+  const int64_t step = std::max<int64_t>(1, kMaxGridBlocks * (kThreads / kWave) / per_row);
+  const size_t esize = dtype == 1 ? 2 : 4;
+  for (int64_t r0 = 0; r0 < rows; r0 += step) {
+    const int64_t n = std::min(rows - r0, step);
+    const int64_t blocks = (n * per_row + kThreads / kWave - 1) / (kThreads / kWave);
+    const void* xr = static_cast<const char*>(x) + (size_t)(r0 * cols) * esize;
+    if (dtype == 1)
+      hipLaunchKernelGGL(quant_w4_kernel<uint16_t>, dim3((uint32_t)blocks), dim3(kThreads), 0, stream,
+                         static_cast<const uint16_t*>(xr), n, cols, q + r0 * (cols / 2), scale + r0 * per_row);
+    else
+      hipLaunchKernelGGL(quant_w4_kernel<float>, dim3((uint32_t)blocks), dim3(kThreads), 0, stream,
+                         static_cast<const float*>(xr), n, cols, q + r0 * (cols / 2), scale + r0 * per_row);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t quant_blocks(const void* x, int32_t dtype, int64_t rows, int64_t cols, int64_t br, int64_t bc,

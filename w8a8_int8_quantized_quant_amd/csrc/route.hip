@@ -6,6 +6,8 @@
 // best scores, keep topk_group groups), top-k, weights normalised and scaled.
 // Order is a strict total order: larger score first, equal scores to the
 // lower index, for groups and for experts.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -207,23 +209,32 @@ hipError_t topk_route(const float* logits, int64_t T, int64_t E, int64_t k, int3
                       int64_t topk_group, int32_t renormalize, float routed_scaling, const float* bias,
                       int32_t* ids, float* weights, hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  const dim3 grid((uint32_t)((T + kWavesPerBlock - 1) / kWavesPerBlock)), block(kThreads);
   const int npl = (int)((E + kWave - 1) / kWave);
+  // Tokens go in pieces of at most kMaxGridBlocks workgroups (each token is routed on its own).
+  const int64_t step = kMaxGridBlocks * kWavesPerBlock;
+  for (int64_t t0 = 0; t0 < T; t0 += step) {
+    const int64_t n = std::min(T - t0, step);
+    const dim3 grid((uint32_t)((n + kWavesPerBlock - 1) / kWavesPerBlock)), block(kThreads);
+    const float* lg = logits + t0 * E;
+    int32_t* id = ids + t0 * k;
+    float* wt = weights + t0 * k;
 #define W8A8_ROUTE(N)                                                                                           \
-  hipLaunchKernelGGL(route_kernel<N>, grid, block, 0, stream, logits, T, (int)E, (int)k, (int)score_fn,        \
-                     (int)n_group, (int)topk_group, (int)renormalize, routed_scaling, bias, ids, weights)
-  if (npl <= 1)
-    W8A8_ROUTE(1);
-  else if (npl <= 2)
-    W8A8_ROUTE(2);
-  else if (npl <= 4)
-    W8A8_ROUTE(4);
-  else if (npl <= 8)
-    W8A8_ROUTE(8);
-  else
-    W8A8_ROUTE(16);
+  hipLaunchKernelGGL(route_kernel<N>, grid, block, 0, stream, lg, n, (int)E, (int)k, (int)score_fn, (int)n_group, \
+                     (int)topk_group, (int)renormalize, routed_scaling, bias, id, wt)
+    if (npl <= 1)
+      W8A8_ROUTE(1);
+    else if (npl <= 2)
+      W8A8_ROUTE(2);
+    else if (npl <= 4)
+      W8A8_ROUTE(4);
+    else if (npl <= 8)
+      W8A8_ROUTE(8);
+    else
+      W8A8_ROUTE(16);
 #undef W8A8_ROUTE
-  return hipGetLastError();
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace w8a8
