@@ -489,6 +489,11 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(const Params p) 
 
 constexpr int kWorkFields = 5;  // ints per work-list tile
 constexpr int64_t kSuperRows = 4;  // row tiles per super-row of the DMA engine's work order
+// The ring engine's super-rows hold up to 16 row tiles: with skewed routing a hot expert has ~13
+// 128-row tiles, and one super-row streams each of its weight tiles once instead of once per 4 row
+// tiles (its activation rows are re-read per N-tile instead).  Experts with one row tile, the
+// common case at mid-size batches, are unaffected.
+constexpr int64_t kRingSuperRows = 16;
 constexpr int kDmaBK = 128;  // K bytes per LDS stage: two MFMA K-steps, whole 128-byte L2 lines
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -1037,10 +1042,11 @@ __global__ __launch_bounds__(WM * WN * kWave, 1) void grouped_gemm_ring_kernel(c
     count = any[4];
   }
   const int64_t local = logical - p.n_tiles * first;
-  const int64_t sr = local / (kSuperRows * p.n_tiles);
-  const int64_t in_sr = count - sr * kSuperRows < kSuperRows ? count - sr * kSuperRows : kSuperRows;
-  const int64_t rem = local - sr * kSuperRows * p.n_tiles;
-  const int64_t nt = rem / in_sr, ti = first + sr * kSuperRows + rem % in_sr;
+  const int64_t sr = local / (kRingSuperRows * p.n_tiles);
+  const int64_t in_sr =
+      count - sr * kRingSuperRows < kRingSuperRows ? count - sr * kRingSuperRows : kRingSuperRows;
+  const int64_t rem = local - sr * kRingSuperRows * p.n_tiles;
+  const int64_t nt = rem / in_sr, ti = first + sr * kRingSuperRows + rem % in_sr;
   int64_t e = 0, row0 = ti * BM;
   int nrows = (int)(p.P - row0 < BM ? p.P - row0 : BM);
   if (work) {
