@@ -731,7 +731,10 @@ __device__ __forceinline__ float half_wave_max(float v) {
 // pass turns the accumulators of a band of fragment rows into fp32 values in LDS (wavefront-half
 // wm in buffer wm), then whole rows leave as contiguous float4 stores.  Second GEMM: y rows of BN
 // columns.  First GEMM: SiLU(gate) * up rows of BN / 2 columns, plus the row maximum of |h| over
-// them, which a half wavefront reduces while it stores the row.
+// them, which a half wavefront reduces while it stores the row.  The fp32 rows are stored with
+// the non-temporal policy: in the layer they are read back once, by the requantization or the
+// combine pass after the whole GEMM (at 8192 tokens 0.5 and 1.9 GB, more than the caches hold);
+// the dense linear's rows are its output.
 template <int BM, int BN, int WM, int WN, int STAGE_BYTES, BMap MAP, Epi EPI, bool ILV = false>
 __device__ __forceinline__ void dma_epilogue(const Params& p, const i32x4 (&acc)[BM / WM / 16][BN / WN / 16],
                                              const int32_t* sh_pid, const float* sh_as, int8_t* buf0, int8_t* buf1,
@@ -799,7 +802,8 @@ __device__ __forceinline__ void dma_epilogue(const Params& p, const i32x4 (&acc)
         if (in) v = *reinterpret_cast<const float4*>((hf == 0 ? buf0 : buf1) + lr * STRIDE + hl * 16);
         const float m = half_wave_max(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
         if (pid < p.P) {
-          reinterpret_cast<float4*>(p.out_f32 + (row0 + trow) * I + nt * (BN / 2))[hl] = v;
+          __builtin_nontemporal_store(f32x4{v.x, v.y, v.z, v.w},
+                                      reinterpret_cast<f32x4*>(p.out_f32 + (row0 + trow) * I + nt * (BN / 2)) + hl);
           if (hl == 16) p.part_amax[(row0 + trow) * p.n_tiles + nt] = m;  // lanes 16..31 of a half hold its max
         }
       }
@@ -816,7 +820,8 @@ __device__ __forceinline__ void dma_epilogue(const Params& p, const i32x4 (&acc)
           if constexpr (EPI == Epi::I32)  // int32 bits; a split tile's 4 columns lie in one half (BN / 2 % 4 == 0)
             *reinterpret_cast<float4*>(p.out_i32 + i32_off + (row0 + trow) * p.N + wrow_of<BN, MAP>(nt, 4 * c, I)) = v;
           else
-            reinterpret_cast<float4*>(p.out_f32 + (row0 + trow) * p.N + nt * BN)[c] = v;
+            __builtin_nontemporal_store(f32x4{v.x, v.y, v.z, v.w},
+                                        reinterpret_cast<f32x4*>(p.out_f32 + (row0 + trow) * p.N + nt * BN) + c);
         }
       }
     }
