@@ -243,7 +243,10 @@ __device__ __forceinline__ void epilogue(const Params& p, const AccT (&acc)[FM][
             y = accf[fm][fn][r];
           else
             y = ((float)acc[fm][fn][r] * hs) * p.w_s[e * p.N + n];
-          p.out_f32[grow * p.N + n] = y;
+          if constexpr (kBlock)  // y of a mid-size batch (470 MB at 2048 tokens): read once, by the combine
+            __builtin_nontemporal_store(y, p.out_f32 + grow * p.N + n);
+          else
+            p.out_f32[grow * p.N + n] = y;
         }
       }
   } else if constexpr (EPI == Epi::W13Channel) {
