@@ -173,21 +173,6 @@ __device__ __forceinline__ void block_flush(AccT (&acc)[FM][FN], float (&accf)[F
     for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = AccT{0, 0, 0, 0};
 }
 
-// Maximum over each 16-lane DPP row, left in every lane of the row: partner lanes l^1 and l^2 (quad
-// permutes), then the mirrored lane in the 8-lane half and in the row.  Max is order-free, so this
-// equals any other reduction order.  The whole wavefront must be active.
-template <int CTRL, int ROWS = 0xF>
-__device__ __forceinline__ float dpp_max_step(float v) {
-  return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, ROWS, 0xF,
-                                                             false)));
-}
-__device__ __forceinline__ float row16_max(float v) {
-  v = dpp_max_step<0xB1>(v);   // quad_perm [1, 0, 3, 2]
-  v = dpp_max_step<0x4E>(v);   // quad_perm [2, 3, 0, 1]
-  v = dpp_max_step<0x141>(v);  // row_half_mirror
-  return dpp_max_step<0x140>(v);  // row_mirror
-}
-
 // The channel-wise epilogues scale each tile row by one activation scale: the token's (first GEMM,
 // rows gathered from tokens) or the sorted row's own (second GEMM); 0 for rows that hold no pair.
 // The kernels gather it into LDS (sh_as) while their first stage loads, so the epilogue reads it

@@ -98,6 +98,75 @@ __global__ __launch_bounds__(kThreads) void quant_rows_vec_kernel(const T* __res
   }
 }
 
+// One workgroup per row of at most kRegChunks * kThreads * 8 columns (8192): every thread loads
+// all of its 16-byte chunks before the row maximum, and quantizes them from registers, so a row
+// costs one round of loads instead of a dependent load per chunk and a second pass.
+constexpr int kRegChunks = 4;
+template <typename T, typename C>
+__global__ __launch_bounds__(kThreads) void quant_rows_reg_kernel(const T* __restrict__ x, int64_t cols,
+                                                                  int8_t* __restrict__ q,
+                                                                  float* __restrict__ scale) {
+  __shared__ float red[kThreads / kWave];
+  const int64_t row = blockIdx.x;
+  const T* xr = x + row * cols;
+  int8_t* qr = q + row * cols;
+  const int nchunk = (int)(cols / 8);
+  float v[kRegChunks][8];
+#pragma unroll
+  for (int i = 0; i < kRegChunks; ++i) {
+    const int c = threadIdx.x + i * kThreads;
+    if (c < nchunk) {
+      load8(xr + (int64_t)c * 8, v[i]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[i][e] = 0.0f;
+    }
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kRegChunks; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[i][e]));
+  const float s = C::scale(block_max(amax, red));
+  if (threadIdx.x == 0) scale[row] = s;
+#pragma unroll
+  for (int i = 0; i < kRegChunks; ++i) {
+    const int c = threadIdx.x + i * kThreads;
+    if (c < nchunk)
+      *reinterpret_cast<uint2*>(qr + (int64_t)c * 8) = make_uint2(C::pack4(v[i], s), C::pack4(v[i] + 4, s));
+  }
+}
+
+// Groups of 128 columns (the per-token groups of the block-wise layouts): a group is one 16-lane
+// DPP row, each lane holding 8 consecutive values from one 16-byte load, so the group maximum is
+// four DPP steps inside the row and the values are quantized from registers (one pass, 8-byte
+// stores).  cols % 128 == 0, 16-byte aligned rows.
+template <typename T, typename C>
+__global__ __launch_bounds__(kThreads) void quant_group128_kernel(const T* __restrict__ x, int64_t rows, int64_t cols,
+                                                                  int8_t* __restrict__ q,
+                                                                  float* __restrict__ scale) {
+  const int64_t ngroups = cols / 128;
+  const int64_t g = ((int64_t)blockIdx.x * kThreads + threadIdx.x) / 16;  // group, row-major
+  const int j = (int)(threadIdx.x % 16);
+  const bool in = g < rows * ngroups;
+  const int64_t base = in ? (g / ngroups) * cols + (g % ngroups) * 128 + j * 8 : 0;
+  float v[8];
+  if (in) {
+    load8(x + base, v);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = 0.0f;
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+  const float s = C::scale(row16_max(amax));  // every lane takes part in the DPP steps
+  if (in) {
+    if (j == 0) scale[g] = s;
+    *reinterpret_cast<uint2*>(q + base) = make_uint2(C::pack4(v, s), C::pack4(v + 4, s));
+  }
+}
+
 // One wave per (row, group) for groups of up to a few hundred columns.
 template <typename T, typename C>
 __global__ __launch_bounds__(kThreads) void quant_groups_kernel(const T* __restrict__ x, int64_t rows,
@@ -165,10 +234,25 @@ hipError_t launch_quant(const void* xv, int64_t rows, int64_t cols, int64_t br, 
   const T* x = static_cast<const T*>(xv);
   const bool aligned = (reinterpret_cast<uintptr_t>(x) % 16 == 0) && (reinterpret_cast<uintptr_t>(q) % 8 == 0);
   if (br == 1 && bc == cols && cols % 8 == 0 && aligned) {
+    const bool reg = cols <= 8 * kThreads * kRegChunks;
     for (int64_t r0 = 0; r0 < rows; r0 += kMaxGridBlocks) {
       const int64_t n = std::min(rows - r0, kMaxGridBlocks);
-      hipLaunchKernelGGL((quant_rows_vec_kernel<T, C>), dim3((uint32_t)n), dim3(kThreads), 0, stream, x + r0 * cols,
-                         cols, q + r0 * cols, scale + r0);
+      if (reg)
+        hipLaunchKernelGGL((quant_rows_reg_kernel<T, C>), dim3((uint32_t)n), dim3(kThreads), 0, stream, x + r0 * cols,
+                           cols, q + r0 * cols, scale + r0);
+      else
+        hipLaunchKernelGGL((quant_rows_vec_kernel<T, C>), dim3((uint32_t)n), dim3(kThreads), 0, stream, x + r0 * cols,
+                           cols, q + r0 * cols, scale + r0);
+      if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    }
+  } else if (br == 1 && bc == 128 && cols % 128 == 0 && aligned) {
+    const int64_t ngroups = cols / 128;
+    const int64_t step = kMaxGridBlocks * (kThreads / 16) / ngroups;  // rows per launch (ngroups <= 2^20)
+    for (int64_t r0 = 0; r0 < rows; r0 += step) {
+      const int64_t n = std::min(rows - r0, step);
+      const int64_t blocks = (n * ngroups * 16 + kThreads - 1) / kThreads;
+      hipLaunchKernelGGL((quant_group128_kernel<T, C>), dim3((uint32_t)blocks), dim3(kThreads), 0, stream,
+                         x + r0 * cols, n, cols, q + r0 * cols, scale + r0 * ngroups);
       if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
     }
   } else if (br == 1 && bc <= 512 && cols % bc == 0) {
