@@ -1435,7 +1435,9 @@ __global__ __launch_bounds__(kListThreads) void build_tiles_kernel(const int32_t
 }
 
 // ---------------------------------------------------------------------------------------------
-// Channel-wise requantization of the first GEMM's rows: one wavefront per row (grid stride).
+// Channel-wise requantization of the first GEMM's rows: one wavefront per row (grid stride), each
+// lane with eight float4 loads of its row in flight before it quantizes them (one load round trip
+// per 2048 columns instead of one per 256).
 __global__ __launch_bounds__(kThreads) void requant_rows_kernel(const float* __restrict__ hf,
                                                                 const float* __restrict__ part_amax,
                                                                 const int32_t* __restrict__ sorted,
@@ -1451,12 +1453,24 @@ __global__ __launch_bounds__(kThreads) void requant_rows_kernel(const float* __r
     for (int64_t i = l; i < n_tiles; i += kWave) m = fmaxf(m, part_amax[r * n_tiles + i]);
     const float s = quant_scale(wave_max(m));
     if (l == 0) h_s[r] = s;
-    const float4* src = reinterpret_cast<const float4*>(hf + r * I);
+    const f32x4* src = reinterpret_cast<const f32x4*>(hf + r * I);
     uint32_t* dst = reinterpret_cast<uint32_t*>(h_q + r * I);
-    for (int64_t c = l; c < I / 4; c += kWave) {
-      const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src) + c);
-      dst[c] = (uint32_t)(uint8_t)quant_value(v.x, s) | ((uint32_t)(uint8_t)quant_value(v.y, s) << 8) |
-               ((uint32_t)(uint8_t)quant_value(v.z, s) << 16) | ((uint32_t)(uint8_t)quant_value(v.w, s) << 24);
+    constexpr int U = 8;  // float4 loads in flight per lane
+    for (int64_t c0 = l; c0 < I / 4; c0 += kWave * U) {
+      f32x4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t c = c0 + (int64_t)u * kWave;
+        v[u] = c < I / 4 ? __builtin_nontemporal_load(src + c) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t c = c0 + (int64_t)u * kWave;
+        if (c < I / 4)
+          dst[c] = (uint32_t)(uint8_t)quant_value(v[u].x, s) | ((uint32_t)(uint8_t)quant_value(v[u].y, s) << 8) |
+                   ((uint32_t)(uint8_t)quant_value(v[u].z, s) << 16) |
+                   ((uint32_t)(uint8_t)quant_value(v[u].w, s) << 24);
+      }
     }
   }
 }
