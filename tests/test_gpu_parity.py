@@ -196,6 +196,42 @@ def test_activation_quant_ragged_and_degenerate(rows, cols, group, dtype):
     assert np.all(host(q)[0] == 0)
 
 
+@pytest.mark.parametrize("rows,cols,group,dtype,misalign", [
+    (3, 8192, 0, "bf16", 0),     # per-row kernel from registers, at its 8192-column limit
+    (3, 8200, 0, "f32", 0),      # one chunk past it: the two-pass per-row kernel
+    (1, 8, 0, "f32", 0),         # one chunk per row
+    (5, 128, 128, "f32", 0),     # one 128-wide group per row (one 16-lane DPP row)
+    (7, 384, 128, "bf16", 0),    # 3 groups per row, 21 groups: a wavefront with a partial DPP row set
+    (2, 65536, 128, "bf16", 0),  # 512 groups per row
+    (4, 1024, 0, "bf16", 1),     # input 2 bytes off 16-byte alignment: the groups / blocks kernels
+    (4, 1024, 128, "f32", 1),    # input 4 bytes off: the wavefront-per-group kernel
+])
+def test_activation_quant_kernel_paths(rows, cols, group, dtype, misalign):
+    """Each activation-quantization kernel and the choice between them: the per-row kernel that
+    holds a row in registers (rows of at most 8192 columns) and the two-pass one past that, the
+    128-wide group kernel (16 lanes per group), and the fallbacks taken for inputs that are not
+    16-byte aligned.  Bit for bit against the oracle, with an all-zero row and exact halves."""
+    z = synth.normal(rows * cols, 9, synth.STREAM_MISC, 0).reshape(rows, cols)
+    z[0, :] = 0.0
+    if rows > 1:
+        z[1, ::5] = 0.5
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    zt = torch.from_numpy(z).to(tdt)
+    zf = zt.to(torch.float32).numpy()
+    # a flat buffer with the matrix `misalign` elements in, so its address is off 16-byte alignment
+    flat = torch.zeros(rows * cols + 16, dtype=tdt, device=DEV)
+    flat[misalign:misalign + rows * cols] = zt.reshape(-1).to(DEV)
+    x = flat[misalign:misalign + rows * cols].view(rows, cols)
+    assert (x.data_ptr() % 16 == 0) == (misalign == 0)
+    q = torch.empty((rows, cols), dtype=torch.int8, device=DEV)
+    s = torch.full((rows, cols // group) if group else (rows,), -1.0, dtype=torch.float32, device=DEV)
+    w8.w8a8_quant_per_token(x, group, q, s)
+    rq, rs = oracle.quant_per_token(zf, group)
+    assert np.array_equal(host(q), rq)
+    assert np.array_equal(host(s), rs)
+    assert np.all(host(q)[0] == 0)
+
+
 @pytest.mark.parametrize("shape,block", [((300, 384), (128, 128)), ((256, 7168), (1, 7168)), ((129, 257), (128, 128)),
                                          ((64, 130), (1, 130))])
 def test_weight_quant_blocks_bit_exact(shape, block):
